@@ -1,0 +1,358 @@
+/*
+ * CPU oracle for the compressed-sparse-attention (CSA) indexer: score + top-k.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  The GPU product
+ * path never calls, links or falls back to it.  It shares no code, header,
+ * table or helper with the HIP implementation.
+ *
+ * It is the plain definition written out, slowly and in double precision:
+ * no blocking, no fusion, no reordering of the sums, no SIMD intrinsics and
+ * no fast-math.  OpenMP is used only to run independent query rows at once.
+ *
+ * Sources (page titles as published; section names are the pages' own):
+ *  [FM]   "FlashMemory-DeepSeek-V4" README,
+ *         section "Retriever architecture" (the score formula, the fused head
+ *         weight and the compressed_k dequant) and section "compressed_k
+ *         format" (132-byte rows: 128 fp8 bytes, then an fp32 scale),
+ *         section "Two-level recall algorithm" (Level 2 keeps the top-512,
+ *         with non-resident logits set to -inf).
+ *  [BG]   "feat: DeepSeek-V4-Flash integration + Blackwell (sm120) bring-up"
+ *         (batchgen pull request 153): the c4 fix (the scorer's bound is the
+ *         compressed length seq_len // 4) and the Phase 3 summary (relu is
+ *         applied to each head's score before the gate-weighted sum), and the
+ *         indexer pool row layout [128 B fp8 | 4 B fp32 scale].
+ *  [AT]   "DeepSeek-V4.1 native paged runtime" (ATOM docs), section "Current
+ *         execution scope": one scorer for every shape; each query row has
+ *         its own bound and its own tile list into the paged index plane; a
+ *         padding row carries the id -1 and reads nothing.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *  - fp8 flavour: OCP E4M3 ("e4m3fn"): bias 7, no infinities, S.1111.111 is
+ *    NaN, largest finite 448.
+ *  - the scale is a little-endian IEEE binary32 at bytes HEAD_DIM..HEAD_DIM+3.
+ *  - the product (fp8 value) x (scale) is taken exactly (the pages' fp32
+ *    product differs by at most one fp32 rounding).
+ *  - relu(x) = x if x > 0 else 0.
+ *  - top-k keeps the k largest logits; equal logits go to the lower column;
+ *    -inf (masked) and NaN entries are never selected; rows with fewer than k
+ *    selectable entries are padded with column -1.
+ *
+ * Build: plain C99, `gcc -O2 -fopenmp -shared -fPIC` (no -ffast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* [FM] "compressed_k format": the first HEAD_DIM bytes of a key row are
+ * float8_e4m3 values.  OCP E4M3: sign bit, 4 exponent bits (bias 7), 3
+ * mantissa bits; exponent 0 is subnormal (M * 2^-9); exponent 15 with
+ * mantissa 7 is NaN; there is no infinity. */
+double oracle_e4m3_value(uint8_t u)
+{
+    int sign = u >> 7;
+    int e = (u >> 3) & 15;
+    int m = u & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* bfloat16 is the top half of an IEEE binary32; widening is exact. */
+static double bf16_value(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* [FM] "compressed_k format": bytes[HEAD_DIM:] viewed as float32
+ * (little-endian, assembled byte by byte so the host's order never matters). */
+static double le_f32_value(const uint8_t *p)
+{
+    uint32_t bits = (uint32_t)p[0] | ((uint32_t)p[1] << 8) |
+                    ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+double oracle_scale_value(const uint8_t *row, int32_t head_dim)
+{
+    return le_f32_value(row + head_dim);
+}
+
+/* [AT] "Current execution scope": each query row has its own bound and its
+ * own tile list.  Resolves column `col` of query row `b` to a physical pool
+ * row, or returns -1 when the column scores nothing.
+ *
+ * Columns: without a chunk list, column c is logical entry c.  With a chunk
+ * list, column c = block_size * j + s names entry s of the row's j-th listed
+ * logical block ([FM] "Two-level recall algorithm": only the resident chunks
+ * are scored).  *entry_out receives the logical entry id.
+ *
+ * An entry is scored iff it lies below the row's bound ([BG] c4 fix: the
+ * bound is the compressed length), its logical block is present in the
+ * request's block table (id >= 0 and inside the pool), and the query row is
+ * not padding (request id -1, [AT] "Current execution scope"). */
+int64_t oracle_resolve(int32_t b, int32_t col, int64_t n_pool_rows,
+                       int32_t block_size, const int32_t *block_table,
+                       int32_t n_req, int32_t max_blocks, const int32_t *q_req,
+                       const int32_t *chunk_ids, const int32_t *n_chunks,
+                       int32_t max_chunks, const int32_t *limits,
+                       int64_t *entry_out)
+{
+    int32_t req = q_req ? q_req[b] : b;
+    int32_t j = col / block_size;
+    int32_t s = col % block_size;
+    int64_t beta, entry, prow;
+    *entry_out = -1;
+    if (req < 0)
+        return -1;
+    if (chunk_ids) {
+        int32_t nc = n_chunks[b];
+        if (nc > max_chunks)
+            nc = max_chunks;
+        if (j >= nc)
+            return -1;
+        beta = chunk_ids[(int64_t)b * max_chunks + j];
+        if (beta < 0)
+            return -1;
+    } else {
+        beta = j;
+    }
+    entry = beta * block_size + s;
+    *entry_out = entry;
+    if (entry >= limits[b])
+        return -1;
+    if (block_table) {
+        int64_t pblk;
+        if (req >= n_req || beta >= max_blocks)
+            return -1;
+        pblk = block_table[(int64_t)req * max_blocks + beta];
+        if (pblk < 0 || (pblk + 1) * block_size > n_pool_rows)
+            return -1;
+        prow = pblk * block_size + s;
+    } else {
+        prow = entry;
+        if (prow >= n_pool_rows)
+            return -1;
+    }
+    return prow;
+}
+
+/* One logit, straight from the definition in [FM] "Retriever architecture":
+ *   k_d     = e4m3(byte_d) * scale                       (dequant)
+ *   dot_h   = sum_d k_d * q[h,d]                          (k @ q^T)
+ *   logit   = sum_h relu(dot_h) * w[h]                    (relu per head
+ *             before the weighted sum, [BG] Phase 3)
+ * q_row holds the query row already widened to double (exact for bf16).
+ * Sums run in index order in double. */
+static double logit_of_row(const double *q_row, const float *w_row, int32_t H,
+                           int32_t D, const uint8_t *key_row, double *k)
+{
+    double scale = le_f32_value(key_row + D);
+    double logit = 0.0;
+    int32_t h, d;
+    for (d = 0; d < D; ++d)
+        k[d] = oracle_e4m3_value(key_row[d]) * scale;
+    for (h = 0; h < H; ++h) {
+        double dot = 0.0;
+        for (d = 0; d < D; ++d)
+            dot += k[d] * q_row[(int64_t)h * D + d];
+        logit += (dot > 0.0 ? dot : 0.0) * (double)w_row[h];
+    }
+    return logit;
+}
+
+/* The same logit for a bf16 query row given as raw bits [H, D]. */
+double oracle_logit(const uint16_t *q_row, const float *w_row, int32_t H,
+                    int32_t D, const uint8_t *key_row)
+{
+    double *qd = (double *)malloc(sizeof(double) * (size_t)H * (size_t)D);
+    double *k = (double *)malloc(sizeof(double) * (size_t)D);
+    double v = NAN;
+    int64_t i;
+    if (qd && k) {
+        for (i = 0; i < (int64_t)H * D; ++i)
+            qd[i] = bf16_value(q_row[i]);
+        v = logit_of_row(qd, w_row, H, D, key_row, k);
+    }
+    free(qd);
+    free(k);
+    return v;
+}
+
+/* Logits of every (row, column); unscored columns hold -inf ([FM] "Two-level
+ * recall algorithm": masked logits are -inf).  Returns 0, or -1 on bad sizes
+ * or allocation failure. */
+int oracle_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
+                 int32_t D, const uint8_t *pool, int64_t n_pool_rows,
+                 int32_t block_size, const int32_t *block_table, int32_t n_req,
+                 int32_t max_blocks, const int32_t *q_req,
+                 const int32_t *chunk_ids, const int32_t *n_chunks,
+                 int32_t max_chunks, const int32_t *limits, int32_t n_cols,
+                 double *logits, int32_t n_threads)
+{
+    int64_t row_bytes = (int64_t)D + 4;
+    int32_t b;
+    int failed = 0;
+    if (B < 0 || H <= 0 || D <= 0 || block_size <= 0 || n_cols < 0)
+        return -1;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (b = 0; b < B; ++b) {
+        double *qd = (double *)malloc(sizeof(double) * (size_t)H * (size_t)D);
+        double *k = (double *)malloc(sizeof(double) * (size_t)D);
+        int64_t i;
+        int32_t c;
+        if (!qd || !k) {
+            free(qd);
+            free(k);
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+            continue;
+        }
+        for (i = 0; i < (int64_t)H * D; ++i)
+            qd[i] = bf16_value(q[(int64_t)b * H * D + i]);
+        for (c = 0; c < n_cols; ++c) {
+            int64_t entry;
+            int64_t prow = oracle_resolve(b, c, n_pool_rows, block_size,
+                                          block_table, n_req, max_blocks, q_req,
+                                          chunk_ids, n_chunks, max_chunks,
+                                          limits, &entry);
+            double v = -INFINITY;
+            if (prow >= 0)
+                v = logit_of_row(qd, w + (int64_t)b * H, H, D,
+                                 pool + prow * row_bytes, k);
+            logits[(int64_t)b * n_cols + c] = v;
+        }
+        free(qd);
+        free(k);
+    }
+    return failed ? -1 : 0;
+}
+
+/* [FM] "Retriever architecture": score = sigmoid(logit), the logistic
+ * function; a masked logit (-inf) gives score 0. */
+double oracle_sigmoid(double x)
+{
+    return 1.0 / (1.0 + exp(-x));
+}
+
+typedef struct {
+    double v;
+    int32_t c;
+} vc_pair;
+
+/* Larger value first; equal values: lower column first. */
+static int cmp_desc(const void *pa, const void *pb)
+{
+    const vc_pair *a = (const vc_pair *)pa, *b = (const vc_pair *)pb;
+    if (a->v > b->v)
+        return -1;
+    if (a->v < b->v)
+        return 1;
+    return (a->c > b->c) - (a->c < b->c);
+}
+
+/* [FM] "Two-level recall algorithm": keep the top-k (k = 512 there) of a
+ * row's logits.  Brute force: sort every selectable entry and take the head
+ * of the list.  out_col/out_val are [B, k]; missing places get column -1 and
+ * value -inf.  Returns 0, or -1 on bad sizes / allocation failure. */
+int oracle_topk(const double *vals, int32_t B, int32_t n_cols, int64_t ld,
+                int32_t k, int32_t *out_col, double *out_val, int32_t n_threads)
+{
+    int32_t b;
+    int failed = 0;
+    if (B < 0 || n_cols < 0 || k <= 0 || ld < n_cols)
+        return -1;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (b = 0; b < B; ++b) {
+        vc_pair *buf = (vc_pair *)malloc(sizeof(vc_pair) * (size_t)(n_cols + 1));
+        int32_t n = 0, c, i;
+        if (!buf) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            failed = 1;
+            continue;
+        }
+        for (c = 0; c < n_cols; ++c) {
+            double v = vals[(int64_t)b * ld + c];
+            if (isnan(v) || v == -INFINITY)
+                continue;
+            buf[n].v = v;
+            buf[n].c = c;
+            ++n;
+        }
+        qsort(buf, (size_t)n, sizeof(vc_pair), cmp_desc);
+        for (i = 0; i < k; ++i) {
+            int64_t o = (int64_t)b * k + i;
+            if (i < n) {
+                out_col[o] = buf[i].c;
+                if (out_val)
+                    out_val[o] = buf[i].v;
+            } else {
+                out_col[o] = -1;
+                if (out_val)
+                    out_val[o] = -INFINITY;
+            }
+        }
+        free(buf);
+    }
+    return failed ? -1 : 0;
+}
+
+/* Column -> logical entry id (the id the attention step consumes); -1 stays
+ * -1.  With a chunk list, column 64*j+s is entry chunk_ids[b][j]*64+s. */
+int oracle_cols_to_entries(const int32_t *cols, int32_t B, int32_t k,
+                           int32_t block_size, const int32_t *chunk_ids,
+                           int32_t max_chunks, int32_t *entries)
+{
+    int32_t b, i;
+    for (b = 0; b < B; ++b) {
+        for (i = 0; i < k; ++i) {
+            int32_t c = cols[(int64_t)b * k + i];
+            int32_t e = -1;
+            if (c >= 0) {
+                if (chunk_ids) {
+                    int32_t j = c / block_size, s = c % block_size;
+                    e = chunk_ids[(int64_t)b * max_chunks + j] * block_size + s;
+                } else {
+                    e = c;
+                }
+            }
+            entries[(int64_t)b * k + i] = e;
+        }
+    }
+    return 0;
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,191 @@
+"""ctypes wrapper of the CPU oracle (idx_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the GPU product path.
+
+Functions take plain numpy arrays (or any object with the attributes of a
+workload: q, w, pool, block_size, block_table, q_req, chunk_ids, n_chunks,
+limits, n_cols) and return numpy arrays in double precision.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "idx_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_c_u8p = ctypes.POINTER(ctypes.c_uint8)
+_c_u16p = ctypes.POINTER(ctypes.c_uint16)
+_c_f32p = ctypes.POINTER(ctypes.c_float)
+_c_f64p = ctypes.POINTER(ctypes.c_double)
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C99, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fopenmp",
+               "-shared", "-fPIC", _SRC, "-o", _LIB + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    lib.oracle_e4m3_value.restype = ctypes.c_double
+    lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.oracle_scale_value.restype = ctypes.c_double
+    lib.oracle_scale_value.argtypes = [_c_u8p, ctypes.c_int32]
+    lib.oracle_logit.restype = ctypes.c_double
+    lib.oracle_logit.argtypes = [_c_u16p, _c_f32p, ctypes.c_int32, ctypes.c_int32, _c_u8p]
+    lib.oracle_sigmoid.restype = ctypes.c_double
+    lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+    lib.oracle_score.restype = ctypes.c_int
+    lib.oracle_score.argtypes = [
+        _c_u16p, _c_f32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        _c_u8p, ctypes.c_int64, ctypes.c_int32,
+        _c_i32p, ctypes.c_int32, ctypes.c_int32, _c_i32p,
+        _c_i32p, _c_i32p, ctypes.c_int32, _c_i32p, ctypes.c_int32,
+        _c_f64p, ctypes.c_int32]
+    lib.oracle_topk.restype = ctypes.c_int
+    lib.oracle_topk.argtypes = [_c_f64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                ctypes.c_int32, _c_i32p, _c_f64p, ctypes.c_int32]
+    lib.oracle_cols_to_entries.restype = ctypes.c_int
+    lib.oracle_cols_to_entries.argtypes = [_c_i32p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, _c_i32p, ctypes.c_int32, _c_i32p]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def e4m3_value(u: int) -> float:
+    """Value of one float8_e4m3fn byte (closed form)."""
+    return float(_load().oracle_e4m3_value(ctypes.c_uint8(int(u) & 0xFF)))
+
+
+def scale_value(row: np.ndarray, head_dim: int) -> float:
+    row = np.ascontiguousarray(row, dtype=np.uint8)
+    return float(_load().oracle_scale_value(_ptr(row, ctypes.c_uint8), head_dim))
+
+
+def logit(q_row: np.ndarray, w_row: np.ndarray, key_row: np.ndarray) -> float:
+    """One logit: q_row uint16 [H, D] (bf16 bits), w_row float32 [H], key_row uint8 [D+4]."""
+    q_row = np.ascontiguousarray(q_row, dtype=np.uint16)
+    w_row = np.ascontiguousarray(w_row, dtype=np.float32)
+    key_row = np.ascontiguousarray(key_row, dtype=np.uint8)
+    H, D = q_row.shape
+    assert key_row.shape == (D + 4,) and w_row.shape == (H,)
+    return float(_load().oracle_logit(_ptr(q_row, ctypes.c_uint16), _ptr(w_row, ctypes.c_float),
+                                      H, D, _ptr(key_row, ctypes.c_uint8)))
+
+
+def sigmoid(x) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(x, dtype=np.float64)
+    return np.vectorize(lambda v: lib.oracle_sigmoid(float(v)), otypes=[np.float64])(x)
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
+
+
+def score(wl, rows=None, n_threads: int = 0) -> np.ndarray:
+    """Double logits [B, n_cols] (or [len(rows), n_cols] for a row subset);
+    unscored columns are -inf."""
+    q = np.ascontiguousarray(wl.q, dtype=np.uint16)
+    w = np.ascontiguousarray(wl.w, dtype=np.float32)
+    limits = _i32(wl.limits)
+    q_req = _i32(wl.q_req)
+    chunk_ids = _i32(wl.chunk_ids)
+    n_chunks = _i32(wl.n_chunks)
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        q = np.ascontiguousarray(q[rows])
+        w = np.ascontiguousarray(w[rows])
+        limits = np.ascontiguousarray(limits[rows])
+        if q_req is None:
+            q_req = rows.astype(np.int32)      # keep each row's own request
+        else:
+            q_req = np.ascontiguousarray(q_req[rows])
+        if chunk_ids is not None:
+            chunk_ids = np.ascontiguousarray(chunk_ids[rows])
+            n_chunks = np.ascontiguousarray(n_chunks[rows])
+    B, H, D = q.shape
+    table = _i32(wl.block_table)
+    n_req = 0 if table is None else table.shape[0]
+    max_blocks = 0 if table is None else table.shape[1]
+    max_chunks = 0 if chunk_ids is None else chunk_ids.shape[1]
+    pool = np.ascontiguousarray(wl.pool, dtype=np.uint8)
+    assert pool.shape[1] == D + 4
+    out = np.empty((B, wl.n_cols), dtype=np.float64)
+    rc = _load().oracle_score(
+        _ptr(q, ctypes.c_uint16), _ptr(w, ctypes.c_float), B, H, D,
+        _ptr(pool, ctypes.c_uint8), pool.shape[0], wl.block_size,
+        _ptr(table, ctypes.c_int32), n_req, max_blocks, _ptr(q_req, ctypes.c_int32),
+        _ptr(chunk_ids, ctypes.c_int32), _ptr(n_chunks, ctypes.c_int32), max_chunks,
+        _ptr(limits, ctypes.c_int32), wl.n_cols, _ptr(out, ctypes.c_double), n_threads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_score failed ({rc})")
+    return out
+
+
+def topk(vals: np.ndarray, k: int, n_threads: int = 0):
+    """Top-k columns per row of vals [B, n] (desc value, ties -> lower column;
+    -inf and NaN never selected; -1 padding).  Returns (cols int32, vals f64)."""
+    vals = np.ascontiguousarray(vals, dtype=np.float64)
+    B, n = vals.shape
+    cols = np.empty((B, k), dtype=np.int32)
+    out_v = np.empty((B, k), dtype=np.float64)
+    rc = _load().oracle_topk(_ptr(vals, ctypes.c_double), B, n, n, k,
+                             _ptr(cols, ctypes.c_int32), _ptr(out_v, ctypes.c_double),
+                             n_threads)
+    if rc != 0:
+        raise RuntimeError(f"oracle_topk failed ({rc})")
+    return cols, out_v
+
+
+def cols_to_entries(wl, cols: np.ndarray, rows=None) -> np.ndarray:
+    """Map selected columns to logical entry ids (chunk lists resolved)."""
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    B, k = cols.shape
+    chunk_ids = _i32(wl.chunk_ids)
+    if chunk_ids is not None and rows is not None:
+        chunk_ids = np.ascontiguousarray(chunk_ids[np.asarray(rows)])
+    max_chunks = 0 if chunk_ids is None else chunk_ids.shape[1]
+    out = np.empty_like(cols)
+    _load().oracle_cols_to_entries(_ptr(cols, ctypes.c_int32), B, k, wl.block_size,
+                                   _ptr(chunk_ids, ctypes.c_int32), max_chunks,
+                                   _ptr(out, ctypes.c_int32))
+    return out
+
+
+def score_topk(wl, rows=None, n_threads: int = 0):
+    """Oracle of the whole path: (entry ids [B,k], their logits [B,k], logits [B,n_cols])."""
+    lg = score(wl, rows=rows, n_threads=n_threads)
+    cols, vals = topk(lg, wl.k, n_threads=n_threads)
+    return cols_to_entries(wl, cols, rows=rows), vals, lg

@@ -1,0 +1,88 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a copy of the oracle's C source,
+builds the copy in a temporary directory, points the oracle wrapper at it and
+runs the pins: at least one pin must fail.  The real oracle is never edited.
+"""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+from oracle import oracle
+import tests.test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "idx_oracle.c")
+
+MUTANTS = {
+    "relu-dropped": ("logit += (dot > 0.0 ? dot : 0.0) * (double)w_row[h];",
+                     "logit += dot * (double)w_row[h];"),
+    "q-transposed": ("dot += k[d] * q_row[(int64_t)h * D + d];",
+                     "dot += k[d] * q_row[(int64_t)d * H + h];"),
+    "fp8-bias-8": ("mag = ldexp(1.0 + (double)m / 8.0, e - 7);",
+                   "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
+    "fp8-no-subnormal": ("mag = ldexp((double)m, -9);", "mag = 0.0;"),
+    "scale-magnitude-only": ("k[d] = oracle_e4m3_value(key_row[d]) * scale;",
+                             "k[d] = oracle_e4m3_value(key_row[d]) * fabs(scale);"),
+    "scale-big-endian": ("uint32_t bits = (uint32_t)p[0] | ((uint32_t)p[1] << 8) |",
+                         "uint32_t bits = (uint32_t)p[3] | ((uint32_t)p[2] << 8) |"),
+    "limit-off-by-one": ("if (entry >= limits[b])", "if (entry > limits[b])"),
+    "ties-to-higher-column": ("return (a->c > b->c) - (a->c < b->c);",
+                              "return (a->c < b->c) - (a->c > b->c);"),
+    "nan-selectable": ("if (isnan(v) || v == -INFINITY)", "if (v == -INFINITY)"),
+    "weights-dropped": ("logit += (dot > 0.0 ? dot : 0.0) * (double)w_row[h];",
+                        "logit += (dot > 0.0 ? dot : 0.0);"),
+}
+
+PIN_TESTS = [
+    lambda: pins.test_e4m3_all_bytes_match_torch_e4m3fn(),
+    lambda: [pins.test_e4m3_closed_form_points(u, v) for u, v in
+             [(0x38, 1.0), (0x01, 2.0 ** -9), (0x7E, 448.0)]],
+    lambda: pins.test_scale_is_little_endian_fp32_after_head_dim((0, 0, 0, 0x3F), 0.5),
+    pins.test_one_hot_closed_form,
+    pins.test_relu_applies_per_head_before_weighting,
+    pins.test_negative_scale_is_applied_before_relu,
+    lambda: pins.test_integer_case_matches_numpy_matmul(0),
+    pins.test_limits_mask_exactly_and_poison_never_leaks,
+    lambda: pins.test_topk_matches_brute_force_with_ties(0),
+]
+
+
+def _build_mutant(old, new, tmp):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    path = os.path.join(tmp, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    so = os.path.join(tmp, "libmutant.so")
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC", path,
+                    "-o", so, "-lm"], check=True)
+    return so
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_every_planted_mistake_fails_a_pin(name, monkeypatch):
+    old, new = MUTANTS[name]
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_mutant(old, new, tmp)
+        real = oracle._load()
+        monkeypatch.setattr(oracle, "_LIB", so)
+        monkeypatch.setattr(oracle, "_lib", None)
+        try:
+            oracle._load()
+            caught = []
+            for t in PIN_TESTS:
+                try:
+                    t()
+                except AssertionError:
+                    caught.append(t)
+            assert caught, f"mutant {name} passed every pin"
+        finally:
+            monkeypatch.setattr(oracle, "_lib", real)
+
+
+def test_unmutated_oracle_passes_the_same_pins():
+    for t in PIN_TESTS:
+        t()

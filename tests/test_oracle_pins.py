@@ -1,0 +1,351 @@
+"""Pins of the CPU oracle to facts outside itself (no GPU needed).
+
+Each test fixes part of the oracle against a closed form, a library routine on
+a case that reduces to it, an invariant the definition implies, or brute force
+on tiny inputs.  Together they make a plausible slip anywhere in the oracle
+(wrong fp8 bias, byte order of the scale, transposed q, relu after the head
+sum, a scale factored out of relu, an off-by-one bound, a wrong tie rule)
+fail at least one test.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from sparse_attention_kv_paged_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _key_row(values_f8_bytes, scale):
+    row = np.zeros(len(values_f8_bytes) + 4, dtype=np.uint8)
+    row[:-4] = values_f8_bytes
+    row[-4:] = np.array([scale], dtype="<f4").view(np.uint8)
+    return row
+
+
+def _bf16(x):
+    return W.bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- fp8 decode
+
+def test_e4m3_all_bytes_match_torch_e4m3fn():
+    """Closed-form decoder == torch's float8_e4m3fn view for all 256 bytes."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    mine = np.array([oracle.e4m3_value(u) for u in range(256)])
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+@pytest.mark.parametrize("u,val", [
+    (0x00, 0.0), (0x38, 1.0), (0xB8, -1.0), (0x40, 2.0), (0x3C, 1.5),
+    (0x7E, 448.0), (0xFE, -448.0), (0x08, 2.0 ** -6), (0x01, 2.0 ** -9),
+    (0x07, 7 * 2.0 ** -9), (0x30, 0.5),
+])
+def test_e4m3_closed_form_points(u, val):
+    # OCP E4M3: bias 7, subnormal step 2^-9, max 448 (a bias-8 "fnuz" decode
+    # would give 0x38 -> 0.5 and fail here).
+    assert oracle.e4m3_value(u) == val
+
+
+def test_e4m3_specials():
+    assert math.isnan(oracle.e4m3_value(0x7F)) and math.isnan(oracle.e4m3_value(0xFF))
+    z = oracle.e4m3_value(0x80)
+    assert z == 0.0 and math.copysign(1.0, z) < 0
+
+
+# ---------------------------------------------------------------- layout
+
+def test_page_constants():
+    c = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    r = c["index_row"]
+    assert r["head_dim"] + r["scale_bytes"] == r["row_bytes"] == W.ROW_BYTES
+    assert W.HEAD_DIM == r["head_dim"] and W.BLOCK == c["block_entries"]["value"]
+    assert W.COMPRESS == c["compression"]["tokens_per_record"]
+    n = c["native_c4_record"]
+    assert n["nope_bytes"] + n["rope_bytes"] + n["scale_bytes"] == n["total_bytes"] == 584
+    p = c["packed_c4_record"]
+    assert round(100 * (1 - p["bytes"] / n["total_bytes"]), 2) == p["reduction_percent"]
+    # one 1M-token request: 262,144 rows x 132 B = 34,603,008 B (~34.6 MB)
+    assert (1 << 20) // W.COMPRESS * r["row_bytes"] == 34_603_008
+    assert W.BLOCK * r["row_bytes"] == 8448
+    # KMAX pages x 64 entries ~ 10% of the compressed history
+    for ctx, kmax in (("256K", 256 << 10), ("512K", 512 << 10), ("1M", 1 << 20)):
+        frac = c["kmax_pages"][ctx] * W.BLOCK / (kmax // W.COMPRESS)
+        assert abs(frac - 0.09375) < 1e-12
+    assert W.TOPK == c["topk"]["value"]
+
+
+@pytest.mark.parametrize("scale_bytes,val", [
+    ((0x00, 0x00, 0x00, 0x3F), 0.5),
+    ((0x00, 0x00, 0x80, 0x3F), 1.0),
+    ((0x00, 0x00, 0x20, 0xC1), -10.0),
+])
+def test_scale_is_little_endian_fp32_after_head_dim(scale_bytes, val):
+    row = np.zeros(132, dtype=np.uint8)
+    row[:128] = 0x38
+    row[128:] = scale_bytes
+    assert oracle.scale_value(row, 128) == val
+
+
+# ---------------------------------------------------------------- the score
+
+def test_one_hot_closed_form():
+    """Key = one-hot e_j (fp8 1.0) with scale 1/4; q has distinct values in
+    every (h, d) so a transposed q or a wrong column reads other numbers.
+    dot_h = q[h, j] / 4 = [0.5, -0.25, 0.125, 0.75]
+    logit = 1*0.5 + 4*relu(-0.25) + 2*0.125 + (-0.5)*0.75 = 0.375."""
+    H, D, j = 4, 8, 5
+    q = np.arange(H * D, dtype=np.float32).reshape(H, D) + 100.0
+    q[:, j] = [2.0, -1.0, 0.5, 3.0]
+    f8 = np.zeros(D, dtype=np.uint8)
+    f8[j] = 0x38
+    w = np.array([1.0, 4.0, 2.0, -0.5], dtype=np.float32)
+    assert oracle.logit(_bf16(q), w, _key_row(f8, 0.25)) == 0.375
+
+
+def test_relu_applies_per_head_before_weighting():
+    """Two heads with dots +3 and -5, w = (1, 1): relu per head gives 3 (no
+    relu: -2; relu after the head sum: 0)."""
+    D = 4
+    f8 = np.array([0x38, 0, 0, 0], dtype=np.uint8)        # key e_0
+    q = np.zeros((2, D), dtype=np.float32)
+    q[:, 0] = [3.0, -5.0]
+    w = np.ones(2, dtype=np.float32)
+    assert oracle.logit(_bf16(q), w, _key_row(f8, 1.0)) == 3.0
+
+
+def test_negative_scale_is_applied_before_relu():
+    """relu(s * x) with s = -0.5: heads with x = 2 and x = -2 give dots -1 and
+    +1; only the second survives relu, so logit = w_1 = 3."""
+    D = 4
+    f8 = np.array([0x38, 0, 0, 0], dtype=np.uint8)
+    q = np.zeros((2, D), dtype=np.float32)
+    q[:, 0] = [2.0, -2.0]
+    w = np.array([5.0, 3.0], dtype=np.float32)
+    assert oracle.logit(_bf16(q), w, _key_row(f8, -0.5)) == 3.0
+
+
+def _int_case(seed, H, D, n):
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(-4, 5, size=(n, D))                  # exact in e4m3
+    qv = rng.integers(-2, 3, size=(H, D))                  # exact in bf16
+    wexp = rng.integers(-3, 4, size=H)
+    wsgn = rng.choice([-1.0, 1.0], size=H)
+    w = (wsgn * np.ldexp(1.0, wexp)).astype(np.float32)
+    rows = np.stack([_key_row(W.e4m3_bytes(kv[i].astype(np.float32)), 1.0) for i in range(n)])
+    return kv, qv, w, rows
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_integer_case_matches_numpy_matmul(seed):
+    """Small-integer keys and queries, scale 1, power-of-two weights: every
+    partial sum is exact, so the oracle must equal numpy's integer matmul
+    bit for bit."""
+    H, D, n = 8, 16, 32
+    kv, qv, w, rows = _int_case(seed, H, D, n)
+    S = kv.astype(np.int64) @ qv.T.astype(np.int64)        # [n, H]
+    expect = np.maximum(S, 0).astype(np.float64) @ w.astype(np.float64)
+    q16 = _bf16(qv.astype(np.float32))
+    got = np.array([oracle.logit(q16, w, rows[i]) for i in range(n)])
+    assert np.array_equal(got, expect)
+
+
+def test_single_head_reduces_to_relu_of_matvec():
+    """H = 1, w = 1: logit = relu(k . q) (numpy dot in double)."""
+    rng = np.random.default_rng(7)
+    D, n = 128, 64
+    x = rng.standard_normal((n, D)).astype(np.float32)
+    s = rng.uniform(0.005, 0.05, n).astype(np.float32)
+    rows = W.make_key_rows(x, s)
+    q = rng.standard_normal((1, D)).astype(np.float32)
+    q16 = _bf16(q)
+    qd = torch.from_numpy(q16.view(np.int16)).view(torch.bfloat16).double().numpy()
+    kd = torch.from_numpy(rows[:, :D].copy()).view(torch.float8_e4m3fn).double().numpy()
+    kd = kd * s.astype(np.float64)[:, None]
+    expect = np.maximum(kd @ qd[0], 0.0)
+    got = np.array([oracle.logit(q16, np.ones(1, np.float32), rows[i]) for i in range(n)])
+    np.testing.assert_allclose(got, expect, rtol=1e-13, atol=1e-15)
+
+
+def test_homogeneity_in_scale_and_weights():
+    """Doubling every scale doubles every logit exactly; multiplying w by 2^-3
+    multiplies logits by 2^-3 exactly (both are exact binary scalings)."""
+    wl = W.small_config(1)
+    base = oracle.score(wl)
+    wl2 = W.small_config(1)
+    sc = wl2.pool[:, 128:].copy().view("<f4")
+    fin = np.isfinite(sc)
+    sc[fin] *= 2
+    wl2.pool[:, 128:] = sc.view(np.uint8)
+    wl2.w = (wl2.w * np.float32(0.125)).astype(np.float32)
+    got = oracle.score(wl2)
+    fm = np.isfinite(base)
+    assert np.array_equal(np.isfinite(got), fm)
+    assert np.array_equal(got[fm], base[fm] * 0.25)
+
+
+# ---------------------------------------------------------------- paging
+
+def test_paging_is_a_relabelling():
+    """The same keys, contiguous vs behind a shuffled block table: identical
+    logits.  And a second permutation of the physical blocks changes nothing."""
+    rng = np.random.default_rng(11)
+    n_entries, B = 64 * 7 + 19, 3
+    wl = W.contiguous(n_entries, B=B, seed=5)
+    ref = oracle.score(wl)
+    nblk = -(-n_entries // 64)
+    for trial in range(2):
+        perm = rng.permutation(nblk + 2)
+        pool = np.full(((nblk + 2) * 64, 132), 0x7F, dtype=np.uint8)
+        padded = np.zeros((nblk * 64, 132), dtype=np.uint8)
+        padded[:n_entries] = wl.pool
+        for beta in range(nblk):
+            pool[perm[beta] * 64:(perm[beta] + 1) * 64] = padded[beta * 64:(beta + 1) * 64]
+        table = np.tile(perm[:nblk].astype(np.int32), (B, 1))
+        pw = W.Workload(name="p", q=wl.q, w=wl.w, pool=pool, limits=wl.limits,
+                        n_cols=n_entries, block_table=table)
+        got = oracle.score(pw)
+        assert np.array_equal(got, ref)
+
+
+def test_resident_subset_equals_masked_full_row():
+    """Scoring a chunk list == scoring the full row with non-resident blocks
+    absent (-inf), read at the listed chunks ("Two-level recall algorithm")."""
+    wl = W.small_config(4)
+    sub = oracle.score(wl)
+    full = W.Workload(name="f", q=wl.q, w=wl.w, pool=wl.pool, limits=wl.limits,
+                      n_cols=wl.block_table.shape[1] * 64, block_table=wl.block_table)
+    fl = oracle.score(full)
+    for b in range(wl.B):
+        for j, beta in enumerate(wl.chunk_ids[b]):
+            assert np.array_equal(sub[b, j * 64:(j + 1) * 64], fl[b, beta * 64:(beta + 1) * 64])
+        keep = np.zeros(fl.shape[1], dtype=bool)
+        for beta in wl.chunk_ids[b]:
+            keep[beta * 64:(beta + 1) * 64] = True
+        assert np.all(fl[b, ~keep] == -np.inf)
+
+
+def test_limits_mask_exactly_and_poison_never_leaks():
+    wl = W.small_config(1)
+    lg = oracle.score(wl)
+    for b in range(wl.B):
+        L = int(wl.limits[b])
+        assert np.all(np.isfinite(lg[b, :L]))          # tail rows are NaN poison
+        assert np.all(lg[b, L:] == -np.inf)
+    # bound L-1 drops exactly one more column
+    wl.limits = (wl.limits - 1).astype(np.int32)
+    lg2 = oracle.score(wl)
+    for b in range(wl.B):
+        L = int(wl.limits[b])
+        assert lg2[b, L] == -np.inf and np.array_equal(lg2[b, :L], lg[b, :L])
+
+
+def test_padding_row_and_absent_blocks():
+    wl = W.small_config(1)
+    wl.q_req = np.arange(wl.B, dtype=np.int32)
+    wl.q_req[2] = -1                                  # padding row
+    wl.block_table = wl.block_table.copy()
+    wl.block_table[0, 1] = -1                         # hole in row 0
+    lg = oracle.score(wl)
+    assert np.all(lg[2] == -np.inf)
+    assert np.all(lg[0, 64:128] == -np.inf) and np.all(np.isfinite(lg[0, :64]))
+
+
+def test_generator_layout_agrees_with_oracle():
+    """The generator's layout-only mask == the oracle's finite columns."""
+    for i in range(5):
+        wl = W.small_config(i)
+        assert np.array_equal(wl.valid_mask(), np.isfinite(oracle.score(wl)))
+
+
+# ---------------------------------------------------------------- top-k
+
+def _brute_topk(vals, k):
+    """numpy lexsort on (column, -value): a different sort from the oracle's."""
+    B, n = vals.shape
+    out = np.full((B, k), -1, dtype=np.int32)
+    for b in range(B):
+        v = vals[b]
+        ok = np.nonzero(~np.isnan(v) & (v != -np.inf))[0]
+        order = ok[np.lexsort((ok, -v[ok]))]
+        m = min(k, len(order))
+        out[b, :m] = order[:m]
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    B, n, k = 4, 1500, 97
+    vals = rng.integers(-20, 20, size=(B, n)).astype(np.float64)   # many exact ties
+    vals[rng.random((B, n)) < 0.1] = -np.inf
+    vals[rng.random((B, n)) < 0.02] = np.nan
+    vals[0, 5] = -0.0
+    vals[0, 6] = 0.0
+    cols, v = oracle.topk(vals, k)
+    assert np.array_equal(cols, _brute_topk(vals, k))
+    sel = cols >= 0
+    assert np.array_equal(v[sel], np.take_along_axis(vals, np.maximum(cols, 0), 1)[sel])
+
+
+def test_topk_pads_with_minus_one():
+    vals = np.full((2, 10), -np.inf)
+    vals[0, [3, 7]] = [1.0, 2.0]
+    cols, v = oracle.topk(vals, 4)
+    assert cols[0].tolist() == [7, 3, -1, -1]
+    assert cols[1].tolist() == [-1] * 4
+    assert np.all(v[1] == -np.inf)
+
+
+def test_topk_on_sigmoid_equals_topk_on_logits():
+    """sigmoid is strictly increasing, so selection on scores == on logits."""
+    wl = W.small_config(2)
+    lg = oracle.score(wl)
+    sc = oracle.sigmoid(lg)
+    assert np.all(sc[lg == -np.inf] == 0.0)
+    c1, _ = oracle.topk(lg, 512)
+    c2, _ = oracle.topk(np.where(lg == -np.inf, -np.inf, sc), 512)
+    assert np.array_equal(c1, c2)
+
+
+def test_topk_merge_associativity():
+    """top-k(A u B) == top-k(top-k(A) u top-k(B)): the rule a cross-block merge
+    relies on."""
+    rng = np.random.default_rng(3)
+    n, k = 5000, 300
+    vals = rng.standard_normal((1, n))
+    full, _ = oracle.topk(vals, k)
+    parts = np.array_split(np.arange(n), 7)
+    cand = []
+    for p in parts:
+        c, _ = oracle.topk(vals[:, p], k)
+        cand.extend(p[c[0][c[0] >= 0]])
+    cand = np.array(sorted(cand))
+    c2, _ = oracle.topk(vals[:, cand], k)
+    assert np.array_equal(cand[c2[0]], full[0])
+
+
+def test_score_topk_maps_chunk_columns_to_entries():
+    wl = W.small_config(4)
+    ent, vals, lg = oracle.score_topk(wl)
+    cols, _ = oracle.topk(lg, wl.k)
+    for b in range(wl.B):
+        for c, e in zip(cols[b], ent[b]):
+            if c < 0:
+                assert e == -1
+            else:
+                assert e == wl.chunk_ids[b][c // 64] * 64 + c % 64
+
+
+def test_generator_is_deterministic():
+    a, b = W.small_config(1), W.small_config(1)
+    assert np.array_equal(a.pool, b.pool) and np.array_equal(a.q, b.q)
+    assert np.array_equal(a.block_table, b.block_table)
