@@ -1,0 +1,239 @@
+"""Benchmark of the CSA indexer hot path (score + top-512) on one MI355X.
+
+One step = one idx_score_topk call over the decode-batch workload (32 requests
+x 1 query, context lengths U[32k, 128k] tokens, N_b = L_b // 4 compressed
+entries in a shuffled paged pool of 64-entry blocks, top-512 per request).
+Inputs are resident in HBM before timing; the pool and q are replicated so
+consecutive steps read different copies (more bytes than the 256 MB MALL), and
+the K timed steps run as replays of a captured HIP graph so host launch cost
+stays out of the GPU timeline.
+
+Prints ONE JSON line.  `value` is scored (query, entry) pairs per second of
+the whole path; `roofline` covers the score kernel (the dominant kernel),
+timed live with HIP events recorded on its own stream around each launch.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+SCORE_SOURCES = ["sparse_attention_kv_paged_amd/csrc/idx_score.hip",
+                 "sparse_attention_kv_paged_amd/csrc/idx_device.h",
+                 "sparse_attention_kv_paged_amd/csrc/idx_internal.h"]
+WORKLOADS = {"tiny-decode": 0, "decode-batch": 1, "long-decode": 2,
+             "chunked-prefill": 3, "resident-subset": 4}
+
+
+def score_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in SCORE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, pairs: int) -> int:
+    """Bytes the score kernel must move at minimum: one 132-byte key row per
+    scored (query, entry) pair for decode shapes (rows shared by every query
+    of a prefill request are counted once), plus q, w, bounds and tables."""
+    if wl.q_req is not None and wl.block_table is not None and wl.block_table.shape[0] == 1:
+        keys = int((wl.block_table >= 0).sum()) * 64 * 132          # one request
+    else:
+        keys = pairs * 132
+    extra = wl.q.nbytes + wl.w.nbytes + wl.limits.nbytes
+    for a in (wl.block_table, wl.q_req, wl.chunk_ids, wl.n_chunks):
+        if a is not None:
+            extra += a.nbytes
+    return keys + extra
+
+
+def read_traffic(workload: str):
+    """HBM bytes per score-kernel launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, f"score_kernel_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, _, val = line.partition("=")
+            kv[key.strip()] = val.strip()
+    if kv.get("score_source_hash") != score_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, pairs: int, min_seconds: float):
+    """The oracle as it stands on the host cores: full workload passes until
+    at least `min_seconds` of wall time."""
+    from oracle import oracle
+    threads = oracle.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.score_topk(wl)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": pairs * reps / el, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full pass(es) of the {wl.name} workload ({pairs} pairs, "
+                      f"score + top-{wl.k}) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=96)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode-batch", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for >= 1 GB)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=2.0)
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run N plain device copies of 1 GiB (for HBM counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              f"this build has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from sparse_attention_kv_paged_amd import lib, workloads
+
+    torch.cuda.set_device(0)
+    cfg = WORKLOADS[args.workload]
+    wl = workloads.config(cfg)
+    pairs = wl.pairs()
+    print(f"[bench] workload {wl.name}: {wl.description}; pairs {pairs}", file=sys.stderr, flush=True)
+    d = lib.to_device(wl)
+    pool_bytes = d.keys.pool.numel()
+    R = args.replicas or max(4, min(64, math.ceil(1.0e9 / max(pool_bytes, 1))))
+    pools = [d.keys.pool] + [d.keys.pool.clone() for _ in range(R - 1)]
+    qs = [d.q] + [d.q.clone() for _ in range(R - 1)]
+    keys = [lib.Keys(pool=p, limits=d.keys.limits, block_table=d.keys.block_table,
+                     q_req=d.keys.q_req, chunk_ids=d.keys.chunk_ids, n_chunks=d.keys.n_chunks)
+            for p in pools]
+    k = wl.k
+    out_idx = torch.empty((wl.B, k), dtype=torch.int32, device="cuda")
+    out_val = torch.empty((wl.B, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(lib.workspace_bytes(lib.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, k),
+                     dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        lib.idx_score_topk(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
+                           out_idx=out_idx, out_val=out_val, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    graphs = []
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        per = min(R, K)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per):
+                step(i)
+        graphs = [g] * (K // per)
+        if K % per:
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2):
+                for i in range(K % per):
+                    step(i)
+            graphs.append(g2)
+        for g_ in set(graphs):
+            g_.replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: K steps
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    if graphs:
+        for g_ in graphs:
+            g_.replay()
+    else:
+        for i in range(K):
+            step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(wall * 1e3, gpu_ms) / K
+
+    # ---- score kernel duration, live: events recorded on the launch stream
+    # around every score-kernel launch of K eager steps, queued behind a busy
+    # wait so the queue never drains while the host enqueues
+    n_ev = K
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    torch.cuda._sleep(int(5e7))
+    for i in range(n_ev):
+        lib.idx_profile_events(*evs[i])
+        step(i)
+    lib.idx_profile_events(None, None)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.copy_calibration):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    algo = algorithmic_bytes(wl, pairs)
+    achieved = algo / (kern_ms * 1e-3) / 1e9
+    traffic = read_traffic(args.workload)
+    out = {
+        "metric": "indexer scored pairs/s + top-512 queries/s; % of HBM/MFMA peak, 1 MI355X",
+        "value": pairs / (ms_per_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "queries": wl.B, "heads": wl.H, "head_dim": wl.D,
+                   "block": wl.block_size, "k": k, "n_cols": wl.n_cols, "pairs": pairs,
+                   "description": wl.description, "replicas": R, "graph": bool(graphs)},
+        "queries_per_s": wl.B / (ms_per_step * 1e-3),
+        "hbm_frac_path": algo / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"kernel": "score_kernel<true>", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes": algo, "kernel_ms": kern_ms},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, pairs, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

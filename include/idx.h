@@ -1,0 +1,197 @@
+/*
+ * idx.h -- C ABI of the MI355X (gfx950) compressed-sparse-attention indexer:
+ * paged fp8 key scoring and per-query top-k selection.
+ *
+ * What it computes ("FlashMemory-DeepSeek-V4" README, section "Retriever
+ * architecture"): for query row b, head h and a compressed key entry with
+ * fp8 bytes k8[0..D) and fp32 scale s ("compressed_k format": a row is
+ * D float8_e4m3 bytes followed by the fp32 scale, 132 bytes at D = 128),
+ *
+ *     k[d]      = e4m3(k8[d]) * s
+ *     logit     = sum_h relu( sum_d k[d] * q[b,h,d] ) * w[b,h]
+ *     score     = sigmoid(logit)
+ *
+ * with relu applied to each head before the weighted head sum ("feat:
+ * DeepSeek-V4-Flash integration + Blackwell (sm120) bring-up", Phase 3
+ * summary).  Level 2 of the pages' "Two-level recall algorithm" keeps the
+ * top-512 logits of each query, with non-resident entries at -inf.
+ *
+ * Tile lists ("DeepSeek-V4.1 native paged runtime", section "Current
+ * execution scope"): every query row carries its own bound (limits[b], the
+ * compressed length seq_len // 4 per the c4 fix in the batchgen pull request)
+ * and its own list of 64-entry blocks read in place from the paged pool; a
+ * prefill token, a decode token and a ragged batch are all the same shape.
+ *
+ * Conventions for every entry point:
+ *  - Every array pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees, synchronises, or reads device memory on the
+ *    host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns before it finishes.  Bounds, block ids and chunk
+ *    lists stay on the device, so calls can be captured in a HIP graph.
+ *  - Supported shapes: H = 64 heads, D = 128, block_size = 64, 1 <= k <= 2048.
+ *  - The return value is IDX_OK (0) or an IDX_E_* code; nothing is launched
+ *    when a host-side check fails.  idx_last_error() gives a message for the
+ *    calling thread's last failure.
+ *  - Data that only the device can see is never trusted: a bound above the
+ *    tile list's capacity is clamped, a block id of -1 means "absent", and an
+ *    out-of-range block id, chunk id or request id is treated as absent; the
+ *    corresponding columns are -inf and, when keys->status is given, a bit is
+ *    OR-ed into it (IDX_STATUS_*).  No kernel reads outside the pool.
+ *  - Key rows at scored positions must hold finite values; NaN/inf there give
+ *    an unspecified logit.
+ */
+#ifndef IDX_H
+#define IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum idx_status_code {
+    IDX_OK = 0,
+    IDX_E_ARG = 1,        /* a required pointer is NULL or a count is negative */
+    IDX_E_SHAPE = 2,      /* unsupported H, D, block_size, k, or inconsistent sizes */
+    IDX_E_ALIGN = 3,      /* q, pool, logits or workspace not 16-byte aligned */
+    IDX_E_WORKSPACE = 4,  /* ws_bytes below idx_workspace_bytes(...) */
+    IDX_E_HIP = 5         /* a HIP launch failed; idx_last_error() has the text */
+};
+
+/* op argument of idx_workspace_bytes */
+enum idx_op { IDX_OP_SCORE = 0, IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
+
+/* bits OR-ed into *keys->status by the device */
+#define IDX_STATUS_LIMIT_CLAMPED 0x1u  /* limits[b] exceeded the tile list's capacity */
+#define IDX_STATUS_BAD_BLOCK 0x2u      /* a block-table entry < -1 or past the pool's end */
+#define IDX_STATUS_BAD_REQUEST 0x4u    /* q_req[b] >= n_req (row treated as padding) */
+#define IDX_STATUS_BAD_CHUNK 0x8u      /* chunk id < 0 or >= max_blocks, or n_chunks[b] > max_chunks */
+
+#define IDX_HEADS 64
+#define IDX_HEAD_DIM 128
+#define IDX_BLOCK 64
+#define IDX_ROW_BYTES (IDX_HEAD_DIM + 4)
+#define IDX_MAX_K 2048
+
+/*
+ * The paged index plane and each query row's tile list.  Host struct holding
+ * device pointers; read by the call, not retained.
+ *
+ * pool         uint8 [n_pool_rows, D + 4]: row r = D e4m3fn bytes, then the
+ *              fp32 scale (little-endian).  16-byte aligned.  Rows of one
+ *              64-entry block are contiguous (a block is 8448 bytes).
+ * n_pool_rows  rows in the pool (with a block table: a multiple of 64).
+ * block_size   entries per block; must be 64.
+ * block_table  int32 [n_req, max_blocks]: logical block -> pool block, -1 =
+ *              absent.  NULL = contiguous: logical entry e is pool row e for
+ *              every request.
+ * q_req        int32 [B]: request (block-table row) of each query row;
+ *              -1 = padding row (all columns -inf, top-k all -1).
+ *              NULL = identity (row b uses table row b).
+ * chunk_ids    int32 [B, max_chunks]: the logical blocks row b scores (the
+ *              resident subset); NULL = blocks 0, 1, 2, ... of the request.
+ * n_chunks     int32 [B]: listed chunks per row; required iff chunk_ids.
+ * limits       int32 [B]: row b scores logical entries e < limits[b].
+ * status       optional uint32 device word; see IDX_STATUS_*.  Not cleared
+ *              by the library.
+ *
+ * Column c of row b (the logits' second index):
+ *   without chunk_ids: c is the logical entry id;
+ *   with chunk_ids:    c = 64*j + s is entry s of block chunk_ids[b][j],
+ *                      i.e. logical entry chunk_ids[b][j]*64 + s.
+ * A column is scored iff it maps to an entry below limits[b] whose block is
+ * present; every other column is -inf.
+ */
+typedef struct idx_keys {
+    const uint8_t *pool;
+    int64_t n_pool_rows;
+    int32_t block_size;
+    int32_t n_req;
+    const int32_t *block_table;
+    int32_t max_blocks;
+    int32_t max_chunks;
+    const int32_t *q_req;
+    const int32_t *chunk_ids;
+    const int32_t *n_chunks;
+    const int32_t *limits;
+    uint32_t *status;
+} idx_keys;
+
+/*
+ * idx_score: logits (and optionally sigmoid scores) of every column.
+ *
+ * q        bf16 bit patterns [B, H, D], 16-byte aligned.
+ * w        fp32 [B, H]: fused head weights (weights_proj output already
+ *          multiplied by D^-0.5 * H^-0.5, "Retriever architecture").
+ * n_cols   columns per row of the outputs (>= 1).
+ * logits   fp32 [B, n_cols] out, 16-byte aligned: the logit, or -inf for an
+ *          unscored column.
+ * scores   fp32 [B, n_cols] out, or NULL: sigmoid(logit), 0 where unscored.
+ */
+int idx_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
+              int32_t D, const idx_keys *keys, int32_t n_cols, float *logits,
+              float *scores, void *stream);
+
+/*
+ * idx_topk: the k largest values of each row of a logits matrix.
+ *
+ * logits   fp32 [B, ld] in (row stride ld >= n_cols); -inf and NaN entries
+ *          are never selected.
+ * out_col  int32 [B, k] out: selected columns, ordered by value descending,
+ *          equal values by column ascending; rows with fewer than k
+ *          selectable entries end in -1.
+ * out_val  fp32 [B, k] out or NULL: the selected values (-inf for -1).
+ * workspace / ws_bytes: device scratch of at least
+ *          idx_workspace_bytes(IDX_OP_TOPK, B, n_cols, k) bytes, 256-byte
+ *          aligned; contents on entry do not matter.
+ */
+int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld,
+             int32_t k, int32_t *out_col, float *out_val, void *workspace,
+             size_t ws_bytes, void *stream);
+
+/*
+ * idx_score_topk: the whole path: score every column as idx_score would,
+ * then select the top-k of each row as idx_topk would.
+ *
+ * out_idx  int32 [B, k] out: LOGICAL entry ids (chunk lists resolved),
+ *          ordered by logit descending, ties by column ascending; -1 pads.
+ * out_val  fp32 [B, k] out or NULL: their logits.
+ * workspace / ws_bytes: at least
+ *          idx_workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k) bytes.
+ */
+int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H,
+                   int32_t D, const idx_keys *keys, int32_t n_cols, int32_t k,
+                   int32_t *out_idx, float *out_val, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+/* Workspace bytes an op needs for B rows of n_cols columns and top-k
+ * (0 for IDX_OP_SCORE); (size_t)-1 for invalid arguments. */
+size_t idx_workspace_bytes(int32_t op, int32_t B, int32_t n_cols, int32_t k);
+
+/* Static text of an IDX_* code. */
+const char *idx_error_string(int32_t code);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char *idx_last_error(void);
+
+/*
+ * idx_profile_events: measurement hook for benchmark harnesses.  When both
+ * are non-NULL (hipEvent_t handles created by the caller), every later
+ * idx_score / idx_score_topk call on this thread records `before` right
+ * before its score kernel and `after` right after it, on the call's stream,
+ * so hipEventElapsedTime(before, after) is that kernel's duration.  Pass
+ * NULL, NULL to stop.  Returns IDX_OK.
+ */
+int idx_profile_events(void *before, void *after);
+
+/* ABI version of this header (increments on incompatible change). */
+int32_t idx_abi_version(void);
+
+#define IDX_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_H */

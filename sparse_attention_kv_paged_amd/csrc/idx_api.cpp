@@ -1,0 +1,272 @@
+// C-ABI layer of libidx.so: host-side validation, workspace layout and launch
+// configuration.  Never allocates, synchronises or reads device memory.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/idx.h"
+#include "idx_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+hipError_t launch_score_timed(const idx::ScoreArgs &a, hipStream_t s) {
+    if (g_ev_before && g_ev_after) {
+        hipError_t e = hipEventRecord(g_ev_before, s);
+        if (e != hipSuccess) return e;
+        if ((e = idx::launch_score(a, s)) != hipSuccess) return e;
+        return hipEventRecord(g_ev_after, s);
+    }
+    return idx::launch_score(a, s);
+}
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Workspace of the top-k pipeline, each piece 256-byte aligned.
+struct TopkLayout {
+    size_t logits, hist, counters, sure, cand, total;
+    int64_t ld, ldc;
+};
+
+TopkLayout topk_layout(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
+    TopkLayout L{};
+    L.ld = round_up(std::max<int64_t>(n_cols, 1), 64);
+    L.ldc = L.ld;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += (size_t)round_up((int64_t)bytes, 256);
+        return at;
+    };
+    L.logits = with_logits ? take((size_t)B * L.ld * sizeof(float)) : 0;
+    L.hist = take((size_t)B * idx::kHistBins * sizeof(uint32_t));
+    L.counters = take((size_t)B * idx::kCounters * sizeof(uint32_t));
+    L.sure = take((size_t)B * k * sizeof(uint2));
+    L.cand = take((size_t)B * L.ldc * sizeof(uint2));
+    L.total = off;
+    return L;
+}
+
+int check_qw(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D) {
+    if (B < 0) return fail(IDX_E_ARG, "B must be >= 0 (got %d)", B);
+    if (H != idx::kHeads || D != idx::kHeadDim)
+        return fail(IDX_E_SHAPE, "only H=64, D=128 are supported (got H=%d, D=%d)", H, D);
+    if (B > 0 && (!q || !w)) return fail(IDX_E_ARG, "q and w must be non-null");
+    if (!aligned(q, 16) || !aligned(w, 16)) return fail(IDX_E_ALIGN, "q and w must be 16-byte aligned");
+    return IDX_OK;
+}
+
+int check_keys(const idx_keys *keys, int32_t B) {
+    if (!keys) return fail(IDX_E_ARG, "keys must be non-null");
+    if (keys->block_size != idx::kBlock)
+        return fail(IDX_E_SHAPE, "block_size must be 64 (got %d)", keys->block_size);
+    if (keys->n_pool_rows < 0) return fail(IDX_E_ARG, "n_pool_rows must be >= 0");
+    if (keys->n_pool_rows > 0 && !keys->pool) return fail(IDX_E_ARG, "pool is null");
+    if (!aligned(keys->pool, 16)) return fail(IDX_E_ALIGN, "pool must be 16-byte aligned");
+    if (B > 0 && !keys->limits) return fail(IDX_E_ARG, "limits must be non-null");
+    if (keys->block_table) {
+        if (keys->n_req <= 0 || keys->max_blocks <= 0)
+            return fail(IDX_E_SHAPE, "a block table needs n_req >= 1 and max_blocks >= 1");
+        if (keys->n_pool_rows % idx::kBlock)
+            return fail(IDX_E_SHAPE, "with a block table, n_pool_rows must be a multiple of 64");
+        if ((int64_t)keys->max_blocks * idx::kBlock > INT32_MAX)
+            return fail(IDX_E_SHAPE, "max_blocks too large");
+    } else if (!keys->q_req && B > 0) {
+        // contiguous pool: every row reads the same rows; nothing else to check
+    }
+    if (keys->chunk_ids) {
+        if (!keys->n_chunks) return fail(IDX_E_ARG, "n_chunks is required with chunk_ids");
+        if (keys->max_chunks <= 0) return fail(IDX_E_SHAPE, "max_chunks must be >= 1");
+    }
+    if (keys->n_pool_rows > ((int64_t)1 << 40)) return fail(IDX_E_SHAPE, "pool too large");
+    return IDX_OK;
+}
+
+idx::ScoreArgs score_args(const uint16_t *q, const float *w, int32_t B, const idx_keys *keys,
+                          int32_t n_cols) {
+    idx::ScoreArgs a{};
+    a.q = q;
+    a.w = w;
+    a.B = B;
+    a.pool = keys->pool;
+    a.n_pool_rows = keys->n_pool_rows;
+    a.block_table = keys->block_table;
+    a.n_req = keys->n_req;
+    a.max_blocks = keys->max_blocks;
+    a.q_req = keys->q_req;
+    a.chunk_ids = keys->chunk_ids;
+    a.n_chunks = keys->n_chunks;
+    a.max_chunks = keys->max_chunks;
+    a.limits = keys->limits;
+    a.status = keys->status;
+    a.n_cols = n_cols;
+    // Launch shape: about 4096 waves over the whole problem, at most one
+    // workgroup per row (so q[b] is loaded once per wave and reused over
+    // `slots_per_wave` blocks).
+    const int64_t slots = (n_cols + idx::kBlock - 1) / idx::kBlock;
+    const int64_t total = (int64_t)B * slots;
+    int64_t spw = std::max<int64_t>(1, (total + 4095) / 4096);
+    spw = std::min<int64_t>(spw, std::max<int64_t>(1, (slots + idx::kWaves - 1) / idx::kWaves));
+    a.slots_per_wave = (int32_t)spw;
+    a.splits = (int32_t)std::max<int64_t>(1, (slots + idx::kWaves * spw - 1) / (idx::kWaves * spw));
+    return a;
+}
+
+idx::TopkArgs topk_args(const TopkLayout &L, char *ws, int32_t B, int32_t n_cols, int32_t k) {
+    idx::TopkArgs t{};
+    t.B = B;
+    t.n_cols = n_cols;
+    t.k = k;
+    t.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
+    t.counters = reinterpret_cast<uint32_t *>(ws + L.counters);
+    t.sure = reinterpret_cast<uint2 *>(ws + L.sure);
+    t.cand = reinterpret_cast<uint2 *>(ws + L.cand);
+    t.ldc = L.ldc;
+    t.cols_per_wg = 4096;
+    t.parts = (int32_t)std::max<int64_t>(1, ((int64_t)n_cols + t.cols_per_wg - 1) / t.cols_per_wg);
+    return t;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(IDX_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t idx_abi_version(void) { return IDX_ABI_VERSION; }
+
+const char *idx_error_string(int32_t code) {
+    switch (code) {
+    case IDX_OK: return "ok";
+    case IDX_E_ARG: return "invalid argument";
+    case IDX_E_SHAPE: return "unsupported or inconsistent shape";
+    case IDX_E_ALIGN: return "misaligned pointer";
+    case IDX_E_WORKSPACE: return "workspace too small";
+    case IDX_E_HIP: return "HIP launch failure";
+    default: return "unknown error";
+    }
+}
+
+const char *idx_last_error(void) { return g_last_error; }
+
+int idx_profile_events(void *before, void *after) {
+    g_ev_before = (before && after) ? static_cast<hipEvent_t>(before) : nullptr;
+    g_ev_after = (before && after) ? static_cast<hipEvent_t>(after) : nullptr;
+    return IDX_OK;
+}
+
+size_t idx_workspace_bytes(int32_t op, int32_t B, int32_t n_cols, int32_t k) {
+    if (B < 0 || n_cols < 0 || (op != IDX_OP_SCORE && (k < 1 || k > idx::kMaxK))) return (size_t)-1;
+    switch (op) {
+    case IDX_OP_SCORE: return 0;
+    case IDX_OP_TOPK: return topk_layout(false, B, n_cols, k).total;
+    case IDX_OP_SCORE_TOPK: return topk_layout(true, B, n_cols, k).total;
+    default: return (size_t)-1;
+    }
+}
+
+int idx_score(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D,
+              const idx_keys *keys, int32_t n_cols, float *logits, float *scores, void *stream) {
+    g_last_error[0] = 0;
+    int rc = check_qw(q, w, B, H, D);
+    if (rc) return rc;
+    if ((rc = check_keys(keys, B))) return rc;
+    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if (B == 0) return IDX_OK;
+    if (!logits) return fail(IDX_E_ARG, "logits must be non-null");
+    if (!aligned(logits, 16) || !aligned(scores, 4)) return fail(IDX_E_ALIGN, "logits must be 16-byte aligned");
+    idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
+    a.ld = n_cols;
+    a.logits = logits;
+    a.scores = scores;
+    hipError_t e = launch_score_timed(a, (hipStream_t)stream);
+    return e == hipSuccess ? IDX_OK : hip_fail(e, "score kernel");
+}
+
+int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t k, int32_t *out_col,
+             float *out_val, void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    if (B < 0 || n_cols < 1 || ld < n_cols) return fail(IDX_E_SHAPE, "need B >= 0, n_cols >= 1, ld >= n_cols");
+    if (k < 1 || k > idx::kMaxK) return fail(IDX_E_SHAPE, "k must be in [1, 2048] (got %d)", k);
+    if (B == 0) return IDX_OK;
+    if (!logits || !out_col) return fail(IDX_E_ARG, "logits and out_col must be non-null");
+    if (!aligned(logits, 4) || !aligned(out_col, 4) || !aligned(out_val, 4))
+        return fail(IDX_E_ALIGN, "logits/out_col/out_val must be 4-byte aligned");
+    const TopkLayout L = topk_layout(false, B, n_cols, k);
+    if (!workspace || ws_bytes < L.total)
+        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+    if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
+    idx::TopkArgs t = topk_args(L, static_cast<char *>(workspace), B, n_cols, k);
+    t.logits = logits;
+    t.ld = ld;
+    t.out_col = out_col;
+    t.out_val = out_val;
+    t.set_cols = 1;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = idx::launch_topk_init(t, s)) != hipSuccess) return hip_fail(e, "top-k init");
+    if ((e = idx::launch_topk_hist(t, s)) != hipSuccess) return hip_fail(e, "top-k histogram");
+    if ((e = idx::launch_topk_select(t, s)) != hipSuccess) return hip_fail(e, "top-k select");
+    if ((e = idx::launch_topk_final(t, s)) != hipSuccess) return hip_fail(e, "top-k final");
+    return IDX_OK;
+}
+
+int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D,
+                   const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
+                   void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    int rc = check_qw(q, w, B, H, D);
+    if (rc) return rc;
+    if ((rc = check_keys(keys, B))) return rc;
+    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if (k < 1 || k > idx::kMaxK) return fail(IDX_E_SHAPE, "k must be in [1, 2048] (got %d)", k);
+    if (B == 0) return IDX_OK;
+    if (!out_idx) return fail(IDX_E_ARG, "out_idx must be non-null");
+    if (!aligned(out_idx, 4) || !aligned(out_val, 4)) return fail(IDX_E_ALIGN, "outputs must be 4-byte aligned");
+    const TopkLayout L = topk_layout(true, B, n_cols, k);
+    if (!workspace || ws_bytes < L.total)
+        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+    if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+    idx::TopkArgs t = topk_args(L, ws, B, n_cols, k);
+    t.logits = reinterpret_cast<const float *>(ws + L.logits);
+    t.ld = L.ld;
+    t.out_col = out_idx;
+    t.out_val = out_val;
+    t.chunk_ids = keys->chunk_ids;
+    t.max_chunks = keys->max_chunks;
+    t.map_entries = 1;
+    t.set_cols = 0;
+    idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
+    a.ld = L.ld;
+    a.logits = reinterpret_cast<float *>(ws + L.logits);
+    a.scores = nullptr;
+    a.hist = t.hist;
+    a.counters = t.counters;
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = idx::launch_topk_init(t, s)) != hipSuccess) return hip_fail(e, "top-k init");
+    if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
+    if ((e = idx::launch_topk_select(t, s)) != hipSuccess) return hip_fail(e, "top-k select");
+    if ((e = idx::launch_topk_final(t, s)) != hipSuccess) return hip_fail(e, "top-k final");
+    return IDX_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,282 @@
+// Score kernel of the CSA indexer for gfx950 (MI355X).
+//
+// logit(b, e) = sum_h relu( sum_d k[e,d] * q[b,h,d] ) * w[b,h],
+// k[e,d] = e4m3(byte) * scale      ("FlashMemory-DeepSeek-V4" README,
+// "Retriever architecture" and "compressed_k format"; relu per head before
+// the weighted head sum per the batchgen pull request's Phase 3 summary).
+//
+// Work decomposition: a workgroup is 4 independent waves on ONE query row;
+// wave w of split s owns `slots_per_wave` consecutive 64-entry slots of that
+// row's tile list ("DeepSeek-V4.1 native paged runtime", "Current execution
+// scope": per-row bound + per-row tile list read in place).  A slot is one
+// paged block, scored as two 32-entry tiles.
+//
+// Per tile, on MFMA v_mfma_f32_32x32x16_bf16 with heads as the 32 rows and
+// entries as the 32 columns:
+//   A (resident, registers) = q[b] as 2 head blocks x 8 k-steps of 16 dims
+//   B (streamed)            = 32 key rows, each lane holding 64 contiguous
+//                             fp8 bytes of one row, converted exactly to
+//                             bf16 in registers (v_cvt_scalef32_pk_bf16_fp8,
+//                             scale 1.0)
+// The reduction index d is permuted identically in A and B: k-step kk, lane
+// half hf covers d = 64*hf + 8*kk + 0..7, so each lane streams one contiguous
+// 64-byte half row with four 16-byte loads and never re-reads it.
+// The accumulator gives each lane 16 heads x 1 entry per head block, so the
+// relu / head-weight / head-sum epilogue is 32 in-register FMAs plus one
+// cross-half add.  The row scale s is applied after the head sum as
+// |s| * sum_h relu(x_h) w_h, which equals the definition because
+// relu(s x) = |s| relu(sign(s) x); for s < 0 the fp8 sign bits are flipped
+// before conversion (exact).
+#include "idx_device.h"
+#include "idx_internal.h"
+
+namespace idx {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+struct RowCtx {
+    int32_t req;      // request row, -1 = padding
+    int32_t nslots;   // slots of the tile list that may hold scored entries
+    int32_t limit;    // bound on logical entry ids, clamped to capacity
+};
+
+__device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, int b, uint32_t &st) {
+    RowCtx r;
+    r.req = a.q_req ? a.q_req[b] : b;
+    r.limit = a.limits[b];
+    r.nslots = 0;
+    if (r.req >= 0 && a.block_table && r.req >= a.n_req) {
+        st |= 0x4u;                                   // IDX_STATUS_BAD_REQUEST
+        r.req = -1;
+    }
+    if (r.req < 0) return r;
+    const int64_t cap = a.block_table ? (int64_t)a.max_blocks * kBlock : a.n_pool_rows;
+    if ((int64_t)r.limit > cap) {
+        st |= 0x1u;                                   // IDX_STATUS_LIMIT_CLAMPED
+        r.limit = (int32_t)cap;
+    }
+    if (r.limit < 0) r.limit = 0;
+    if (a.chunk_ids) {
+        int32_t nc = a.n_chunks[b];
+        if (nc > a.max_chunks) {
+            st |= 0x8u;                               // IDX_STATUS_BAD_CHUNK
+            nc = a.max_chunks;
+        }
+        r.nslots = nc < 0 ? 0 : nc;
+    } else {
+        r.nslots = (r.limit + kBlock - 1) / kBlock;
+    }
+    return r;
+}
+
+// First pool row of slot j of row b, or -1 when the slot's block is absent.
+// *ebase receives the logical entry id of the slot's first entry.
+__device__ __forceinline__ int64_t resolve_slot(const ScoreArgs &a, const RowCtx &r, int b,
+                                                int j, int32_t &ebase, uint32_t &st) {
+    int64_t beta = j;
+    ebase = 0;
+    if (r.req < 0 || j >= r.nslots) return -1;
+    if (a.chunk_ids) {
+        beta = a.chunk_ids[(int64_t)b * a.max_chunks + j];
+        if (beta < 0) {
+            if (beta != -1) st |= 0x8u;
+            return -1;
+        }
+        if (a.block_table ? beta >= a.max_blocks : beta * kBlock >= a.n_pool_rows) {
+            st |= 0x8u;
+            return -1;
+        }
+    }
+    ebase = (int32_t)(beta * kBlock);
+    if (ebase >= r.limit) return -1;
+    if (!a.block_table) return beta * kBlock;
+    const int64_t pblk = a.block_table[(int64_t)r.req * a.max_blocks + beta];
+    if (pblk < 0) {
+        if (pblk != -1) st |= 0x2u;                   // IDX_STATUS_BAD_BLOCK
+        return -1;
+    }
+    if ((pblk + 1) * kBlock > a.n_pool_rows) {
+        st |= 0x2u;
+        return -1;
+    }
+    return pblk * kBlock;
+}
+
+struct KeyHalf {
+    u32x4 v[4];   // 64 fp8 bytes: d = 64*hf .. 64*hf + 63 of one key row
+    float s;      // the row's scale
+};
+
+__device__ __forceinline__ KeyHalf load_key_half(const uint8_t *pool, int64_t prow, int hf) {
+    const uint8_t *rp = pool + prow * kRowBytes;
+    const u32x4_a4 *p = reinterpret_cast<const u32x4_a4 *>(rp + 64 * hf);
+    KeyHalf k;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        u32x4_a4 t = p[i];
+        k.v[i] = u32x4{t.x, t.y, t.z, t.w};
+    }
+    k.s = *reinterpret_cast<const float *>(rp + kHeadDim);
+    return k;
+}
+
+// fp8 bytes [2*HI, 2*HI+1] of x -> two bf16 in one dword, exact (scale 1).
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt_fp8x2_bf16x2(uint32_t x) {
+    auto r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 fp8 bytes (two dwords) -> 8 bf16 (one MFMA operand), exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t d0, uint32_t d1) {
+    u32x4 o{cvt_fp8x2_bf16x2<false>(d0), cvt_fp8x2_bf16x2<true>(d0),
+            cvt_fp8x2_bf16x2<false>(d1), cvt_fp8x2_bf16x2<true>(d1)};
+    return __builtin_bit_cast(bf16x8, o);
+}
+
+template <bool TOPK>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+    __shared__ uint32_t sh_hist[TOPK ? kHistBins : 1];
+
+    const int b = blockIdx.x / a.splits;
+    const int split = blockIdx.x - b * a.splits;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int hf = lane >> 5;
+    const int n32 = lane & 31;
+
+    uint32_t st = 0;
+    const RowCtx r = row_context(a, b, st);
+    const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
+    const int col_end = TOPK ? min(r.nslots * kBlock, a.n_cols) : a.n_cols;
+    const int slot_stop = TOPK ? min(r.nslots, slot_cols) : slot_cols;
+
+    if (TOPK) {
+        for (int i = threadIdx.x; i < kHistBins; i += 256) sh_hist[i] = 0u;
+        if (split == 0 && threadIdx.x == 0)
+            a.counters[(int64_t)b * kCounters + kCntCols] = (uint32_t)max(col_end, 0);
+        __syncthreads();
+    }
+
+    const int slot0 = (split * kWaves + wave) * a.slots_per_wave;
+    const int slot_end = min(slot0 + a.slots_per_wave, slot_stop);
+    float *out_row = a.logits + (int64_t)b * a.ld;
+    float *score_row = a.scores ? a.scores + (int64_t)b * a.ld : nullptr;
+
+    if (slot0 < slot_end) {
+        // Resident operands: q[b] (A fragments) and the head weights matching
+        // this lane's accumulator rows.
+        bf16x8 qa[2][8];
+        float wr[2][16];
+        const bool live = r.req >= 0 && slot0 < r.nslots;
+        if (live) {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+                    a.q + ((int64_t)b * kHeads + 32 * hb + n32) * kHeadDim + 64 * hf);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+                // accumulator register i holds head 32*hb + 8*(i/4) + 4*hf + i%4
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 wv = *reinterpret_cast<const float4 *>(
+                        a.w + (int64_t)b * kHeads + 32 * hb + 8 * g + 4 * hf);
+                    wr[hb][4 * g + 0] = wv.x;
+                    wr[hb][4 * g + 1] = wv.y;
+                    wr[hb][4 * g + 2] = wv.z;
+                    wr[hb][4 * g + 3] = wv.w;
+                }
+            }
+        }
+
+        const int ntiles = 2 * (slot_end - slot0);
+        int32_t ebase_cur = 0;
+        int64_t prow0_cur = live ? resolve_slot(a, r, b, slot0, ebase_cur, st) : -1;
+        const int64_t last_row = a.n_pool_rows - 1;
+        KeyHalf kv_cur;
+        if (prow0_cur >= 0) kv_cur = load_key_half(a.pool, min(prow0_cur + n32, last_row), hf);
+
+        for (int tau = 0; tau < ntiles; ++tau) {
+            const int slot = slot0 + (tau >> 1);
+            const int t = tau & 1;
+            // prefetch the next tile
+            int32_t ebase_nxt = ebase_cur;
+            int64_t prow0_nxt = prow0_cur;
+            KeyHalf kv_nxt;
+            if (tau + 1 < ntiles) {
+                if (t == 1) prow0_nxt = live ? resolve_slot(a, r, b, slot + 1, ebase_nxt, st) : -1;
+                if (prow0_nxt >= 0) {
+                    const int tn = (tau + 1) & 1;
+                    kv_nxt = load_key_half(a.pool, min(prow0_nxt + 32 * tn + n32, last_row), hf);
+                }
+            }
+
+            const int col = slot * kBlock + 32 * t + n32;
+            float logit = -__builtin_inff();
+            if (prow0_cur >= 0) {
+                KeyHalf k = kv_cur;
+                // relu(s x) = |s| relu(sign(s) x): flip fp8 signs for s < 0
+                if (__any(k.s < 0.f)) {
+                    const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) k.v[i] ^= u32x4{m, m, m, m};
+                }
+                f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const u32x4 &v = k.v[kk >> 1];
+                    const bf16x8 kb = (kk & 1) ? fp8x8_to_bf16x8(v.z, v.w) : fp8x8_to_bf16x8(v.x, v.y);
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kk], kb, acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kk], kb, acc1, 0, 0, 0);
+                }
+                float T = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc0[i], 0.f), wr[0][i], T);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc1[i], 0.f), wr[1][i], T);
+                T += __shfl_xor(T, 32, 64);
+                const int e = ebase_cur + 32 * t + n32;
+                if (e < r.limit) logit = fabsf(k.s) * T;
+            }
+            if (hf == 0 && col < col_end) {
+                out_row[col] = logit;
+                if (score_row) score_row[col] = 1.0f / (1.0f + expf(-logit));
+                if (TOPK) {
+                    const uint32_t key = order_key(logit);
+                    if (key) atomicAdd(&sh_hist[key >> kHistShift], 1u);
+                }
+            }
+            kv_cur = kv_nxt;
+            prow0_cur = prow0_nxt;
+            ebase_cur = ebase_nxt;
+        }
+    }
+
+    if (TOPK) {
+        __syncthreads();
+        uint32_t *gh = a.hist + (int64_t)b * kHistBins;
+        for (int i = threadIdx.x; i < kHistBins; i += 256) {
+            const uint32_t c = sh_hist[i];
+            if (c) atomicAdd(gh + i, c);
+        }
+    }
+    if (st && a.status && lane == 0) atomicOr(a.status, st);
+}
+
+}  // namespace
+
+hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
+    const int64_t grid = (int64_t)a.B * a.splits;
+    if (grid <= 0) return hipSuccess;
+    if (a.hist)
+        hipLaunchKernelGGL(score_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(score_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace idx

@@ -1,0 +1,259 @@
+"""ctypes binding of libidx.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (include/idx.h);
+all computation runs in the library's HIP kernels.  PyTorch supplies device
+memory and the current stream.  There is no CPU fallback: if the library is
+missing the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libidx.so")
+
+IDX_OK, IDX_E_ARG, IDX_E_SHAPE, IDX_E_ALIGN, IDX_E_WORKSPACE, IDX_E_HIP = range(6)
+IDX_OP_SCORE, IDX_OP_TOPK, IDX_OP_SCORE_TOPK = range(3)
+STATUS_LIMIT_CLAMPED, STATUS_BAD_BLOCK, STATUS_BAD_REQUEST, STATUS_BAD_CHUNK = 1, 2, 4, 8
+
+EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_workspace_bytes",
+           "idx_error_string", "idx_last_error", "idx_profile_events", "idx_abi_version")
+
+
+class IdxKeys(ctypes.Structure):
+    """Mirror of `struct idx_keys`."""
+    _fields_ = [
+        ("pool", ctypes.c_void_p),
+        ("n_pool_rows", ctypes.c_int64),
+        ("block_size", ctypes.c_int32),
+        ("n_req", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+        ("max_blocks", ctypes.c_int32),
+        ("max_chunks", ctypes.c_int32),
+        ("q_req", ctypes.c_void_p),
+        ("chunk_ids", ctypes.c_void_p),
+        ("n_chunks", ctypes.c_void_p),
+        ("limits", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
+    ]
+
+
+class IdxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"idx error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libidx.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m sparse_attention_kv_paged_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    kp = ctypes.POINTER(IdxKeys)
+    lib.idx_score.argtypes = [vp, vp, i32, i32, i32, kp, i32, vp, vp, vp]
+    lib.idx_score.restype = ctypes.c_int
+    lib.idx_topk.argtypes = [vp, i32, i32, i64, i32, vp, vp, vp, sz, vp]
+    lib.idx_topk.restype = ctypes.c_int
+    lib.idx_score_topk.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
+    lib.idx_score_topk.restype = ctypes.c_int
+    lib.idx_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.idx_workspace_bytes.restype = sz
+    lib.idx_error_string.argtypes = [i32]
+    lib.idx_error_string.restype = ctypes.c_char_p
+    lib.idx_last_error.argtypes = []
+    lib.idx_last_error.restype = ctypes.c_char_p
+    lib.idx_profile_events.argtypes = [vp, vp]
+    lib.idx_profile_events.restype = ctypes.c_int
+    lib.idx_abi_version.argtypes = []
+    lib.idx_abi_version.restype = i32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != IDX_OK:
+        lib = load()
+        raise IdxError(rc, f"{lib.idx_error_string(rc).decode()}: {lib.idx_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: Optional[torch.Tensor], dtype, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA {dtype} tensor")
+    return t
+
+
+@dataclass
+class Keys:
+    """Device tensors of the paged index plane and the per-row tile lists
+    (fields as in `struct idx_keys`)."""
+    pool: torch.Tensor                          # uint8 [n_pool_rows, 132]
+    limits: torch.Tensor                        # int32 [B]
+    block_table: Optional[torch.Tensor] = None  # int32 [n_req, max_blocks]
+    q_req: Optional[torch.Tensor] = None        # int32 [B]
+    chunk_ids: Optional[torch.Tensor] = None    # int32 [B, max_chunks]
+    n_chunks: Optional[torch.Tensor] = None     # int32 [B]
+    status: Optional[torch.Tensor] = None       # int32 [1] (bits OR-ed in)
+    block_size: int = 64
+
+    def struct(self) -> IdxKeys:
+        pool = _dev(self.pool, torch.uint8, "pool")
+        bt = _dev(self.block_table, torch.int32, "block_table")
+        ci = _dev(self.chunk_ids, torch.int32, "chunk_ids")
+        k = IdxKeys()
+        k.pool = pool.data_ptr()
+        k.n_pool_rows = pool.shape[0]
+        k.block_size = self.block_size
+        k.n_req = 0 if bt is None else bt.shape[0]
+        k.block_table = None if bt is None else bt.data_ptr()
+        k.max_blocks = 0 if bt is None else bt.shape[1]
+        k.max_chunks = 0 if ci is None else ci.shape[1]
+        k.q_req = None if self.q_req is None else _dev(self.q_req, torch.int32, "q_req").data_ptr()
+        k.chunk_ids = None if ci is None else ci.data_ptr()
+        k.n_chunks = None if self.n_chunks is None else _dev(self.n_chunks, torch.int32, "n_chunks").data_ptr()
+        k.limits = _dev(self.limits, torch.int32, "limits").data_ptr()
+        k.status = None if self.status is None else _dev(self.status, torch.int32, "status").data_ptr()
+        return k
+
+
+def idx_profile_events(before, after) -> None:
+    """Record hipEvents (torch.cuda.Event objects, or None to stop) around
+    every later score-kernel launch on this thread."""
+    bp = None if before is None else ctypes.c_void_p(before.cuda_event)
+    ap = None if after is None else ctypes.c_void_p(after.cuda_event)
+    _check(load().idx_profile_events(bp, ap))
+
+
+def workspace_bytes(op: int, B: int, n_cols: int, k: int) -> int:
+    n = load().idx_workspace_bytes(op, B, n_cols, k)
+    if n == ctypes.c_size_t(-1).value:
+        raise IdxError(IDX_E_ARG, "invalid workspace request")
+    return int(n)
+
+
+def idx_workspace_bytes(op: int, B: int, n_cols: int, k: int) -> int:
+    return workspace_bytes(op, B, n_cols, k)
+
+
+def _workspace(n: int, device) -> torch.Tensor:
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def _qw(q, w):
+    if q.dtype == torch.bfloat16:
+        q = q.view(torch.int16)
+    q = _dev(q, torch.int16, "q (bf16 bits)")
+    w = _dev(w, torch.float32, "w")
+    if q.dim() != 3 or w.dim() != 2 or w.shape != q.shape[:2]:
+        raise ValueError("q must be [B, H, D] and w [B, H]")
+    return q, w
+
+
+def idx_score(q, w, keys: Keys, n_cols: int, with_scores: bool = False,
+              logits: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+              stream=None):
+    """Logits [B, n_cols] (fp32, -inf where unscored) and optionally scores."""
+    q, w = _qw(q, w)
+    B, H, D = q.shape
+    if logits is None:
+        logits = torch.empty((B, n_cols), dtype=torch.float32, device=q.device)
+    if with_scores and scores is None:
+        scores = torch.empty((B, n_cols), dtype=torch.float32, device=q.device)
+    _dev(logits, torch.float32, "logits")
+    _dev(scores, torch.float32, "scores")
+    ks = keys.struct()
+    _check(load().idx_score(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols,
+                            _ptr(logits), _ptr(scores), _stream(stream)))
+    return (logits, scores) if with_scores else logits
+
+
+def idx_topk(logits: torch.Tensor, k: int, n_cols: Optional[int] = None,
+             out_col=None, out_val=None, workspace=None, stream=None):
+    """Top-k columns [B, k] (int32) and values [B, k] of each logits row."""
+    if logits.dim() != 2 or logits.dtype != torch.float32 or not logits.is_cuda or logits.stride(1) != 1:
+        raise ValueError("logits must be a CUDA float32 [B, ld] tensor with unit column stride")
+    B = logits.shape[0]
+    n_cols = logits.shape[1] if n_cols is None else n_cols
+    ld = logits.stride(0) if B > 1 else max(n_cols, logits.shape[1])
+    if out_col is None:
+        out_col = torch.empty((B, k), dtype=torch.int32, device=logits.device)
+    if out_val is None:
+        out_val = torch.empty((B, k), dtype=torch.float32, device=logits.device)
+    need = workspace_bytes(IDX_OP_TOPK, B, n_cols, k)
+    if workspace is None:
+        workspace = _workspace(need, logits.device)
+    _check(load().idx_topk(_ptr(logits), B, n_cols, ld, k, _ptr(out_col), _ptr(out_val),
+                           _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out_col, out_val
+
+
+def idx_score_topk(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=None,
+                   workspace=None, stream=None):
+    """Top-k logical entry ids [B, k] (int32, -1 padded) and their logits."""
+    q, w = _qw(q, w)
+    B, H, D = q.shape
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    if out_val is None:
+        out_val = torch.empty((B, k), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    ks = keys.struct()
+    _check(load().idx_score_topk(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
+                                 _ptr(out_idx), _ptr(out_val), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+    return out_idx, out_val
+
+
+# ---------------------------------------------------------------------------
+# host workload -> device tensors
+
+@dataclass
+class DeviceInputs:
+    q: torch.Tensor
+    w: torch.Tensor
+    keys: Keys
+    n_cols: int
+    k: int
+
+
+def to_device(wl, device="cuda", status: bool = False) -> DeviceInputs:
+    """Copy a host workload (numpy arrays) to device tensors."""
+    def t(a, dtype=None):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            x = x.view(dtype)
+        return x.to(device)
+    q = t(wl.q.view(np.int16)).view(torch.bfloat16)
+    keys = Keys(pool=t(wl.pool), limits=t(wl.limits), block_table=t(wl.block_table),
+                q_req=t(wl.q_req), chunk_ids=t(wl.chunk_ids), n_chunks=t(wl.n_chunks),
+                status=torch.zeros(1, dtype=torch.int32, device=device) if status else None,
+                block_size=wl.block_size)
+    return DeviceInputs(q=q, w=t(wl.w), keys=keys, n_cols=wl.n_cols, k=wl.k)

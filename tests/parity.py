@@ -1,0 +1,53 @@
+"""Comparison rules shared by the GPU parity tests.
+
+Tolerance (fp32 accumulation vs the double oracle): a scored column passes if
+|gpu - oracle| <= ATOL + RTOL * |oracle|; an unscored column must be exactly
+-inf on both sides.  Top-k sets may differ only at near-ties: every entry in
+the symmetric difference of the GPU and oracle sets must have an oracle logit
+within the same tolerance of the oracle's k-th value.
+"""
+import numpy as np
+
+ATOL = 1e-4
+RTOL = 2e-3
+
+
+def assert_logits_close(gpu, ref, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    masked = ref == -np.inf
+    assert np.array_equal(gpu == -np.inf, masked), f"{what}: -inf pattern differs"
+    g, r = gpu[~masked], ref[~masked]
+    assert np.all(np.isfinite(g)), f"{what}: non-finite logit at a scored column"
+    err = np.abs(g - r)
+    bound = ATOL + RTOL * np.abs(r)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} logits out of tolerance; "
+                           f"worst err {err.max():.3e} (bound there {bound[np.argmax(err)]:.3e})")
+
+
+def assert_topk_near_tie(gpu_idx, ref_idx, ref_logit_of_entry, k, what=""):
+    """gpu_idx/ref_idx: [B, k] logical entry ids (-1 padded);
+    ref_logit_of_entry(b, ids) -> oracle logits of those entries (double)."""
+    gpu_idx = np.asarray(gpu_idx)
+    ref_idx = np.asarray(ref_idx)
+    for b in range(ref_idx.shape[0]):
+        ref_set = ref_idx[b][ref_idx[b] >= 0]
+        gpu_set = gpu_idx[b][gpu_idx[b] >= 0]
+        assert len(np.unique(gpu_set)) == len(gpu_set), f"{what} row {b}: duplicate ids"
+        assert len(gpu_set) == len(ref_set), f"{what} row {b}: {len(gpu_set)} vs {len(ref_set)} selected"
+        if len(ref_set) == 0:
+            continue
+        assert np.all(gpu_idx[b][len(gpu_set):] == -1), f"{what} row {b}: padding not at the end"
+        diff = np.setxor1d(gpu_set, ref_set)
+        if len(diff) == 0:
+            continue
+        if len(ref_set) < k:
+            raise AssertionError(f"{what} row {b}: sets differ although all entries fit")
+        lg = ref_logit_of_entry(b, diff)
+        t = ref_logit_of_entry(b, ref_set[-1:])[0]     # oracle's k-th value
+        tol = ATOL + RTOL * abs(t)
+        far = np.abs(lg - t) > tol
+        assert not far.any(), (f"{what} row {b}: {far.sum()} differing ids are not near-ties "
+                               f"(k-th {t:.6g}, offending {lg[far][:4]})")

@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/idx.h declares, and rejects bad host-side arguments before launching
+anything (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_kv_paged_amd import lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "idx.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(idx_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(L.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_error_strings(lib):
+    assert lib.idx_abi_version() == 1
+    assert lib.idx_error_string(0) == b"ok"
+    for code in range(1, 6):
+        assert lib.idx_error_string(code) not in (b"ok", b"unknown error")
+    assert lib.idx_error_string(99) == b"unknown error"
+
+
+def test_keys_struct_layout_matches_header():
+    # pointer/int64 fields are 8-byte aligned; the struct is 80 bytes on x86-64
+    assert ctypes.sizeof(L.IdxKeys) == 80
+    assert L.IdxKeys.block_table.offset == 24 and L.IdxKeys.status.offset == 72
+
+
+def test_workspace_bytes(lib):
+    assert L.workspace_bytes(L.IDX_OP_SCORE, 4, 1000, 512) == 0
+    a = L.workspace_bytes(L.IDX_OP_TOPK, 4, 1000, 512)
+    b = L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 4, 1000, 512)
+    # score_topk also holds the logits: 4 rows x 1024 padded columns x 4 B
+    assert b - a == 4 * 1024 * 4
+    assert a >= 4 * 2048 * 4 + 4 * 512 * 8 + 4 * 1024 * 8
+    assert lib.idx_workspace_bytes(L.IDX_OP_TOPK, 1, 10, 0) == ctypes.c_size_t(-1).value
+    assert lib.idx_workspace_bytes(L.IDX_OP_TOPK, 1, 10, 2049) == ctypes.c_size_t(-1).value
+    assert lib.idx_workspace_bytes(7, 1, 10, 1) == ctypes.c_size_t(-1).value
+
+
+def _keys(**kw):
+    k = L.IdxKeys()
+    k.pool = kw.get("pool", 0x1000)
+    k.n_pool_rows = kw.get("n_pool_rows", 64)
+    k.block_size = kw.get("block_size", 64)
+    k.limits = kw.get("limits", 0x2000)
+    k.block_table = kw.get("block_table", None)
+    k.n_req = kw.get("n_req", 0)
+    k.max_blocks = kw.get("max_blocks", 0)
+    k.chunk_ids = kw.get("chunk_ids", None)
+    k.n_chunks = kw.get("n_chunks", None)
+    k.max_chunks = kw.get("max_chunks", 0)
+    return k
+
+
+def _score(lib, q=0x1000, w=0x1000, B=1, H=64, D=128, keys=None, n_cols=64, logits=0x3000):
+    keys = _keys() if keys is None else keys
+    return lib.idx_score(q, w, B, H, D, ctypes.byref(keys), n_cols, logits, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=32), L.IDX_E_SHAPE),
+    (dict(D=64), L.IDX_E_SHAPE),
+    (dict(B=-1), L.IDX_E_ARG),
+    (dict(n_cols=0), L.IDX_E_SHAPE),
+    (dict(q=None), L.IDX_E_ARG),
+    (dict(q=0x1004), L.IDX_E_ALIGN),
+    (dict(w=0x1008), L.IDX_E_ALIGN),
+    (dict(logits=None), L.IDX_E_ARG),
+    (dict(logits=0x3004), L.IDX_E_ALIGN),
+    (dict(keys=_keys(block_size=16)), L.IDX_E_SHAPE),
+    (dict(keys=_keys(pool=0x1001)), L.IDX_E_ALIGN),
+    (dict(keys=_keys(limits=None)), L.IDX_E_ARG),
+    (dict(keys=_keys(block_table=0x4000, n_req=0, max_blocks=4)), L.IDX_E_SHAPE),
+    (dict(keys=_keys(block_table=0x4000, n_req=1, max_blocks=4, n_pool_rows=100)), L.IDX_E_SHAPE),
+    (dict(keys=_keys(chunk_ids=0x5000, max_chunks=4)), L.IDX_E_ARG),
+    (dict(keys=_keys(chunk_ids=0x5000, n_chunks=0x6000, max_chunks=0)), L.IDX_E_SHAPE),
+])
+def test_score_rejects_bad_arguments(lib, kw, code):
+    assert _score(lib, **kw) == code
+    assert lib.idx_last_error() != b""
+
+
+def test_score_with_no_rows_is_a_no_op(lib):
+    assert _score(lib, B=0, q=None, w=None, logits=None) == L.IDX_OK
+
+
+def test_topk_rejects_bad_arguments(lib):
+    need = L.workspace_bytes(L.IDX_OP_TOPK, 2, 100, 8)
+    ok = dict(logits=0x1000, B=2, n_cols=100, ld=100, k=8, out_col=0x2000, out_val=None,
+              ws=0x10000, ws_bytes=need)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.idx_topk(a["logits"], a["B"], a["n_cols"], a["ld"], a["k"], a["out_col"],
+                            a["out_val"], a["ws"], a["ws_bytes"], None)
+    assert call(k=0) == L.IDX_E_SHAPE
+    assert call(k=2049) == L.IDX_E_SHAPE
+    assert call(ld=99) == L.IDX_E_SHAPE
+    assert call(n_cols=0) == L.IDX_E_SHAPE
+    assert call(ws_bytes=need - 1) == L.IDX_E_WORKSPACE
+    assert call(ws=None) == L.IDX_E_WORKSPACE
+    assert call(ws=0x10010) == L.IDX_E_ALIGN
+    assert call(out_col=None) == L.IDX_E_ARG
+    assert call(B=0) == L.IDX_OK
+
+
+def test_score_topk_rejects_small_workspace(lib):
+    keys = _keys()
+    need = L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 1, 64, 16)
+    rc = lib.idx_score_topk(0x1000, 0x1000, 1, 64, 128, ctypes.byref(keys), 64, 16, 0x2000, None,
+                            0x10000, need - 256, None)
+    assert rc == L.IDX_E_WORKSPACE
+    rc = lib.idx_score_topk(0x1000, 0x1000, 1, 64, 128, ctypes.byref(keys), 64, 4096, 0x2000, None,
+                            0x10000, need, None)
+    assert rc == L.IDX_E_SHAPE

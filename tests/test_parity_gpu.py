@@ -1,0 +1,276 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs are the seeded synthetic workloads; expected values come only from
+the oracle.  Logits must match to |g - o| <= 1e-4 + 2e-3 |o| (exactly -inf
+where unscored); integer-exact inputs must match bit for bit; top-k index
+work must be exact given the same fp32 values, and against the oracle's
+double logits may differ only at near-ties.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from sparse_attention_kv_paged_amd import lib as L
+from sparse_attention_kv_paged_amd import workloads as W
+from tests.parity import assert_logits_close, assert_topk_near_tie
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _entry_logit_fn(wl, ref_logits, rows=None):
+    """(b, entry ids) -> oracle logits, resolving chunk lists to columns."""
+    def f(b, ids):
+        ids = np.asarray(ids, dtype=np.int64)
+        if wl.chunk_ids is None:
+            cols = ids
+        else:
+            row = b if rows is None else rows[b]
+            pos = {int(c): j for j, c in enumerate(wl.chunk_ids[row])}
+            cols = np.array([pos[int(e) // 64] * 64 + int(e) % 64 for e in ids])
+        return ref_logits[b, cols]
+    return f
+
+
+def _gpu_logits(d, with_scores=False):
+    out = L.idx_score(d.q, d.w, d.keys, d.n_cols, with_scores=with_scores)
+    torch.cuda.synchronize()
+    if with_scores:
+        return out[0].cpu().numpy(), out[1].cpu().numpy()
+    return out.cpu().numpy()
+
+
+def _check_workload(wl, rows=None, check_topk=True, tag=""):
+    """Full comparison on all rows (or oracle on a row subset)."""
+    _log(f"[parity] {tag} {wl.name}: {wl.description} rows={'all' if rows is None else len(rows)}")
+    d = L.to_device(wl)
+    g_logits, g_scores = _gpu_logits(d, with_scores=True)
+    ref = oracle.score(wl, rows=rows)
+    sel = slice(None) if rows is None else np.asarray(rows)
+    assert_logits_close(g_logits[sel], ref, f"{wl.name} logits")
+    # sigmoid scores: 0 where unscored, else close to the oracle's
+    ref_sc = np.where(ref == -np.inf, 0.0, 1.0 / (1.0 + np.exp(-np.where(ref == -np.inf, 0, ref))))
+    err = np.abs(g_scores[sel] - ref_sc)
+    assert np.all(err <= 1e-4 + 2e-3 * ref_sc), f"{wl.name} scores: worst {err.max():.3e}"
+    if not check_topk:
+        return
+    g_idx, g_val = L.idx_score_topk(d.q, d.w, d.keys, d.n_cols, wl.k)
+    torch.cuda.synchronize()
+    g_idx, g_val = g_idx.cpu().numpy(), g_val.cpu().numpy()
+    # (1) same precision as the kernel: exact top-k of the GPU's own logits
+    own_cols, own_vals = oracle.topk(g_logits.astype(np.float64), wl.k)
+    own_ids = oracle.cols_to_entries(wl, own_cols)
+    assert np.array_equal(g_idx, own_ids), f"{wl.name}: score_topk != top-k of its own logits"
+    ok = own_cols >= 0
+    assert np.array_equal(g_val[ok], own_vals[ok].astype(np.float32))
+    # (2) idx_topk on the same logits: columns, bit-exact
+    t_cols, t_vals = L.idx_topk(torch.from_numpy(g_logits).cuda(), wl.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(t_cols.cpu().numpy(), own_cols), f"{wl.name}: idx_topk columns differ"
+    # (3) against the oracle's double logits: equal up to near-ties
+    ref_cols, _ = oracle.topk(ref, wl.k)
+    ref_ids = oracle.cols_to_entries(wl, ref_cols, rows=rows)
+    assert_topk_near_tie(g_idx[sel], ref_ids, _entry_logit_fn(wl, ref, rows), wl.k, wl.name)
+
+
+# --------------------------------------------------------------- exactness
+
+def test_fp8_decode_table_on_device():
+    """Each of the 254 finite e4m3fn bytes decodes exactly: row r holds byte r
+    at d = 0; q[:, 0] = 1, w = e_0, so logit = relu(s * e4m3(r)); scales +1
+    and -1 recover positive and negative values."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    q = np.zeros((1, 64, 128), dtype=np.float32)
+    q[0, :, 0] = 1.0
+    w = np.zeros((1, 64), dtype=np.float32)
+    w[0, 0] = 1.0
+    got = {}
+    for s in (1.0, -1.0):
+        f8 = np.zeros((256, 128), dtype=np.uint8)
+        f8[:, 0] = np.arange(256)
+        pool = np.zeros((256, 132), dtype=np.uint8)
+        pool[:, :128] = f8
+        pool[:, 128:] = np.array([s], "<f4").view(np.uint8)
+        wl = W.Workload(name="fp8", q=W.bf16_bits(q), w=w, pool=pool,
+                        limits=np.array([256], np.int32), n_cols=256)
+        got[s] = _gpu_logits(L.to_device(wl))[0]
+    fin = ~np.isnan(ref)
+    dec = np.where(ref > 0, got[1.0], -got[-1.0])
+    assert np.array_equal(dec[fin & (ref != 0)], ref[fin & (ref != 0)])
+    assert np.all(got[1.0][ref == 0] == 0) and np.all(got[-1.0][ref == 0] == 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_integer_case_is_bit_exact(seed):
+    """Small-integer keys, bf16 integer queries, power-of-two weights and
+    scales: every partial sum is exact, so GPU == oracle bit for bit."""
+    rng = np.random.default_rng(seed)
+    n, B = 64 * 5 + 17, 3
+    kv = rng.integers(-4, 5, size=(n, 128)).astype(np.float32)
+    scales = np.ldexp(1.0, rng.integers(-2, 3, size=n)).astype(np.float32)
+    scales[rng.random(n) < 0.2] *= -1                       # negative scales too
+    pool = np.zeros((n, 132), dtype=np.uint8)
+    pool[:, :128] = W.e4m3_bytes(kv)
+    pool[:, 128:] = scales.astype("<f4").view(np.uint8).reshape(n, 4)
+    q = rng.integers(-2, 3, size=(B, 64, 128)).astype(np.float32)
+    w = (rng.choice([-1.0, 1.0], size=(B, 64)) * np.ldexp(1.0, rng.integers(-3, 4, size=(B, 64)))).astype(np.float32)
+    wl = W.Workload(name="int", q=W.bf16_bits(q), w=w, pool=pool,
+                    limits=np.array([n, n - 40, 70], np.int32), n_cols=n + 30)
+    g = _gpu_logits(L.to_device(wl))
+    ref = oracle.score(wl)
+    assert np.array_equal(g.astype(np.float64), ref)
+
+
+# --------------------------------------------------------------- workloads
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_small_workloads(cfg):
+    _check_workload(W.small_config(cfg), tag=f"small{cfg}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 4])
+def test_full_size_workloads(cfg):
+    _check_workload(W.config(cfg), tag=f"full{cfg}")
+
+
+def test_full_size_prefill_sampled_rows():
+    """4096-row prefill: the oracle scores a spread of rows (first, last, and
+    rows around block boundaries of the causal bound)."""
+    wl = W.config(3)
+    rows = sorted({0, 1, 2, 3, 63, 64, 65, 255, 256, 1023, 2047, 2048, 3000, 4092, 4093, 4094, 4095}
+                  | set(np.random.default_rng(3).integers(0, 4096, 15).tolist()))
+    _check_workload(wl, rows=rows, tag="full3")
+
+
+# --------------------------------------------------------------- edge cases
+
+def _small_paged(seed=7, entries=(700, 64, 1, 129, 2048)):
+    return W.paged_decode(list(entries), seed=seed, max_blocks=40, k=512, name="edge")
+
+
+def test_ragged_rows_fewer_entries_than_k():
+    wl = _small_paged()
+    _check_workload(wl, tag="edge-ragged")
+    d = L.to_device(wl)
+    idx, _ = L.idx_score_topk(d.q, d.w, d.keys, d.n_cols, wl.k)
+    idx = idx.cpu().numpy()
+    assert np.all(idx[1, 64:] == -1) and np.all(idx[2, 1:] == -1)      # 64 and 1 entries
+
+
+def test_padding_rows_holes_and_status_bits():
+    wl = _small_paged()
+    wl.q_req = np.arange(wl.B, dtype=np.int32)
+    wl.q_req[3] = -1                                           # padding row
+    wl.block_table = wl.block_table.copy()
+    wl.block_table[0, 2] = -1                                  # hole
+    _check_workload(wl, tag="edge-padding")
+    # out-of-range ids are absent and flagged
+    wl2 = _small_paged()
+    wl2.block_table = wl2.block_table.copy()
+    wl2.block_table[4, 5] = 10 ** 6                            # past the pool
+    wl2.limits = wl2.limits.copy()
+    wl2.limits[0] = 10 ** 7                                    # above capacity
+    wl2.q_req = np.arange(wl2.B, dtype=np.int32)
+    wl2.q_req[1] = 99                                          # no such request
+    d = L.to_device(wl2, status=True)
+    g = L.idx_score(d.q, d.w, d.keys, d.n_cols).cpu().numpy()
+    st = int(d.keys.status.cpu().item())
+    assert st & L.STATUS_BAD_BLOCK and st & L.STATUS_LIMIT_CLAMPED and st & L.STATUS_BAD_REQUEST
+    wl2.block_table[4, 5] = -1                                 # what "absent" means
+    wl2.q_req[1] = -1
+    assert_logits_close(g, oracle.score(wl2), "status case")
+
+
+def test_zero_limits_and_unaligned_columns():
+    wl = _small_paged(entries=(0, 5, 191))
+    wl.n_cols = 200                                            # not a multiple of 64
+    _check_workload(wl, tag="edge-limits")
+
+
+def test_degenerate_all_equal_logits_ties_go_to_low_columns():
+    """w = 0 makes every scored logit 0: the top-k is the k lowest scored
+    columns (ties resolved by column)."""
+    wl = W.small_config(2)
+    wl.w = np.zeros_like(wl.w)
+    _check_workload(wl, tag="edge-ties")
+    d = L.to_device(wl)
+    idx, val = L.idx_score_topk(d.q, d.w, d.keys, d.n_cols, 512)
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(512, dtype=np.int32), (wl.B, 1)))
+    assert np.all(val.cpu().numpy() == 0)
+
+
+@pytest.mark.parametrize("k", [1, 7, 512, 2048])
+def test_k_values(k):
+    wl = W.small_config(1)
+    wl.k = k
+    _check_workload(wl, tag=f"k{k}")
+
+
+def test_negative_and_zero_scales():
+    wl = W.small_config(0)
+    sc = wl.pool[:, 128:].copy().view("<f4")
+    rng = np.random.default_rng(5)
+    sc[rng.random(len(sc)) < 0.3] *= -1
+    sc[rng.random(len(sc)) < 0.05] = 0.0
+    wl.pool[:, 128:] = sc.view(np.uint8)
+    _check_workload(wl, tag="edge-scales")
+
+
+def test_contiguous_chunk_list():
+    """Chunk lists over a contiguous pool (no block table)."""
+    base = W.contiguous(64 * 20, B=3, seed=9)
+    rng = np.random.default_rng(9)
+    chunk_ids = np.stack([rng.choice(20, 6, replace=False) for _ in range(3)]).astype(np.int32)
+    chunk_ids[1, 4] = -1                                       # absent chunk
+    wl = W.Workload(name="contig-chunks", q=base.q, w=base.w, pool=base.pool,
+                    limits=np.array([64 * 20, 64 * 10, 64 * 20 - 3], np.int32), n_cols=6 * 64,
+                    k=100, chunk_ids=chunk_ids, n_chunks=np.array([6, 5, 6], np.int32))
+    _check_workload(wl, tag="edge-contig-chunks")
+
+
+def test_topk_standalone_exact_with_ties_nan_and_signed_zero():
+    rng = np.random.default_rng(1)
+    B, n, k = 5, 70000, 512
+    vals = rng.integers(-50, 50, size=(B, n)).astype(np.float32) / 8    # heavy ties
+    vals[rng.random((B, n)) < 0.1] = -np.inf
+    vals[rng.random((B, n)) < 0.01] = np.nan
+    vals[0, :100] = -0.0
+    vals[1] = -np.inf
+    vals[1, [5, 9]] = [1.0, 1.0]
+    vals[2] = rng.standard_normal(n).astype(np.float32)
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = oracle.topk(vals.astype(np.float64), k)
+    assert np.array_equal(cols.cpu().numpy(), ref_cols)
+    ok = ref_cols >= 0
+    assert np.array_equal(v.cpu().numpy()[ok], ref_v[ok].astype(np.float32))
+
+
+def test_repeat_runs_are_bitwise_identical():
+    wl = W.small_config(4)
+    d = L.to_device(wl)
+    first = [x.cpu().numpy() for x in L.idx_score_topk(d.q, d.w, d.keys, d.n_cols, wl.k)]
+    lg0 = L.idx_score(d.q, d.w, d.keys, d.n_cols).cpu().numpy()
+    for _ in range(20):
+        again = [x.cpu().numpy() for x in L.idx_score_topk(d.q, d.w, d.keys, d.n_cols, wl.k)]
+        assert all(np.array_equal(a, b) for a, b in zip(first, again))
+        assert np.array_equal(L.idx_score(d.q, d.w, d.keys, d.n_cols).cpu().numpy(), lg0)
+
+
+def test_empty_batch():
+    wl = W.small_config(0)
+    d = L.to_device(wl)
+    L.idx_score(d.q[:0], d.w[:0], d.keys, d.n_cols)
+    idx, _ = L.idx_score_topk(d.q[:0], d.w[:0], d.keys, d.n_cols, 16)
+    assert idx.shape == (0, 16)
