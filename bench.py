@@ -184,12 +184,18 @@ def main():
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = max(wall * 1e3, gpu_ms) / K
+    print(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall * 1e3:.3f} ms, "
+          f"events {gpu_ms:.3f} ms)", file=sys.stderr, flush=True)
 
     # ---- score kernel duration, live: events recorded on the launch stream
     # around every score-kernel launch of K eager steps, queued behind a busy
     # wait so the queue never drains while the host enqueues
     n_ev = K
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for a, b in evs:            # create the hipEvents; the library re-records them
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
     torch.cuda._sleep(int(5e7))
     for i in range(n_ev):
         lib.idx_profile_events(*evs[i])

@@ -138,13 +138,14 @@ int idx_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
  *
  * logits   fp32 [B, ld] in (row stride ld >= n_cols); -inf and NaN entries
  *          are never selected.
- * out_col  int32 [B, k] out: selected columns, ordered by value descending,
- *          equal values by column ascending; rows with fewer than k
- *          selectable entries end in -1.
+ * out_col  int32 [B, k] out: the selected columns in ascending column
+ *          order; among equal values at the cut the lower columns win; rows
+ *          with fewer than k selectable entries end in -1.
  * out_val  fp32 [B, k] out or NULL: the selected values (-inf for -1).
  * workspace / ws_bytes: device scratch of at least
  *          idx_workspace_bytes(IDX_OP_TOPK, B, n_cols, k) bytes, 256-byte
- *          aligned; contents on entry do not matter.
+ *          aligned; contents on entry do not matter (the library keeps no
+ *          state in it between calls).
  */
 int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld,
              int32_t k, int32_t *out_col, float *out_val, void *workspace,
@@ -154,8 +155,9 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld,
  * idx_score_topk: the whole path: score every column as idx_score would,
  * then select the top-k of each row as idx_topk would.
  *
- * out_idx  int32 [B, k] out: LOGICAL entry ids (chunk lists resolved),
- *          ordered by logit descending, ties by column ascending; -1 pads.
+ * out_idx  int32 [B, k] out: LOGICAL entry ids (chunk lists resolved) of
+ *          the selected columns, in ascending column order; among equal
+ *          logits at the cut the lower columns win; -1 pads.
  * out_val  fp32 [B, k] out or NULL: their logits.
  * workspace / ws_bytes: at least
  *          idx_workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k) bytes.

@@ -37,29 +37,93 @@ bool aligned(const void *p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Workspace of the top-k pipeline, each piece 256-byte aligned.
-struct TopkLayout {
-    size_t logits, hist, counters, sure, cand, total;
-    int64_t ld, ldc;
+// Top-k launch plan and workspace, each workspace piece 256-byte aligned.
+//   level 0: segments of `cap0` logits per workgroup, `parts0` per row;
+//   level >= 1: merge up to kSegListCap / k lists per workgroup until one
+//   workgroup per row remains.  Lists ping-pong between two buffers.
+struct TopkPlan {
+    int cap0 = 0, parts0 = 0;
+    size_t logits = 0, row_cols = 0, list[2] = {0, 0}, cnt[2] = {0, 0}, total = 0;
+    int64_t ld = 0;
 };
 
-TopkLayout topk_layout(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
-    TopkLayout L{};
-    L.ld = round_up(std::max<int64_t>(n_cols, 1), 64);
-    L.ldc = L.ld;
+int seg_cap_for(int32_t n_cols) {
+    for (int c : {4096, 8192, 16384})
+        if (n_cols <= c) return c;
+    return idx::kSegLogitCap;
+}
+
+TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
+    TopkPlan P;
+    P.ld = round_up(std::max<int64_t>(n_cols, 1), 64);
+    P.cap0 = seg_cap_for(n_cols);
+    P.parts0 = (int)std::max<int64_t>(1, ((int64_t)n_cols + P.cap0 - 1) / P.cap0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
-        off += (size_t)round_up((int64_t)bytes, 256);
+        off += (size_t)round_up((int64_t)std::max<size_t>(bytes, 1), 256);
         return at;
     };
-    L.logits = with_logits ? take((size_t)B * L.ld * sizeof(float)) : 0;
-    L.hist = take((size_t)B * idx::kHistBins * sizeof(uint32_t));
-    L.counters = take((size_t)B * idx::kCounters * sizeof(uint32_t));
-    L.sure = take((size_t)B * k * sizeof(uint2));
-    L.cand = take((size_t)B * L.ldc * sizeof(uint2));
-    L.total = off;
-    return L;
+    if (with_logits) {
+        P.logits = take((size_t)B * P.ld * sizeof(float));
+        P.row_cols = take((size_t)B * sizeof(uint32_t));
+    }
+    if (P.parts0 > 1) {
+        const int per = std::max(1, idx::kSegListCap / k);
+        const int parts1 = (P.parts0 + per - 1) / per;
+        P.list[0] = take((size_t)B * P.parts0 * k * sizeof(uint2));
+        P.cnt[0] = take((size_t)B * P.parts0 * sizeof(uint32_t));
+        P.list[1] = take((size_t)B * parts1 * k * sizeof(uint2));
+        P.cnt[1] = take((size_t)B * parts1 * sizeof(uint32_t));
+    }
+    P.total = off;
+    return P;
+}
+
+// Enqueue the top-k launches for logits [B, ld] (row_cols optional).
+hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_t ld,
+                        const uint32_t *row_cols, int32_t B, int32_t n_cols, int32_t k,
+                        int32_t *out_idx, float *out_val, const int32_t *chunk_ids,
+                        int32_t max_chunks, hipStream_t s) {
+    idx::SegArgs a{};
+    a.B = B;
+    a.k = k;
+    a.logits = logits;
+    a.ld = ld;
+    a.n_cols = n_cols;
+    a.row_cols = row_cols;
+    a.parts = P.parts0;
+    a.out_idx = out_idx;
+    a.out_val = out_val;
+    a.chunk_ids = chunk_ids;
+    a.max_chunks = max_chunks;
+    if (P.parts0 == 1) return idx::launch_topk_segment(a, false, P.cap0, s);
+    a.out_list = reinterpret_cast<uint2 *>(ws + P.list[0]);
+    a.out_cnt = reinterpret_cast<uint32_t *>(ws + P.cnt[0]);
+    hipError_t e = idx::launch_topk_segment(a, false, P.cap0, s);
+    if (e != hipSuccess) return e;
+    const int per = std::max(1, idx::kSegListCap / k);
+    int in_parts = P.parts0, cur = 0;
+    while (true) {
+        idx::SegArgs m = a;
+        m.logits = nullptr;
+        m.row_cols = nullptr;
+        m.in_list = reinterpret_cast<const uint2 *>(ws + P.list[cur]);
+        m.in_cnt = reinterpret_cast<const uint32_t *>(ws + P.cnt[cur]);
+        m.in_parts = in_parts;
+        m.in_cap = k;
+        m.parts = (in_parts + per - 1) / per;
+        if (m.parts == 1) {
+            m.out_list = nullptr;
+            m.out_cnt = nullptr;
+            return idx::launch_topk_segment(m, true, idx::kSegListCap, s);
+        }
+        m.out_list = reinterpret_cast<uint2 *>(ws + P.list[cur ^ 1]);
+        m.out_cnt = reinterpret_cast<uint32_t *>(ws + P.cnt[cur ^ 1]);
+        if ((e = idx::launch_topk_segment(m, true, idx::kSegListCap, s)) != hipSuccess) return e;
+        in_parts = m.parts;
+        cur ^= 1;
+    }
 }
 
 int check_qw(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D) {
@@ -127,21 +191,6 @@ idx::ScoreArgs score_args(const uint16_t *q, const float *w, int32_t B, const id
     return a;
 }
 
-idx::TopkArgs topk_args(const TopkLayout &L, char *ws, int32_t B, int32_t n_cols, int32_t k) {
-    idx::TopkArgs t{};
-    t.B = B;
-    t.n_cols = n_cols;
-    t.k = k;
-    t.hist = reinterpret_cast<uint32_t *>(ws + L.hist);
-    t.counters = reinterpret_cast<uint32_t *>(ws + L.counters);
-    t.sure = reinterpret_cast<uint2 *>(ws + L.sure);
-    t.cand = reinterpret_cast<uint2 *>(ws + L.cand);
-    t.ldc = L.ldc;
-    t.cols_per_wg = 4096;
-    t.parts = (int32_t)std::max<int64_t>(1, ((int64_t)n_cols + t.cols_per_wg - 1) / t.cols_per_wg);
-    return t;
-}
-
 int hip_fail(hipError_t e, const char *what) {
     return fail(IDX_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -176,8 +225,8 @@ size_t idx_workspace_bytes(int32_t op, int32_t B, int32_t n_cols, int32_t k) {
     if (B < 0 || n_cols < 0 || (op != IDX_OP_SCORE && (k < 1 || k > idx::kMaxK))) return (size_t)-1;
     switch (op) {
     case IDX_OP_SCORE: return 0;
-    case IDX_OP_TOPK: return topk_layout(false, B, n_cols, k).total;
-    case IDX_OP_SCORE_TOPK: return topk_layout(true, B, n_cols, k).total;
+    case IDX_OP_TOPK: return topk_plan(false, B, n_cols, k).total;
+    case IDX_OP_SCORE_TOPK: return topk_plan(true, B, n_cols, k).total;
     default: return (size_t)-1;
     }
 }
@@ -209,23 +258,13 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t
     if (!logits || !out_col) return fail(IDX_E_ARG, "logits and out_col must be non-null");
     if (!aligned(logits, 4) || !aligned(out_col, 4) || !aligned(out_val, 4))
         return fail(IDX_E_ALIGN, "logits/out_col/out_val must be 4-byte aligned");
-    const TopkLayout L = topk_layout(false, B, n_cols, k);
-    if (!workspace || ws_bytes < L.total)
-        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+    const TopkPlan P = topk_plan(false, B, n_cols, k);
+    if (P.total > 0 && (!workspace || ws_bytes < P.total))
+        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
     if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
-    idx::TopkArgs t = topk_args(L, static_cast<char *>(workspace), B, n_cols, k);
-    t.logits = logits;
-    t.ld = ld;
-    t.out_col = out_col;
-    t.out_val = out_val;
-    t.set_cols = 1;
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    if ((e = idx::launch_topk_init(t, s)) != hipSuccess) return hip_fail(e, "top-k init");
-    if ((e = idx::launch_topk_hist(t, s)) != hipSuccess) return hip_fail(e, "top-k histogram");
-    if ((e = idx::launch_topk_select(t, s)) != hipSuccess) return hip_fail(e, "top-k select");
-    if ((e = idx::launch_topk_final(t, s)) != hipSuccess) return hip_fail(e, "top-k final");
-    return IDX_OK;
+    hipError_t e = enqueue_topk(P, static_cast<char *>(workspace), logits, ld, nullptr, B, n_cols, k,
+                                out_col, out_val, nullptr, 0, (hipStream_t)stream);
+    return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
 }
 
 int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D,
@@ -240,33 +279,22 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H, int3
     if (B == 0) return IDX_OK;
     if (!out_idx) return fail(IDX_E_ARG, "out_idx must be non-null");
     if (!aligned(out_idx, 4) || !aligned(out_val, 4)) return fail(IDX_E_ALIGN, "outputs must be 4-byte aligned");
-    const TopkLayout L = topk_layout(true, B, n_cols, k);
-    if (!workspace || ws_bytes < L.total)
-        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total, ws_bytes);
+    const TopkPlan P = topk_plan(true, B, n_cols, k);
+    if (P.total > 0 && (!workspace || ws_bytes < P.total))
+        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
     if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
     char *ws = static_cast<char *>(workspace);
-    idx::TopkArgs t = topk_args(L, ws, B, n_cols, k);
-    t.logits = reinterpret_cast<const float *>(ws + L.logits);
-    t.ld = L.ld;
-    t.out_col = out_idx;
-    t.out_val = out_val;
-    t.chunk_ids = keys->chunk_ids;
-    t.max_chunks = keys->max_chunks;
-    t.map_entries = 1;
-    t.set_cols = 0;
     idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
-    a.ld = L.ld;
-    a.logits = reinterpret_cast<float *>(ws + L.logits);
+    a.ld = P.ld;
+    a.logits = reinterpret_cast<float *>(ws + P.logits);
     a.scores = nullptr;
-    a.hist = t.hist;
-    a.counters = t.counters;
+    a.row_cols = reinterpret_cast<uint32_t *>(ws + P.row_cols);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if ((e = idx::launch_topk_init(t, s)) != hipSuccess) return hip_fail(e, "top-k init");
     if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
-    if ((e = idx::launch_topk_select(t, s)) != hipSuccess) return hip_fail(e, "top-k select");
-    if ((e = idx::launch_topk_final(t, s)) != hipSuccess) return hip_fail(e, "top-k final");
-    return IDX_OK;
+    e = enqueue_topk(P, ws, a.logits, P.ld, a.row_cols, B, n_cols, k, out_idx, out_val,
+                     keys->chunk_ids, keys->max_chunks, s);
+    return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
 }
 
 }  // extern "C"

@@ -13,14 +13,9 @@ constexpr int kHeadDim = 128;
 constexpr int kBlock = 64;                   // entries per paged block
 constexpr int kRowBytes = kHeadDim + 4;      // 128 e4m3 bytes + fp32 scale
 constexpr int kWaves = 4;                    // waves per score workgroup
-constexpr int kHistBits = 11;                // first-level top-k histogram
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kHistShift = 32 - kHistBits;
 constexpr int kMaxK = 2048;
-constexpr int kCounters = 4;                 // per row: sure, cand, cols, spare
-
-// Per-row counters in the top-k workspace.
-enum { kCntSure = 0, kCntCand = 1, kCntCols = 2 };
+constexpr int kSegLogitCap = 32768;          // logits per top-k workgroup
+constexpr int kSegListCap = 16384;           // (key, column) items per merge workgroup
 
 struct ScoreArgs {
     const uint16_t *q;          // [B, 64, 128] bf16
@@ -41,39 +36,42 @@ struct ScoreArgs {
     int64_t ld;                 // output row stride (floats)
     float *logits;              // [B, ld]
     float *scores;              // [B, ld] or null
-    // top-k mode (hist != null): histogram + per-row counters, and only the
-    // row's own columns are written
-    uint32_t *hist;             // [B, kHistBins]
-    uint32_t *counters;         // [B, kCounters]
+    // top-k feed (row_cols != null): only each row's own columns are written
+    // (those below 64 x its tile-list length) and that count goes to row_cols
+    uint32_t *row_cols;         // [B]
     int32_t slots_per_wave;
     int32_t splits;             // workgroups per row
 };
 
-struct TopkArgs {
+// One launch of the segment top-k (idx_topk.hip).  Input is either a logits
+// matrix cut into `parts` segments of the kernel's capacity per row, or the
+// per-part (key, column) lists of a previous launch; output is either lists
+// (out_list != null) or the final ids.
+struct SegArgs {
+    int32_t B;
+    int32_t k;
+    int32_t parts;              // workgroups per row
+    // logits input
     const float *logits;        // [B, ld]
     int64_t ld;
-    int32_t B;
     int32_t n_cols;
-    int32_t k;
-    uint32_t *hist;             // [B, kHistBins]
-    uint32_t *counters;         // [B, kCounters]
-    uint2 *sure;                // [B, k]      (key, column)
-    uint2 *cand;                // [B, ldc]    (key, column)
-    int64_t ldc;
-    int32_t cols_per_wg;        // select/hist kernels: columns per workgroup
-    int32_t parts;              // workgroups per row
-    int32_t *out_col;           // [B, k]
+    const uint32_t *row_cols;   // [B] columns per row, or null (= n_cols)
+    // list input
+    const uint2 *in_list;       // [B, in_parts, in_cap]
+    const uint32_t *in_cnt;     // [B, in_parts]
+    int32_t in_parts;
+    int32_t in_cap;
+    // intermediate output
+    uint2 *out_list;            // [B, parts, k] or null
+    uint32_t *out_cnt;          // [B, parts]
+    // final output
+    int32_t *out_idx;           // [B, k]
     float *out_val;             // [B, k] or null
-    const int32_t *chunk_ids;   // map columns to entries (score_topk), or null
+    const int32_t *chunk_ids;   // columns -> logical entries, or null
     int32_t max_chunks;
-    int32_t map_entries;        // 1: write logical entry ids
-    int32_t set_cols;           // init kernel: counters[b][kCntCols] = n_cols
 };
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
-hipError_t launch_topk_init(const TopkArgs &a, hipStream_t s);
-hipError_t launch_topk_hist(const TopkArgs &a, hipStream_t s);
-hipError_t launch_topk_select(const TopkArgs &a, hipStream_t s);
-hipError_t launch_topk_final(const TopkArgs &a, hipStream_t s);
+hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, hipStream_t s);
 
 }  // namespace idx

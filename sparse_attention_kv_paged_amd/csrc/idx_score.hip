@@ -138,10 +138,43 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t d0, uint32_t d1) {
     return __builtin_bit_cast(bf16x8, o);
 }
 
-template <bool TOPK>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-    __shared__ uint32_t sh_hist[TOPK ? kHistBins : 1];
+__device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), lane);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
+// One 32-entry tile: MFMA contraction, relu / head-weight / head-sum epilogue,
+// scale and bound.  Returns the logit of entry (lane & 31) on every lane.
+__device__ __forceinline__ float score_tile(KeyHalf k, const bf16x8 (&qa)[2][8],
+                                            const float (&wr)[2][16], int e, int limit) {
+    // relu(s x) = |s| relu(sign(s) x): flip the fp8 signs of rows with s < 0
+    if (__any(k.s < 0.f)) {
+        const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k.v[i] ^= u32x4{m, m, m, m};
+    }
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const u32x4 &v = k.v[kk >> 1];
+        const bf16x8 kb = (kk & 1) ? fp8x8_to_bf16x8(v.z, v.w) : fp8x8_to_bf16x8(v.x, v.y);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kk], kb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kk], kb, acc1, 0, 0, 0);
+    }
+    float T = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc0[i], 0.f), wr[0][i], T);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc1[i], 0.f), wr[1][i], T);
+    T += __shfl_xor(T, 32, 64);
+    return e < limit ? fabsf(k.s) * T : -__builtin_inff();
+}
+
+constexpr int kRing = 3;   // key tiles in flight per wave
+
+template <bool OWN_COLS>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int b = blockIdx.x / a.splits;
     const int split = blockIdx.x - b * a.splits;
     const int wave = threadIdx.x >> 6;
@@ -152,119 +185,99 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     uint32_t st = 0;
     const RowCtx r = row_context(a, b, st);
     const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
-    const int col_end = TOPK ? min(r.nslots * kBlock, a.n_cols) : a.n_cols;
-    const int slot_stop = TOPK ? min(r.nslots, slot_cols) : slot_cols;
-
-    if (TOPK) {
-        for (int i = threadIdx.x; i < kHistBins; i += 256) sh_hist[i] = 0u;
-        if (split == 0 && threadIdx.x == 0)
-            a.counters[(int64_t)b * kCounters + kCntCols] = (uint32_t)max(col_end, 0);
-        __syncthreads();
-    }
+    // OWN_COLS: write only the columns the row's tile list can reach (the
+    // top-k reads exactly those); otherwise every column up to n_cols.
+    const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
+    const int slot_stop = OWN_COLS ? min(r.nslots, slot_cols) : slot_cols;
+    if (OWN_COLS && split == 0 && threadIdx.x == 0) a.row_cols[b] = (uint32_t)col_end;
 
     const int slot0 = (split * kWaves + wave) * a.slots_per_wave;
     const int slot_end = min(slot0 + a.slots_per_wave, slot_stop);
+    if (slot0 >= slot_end) {
+        if (st && a.status && lane == 0) atomicOr(a.status, st);
+        return;
+    }
     float *out_row = a.logits + (int64_t)b * a.ld;
     float *score_row = a.scores ? a.scores + (int64_t)b * a.ld : nullptr;
+    const bool live = r.req >= 0 && slot0 < r.nslots;
+    const int64_t last_row = a.n_pool_rows - 1;
 
-    if (slot0 < slot_end) {
-        // Resident operands: q[b] (A fragments) and the head weights matching
-        // this lane's accumulator rows.
-        bf16x8 qa[2][8];
-        float wr[2][16];
-        const bool live = r.req >= 0 && slot0 < r.nslots;
-        if (live) {
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                const u32x4 *qp = reinterpret_cast<const u32x4 *>(
-                    a.q + ((int64_t)b * kHeads + 32 * hb + n32) * kHeadDim + 64 * hf);
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
-                // accumulator register i holds head 32*hb + 8*(i/4) + 4*hf + i%4
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 wv = *reinterpret_cast<const float4 *>(
-                        a.w + (int64_t)b * kHeads + 32 * hb + 8 * g + 4 * hf);
-                    wr[hb][4 * g + 0] = wv.x;
-                    wr[hb][4 * g + 1] = wv.y;
-                    wr[hb][4 * g + 2] = wv.z;
-                    wr[hb][4 * g + 3] = wv.w;
-                }
-            }
+    // Block-table resolution, 64 slots at a time: lane j resolves slot j of
+    // the current group with vector loads; tiles read it back with readlane.
+    int cached_group = -1;
+    int64_t lane_prow0 = -1;
+    int32_t lane_ebase = 0;
+    auto slot_info = [&](int j, int64_t &prow0, int32_t &ebase) {
+        const int grp = (j - slot0) >> 6;
+        if (grp != cached_group) {
+            cached_group = grp;
+            const int js = slot0 + (grp << 6) + lane;
+            lane_prow0 = -1;
+            lane_ebase = 0;
+            if (live && js < slot_end) lane_prow0 = resolve_slot(a, r, b, js, lane_ebase, st);
         }
+        const int src = (j - slot0) & 63;
+        prow0 = readlane64(lane_prow0, src);
+        ebase = __builtin_amdgcn_readlane(lane_ebase, src);
+    };
 
-        const int ntiles = 2 * (slot_end - slot0);
-        int32_t ebase_cur = 0;
-        int64_t prow0_cur = live ? resolve_slot(a, r, b, slot0, ebase_cur, st) : -1;
-        const int64_t last_row = a.n_pool_rows - 1;
-        KeyHalf kv_cur;
-        if (prow0_cur >= 0) kv_cur = load_key_half(a.pool, min(prow0_cur + n32, last_row), hf);
-
-        for (int tau = 0; tau < ntiles; ++tau) {
-            const int slot = slot0 + (tau >> 1);
-            const int t = tau & 1;
-            // prefetch the next tile
-            int32_t ebase_nxt = ebase_cur;
-            int64_t prow0_nxt = prow0_cur;
-            KeyHalf kv_nxt;
-            if (tau + 1 < ntiles) {
-                if (t == 1) prow0_nxt = live ? resolve_slot(a, r, b, slot + 1, ebase_nxt, st) : -1;
-                if (prow0_nxt >= 0) {
-                    const int tn = (tau + 1) & 1;
-                    kv_nxt = load_key_half(a.pool, min(prow0_nxt + 32 * tn + n32, last_row), hf);
-                }
+    // Resident operands: q[b] (A fragments) and the head weights matching
+    // this lane's accumulator rows.
+    bf16x8 qa[2][8];
+    float wr[2][16];
+    if (live) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+                a.q + ((int64_t)b * kHeads + 32 * hb + n32) * kHeadDim + 64 * hf);
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+            // accumulator register i holds head 32*hb + 8*(i/4) + 4*hf + i%4
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 wv = *reinterpret_cast<const float4 *>(
+                    a.w + (int64_t)b * kHeads + 32 * hb + 8 * g + 4 * hf);
+                wr[hb][4 * g + 0] = wv.x;
+                wr[hb][4 * g + 1] = wv.y;
+                wr[hb][4 * g + 2] = wv.z;
+                wr[hb][4 * g + 3] = wv.w;
             }
-
-            const int col = slot * kBlock + 32 * t + n32;
-            float logit = -__builtin_inff();
-            if (prow0_cur >= 0) {
-                KeyHalf k = kv_cur;
-                // relu(s x) = |s| relu(sign(s) x): flip fp8 signs for s < 0
-                if (__any(k.s < 0.f)) {
-                    const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) k.v[i] ^= u32x4{m, m, m, m};
-                }
-                f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const u32x4 &v = k.v[kk >> 1];
-                    const bf16x8 kb = (kk & 1) ? fp8x8_to_bf16x8(v.z, v.w) : fp8x8_to_bf16x8(v.x, v.y);
-                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kk], kb, acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kk], kb, acc1, 0, 0, 0);
-                }
-                float T = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc0[i], 0.f), wr[0][i], T);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc1[i], 0.f), wr[1][i], T);
-                T += __shfl_xor(T, 32, 64);
-                const int e = ebase_cur + 32 * t + n32;
-                if (e < r.limit) logit = fabsf(k.s) * T;
-            }
-            if (hf == 0 && col < col_end) {
-                out_row[col] = logit;
-                if (score_row) score_row[col] = 1.0f / (1.0f + expf(-logit));
-                if (TOPK) {
-                    const uint32_t key = order_key(logit);
-                    if (key) atomicAdd(&sh_hist[key >> kHistShift], 1u);
-                }
-            }
-            kv_cur = kv_nxt;
-            prow0_cur = prow0_nxt;
-            ebase_cur = ebase_nxt;
         }
     }
 
-    if (TOPK) {
-        __syncthreads();
-        uint32_t *gh = a.hist + (int64_t)b * kHistBins;
-        for (int i = threadIdx.x; i < kHistBins; i += 256) {
-            const uint32_t c = sh_hist[i];
-            if (c) atomicAdd(gh + i, c);
+    const int ntiles = 2 * (slot_end - slot0);
+    // ring of kRing tiles in flight: tile tau lives in ring slot tau % kRing
+    KeyHalf kv[kRing];
+    int64_t prow_t[kRing];
+    int32_t ebase_t[kRing];
+    auto issue = [&](int tau, KeyHalf &dst, int64_t &prow0, int32_t &ebase) {
+        prow0 = -1;
+        ebase = 0;
+        if (tau >= ntiles) return;
+        slot_info(slot0 + (tau >> 1), prow0, ebase);
+        if (prow0 >= 0) dst = load_key_half(a.pool, min(prow0 + 32 * (tau & 1) + n32, last_row), hf);
+    };
+    auto consume = [&](int tau, const KeyHalf &src, int64_t prow0, int32_t ebase) {
+        if (tau >= ntiles) return;
+        const int t = tau & 1;
+        const int col = (slot0 + (tau >> 1)) * kBlock + 32 * t + n32;
+        float logit = -__builtin_inff();
+        if (prow0 >= 0) logit = score_tile(src, qa, wr, ebase + 32 * t + n32, r.limit);
+        if (hf == 0 && col < col_end) {
+            out_row[col] = logit;
+            if (score_row) score_row[col] = 1.0f / (1.0f + expf(-logit));
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i, kv[i], prow_t[i], ebase_t[i]);
+    for (int base = 0; base < ntiles; base += kRing) {
+#pragma unroll
+        for (int i = 0; i < kRing; ++i) {
+            consume(base + i, kv[i], prow_t[i], ebase_t[i]);
+            issue(base + i + kRing, kv[i], prow_t[i], ebase_t[i]);
         }
     }
-    if (st && a.status && lane == 0) atomicOr(a.status, st);
+    if (st && a.status) atomicOr(a.status, st);
 }
 
 }  // namespace
@@ -272,7 +285,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
     const int64_t grid = (int64_t)a.B * a.splits;
     if (grid <= 0) return hipSuccess;
-    if (a.hist)
+    if (a.row_cols)
         hipLaunchKernelGGL(score_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(score_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, a);

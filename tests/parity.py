@@ -51,3 +51,18 @@ def assert_topk_near_tie(gpu_idx, ref_idx, ref_logit_of_entry, k, what=""):
         far = np.abs(lg - t) > tol
         assert not far.any(), (f"{what} row {b}: {far.sum()} differing ids are not near-ties "
                                f"(k-th {t:.6g}, offending {lg[far][:4]})")
+
+
+def column_order(cols, vals=None):
+    """Reorder each row's selected columns ascending (-1 padding last), the
+    order the GPU top-k writes; the oracle lists them by value."""
+    cols = np.asarray(cols)
+    out_c = np.full_like(cols, -1)
+    out_v = None if vals is None else np.full(np.shape(vals), -np.inf, dtype=np.asarray(vals).dtype)
+    for b in range(cols.shape[0]):
+        sel = np.nonzero(cols[b] >= 0)[0]
+        order = sel[np.argsort(cols[b][sel], kind="stable")]
+        out_c[b, :len(order)] = cols[b][order]
+        if vals is not None:
+            out_v[b, :len(order)] = np.asarray(vals)[b][order]
+    return (out_c, out_v) if vals is not None else out_c

@@ -48,11 +48,15 @@ def test_keys_struct_layout_matches_header():
 
 def test_workspace_bytes(lib):
     assert L.workspace_bytes(L.IDX_OP_SCORE, 4, 1000, 512) == 0
-    a = L.workspace_bytes(L.IDX_OP_TOPK, 4, 1000, 512)
-    b = L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 4, 1000, 512)
-    # score_topk also holds the logits: 4 rows x 1024 padded columns x 4 B
-    assert b - a == 4 * 1024 * 4
-    assert a >= 4 * 2048 * 4 + 4 * 512 * 8 + 4 * 1024 * 8
+    # rows that fit one top-k workgroup need no scratch of their own
+    assert L.workspace_bytes(L.IDX_OP_TOPK, 4, 1000, 512) == 0
+    # score_topk holds the logits (4 rows x 1024 padded columns x 4 B) and
+    # one column count per row, each piece 256-byte aligned
+    assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 4, 1000, 512) == 4 * 1024 * 4 + 256
+    # long rows: per-part (key, column) lists of k items and their counts
+    parts = -(-262144 // 32768)
+    need = L.workspace_bytes(L.IDX_OP_TOPK, 8, 262144, 512)
+    assert need >= 8 * parts * 512 * 8 + 8 * 512 * 8
     assert lib.idx_workspace_bytes(L.IDX_OP_TOPK, 1, 10, 0) == ctypes.c_size_t(-1).value
     assert lib.idx_workspace_bytes(L.IDX_OP_TOPK, 1, 10, 2049) == ctypes.c_size_t(-1).value
     assert lib.idx_workspace_bytes(7, 1, 10, 1) == ctypes.c_size_t(-1).value
@@ -118,6 +122,9 @@ def test_topk_rejects_bad_arguments(lib):
     assert call(k=2049) == L.IDX_E_SHAPE
     assert call(ld=99) == L.IDX_E_SHAPE
     assert call(n_cols=0) == L.IDX_E_SHAPE
+    assert need == 0
+    need = L.workspace_bytes(L.IDX_OP_TOPK, 2, 100000, 8)
+    ok.update(n_cols=100000, ld=100000, ws_bytes=need)
     assert call(ws_bytes=need - 1) == L.IDX_E_WORKSPACE
     assert call(ws=None) == L.IDX_E_WORKSPACE
     assert call(ws=0x10010) == L.IDX_E_ALIGN

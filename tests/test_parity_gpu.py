@@ -13,7 +13,7 @@ import torch
 from oracle import oracle
 from sparse_attention_kv_paged_amd import lib as L
 from sparse_attention_kv_paged_amd import workloads as W
-from tests.parity import assert_logits_close, assert_topk_near_tie
+from tests.parity import assert_logits_close, assert_topk_near_tie, column_order
 
 pytestmark = pytest.mark.gpu
 
@@ -69,7 +69,7 @@ def _check_workload(wl, rows=None, check_topk=True, tag=""):
     torch.cuda.synchronize()
     g_idx, g_val = g_idx.cpu().numpy(), g_val.cpu().numpy()
     # (1) same precision as the kernel: exact top-k of the GPU's own logits
-    own_cols, own_vals = oracle.topk(g_logits.astype(np.float64), wl.k)
+    own_cols, own_vals = column_order(*oracle.topk(g_logits.astype(np.float64), wl.k))
     own_ids = oracle.cols_to_entries(wl, own_cols)
     assert np.array_equal(g_idx, own_ids), f"{wl.name}: score_topk != top-k of its own logits"
     ok = own_cols >= 0
@@ -180,15 +180,15 @@ def test_padding_rows_holes_and_status_bits():
     wl2.block_table = wl2.block_table.copy()
     wl2.block_table[4, 5] = 10 ** 6                            # past the pool
     wl2.limits = wl2.limits.copy()
-    wl2.limits[0] = 10 ** 7                                    # above capacity
+    wl2.limits[1] = 10 ** 7            # above capacity (row 1 holds one full block)
     wl2.q_req = np.arange(wl2.B, dtype=np.int32)
-    wl2.q_req[1] = 99                                          # no such request
+    wl2.q_req[3] = 99                                          # no such request
     d = L.to_device(wl2, status=True)
     g = L.idx_score(d.q, d.w, d.keys, d.n_cols).cpu().numpy()
     st = int(d.keys.status.cpu().item())
     assert st & L.STATUS_BAD_BLOCK and st & L.STATUS_LIMIT_CLAMPED and st & L.STATUS_BAD_REQUEST
     wl2.block_table[4, 5] = -1                                 # what "absent" means
-    wl2.q_req[1] = -1
+    wl2.q_req[3] = -1
     assert_logits_close(g, oracle.score(wl2), "status case")
 
 
@@ -251,7 +251,7 @@ def test_topk_standalone_exact_with_ties_nan_and_signed_zero():
     vals[2] = rng.standard_normal(n).astype(np.float32)
     cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
     torch.cuda.synchronize()
-    ref_cols, ref_v = oracle.topk(vals.astype(np.float64), k)
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
     assert np.array_equal(cols.cpu().numpy(), ref_cols)
     ok = ref_cols >= 0
     assert np.array_equal(v.cpu().numpy()[ok], ref_v[ok].astype(np.float32))
@@ -274,3 +274,19 @@ def test_empty_batch():
     L.idx_score(d.q[:0], d.w[:0], d.keys, d.n_cols)
     idx, _ = L.idx_score_topk(d.q[:0], d.w[:0], d.keys, d.n_cols, 16)
     assert idx.shape == (0, 16)
+
+
+@pytest.mark.parametrize("n,k", [(300000, 2048), (100000, 7), (40000, 512), (4096, 4096 // 8)])
+def test_topk_standalone_multilevel(n, k):
+    """Rows longer than one top-k workgroup: per-part lists merged over one or
+    more further launches (300000 columns at k=2048 needs three levels)."""
+    rng = np.random.default_rng(n + k)
+    B = 3
+    vals = rng.standard_normal((B, n)).astype(np.float32)
+    vals[1, ::3] = -np.inf
+    vals[2, :] = np.round(vals[2, :] * 4) / 4                 # many exact ties
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    assert np.array_equal(cols.cpu().numpy(), ref_cols)
+    assert np.array_equal(v.cpu().numpy(), ref_v.astype(np.float32))
