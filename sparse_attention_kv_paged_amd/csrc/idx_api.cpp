@@ -47,16 +47,21 @@ struct TopkPlan {
     int64_t ld = 0;
 };
 
-int seg_cap_for(int32_t n_cols) {
+int seg_cap_for(int64_t cols) {
     for (int c : {4096, 8192, 16384})
-        if (n_cols <= c) return c;
+        if (cols <= c) return c;
     return idx::kSegLogitCap;
 }
 
+// Level-0 split: enough parts per row that the whole launch covers the GPU's
+// 256 CUs (few long rows), each part holding 4096..32768 columns.
 TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
     TopkPlan P;
     P.ld = round_up(std::max<int64_t>(n_cols, 1), 64);
-    P.cap0 = seg_cap_for(n_cols);
+    const int64_t want = std::max<int64_t>(1, (256 + std::max(B, 1) - 1) / std::max(B, 1));
+    const int64_t most = std::max<int64_t>(1, ((int64_t)n_cols + 4095) / 4096);
+    const int64_t parts = std::min(want, most);
+    P.cap0 = seg_cap_for(((int64_t)n_cols + parts - 1) / parts);
     P.parts0 = (int)std::max<int64_t>(1, ((int64_t)n_cols + P.cap0 - 1) / P.cap0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -113,10 +118,12 @@ hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_
         m.in_parts = in_parts;
         m.in_cap = k;
         m.parts = (in_parts + per - 1) / per;
+        // the small merge variant when a row's lists fit in 4096 items
+        const int cap = (int64_t)in_parts * k <= 4096 ? 4096 : idx::kSegListCap;
         if (m.parts == 1) {
             m.out_list = nullptr;
             m.out_cnt = nullptr;
-            return idx::launch_topk_segment(m, true, idx::kSegListCap, s);
+            return idx::launch_topk_segment(m, true, cap, s);
         }
         m.out_list = reinterpret_cast<uint2 *>(ws + P.list[cur ^ 1]);
         m.out_cnt = reinterpret_cast<uint32_t *>(ws + P.cnt[cur ^ 1]);
@@ -179,12 +186,13 @@ idx::ScoreArgs score_args(const uint16_t *q, const float *w, int32_t B, const id
     a.limits = keys->limits;
     a.status = keys->status;
     a.n_cols = n_cols;
-    // Launch shape: about 4096 waves over the whole problem, at most one
-    // workgroup per row (so q[b] is loaded once per wave and reused over
-    // `slots_per_wave` blocks).
+    // Launch shape: about one resident round of waves (256 CUs x 8 waves)
+    // over the whole problem, at most one workgroup per row, so each wave
+    // pays its start-up latency (bound, table, q) once and then streams
+    // `slots_per_wave` blocks with its ring of loads in flight.
     const int64_t slots = (n_cols + idx::kBlock - 1) / idx::kBlock;
     const int64_t total = (int64_t)B * slots;
-    int64_t spw = std::max<int64_t>(1, (total + 4095) / 4096);
+    int64_t spw = std::max<int64_t>(1, (total + 2047) / 2048);
     spw = std::min<int64_t>(spw, std::max<int64_t>(1, (slots + idx::kWaves - 1) / idx::kWaves));
     a.slots_per_wave = (int32_t)spw;
     a.splits = (int32_t)std::max<int64_t>(1, (slots + idx::kWaves * spw - 1) / (idx::kWaves * spw));

@@ -27,6 +27,8 @@
 // |s| * sum_h relu(x_h) w_h, which equals the definition because
 // relu(s x) = |s| relu(sign(s) x); for s < 0 the fp8 sign bits are flipped
 // before conversion (exact).
+#include <algorithm>
+
 #include "idx_device.h"
 #include "idx_internal.h"
 
@@ -73,17 +75,32 @@ __device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, int b, uint32_
     return r;
 }
 
+// The table reads of slot j, issued under bounds the host guarantees (j <
+// max_chunks, beta < max_blocks, req < n_req) and before the row's bound is
+// known, so they overlap the bound's own load.
+struct SlotRaw {
+    int64_t beta;   // logical block (chunk id), -1 if none
+    int64_t pblk;   // pool block from the table, -1 if none
+};
+
+__device__ __forceinline__ SlotRaw slot_raw(const ScoreArgs &a, int req, int b, int j) {
+    SlotRaw s{j, -1};
+    if (a.chunk_ids) s.beta = j < a.max_chunks ? a.chunk_ids[(int64_t)b * a.max_chunks + j] : -1;
+    if (a.block_table && req >= 0 && req < a.n_req && s.beta >= 0 && s.beta < a.max_blocks)
+        s.pblk = a.block_table[(int64_t)req * a.max_blocks + s.beta];
+    return s;
+}
+
 // First pool row of slot j of row b, or -1 when the slot's block is absent.
 // *ebase receives the logical entry id of the slot's first entry.
-__device__ __forceinline__ int64_t resolve_slot(const ScoreArgs &a, const RowCtx &r, int b,
+__device__ __forceinline__ int64_t resolve_slot(const ScoreArgs &a, const RowCtx &r, const SlotRaw &raw,
                                                 int j, int32_t &ebase, uint32_t &st) {
-    int64_t beta = j;
+    const int64_t beta = raw.beta;
     ebase = 0;
     if (r.req < 0 || j >= r.nslots) return -1;
     if (a.chunk_ids) {
-        beta = a.chunk_ids[(int64_t)b * a.max_chunks + j];
         if (beta < 0) {
-            if (beta != -1) st |= 0x8u;
+            if (beta != -1) st |= 0x8u;                   // IDX_STATUS_BAD_CHUNK
             return -1;
         }
         if (a.block_table ? beta >= a.max_blocks : beta * kBlock >= a.n_pool_rows) {
@@ -94,9 +111,9 @@ __device__ __forceinline__ int64_t resolve_slot(const ScoreArgs &a, const RowCtx
     ebase = (int32_t)(beta * kBlock);
     if (ebase >= r.limit) return -1;
     if (!a.block_table) return beta * kBlock;
-    const int64_t pblk = a.block_table[(int64_t)r.req * a.max_blocks + beta];
+    const int64_t pblk = raw.pblk;
     if (pblk < 0) {
-        if (pblk != -1) st |= 0x2u;                   // IDX_STATUS_BAD_BLOCK
+        if (pblk != -1) st |= 0x2u;                       // IDX_STATUS_BAD_BLOCK
         return -1;
     }
     if ((pblk + 1) * kBlock > a.n_pool_rows) {
@@ -111,17 +128,21 @@ struct KeyHalf {
     float s;      // the row's scale
 };
 
-__device__ __forceinline__ KeyHalf load_key_half(const uint8_t *pool, int64_t prow, int hf) {
-    const uint8_t *rp = pool + prow * kRowBytes;
-    const u32x4_a4 *p = reinterpret_cast<const u32x4_a4 *>(rp + 64 * hf);
-    KeyHalf k;
+// Buffer descriptor (gfx9 raw buffer, stride 0): accesses at byte offsets
+// >= `bytes` read 0 / are dropped without touching memory.  Every load and
+// store of the tile loop goes through one, so none of them sits behind a
+// branch and the compiler's wait counts stay exact across the ring.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// The lane's half row: 64 fp8 bytes at voff (row * 132 + 64 * hf) and the
+// scale at soff (row * 132 + 128) of the block described by r.
+__device__ __forceinline__ void load_key_half(KeyHalf &k, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        u32x4_a4 t = p[i];
-        k.v[i] = u32x4{t.x, t.y, t.z, t.w};
-    }
-    k.s = *reinterpret_cast<const float *>(rp + kHeadDim);
-    return k;
+    for (int i = 0; i < 4; ++i) k.v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, 0, 0);
+    k.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, soff, 0, 0));
 }
 
 // fp8 bytes [2*HI, 2*HI+1] of x -> two bf16 in one dword, exact (scale 1).
@@ -146,8 +167,10 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
 
 // One 32-entry tile: MFMA contraction, relu / head-weight / head-sum epilogue,
 // scale and bound.  Returns the logit of entry (lane & 31) on every lane.
-__device__ __forceinline__ float score_tile(KeyHalf k, const bf16x8 (&qa)[2][8],
-                                            const float (&wr)[2][16], int e, int limit) {
+// sh_w holds w[b]; accumulator register i of head block hb is head
+// 32*hb + 8*(i/4) + 4*hf + i%4, so lanes of one half read the same weights.
+__device__ __forceinline__ float score_tile(KeyHalf &k, const bf16x8 (&qa)[2][8],
+                                            const float *sh_w, int hf, int e, int limit) {
     // relu(s x) = |s| relu(sign(s) x): flip the fp8 signs of rows with s < 0
     if (__any(k.s < 0.f)) {
         const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
@@ -162,69 +185,57 @@ __device__ __forceinline__ float score_tile(KeyHalf k, const bf16x8 (&qa)[2][8],
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kk], kb, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kk], kb, acc1, 0, 0, 0);
     }
-    float T = 0.f;
+    // relu as a signed-integer max on the float's bits (negative floats,
+    // -0.0 included, have the sign bit set and become +0.0): one VALU op with
+    // no NaN canonicalisation; four partial sums break the FMA chain
+    const float4 *w4 = reinterpret_cast<const float4 *>(sh_w);
+    float Tp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc0[i], 0.f), wr[0][i], T);
+    for (int hb = 0; hb < 2; ++hb) {
+        const f32x16 &acc = hb ? acc1 : acc0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) T = fmaf(fmaxf(acc1[i], 0.f), wr[1][i], T);
+        for (int g = 0; g < 4; ++g) {
+            const float4 wv = w4[8 * hb + 2 * g + hf];
+            const float wg[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = __int_as_float(max(__float_as_int(acc[4 * g + e]), 0));
+                Tp[e] = fmaf(x, wg[e], Tp[e]);
+            }
+        }
+    }
+    float T = (Tp[0] + Tp[1]) + (Tp[2] + Tp[3]);
     T += __shfl_xor(T, 32, 64);
     return e < limit ? fabsf(k.s) * T : -__builtin_inff();
 }
 
-constexpr int kRing = 3;   // key tiles in flight per wave
+constexpr int kRing = 5;        // key tiles in flight per wave
+constexpr int kFlatRows = 512;  // rows up to which waves share work evenly
 
+__device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_t &st) {
+    RowCtx r = row_context(a, b, st);
+    // wave-uniform values stay in scalar registers, so the tile loop is
+    // uniform control flow and its loads stay in flight across iterations
+    r.req = __builtin_amdgcn_readfirstlane(r.req);
+    r.nslots = __builtin_amdgcn_readfirstlane(r.nslots);
+    r.limit = __builtin_amdgcn_readfirstlane(r.limit);
+    return r;
+}
+
+// Score slots [j0, j1) of row b with the calling wave.  sh_w is the wave's
+// own 64-float LDS slot for w[b].  Columns >= col_end are not written.
 template <bool OWN_COLS>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-    const int b = blockIdx.x / a.splits;
-    const int split = blockIdx.x - b * a.splits;
-    const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
+                                           int col_end, float *sh_w, uint32_t &st) {
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int n32 = lane & 31;
-
-    uint32_t st = 0;
-    const RowCtx r = row_context(a, b, st);
-    const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
-    // OWN_COLS: write only the columns the row's tile list can reach (the
-    // top-k reads exactly those); otherwise every column up to n_cols.
-    const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-    const int slot_stop = OWN_COLS ? min(r.nslots, slot_cols) : slot_cols;
-    if (OWN_COLS && split == 0 && threadIdx.x == 0) a.row_cols[b] = (uint32_t)col_end;
-
-    const int slot0 = (split * kWaves + wave) * a.slots_per_wave;
-    const int slot_end = min(slot0 + a.slots_per_wave, slot_stop);
-    if (slot0 >= slot_end) {
-        if (st && a.status && lane == 0) atomicOr(a.status, st);
-        return;
-    }
+    const bool live = r.req >= 0 && j0 < r.nslots;
     float *out_row = a.logits + (int64_t)b * a.ld;
     float *score_row = a.scores ? a.scores + (int64_t)b * a.ld : nullptr;
-    const bool live = r.req >= 0 && slot0 < r.nslots;
-    const int64_t last_row = a.n_pool_rows - 1;
 
-    // Block-table resolution, 64 slots at a time: lane j resolves slot j of
-    // the current group with vector loads; tiles read it back with readlane.
-    int cached_group = -1;
-    int64_t lane_prow0 = -1;
-    int32_t lane_ebase = 0;
-    auto slot_info = [&](int j, int64_t &prow0, int32_t &ebase) {
-        const int grp = (j - slot0) >> 6;
-        if (grp != cached_group) {
-            cached_group = grp;
-            const int js = slot0 + (grp << 6) + lane;
-            lane_prow0 = -1;
-            lane_ebase = 0;
-            if (live && js < slot_end) lane_prow0 = resolve_slot(a, r, b, js, lane_ebase, st);
-        }
-        const int src = (j - slot0) & 63;
-        prow0 = readlane64(lane_prow0, src);
-        ebase = __builtin_amdgcn_readlane(lane_ebase, src);
-    };
-
-    // Resident operands: q[b] (A fragments) and the head weights matching
-    // this lane's accumulator rows.
+    // Resident operands: q[b] (A fragments, registers) and w[b] (LDS).
     bf16x8 qa[2][8];
-    float wr[2][16];
     if (live) {
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
@@ -232,49 +243,147 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
                 a.q + ((int64_t)b * kHeads + 32 * hb + n32) * kHeadDim + 64 * hf);
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
-            // accumulator register i holds head 32*hb + 8*(i/4) + 4*hf + i%4
+        }
+        sh_w[lane] = a.w[(int64_t)b * kHeads + lane];
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // Slots go in groups of up to 64: lane j resolves slot j of the group
+    // (one vector load per table level), then the group's tiles stream
+    // through a ring of kRing tiles in flight.  Tiles of absent blocks and
+    // ring slots past the group's end get an empty descriptor (no traffic).
+    const __amdgpu_buffer_rsrc_t out_r = make_rsrc(out_row, (uint32_t)col_end * 4u);
+    const __amdgpu_buffer_rsrc_t sc_r =
+        make_rsrc(score_row ? score_row : out_row, score_row ? (uint32_t)col_end * 4u : 0u);
+    const uint32_t lane_row = (uint32_t)n32 * kRowBytes;
+    constexpr uint32_t kDrop = 0x7FFFFFF0u;            // an offset every descriptor rejects
+    for (int g0 = j0; g0 < j1; g0 += 64) {
+        const int gn = min(64, j1 - g0);
+        int32_t lane_ebase = 0;
+        int64_t lane_prow0 = -1;
+        if (live && lane < gn) lane_prow0 = resolve_slot(a, r, slot_raw(a, r.req, b, g0 + lane), g0 + lane,
+                                                         lane_ebase, st);
+        const int ntiles = 2 * gn;
+        KeyHalf kv[kRing];
+        int64_t prow_t[kRing];
+        int32_t ebase_t[kRing];
+        auto issue = [&](int tau, KeyHalf &dst, int64_t &prow0, int32_t &ebase) {
+            const int j = min(tau >> 1, gn - 1);
+            prow0 = tau < ntiles ? readlane64(lane_prow0, j) : -1;
+            ebase = __builtin_amdgcn_readlane(lane_ebase, j);
+            uint32_t bytes = 0;
+            const uint8_t *base = a.pool;
+            if (prow0 >= 0) {
+                base = a.pool + prow0 * kRowBytes;
+                bytes = (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - prow0) * kRowBytes;
+            }
+            const __amdgpu_buffer_rsrc_t kr = make_rsrc(base, bytes);
+            const uint32_t row = (uint32_t)(32 * (tau & 1)) * kRowBytes + lane_row;
+            load_key_half(dst, kr, row + 64u * (uint32_t)hf, row + (uint32_t)kHeadDim);
+        };
+        auto consume = [&](int tau, KeyHalf &src, int64_t prow0, int32_t ebase) {
+            const int t = tau & 1;
+            const int col = (g0 + (tau >> 1)) * kBlock + 32 * t + n32;
+            float logit = -__builtin_inff();
+            if (prow0 >= 0) logit = score_tile(src, qa, sh_w, hf, ebase + 32 * t + n32, r.limit);
+            const uint32_t off = (tau < ntiles && hf == 0) ? (uint32_t)col * 4u : kDrop;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, 0);
+            const float score = score_row ? 1.0f / (1.0f + expf(-logit)) : 0.f;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), sc_r, off, 0, 0);
+        };
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const float4 wv = *reinterpret_cast<const float4 *>(
-                    a.w + (int64_t)b * kHeads + 32 * hb + 8 * g + 4 * hf);
-                wr[hb][4 * g + 0] = wv.x;
-                wr[hb][4 * g + 1] = wv.y;
-                wr[hb][4 * g + 2] = wv.z;
-                wr[hb][4 * g + 3] = wv.w;
+        for (int i = 0; i < kRing; ++i) issue(i, kv[i], prow_t[i], ebase_t[i]);
+        for (int base = 0; base < ntiles; base += kRing) {
+#pragma unroll
+            for (int i = 0; i < kRing; ++i) {
+                consume(base + i, kv[i], prow_t[i], ebase_t[i]);
+                issue(base + i + kRing, kv[i], prow_t[i], ebase_t[i]);
             }
         }
     }
+}
 
-    const int ntiles = 2 * (slot_end - slot0);
-    // ring of kRing tiles in flight: tile tau lives in ring slot tau % kRing
-    KeyHalf kv[kRing];
-    int64_t prow_t[kRing];
-    int32_t ebase_t[kRing];
-    auto issue = [&](int tau, KeyHalf &dst, int64_t &prow0, int32_t &ebase) {
-        prow0 = -1;
-        ebase = 0;
-        if (tau >= ntiles) return;
-        slot_info(slot0 + (tau >> 1), prow0, ebase);
-        if (prow0 >= 0) dst = load_key_half(a.pool, min(prow0 + 32 * (tau & 1) + n32, last_row), hf);
-    };
-    auto consume = [&](int tau, const KeyHalf &src, int64_t prow0, int32_t ebase) {
-        if (tau >= ntiles) return;
-        const int t = tau & 1;
-        const int col = (slot0 + (tau >> 1)) * kBlock + 32 * t + n32;
-        float logit = -__builtin_inff();
-        if (prow0 >= 0) logit = score_tile(src, qa, wr, ebase + 32 * t + n32, r.limit);
-        if (hf == 0 && col < col_end) {
-            out_row[col] = logit;
-            if (score_row) score_row[col] = 1.0f / (1.0f + expf(-logit));
+// OWN_COLS: write only the columns each row's tile list can reach (what the
+// top-k reads; the count goes to row_cols), else every column up to n_cols.
+// FLAT: the (row, slot) work of all rows is flattened and split evenly over
+// every wave of the grid (rows of very different lengths); otherwise each
+// workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
+template <bool OWN_COLS, bool FLAT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
+    __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
+    __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
+    __shared__ uint32_t sh_scan[kWaves];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int lane = threadIdx.x & 63;
+    const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
+    uint32_t st = 0;
+
+    if (!FLAT) {
+        const int b = blockIdx.x / a.splits;
+        const int split = blockIdx.x - b * a.splits;
+        const RowCtx r = uniform_row(a, b, st);
+        const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
+        const int slot_stop = OWN_COLS ? min(r.nslots, slot_cols) : slot_cols;
+        if (OWN_COLS && split == 0 && threadIdx.x == 0) a.row_cols[b] = (uint32_t)col_end;
+        const int j0 = (split * kWaves + wave) * a.slots_per_wave;
+        const int j1 = min(j0 + a.slots_per_wave, slot_stop);
+        if (j0 < j1) score_span<OWN_COLS>(a, b, j0, j1, r, col_end, sh_w[wave], st);
+    } else {
+        // per-row work (slots) and its prefix over rows, in LDS
+        uint32_t st_rows = 0;
+        int32_t cnt[2] = {0, 0};
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int row = 2 * threadIdx.x + k2;
+            if (row < a.B) {
+                const RowCtx rr = row_context(a, row, st_rows);
+                cnt[k2] = OWN_COLS ? max(0, min(rr.nslots, slot_cols)) : slot_cols;
+                if (OWN_COLS && blockIdx.x == 0)
+                    a.row_cols[row] = (uint32_t)max(0, min(rr.nslots * kBlock, a.n_cols));
+            }
         }
-    };
+        if (blockIdx.x == 0) st |= st_rows;
+        // block exclusive scan of the pairs
+        uint32_t v = (uint32_t)(cnt[0] + cnt[1]);
+        uint32_t incl = v;
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) issue(i, kv[i], prow_t[i], ebase_t[i]);
-    for (int base = 0; base < ntiles; base += kRing) {
-#pragma unroll
-        for (int i = 0; i < kRing; ++i) {
-            consume(base + i, kv[i], prow_t[i], ebase_t[i]);
-            issue(base + i + kRing, kv[i], prow_t[i], ebase_t[i]);
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t o = __shfl_up(incl, d, 64);
+            if (lane >= d) incl += o;
+        }
+        if (lane == 63) sh_scan[wave] = incl;
+        __syncthreads();
+        uint32_t add = 0;
+        for (int i = 0; i < wave; ++i) add += sh_scan[i];
+        const uint32_t excl = incl - v + add;
+        if (2 * (int)threadIdx.x < a.B) sh_pre[2 * threadIdx.x] = (int32_t)excl;
+        if (2 * (int)threadIdx.x + 1 < a.B) sh_pre[2 * threadIdx.x + 1] = (int32_t)(excl + cnt[0]);
+        if (threadIdx.x == 255) sh_pre[a.B] = (int32_t)(incl + add);
+        __syncthreads();
+
+        const int total = __builtin_amdgcn_readfirstlane(sh_pre[a.B]);
+        const int nw = (int)gridDim.x * kWaves;
+        const int chunk = (total + nw - 1) / nw;
+        int f = ((int)blockIdx.x * kWaves + wave) * chunk;
+        const int fend = min(f + chunk, total);
+        if (f < fend) {
+            // first row whose work range contains f
+            int lo = 0, hi = a.B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sh_pre[mid] <= f) lo = mid; else hi = mid - 1;
+            }
+            int b = __builtin_amdgcn_readfirstlane(lo);
+            while (f < fend) {
+                const int pb = __builtin_amdgcn_readfirstlane(sh_pre[b]);
+                const int pe = __builtin_amdgcn_readfirstlane(sh_pre[b + 1]);
+                if (pe > f) {
+                    const RowCtx r = uniform_row(a, b, st);
+                    const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
+                    score_span<OWN_COLS>(a, b, f - pb, min(fend, pe) - pb, r, col_end, sh_w[wave], st);
+                    f = min(fend, pe);
+                }
+                ++b;
+            }
         }
     }
     if (st && a.status) atomicOr(a.status, st);
@@ -283,12 +392,24 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 }  // namespace
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
-    const int64_t grid = (int64_t)a.B * a.splits;
-    if (grid <= 0) return hipSuccess;
-    if (a.row_cols)
-        hipLaunchKernelGGL(score_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL(score_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, a);
+    if (a.B <= 0) return hipSuccess;
+    const bool own = a.row_cols != nullptr;
+    if (a.B <= kFlatRows) {
+        // one resident round: up to 2 workgroups per CU, never more waves
+        // than (row, slot) pairs
+        const int64_t slots = (a.n_cols + kBlock - 1) / kBlock;
+        const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(512, ((int64_t)a.B * slots + kWaves - 1) / kWaves));
+        if (own)
+            hipLaunchKernelGGL((score_kernel<true, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((score_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    } else {
+        const int64_t grid = (int64_t)a.B * a.splits;
+        if (own)
+            hipLaunchKernelGGL((score_kernel<true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((score_kernel<false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 
