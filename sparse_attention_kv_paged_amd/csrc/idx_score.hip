@@ -234,9 +234,16 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     float *out_row = a.logits + (int64_t)b * a.ld;
     float *score_row = a.scores ? a.scores + (int64_t)b * a.ld : nullptr;
 
-    // Resident operands: q[b] (A fragments, registers) and w[b] (LDS).
+    // Start-up reads, issued back to back in the order they are needed (the
+    // vector memory counter retires in order): w[b], the first group's
+    // block-table entries, then q[b] -- resolving the table then leaves q in
+    // flight, and the first ring of key loads goes out before q is waited on.
+    float w_lane = 0.f;
+    SlotRaw raw0{-1, -1};
     bf16x8 qa[2][8];
     if (live) {
+        w_lane = a.w[(int64_t)b * kHeads + lane];
+        if (lane < min(64, j1 - j0)) raw0 = slot_raw(a, r.req, b, j0 + lane);
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
             const u32x4 *qp = reinterpret_cast<const u32x4 *>(
@@ -244,9 +251,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
         }
-        sh_w[lane] = a.w[(int64_t)b * kHeads + lane];
     }
-    __builtin_amdgcn_wave_barrier();
 
     // Slots go in groups of up to 64: lane j resolves slot j of the group
     // (one vector load per table level), then the group's tiles stream
@@ -261,8 +266,9 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         const int gn = min(64, j1 - g0);
         int32_t lane_ebase = 0;
         int64_t lane_prow0 = -1;
-        if (live && lane < gn) lane_prow0 = resolve_slot(a, r, slot_raw(a, r.req, b, g0 + lane), g0 + lane,
-                                                         lane_ebase, st);
+        if (live && lane < gn)
+            lane_prow0 = resolve_slot(a, r, g0 == j0 ? raw0 : slot_raw(a, r.req, b, g0 + lane), g0 + lane,
+                                      lane_ebase, st);
         const int ntiles = 2 * gn;
         KeyHalf kv[kRing];
         int64_t prow_t[kRing];
@@ -293,6 +299,10 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         };
 #pragma unroll
         for (int i = 0; i < kRing; ++i) issue(i, kv[i], prow_t[i], ebase_t[i]);
+        if (g0 == j0) {
+            sh_w[lane] = w_lane;                        // w[b] into the wave's LDS slot
+            __builtin_amdgcn_wave_barrier();
+        }
         for (int base = 0; base < ntiles; base += kRing) {
 #pragma unroll
             for (int i = 0; i < kRing; ++i) {
@@ -312,6 +322,7 @@ template <bool OWN_COLS, bool FLAT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
     __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
+    __shared__ int32_t sh_rreq[FLAT ? kFlatRows : 1], sh_rlim[FLAT ? kFlatRows : 1], sh_rslots[FLAT ? kFlatRows : 1];
     __shared__ uint32_t sh_scan[kWaves];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
@@ -336,6 +347,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int row = 2 * threadIdx.x + k2;
             if (row < a.B) {
                 const RowCtx rr = row_context(a, row, st_rows);
+                sh_rreq[row] = rr.req;
+                sh_rlim[row] = rr.limit;
+                sh_rslots[row] = rr.nslots;
                 cnt[k2] = OWN_COLS ? max(0, min(rr.nslots, slot_cols)) : slot_cols;
                 if (OWN_COLS && blockIdx.x == 0)
                     a.row_cols[row] = (uint32_t)max(0, min(rr.nslots * kBlock, a.n_cols));
@@ -377,7 +391,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 const int pb = __builtin_amdgcn_readfirstlane(sh_pre[b]);
                 const int pe = __builtin_amdgcn_readfirstlane(sh_pre[b + 1]);
                 if (pe > f) {
-                    const RowCtx r = uniform_row(a, b, st);
+                    RowCtx r;
+                    r.req = __builtin_amdgcn_readfirstlane(sh_rreq[b]);
+                    r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
+                    r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
                     const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
                     score_span<OWN_COLS>(a, b, f - pb, min(fend, pe) - pb, r, col_end, sh_w[wave], st);
                     f = min(fend, pe);
