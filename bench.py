@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 SCORE_SOURCES = ["sparse_attention_kv_paged_amd/csrc/idx_score.hip",
                  "sparse_attention_kv_paged_amd/csrc/idx_device.h",
@@ -57,23 +58,101 @@ def algorithmic_bytes(wl, pairs: int) -> int:
     return keys + extra
 
 
+def _read_kv(path):
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, _, val = line.partition("=")
+            kv[key.strip()] = val.strip()
+    return kv
+
+
 def read_traffic(workload: str):
     """HBM bytes per score-kernel launch from the committed rocprofv3 counter
     summary, or None if absent or taken on a different kernel source."""
     path = os.path.join(PROFILE_DIR, f"score_kernel_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
-    kv = {}
-    for line in open(path):
-        if "=" in line and not line.lstrip().startswith("#"):
-            key, _, val = line.partition("=")
-            kv[key.strip()] = val.strip()
+    kv = _read_kv(path)
     if kv.get("score_source_hash") != score_source_hash():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def summarize_trace(trace_dir, workload, command, out):
+    """Kernel-time summary of a `rocprofv3 --kernel-trace --stats
+    --output-format csv` run, as text for profiles/."""
+    rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel statistics, workload {workload}",
+             f"# command: {command}",
+             f"score_source_hash = {score_source_hash()}",
+             f"{'kernel':72s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share':>6s}"]
+    for r in rows:
+        lines.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.3f} "
+                     f"{float(r['MinNs'])/1e3:10.3f} {float(r['MaxNs'])/1e3:10.3f} {float(r['Percentage']):6.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, command, out):
+    """HBM traffic per score-kernel launch from two counter runs (FETCH_SIZE,
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+    for the 1 GiB device copy that `--copy-calibration` runs (1 GiB read and
+    1 GiB written per dispatch)."""
+    def per_kernel(dirpath, counter):
+        vals = {}
+        for r in _csv_rows(_find(dirpath, "counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        score = [v for (n, _), v in vals.items() if "score_kernel" in n]
+        copy = [v for (n, _), v in vals.items() if "copy" in n.lower() and v > 5e5]
+        return score, copy
+    import statistics
+    fs, fc = per_kernel(fetch_dir, "FETCH_SIZE")
+    ws, wc = per_kernel(write_dir, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    fetch_scale = gib_kib / statistics.median(fc)
+    write_scale = gib_kib / statistics.median(wc)
+    fetch_b = statistics.median(fs) * 1024 * fetch_scale
+    write_b = statistics.median(ws) * 1024 * write_scale
+    lines = [f"# rocprofv3 HBM counters for the score kernel, workload {workload}",
+             f"# command: {command}",
+             f"# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by the same",
+             f"# counter's reading for a 1 GiB device copy (1 GiB read, 1 GiB written).",
+             f"score_source_hash = {score_source_hash()}",
+             f"score_dispatches = {len(fs)}",
+             f"fetch_kib_per_launch_raw = {statistics.median(fs):.1f}",
+             f"write_kib_per_launch_raw = {statistics.median(ws):.1f}",
+             f"copy_fetch_kib_raw = {statistics.median(fc):.1f}",
+             f"copy_write_kib_raw = {statistics.median(wc):.1f}",
+             f"fetch_scale = {fetch_scale:.4f}",
+             f"write_scale = {write_scale:.4f}",
+             f"fetch_bytes_per_launch = {fetch_b:.0f}",
+             f"write_bytes_per_launch = {write_b:.0f}",
+             f"hbm_bytes_per_launch = {fetch_b + write_b:.0f}"]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(wl, pairs: int, min_seconds: float):
@@ -105,7 +184,20 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=2.0)
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run N plain device copies of 1 GiB (for HBM counter scaling)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="write profiles/ summary of a kernel-trace run")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summary of FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.workload, args.command,
+                        os.path.join(PROFILE_DIR, f"score_topk_{args.workload}_trace.txt"))
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.command,
+                      os.path.join(PROFILE_DIR, f"score_kernel_{args.workload}_pmc.txt"))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
@@ -212,8 +304,19 @@ def main():
         torch.cuda.synchronize()
 
     algo = algorithmic_bytes(wl, pairs)
-    achieved = algo / (kern_ms * 1e-3) / 1e9
     traffic = read_traffic(args.workload)
+    if args.workload == "chunked-prefill":
+        # one request's keys are shared by every query: the contraction bounds it
+        flop = 2.0 * wl.H * wl.D * pairs
+        roofline = {"kernel": "score_kernel", "bound": "mfma",
+                    "achieved": flop / (kern_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "traffic": traffic, "algorithmic_flop": flop,
+                    "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+    else:
+        roofline = {"kernel": "score_kernel", "bound": "hbm",
+                    "achieved": algo / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "traffic": traffic, "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+    roofline["frac"] = roofline["achieved"] / roofline["peak"]
     out = {
         "metric": "indexer scored pairs/s + top-512 queries/s; % of HBM/MFMA peak, 1 MI355X",
         "value": pairs / (ms_per_step * 1e-3),
@@ -231,10 +334,8 @@ def main():
                    "block": wl.block_size, "k": k, "n_cols": wl.n_cols, "pairs": pairs,
                    "description": wl.description, "replicas": R, "graph": bool(graphs)},
         "queries_per_s": wl.B / (ms_per_step * 1e-3),
-        "hbm_frac_path": algo / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"kernel": "score_kernel<true>", "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "algorithmic_bytes": algo, "kernel_ms": kern_ms},
+        "path_hbm_frac": algo / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, pairs, args.cpu_seconds)
