@@ -39,13 +39,18 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Top-k launch plan and workspace, each workspace piece 256-byte aligned.
 //   level 0: segments of `cap0` logits per workgroup, `parts0` per row;
-//   level >= 1: merge up to kSegListCap / k lists per workgroup until one
+//   level >= 1: merge up to kSegListCap / list_cap(k) lists per workgroup until one
 //   workgroup per row remains.  Lists ping-pong between two buffers.
 struct TopkPlan {
     int cap0 = 0, parts0 = 0;
-    size_t logits = 0, row_cols = 0, list[2] = {0, 0}, cnt[2] = {0, 0}, total = 0;
+    bool fused = false;         // one launch: the row's last part merges the lists
+    size_t logits = 0, row_cols = 0, row_done = 0, list[2] = {0, 0}, total = 0;
     int64_t ld = 0;
 };
+
+// Items per merge list: k rounded up to even (the kernels pad every list
+// with never-selectable items to this length).
+int list_cap(int32_t k) { return (k + 1) & ~1; }
 
 int seg_cap_for(int64_t cols) {
     for (int c : {4096, 8192, 16384})
@@ -72,14 +77,15 @@ TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
     if (with_logits) {
         P.logits = take((size_t)B * P.ld * sizeof(float));
         P.row_cols = take((size_t)B * sizeof(uint32_t));
+        P.row_done = take((size_t)B * sizeof(uint32_t));
+        // the score kernel zeroes row_done, so score_topk can merge in place
+        P.fused = P.parts0 > 1 && P.cap0 <= 8192 && (int64_t)P.parts0 * list_cap(k) <= 2 * (int64_t)P.cap0;
     }
     if (P.parts0 > 1) {
-        const int per = std::max(1, idx::kSegListCap / k);
+        const int per = idx::kSegListCap / list_cap(k);
         const int parts1 = (P.parts0 + per - 1) / per;
-        P.list[0] = take((size_t)B * P.parts0 * k * sizeof(uint2));
-        P.cnt[0] = take((size_t)B * P.parts0 * sizeof(uint32_t));
-        P.list[1] = take((size_t)B * parts1 * k * sizeof(uint2));
-        P.cnt[1] = take((size_t)B * parts1 * sizeof(uint32_t));
+        P.list[0] = take((size_t)B * P.parts0 * list_cap(k) * sizeof(uint2));
+        P.list[1] = take((size_t)B * parts1 * list_cap(k) * sizeof(uint2));
     }
     P.total = off;
     return P;
@@ -102,32 +108,33 @@ hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_
     a.out_val = out_val;
     a.chunk_ids = chunk_ids;
     a.max_chunks = max_chunks;
-    if (P.parts0 == 1) return idx::launch_topk_segment(a, false, P.cap0, s);
+    if (P.parts0 == 1) return idx::launch_topk_segment(a, false, P.cap0, false, s);
     a.out_list = reinterpret_cast<uint2 *>(ws + P.list[0]);
-    a.out_cnt = reinterpret_cast<uint32_t *>(ws + P.cnt[0]);
-    hipError_t e = idx::launch_topk_segment(a, false, P.cap0, s);
+    if (P.fused) {
+        a.row_done = reinterpret_cast<uint32_t *>(ws + P.row_done);
+        return idx::launch_topk_segment(a, false, P.cap0, true, s);
+    }
+    hipError_t e = idx::launch_topk_segment(a, false, P.cap0, false, s);
     if (e != hipSuccess) return e;
-    const int per = std::max(1, idx::kSegListCap / k);
+    const int lcap = list_cap(k);
+    const int per = idx::kSegListCap / lcap;
     int in_parts = P.parts0, cur = 0;
     while (true) {
         idx::SegArgs m = a;
         m.logits = nullptr;
         m.row_cols = nullptr;
         m.in_list = reinterpret_cast<const uint2 *>(ws + P.list[cur]);
-        m.in_cnt = reinterpret_cast<const uint32_t *>(ws + P.cnt[cur]);
         m.in_parts = in_parts;
-        m.in_cap = k;
+        m.in_cap = lcap;
         m.parts = (in_parts + per - 1) / per;
         // the small merge variant when a row's lists fit in 4096 items
-        const int cap = (int64_t)in_parts * k <= 4096 ? 4096 : idx::kSegListCap;
+        const int cap = (int64_t)in_parts * lcap <= 4096 ? 4096 : idx::kSegListCap;
         if (m.parts == 1) {
             m.out_list = nullptr;
-            m.out_cnt = nullptr;
-            return idx::launch_topk_segment(m, true, cap, s);
+            return idx::launch_topk_segment(m, true, cap, false, s);
         }
         m.out_list = reinterpret_cast<uint2 *>(ws + P.list[cur ^ 1]);
-        m.out_cnt = reinterpret_cast<uint32_t *>(ws + P.cnt[cur ^ 1]);
-        if ((e = idx::launch_topk_segment(m, true, idx::kSegListCap, s)) != hipSuccess) return e;
+        if ((e = idx::launch_topk_segment(m, true, idx::kSegListCap, false, s)) != hipSuccess) return e;
         in_parts = m.parts;
         cur ^= 1;
     }
@@ -297,6 +304,7 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H, int3
     a.logits = reinterpret_cast<float *>(ws + P.logits);
     a.scores = nullptr;
     a.row_cols = reinterpret_cast<uint32_t *>(ws + P.row_cols);
+    a.row_done = reinterpret_cast<uint32_t *>(ws + P.row_done);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
     if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");

@@ -21,4 +21,14 @@ __device__ __forceinline__ float key_value(uint32_t key) {
     return __uint_as_float(u);
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads outside the range
+// return 0 and stores outside it are dropped, so bounds need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache-policy operand of buffer loads/stores: sc1 (device scope), i.e. the
+// access is coherent across the per-XCD L2 caches.
+constexpr int kDeviceCoherent = 16;
+
 }  // namespace idx

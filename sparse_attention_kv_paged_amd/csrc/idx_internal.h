@@ -39,6 +39,7 @@ struct ScoreArgs {
     // top-k feed (row_cols != null): only each row's own columns are written
     // (those below 64 x its tile-list length) and that count goes to row_cols
     uint32_t *row_cols;         // [B]
+    uint32_t *row_done;         // [B] zeroed here for the top-k's fused merge (or null)
     int32_t slots_per_wave;
     int32_t splits;             // workgroups per row
 };
@@ -56,14 +57,14 @@ struct SegArgs {
     int64_t ld;
     int32_t n_cols;
     const uint32_t *row_cols;   // [B] columns per row, or null (= n_cols)
-    // list input
+    // list input: in_parts lists of in_cap (= k) items per row, each padded
+    // with key 0 after its winners
     const uint2 *in_list;       // [B, in_parts, in_cap]
-    const uint32_t *in_cnt;     // [B, in_parts]
     int32_t in_parts;
     int32_t in_cap;
-    // intermediate output
+    // intermediate output (same layout)
     uint2 *out_list;            // [B, parts, k] or null
-    uint32_t *out_cnt;          // [B, parts]
+    uint32_t *row_done;         // [B] arrival counters of the fused merge (zeroed)
     // final output
     int32_t *out_idx;           // [B, k]
     float *out_val;             // [B, k] or null
@@ -72,6 +73,6 @@ struct SegArgs {
 };
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
-hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, hipStream_t s);
+hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused, hipStream_t s);
 
 }  // namespace idx

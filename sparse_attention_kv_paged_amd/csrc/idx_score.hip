@@ -128,13 +128,9 @@ struct KeyHalf {
     float s;      // the row's scale
 };
 
-// Buffer descriptor (gfx9 raw buffer, stride 0): accesses at byte offsets
-// >= `bytes` read 0 / are dropped without touching memory.  Every load and
-// store of the tile loop goes through one, so none of them sits behind a
-// branch and the compiler's wait counts stay exact across the ring.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
-}
+// Every load and store of the tile loop goes through a buffer descriptor
+// (make_rsrc), so none of them sits behind a branch and the compiler's wait
+// counts stay exact across the ring.
 
 // The lane's half row: 64 fp8 bytes at voff (row * 132 + 64 * hf) and the
 // scale at soff (row * 132 + 128) of the block described by r.
@@ -209,7 +205,11 @@ __device__ __forceinline__ float score_tile(KeyHalf &k, const bf16x8 (&qa)[2][8]
     return e < limit ? fabsf(k.s) * T : -__builtin_inff();
 }
 
-constexpr int kRing = 5;        // key tiles in flight per wave
+// Key tiles in flight per wave.  Two per wave over the whole grid already
+// keep more bytes in flight than HBM needs at its loaded latency; deeper
+// rings only lengthen the memory queues, which delays the dependent
+// block-table reads of the waves that start last.
+constexpr int kRing = 2;
 constexpr int kFlatRows = 512;  // rows up to which waves share work evenly
 
 __device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_t &st) {
@@ -335,7 +335,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const RowCtx r = uniform_row(a, b, st);
         const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
         const int slot_stop = OWN_COLS ? min(r.nslots, slot_cols) : slot_cols;
-        if (OWN_COLS && split == 0 && threadIdx.x == 0) a.row_cols[b] = (uint32_t)col_end;
+        if (OWN_COLS && split == 0 && threadIdx.x == 0) {
+            a.row_cols[b] = (uint32_t)col_end;
+            if (a.row_done) a.row_done[b] = 0u;
+        }
         const int j0 = (split * kWaves + wave) * a.slots_per_wave;
         const int j1 = min(j0 + a.slots_per_wave, slot_stop);
         if (j0 < j1) score_span<OWN_COLS>(a, b, j0, j1, r, col_end, sh_w[wave], st);
@@ -351,8 +354,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 sh_rlim[row] = rr.limit;
                 sh_rslots[row] = rr.nslots;
                 cnt[k2] = OWN_COLS ? max(0, min(rr.nslots, slot_cols)) : slot_cols;
-                if (OWN_COLS && blockIdx.x == 0)
+                if (OWN_COLS && blockIdx.x == 0) {
                     a.row_cols[row] = (uint32_t)max(0, min(rr.nslots * kBlock, a.n_cols));
+                    if (a.row_done) a.row_done[row] = 0u;
+                }
             }
         }
         if (blockIdx.x == 0) st |= st_rows;

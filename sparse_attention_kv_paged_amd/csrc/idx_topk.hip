@@ -21,8 +21,9 @@
 //      needed, lowest columns first) in column order: one block scan of the
 //      threads' winner and tie counts gives every thread its output offset.
 // A row longer than one segment is split into parts; each part keeps its own
-// top-k (key, column) list and a second launch merges the lists of a row the
-// same way (lists are concatenated in part order, so column order holds).
+// top-k (key, column) list and the lists of a row are merged the same way
+// (concatenated in part order, so column order holds): by the row's last part
+// in the same launch when the lists fit, else by further launches.
 // The result is deterministic and ordered by column.
 #include "idx_device.h"
 #include "idx_internal.h"
@@ -33,9 +34,10 @@ namespace {
 constexpr int kBins = 2048;
 
 // DPP controls (GFX9): row_shr:n = 0x110 + n, row_bcast:15, row_bcast:31.
+// Lanes the control leaves without a source keep `old`.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+__device__ __forceinline__ uint32_t dpp(uint32_t v, uint32_t old = 0u) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
@@ -50,16 +52,38 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
     return v;
 }
 
-// Inclusive scan over the NT threads of the workgroup; `sh` has NT/64 words.
+// Same pattern for max and min: lane 63 ends with the wave's result.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+    v = max(v, dpp<0x111, 0xF>(v));
+    v = max(v, dpp<0x112, 0xF>(v));
+    v = max(v, dpp<0x114, 0xF>(v));
+    v = max(v, dpp<0x118, 0xF>(v));
+    v = max(v, dpp<0x142, 0xA>(v));
+    v = max(v, dpp<0x143, 0xC>(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+    v = min(v, dpp<0x111, 0xF>(v, ~0u));
+    v = min(v, dpp<0x112, 0xF>(v, ~0u));
+    v = min(v, dpp<0x114, 0xF>(v, ~0u));
+    v = min(v, dpp<0x118, 0xF>(v, ~0u));
+    v = min(v, dpp<0x142, 0xA>(v, ~0u));
+    v = min(v, dpp<0x143, 0xC>(v, ~0u));
+    return v;
+}
+
+// Inclusive scan over the NT threads of the workgroup; `sh` has NT/64 words
+// and must not be written again before every thread has passed another
+// barrier.
 template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *sh) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     v = wave_scan(v);
+    if (NT == 64) return v;
     if (lane == 63) sh[wave] = v;
     __syncthreads();
     uint32_t add = 0;
     for (int i = 0; i < wave; ++i) add += sh[i];
-    __syncthreads();
     return v + add;
 }
 
@@ -96,38 +120,296 @@ __device__ void find_from_top(const uint32_t *h, int nbins, uint32_t need, int32
     __syncthreads();
 }
 
-// Value-linear bin of a selectable key (monotone non-decreasing in value).
-__device__ __forceinline__ int value_bin(uint32_t key, float vmin, float scale) {
-    if (scale == 0.f) return 0;
-    const float x = (key_value(key) - vmin) * scale;
-    return (int)fminf(floorf(x), (float)(kBins - 1));
+// LDS scratch of one selection by NT threads over at most CAND items.  The
+// histogram has 32 extra bins past kBins that absorb non-selectable items,
+// so the histogram's atomics need no branch.
+template <int NT, int CAND>
+struct SelScratch {
+    uint32_t cand[CAND];          // keys of the cut bin's members
+    uint32_t hist[kBins + 32];
+    uint32_t scan_a[NT / 64], scan_b[NT / 64];
+    uint32_t kmin[NT / 64], kmax[NT / 64];
+    uint32_t cnt[NT / 64];
+    int32_t res[2];
+    uint32_t cut[2];
+    uint32_t ncand;
+    uint32_t flag;
+};
+
+// What find_cut expects zeroed (the histogram and the member count); it sees
+// these stores through its first barrier.
+template <int NT, int CAND>
+__device__ __forceinline__ void sel_reset(SelScratch<NT, CAND> &sh) {
+    for (int i = threadIdx.x; i < kBins + 32; i += NT) sh.hist[i] = 0u;
+    if (threadIdx.x == 0) sh.ncand = 0u;
 }
 
-template <int CAP, bool LIST, int NT>
-__global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
-    constexpr int kW = NT / 64;                       // waves per workgroup
-    constexpr int kPer = CAP / NT;                    // items per thread
-    __shared__ uint32_t sh_cand[CAP];                 // keys of the cut bin's members
-    __shared__ uint32_t sh_hist[kBins];
-    __shared__ uint32_t sh_scan[kW];
-    __shared__ float sh_fmin[kW], sh_fmax[kW];
-    __shared__ uint32_t sh_cnt[kW];
-    __shared__ int32_t sh_res[2];
-    __shared__ uint32_t sh_cut[2];
-
+// The exact k-th largest key (kstar) among the items the workgroup holds in
+// registers (thread t: key[0..PER) of a column-ordered sequence; key 0 = not
+// selectable), how many of its copies win (need_ties, lowest columns first)
+// and the number of selectable items (total).  kstar = 0 when every
+// selectable item wins.  All threads call it, after sel_reset.
+//   1. count and key range of the selectable items;
+//   2. histogram of 2048 bins linear in value between min and max;
+//   3. the bin t holding the k-th largest value;
+//   4. t's members go to LDS; one wave ranks up to 64 of them against each
+//      other, larger bins take radix passes over their keys (bits 31:21,
+//      20:10, 9:0).
+template <int NT, int PER, int CAND>
+__device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k, SelScratch<NT, CAND> &sh,
+                                         uint32_t &kstar, uint32_t &need_ties, uint32_t &total) {
+    constexpr int kW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // 1. integer min/max of the order-preserving keys
+    uint32_t n_valid = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        n_valid += key[j] != 0u;
+        kmn = min(kmn, key[j] ? key[j] : 0xFFFFFFFFu);
+        kmx = max(kmx, key[j]);
+    }
+    n_valid = wave_scan(n_valid);
+    kmn = wave_min(kmn);
+    kmx = wave_max(kmx);
+    if (lane == 63) {
+        sh.cnt[wave] = n_valid;
+        sh.kmin[wave] = kmn;
+        sh.kmax[wave] = kmx;
+    }
+    __syncthreads();
+    total = 0;
+    kmn = 0xFFFFFFFFu;
+    kmx = 0u;
+    for (int w = 0; w < kW; ++w) {
+        total += sh.cnt[w];
+        kmn = min(kmn, sh.kmin[w]);
+        kmx = max(kmx, sh.kmax[w]);
+    }
+    kstar = 0u;
+    need_ties = 0u;
+    if (total <= k) return;                           // uniform
+
+    // 2. value-linear bins (monotone in value); other items go to the extra
+    // bins, 32 of them so that a wave's lanes hit distinct LDS banks
+    const float vmin = key_value(kmn), vmax = key_value(kmx);
+    float scale = 0.f;
+    const float range = vmax - vmin;
+    if (range > 0.f && range < __builtin_inff()) scale = (float)kBins / range;
+    if (!(scale < __builtin_inff())) scale = 0.f;
+    const auto bin_of = [&](uint32_t kj) {
+        const int x = __float2int_rz((key_value(kj) - vmin) * scale);        // >= 0 (NaN -> 0)
+        return kj ? min((uint32_t)x, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (lane & 31));
+    };
+    constexpr bool kKeep = PER <= 16;                 // else recomputed (registers)
+    uint32_t bins[kKeep ? PER : 1];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const uint32_t bn = bin_of(key[j]);
+        if (kKeep) bins[kKeep ? j : 0] = bn;
+        atomicAdd(&sh.hist[bn], 1u);
+    }
+    __syncthreads();
+    // 3.
+    find_from_top<NT>(sh.hist, kBins, k, sh.res, sh.scan_a);
+    const uint32_t cbin = (uint32_t)sh.res[0];
+    uint32_t rem = k - (uint32_t)sh.res[1];
+    const uint32_t n_in_bin = sh.hist[cbin];
+    // 4. the members' keys, in any order
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if ((kKeep ? bins[kKeep ? j : 0] : bin_of(key[j])) == cbin) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
+    __syncthreads();
+    if (n_in_bin <= 64u) {
+        if (wave == 0) {
+            const uint32_t my = lane < (int)n_in_bin ? sh.cand[lane] : 0u;
+            uint32_t greater = 0, equal = 0;
+            for (uint32_t j = 0; j < n_in_bin; ++j) {
+                const uint32_t other = (uint32_t)__builtin_amdgcn_readlane((int)my, (int)j);
+                greater += other > my;
+                equal += other == my;
+            }
+            if (lane < (int)n_in_bin && greater < rem && rem <= greater + equal) {
+                sh.cut[0] = my;                      // every such lane holds the same key
+                sh.cut[1] = rem - greater;
+            }
+        }
+        __syncthreads();
+        kstar = sh.cut[0];
+        need_ties = sh.cut[1];
+        return;
+    }
+    uint32_t prefix = 0u;
+    for (int stage = 0; stage < 3; ++stage) {
+        const int hi = stage == 0 ? 32 : (stage == 1 ? 21 : 10);
+        const int lo = stage == 0 ? 21 : (stage == 1 ? 10 : 0);
+        __syncthreads();
+        for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
+        __syncthreads();
+        const uint32_t mask = (1u << (hi - lo)) - 1u;
+        for (uint32_t c = tid; c < n_in_bin; c += NT) {
+            const uint32_t kk = sh.cand[c];
+            if (hi == 32 || (kk >> hi) == prefix) atomicAdd(&sh.hist[(kk >> lo) & mask], 1u);
+        }
+        __syncthreads();
+        find_from_top<NT>(sh.hist, kBins, rem, sh.res, sh.scan_a);
+        rem -= (uint32_t)sh.res[1];
+        prefix = (hi == 32 ? 0u : (prefix << (hi - lo))) | (uint32_t)sh.res[0];
+    }
+    kstar = prefix;
+    need_ties = rem;
+}
+
+constexpr uint32_t kLoses = 0xFFFFFFFFu;              // position of a slot that does not win
+constexpr uint32_t kDrop = 0x7FFFFFF0u;               // a byte offset every descriptor here rejects
+
+__device__ __forceinline__ uint32_t byte_off(uint32_t pos, uint32_t size) {
+    return pos == kLoses ? kDrop : pos * size;
+}
+
+// Output positions of a thread's register slots, visited in slot order:
+// the keys above kstar plus the first need_ties keys equal to it win.
+struct WinCursor {
+    uint32_t p, tie_ord, kstar, need_ties;
+    __device__ __forceinline__ uint32_t next(uint32_t key) {     // kLoses if it does not win
+        bool win = key > kstar;
+        if (kstar != 0u && key == kstar) win = tie_ord++ < need_ties;
+        const uint32_t r = win ? p : kLoses;
+        p += win;
+        return r;
+    }
+};
+
+// Winners numbered in column order from one block scan of packed
+// (winners | ties << 16) per thread: sets the thread's cursor.  All threads
+// call it; it leaves sh.scan_b in use until the next barrier.
+template <int NT, int PER, int CAND>
+__device__ __forceinline__ void scan_winners(const uint32_t (&key)[PER], uint32_t kstar, uint32_t need_ties,
+                                             SelScratch<NT, CAND> &sh, WinCursor &cur) {
+    uint32_t n_win = 0, n_tie = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        n_win += key[j] > kstar;
+        n_tie += kstar != 0u && key[j] == kstar;
+    }
+    const uint32_t packed = n_win | (n_tie << 16);
+    const uint32_t excl = block_scan<NT>(packed, sh.scan_b) - packed;
+    cur.tie_ord = excl >> 16;
+    cur.p = (excl & 0xFFFFu) + min(cur.tie_ord, need_ties);
+    cur.kstar = kstar;
+    cur.need_ties = need_ties;
+}
+
+// Final output of row b: the winners' logical entry ids (a column's chunk
+// resolved through chunk_ids) and values at their positions, -1 / -inf in
+// [count, k).  Every load and store goes through a buffer descriptor, none
+// behind a branch.
+template <int NT, int PER, class ColOf>
+__device__ __forceinline__ void write_final(const SegArgs &a, int b, WinCursor cur, const uint32_t (&key)[PER],
+                                            ColOf col, uint32_t count) {
+    const uint32_t k = (uint32_t)a.k;
+    int32_t *oi = a.out_idx + (int64_t)b * k;
+    float *ov = a.out_val ? a.out_val + (int64_t)b * k : nullptr;
+    const __amdgpu_buffer_rsrc_t ir = make_rsrc(oi, k * 4u);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(ov ? (void *)ov : (void *)oi, ov ? k * 4u : 0u);
+    // groups of 8 slots: their chunk lookups are in flight together
+    constexpr int kG = PER < 8 ? PER : 8;
+#pragma unroll
+    for (int g = 0; g < PER; g += kG) {
+        uint32_t e[kG], pos[kG];
+#pragma unroll
+        for (int j = 0; j < kG; ++j) pos[j] = cur.next(key[g + j]);
+        if (a.chunk_ids) {
+            const __amdgpu_buffer_rsrc_t cr =
+                make_rsrc(a.chunk_ids + (int64_t)b * a.max_chunks, (uint32_t)a.max_chunks * 4u);
+#pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                const uint32_t off = pos[j] == kLoses ? kDrop : (col(g + j) / kBlock) * 4u;
+                e[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, off, 0, 0) * kBlock + col(g + j) % kBlock;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kG; ++j) e[j] = col(g + j);
+        }
+#pragma unroll
+        for (int j = 0; j < kG; ++j) {
+            const uint32_t off = byte_off(pos[j], 4u);
+            __builtin_amdgcn_raw_buffer_store_b32(e[j], ir, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key[g + j])), vr, off, 0, 0);
+        }
+    }
+    for (uint32_t i = count + threadIdx.x; i < k; i += NT) {
+        __builtin_amdgcn_raw_buffer_store_b32(0xFFFFFFFFu, ir, i * 4u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_inff()), vr, i * 4u, 0, 0);
+    }
+}
+
+// Merge lists: every list holds exactly lcap = k rounded up to even items,
+// (key, column) pairs, the winners in column order followed by key 0 (never
+// selectable), so the lists of a row form one contiguous run of memory, a
+// reader needs no counts, and 16-byte accesses never straddle a list's end.
+__host__ __device__ __forceinline__ uint32_t list_cap(uint32_t k) { return (k + 1u) & ~1u; }
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// COHERENT: the list is read by another workgroup of the same launch, so it
+// is stored device-coherent (sc1) past the per-XCD L2s; the reader loads it
+// the same way, and no L2 write-back or invalidate is needed.
+template <int NT, int PER, bool COHERENT, class ColOf>
+__device__ __forceinline__ void write_list(uint2 *dst, uint32_t lcap, WinCursor cur, const uint32_t (&key)[PER],
+                                           ColOf col, uint32_t count) {
+    constexpr int aux = COHERENT ? kDeviceCoherent : 0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(dst, lcap * 8u);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        u32x2 v;
+        v.x = key[j];
+        v.y = col(j);
+        __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off(cur.next(key[j]), 8u), 0, aux);
+    }
+    const u32x2 zero = {0u, 0u};
+    for (uint32_t i = count + threadIdx.x; i < lcap; i += NT) __builtin_amdgcn_raw_buffer_store_b64(zero, r, i * 8u, 0, aux);
+}
+
+// Items [i0, i0 + PER) of the n items at `src` as (key, column); items past
+// n read as key 0.  Loads through a buffer descriptor, none behind a branch.
+template <int PER, bool COHERENT>
+__device__ __forceinline__ void load_items(const uint2 *src, int n, int i0, uint32_t (&key)[PER],
+                                           uint32_t (&col)[PER]) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, (uint32_t)max(n, 0) * 8u);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (uint32_t)(i0 + j) * 8u, 0,
+                                                             COHERENT ? kDeviceCoherent : 0);
+        key[j] = v.x;
+        col[j] = v.y;
+    }
+}
+
+// One workgroup per (row, part).  LIST: the part merges lists of a previous
+// launch.  MMUL > 0 (logits input only): after writing its own list, the
+// last part of a row to finish (per-row arrival counter, zeroed by the score
+// kernel) merges all of the row's lists, up to MMUL x CAP items, in the same
+// launch.
+template <int CAP, bool LIST, int NT, int MMUL>
+__global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
+    constexpr bool kFused = MMUL > 0;
+    constexpr int kPer = CAP / NT;                    // items per thread
+    constexpr int kMPer = kFused ? MMUL * kPer : kPer;    // merge items per thread
+    __shared__ SelScratch<NT, NT * kMPer> sh;
+
+    const int tid = threadIdx.x;
     const int b = blockIdx.x / a.parts;
     const int part = blockIdx.x - b * a.parts;
-    const int k = a.k;
-    const int i0 = tid * kPer;                        // this thread's first item
+    const uint32_t k = (uint32_t)a.k;
+    const uint32_t lcap = list_cap(k);
+    const int i0 = tid * kPer;
+    sel_reset(sh);                                    // while the loads are in flight
 
-    // ---- 1. this thread's keys (key 0 = not selectable), loads all issued
-    // before any is used
+    // logits input: slot j holds column col0 + i0 + j; list input: col[j]
     uint32_t key[kPer];
-    uint32_t colv[LIST ? kPer : 1];
-    int64_t col0 = 0;
-    if (!LIST) {
-        col0 = (int64_t)part * CAP;
+    uint32_t col[LIST ? kPer : 1];
+    const int64_t col0 = (int64_t)part * CAP;
+    if constexpr (!LIST) {
         const int ncols = a.row_cols ? min((int)a.row_cols[b], a.n_cols) : a.n_cols;
         const int n = (int)max<int64_t>(0, min<int64_t>(CAP, ncols - col0));
         const float *src = a.logits + (int64_t)b * a.ld + col0 + i0;
@@ -142,200 +424,83 @@ __global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
                 v[j + 3] = f.w;
             }
         } else {
+            // ragged or unaligned: dword loads at offsets clamped into the
+            // segment, the slots past its end masked
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(src - i0, (uint32_t)n * 4u);
 #pragma unroll
-            for (int j = 0; j < kPer; ++j) v[j] = i0 + j < n ? src[j] : -__builtin_inff();
+            for (int j = 0; j < kPer; ++j) {
+                const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)max(0, min(i0 + j, n - 1)) * 4u, 0, 0);
+                v[j] = i0 + j < n ? __uint_as_float(x) : -__builtin_inff();
+            }
         }
 #pragma unroll
         for (int j = 0; j < kPer; ++j) key[j] = order_key(v[j]);
     } else {
-        // lists [part*G, part*G + G) of row b, each at a fixed stride
+        // lists [G * part, G * part + G) of the row, G = CAP / in_cap
         const int G = CAP / a.in_cap;
         const int l0 = part * G;
         const int n = max(0, min(G, a.in_parts - l0)) * a.in_cap;
-        uint2 it[kPer];
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int i = i0 + j;
-            const int g = i / a.in_cap, jj = i - g * a.in_cap;
-            const int64_t li = (int64_t)b * a.in_parts + l0 + g;
-            it[j] = make_uint2(0u, 0u);
-            if (i < n && (uint32_t)jj < a.in_cnt[li]) it[j] = a.in_list[li * a.in_cap + jj];
-        }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            key[j] = it[j].x;
-            colv[j] = it[j].y;
-        }
+        load_items<kPer, false>(a.in_list + ((int64_t)b * a.in_parts + l0) * a.in_cap, n, i0, key, col);
     }
-    uint32_t n_valid = 0;
-    float fmn = __builtin_inff(), fmx = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        if (key[j]) {
-            const float v = key_value(key[j]);
-            ++n_valid;
-            fmn = fminf(fmn, v);
-            fmx = fmaxf(fmx, v);
-        }
-    }
-    // wave reductions via DPP scans (the last lane holds the total)
-    n_valid = wave_scan(n_valid);
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        fmn = fminf(fmn, __shfl_xor(fmn, d, 64));
-        fmx = fmaxf(fmx, __shfl_xor(fmx, d, 64));
-    }
-    if (lane == 63) sh_cnt[wave] = n_valid;
-    if (lane == 0) {
-        sh_fmin[wave] = fmn;
-        sh_fmax[wave] = fmx;
-    }
-    __syncthreads();
-    uint32_t total = 0;
-    float vmin = __builtin_inff(), vmax = -__builtin_inff();
-    for (int w = 0; w < kW; ++w) {
-        total += sh_cnt[w];
-        vmin = fminf(vmin, sh_fmin[w]);
-        vmax = fmaxf(vmax, sh_fmax[w]);
-    }
+    const auto col_of = [&](int j) { return LIST ? col[LIST ? j : 0] : (uint32_t)(col0 + i0 + j); };
 
-    // ---- 2./3. the exact k-th largest key kstar and how many of its
-    // copies win (lowest columns first); kstar = 0 when all selectable win
-    uint32_t kstar = 0u, need_ties = 0u;
-    if (total > (uint32_t)k) {
-        float scale = 0.f;
-        const float range = vmax - vmin;
-        if (range > 0.f && range < __builtin_inff()) scale = (float)kBins / range;
-        if (!(scale < __builtin_inff())) scale = 0.f;
-        for (int i = tid; i < kBins; i += NT) sh_hist[i] = 0u;
+    uint32_t kstar, need_ties, total;
+    WinCursor cur;
+    find_cut<NT, kPer>(key, k, sh, kstar, need_ties, total);
+    scan_winners<NT, kPer>(key, kstar, need_ties, sh, cur);
+    uint32_t count = min(total, k);
+    if (a.out_list)
+        write_list<NT, kPer, kFused>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key, col_of, count);
+    else
+        write_final<NT, kPer>(a, b, cur, key, col_of, count);
+    if constexpr (kFused) {
+        // ---- fused merge: the row's last part to arrive merges its lists.
+        // Once every list store of the workgroup has completed (vmcnt 0 in
+        // each wave, then the barrier) the arrival is counted; the counter's
+        // atomic and the list accesses are all device-coherent.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        int bins[kPer];
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            bins[j] = key[j] ? value_bin(key[j], vmin, scale) : -1;
-            if (key[j]) atomicAdd(&sh_hist[bins[j]], 1u);
-        }
+        if (tid == 0) sh.flag = atomicAdd(a.row_done + b, 1u) == (uint32_t)(a.parts - 1);
         __syncthreads();
-        find_from_top<NT>(sh_hist, kBins, (uint32_t)k, sh_res, sh_scan);
-        const int cbin = sh_res[0];
-        uint32_t rem = (uint32_t)k - (uint32_t)sh_res[1];
-        const uint32_t n_in_bin = sh_hist[cbin];
-        // members of the cut bin go to LDS, in column order
-        uint32_t mine = 0;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) mine += bins[j] == cbin;
-        uint32_t at = block_scan<NT>(mine, sh_scan) - mine;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j)
-            if (bins[j] == cbin) sh_cand[at++] = key[j];
-        __syncthreads();
-        if (n_in_bin <= 64u) {
-            // few members: wave 0 ranks them against each other directly
-            if (wave == 0) {
-                const uint32_t my = lane < (int)n_in_bin ? sh_cand[lane] : 0u;
-                uint32_t greater = 0, equal = 0;
-                for (uint32_t j = 0; j < n_in_bin; ++j) {
-                    const uint32_t other = (uint32_t)__builtin_amdgcn_readlane((int)my, (int)j);
-                    greater += other > my;
-                    equal += other == my;
-                }
-                if (lane < (int)n_in_bin && greater < rem && rem <= greater + equal) {
-                    sh_cut[0] = my;              // every such lane holds the same key
-                    sh_cut[1] = rem - greater;
-                }
-            }
-            __syncthreads();
-            kstar = sh_cut[0];
-            need_ties = sh_cut[1];
-        } else {
-            // radix passes over the members' keys: bits 31:21, 20:10, 9:0
-            uint32_t prefix = 0u;
-            for (int stage = 0; stage < 3; ++stage) {
-                const int hi = stage == 0 ? 32 : (stage == 1 ? 21 : 10);
-                const int lo = stage == 0 ? 21 : (stage == 1 ? 10 : 0);
-                __syncthreads();
-                for (int i = tid; i < kBins; i += NT) sh_hist[i] = 0u;
-                __syncthreads();
-                const uint32_t mask = (1u << (hi - lo)) - 1u;
-                for (uint32_t c = tid; c < n_in_bin; c += NT) {
-                    const uint32_t kk = sh_cand[c];
-                    if (hi == 32 || (kk >> hi) == prefix) atomicAdd(&sh_hist[(kk >> lo) & mask], 1u);
-                }
-                __syncthreads();
-                find_from_top<NT>(sh_hist, kBins, rem, sh_res, sh_scan);
-                rem -= (uint32_t)sh_res[1];
-                prefix = (hi == 32 ? 0u : (prefix << (hi - lo))) | (uint32_t)sh_res[0];
-            }
-            kstar = prefix;
-            need_ties = rem;
-        }
-    }
-
-    // ---- 4. winners (key > kstar, plus the first need_ties keys == kstar)
-    // in column order; one scan of packed (winners | ties << 16) per thread
-    uint32_t n_win = 0, n_tie = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        n_win += key[j] > kstar;
-        n_tie += kstar != 0u && key[j] == kstar;
-    }
-    const uint32_t packed = n_win | (n_tie << 16);
-    const uint32_t excl = block_scan<NT>(packed, sh_scan) - packed;
-    if (tid == NT - 1) {
-        sh_cut[0] = (excl + packed) & 0xFFFFu;                  // all certain winners
-        sh_cut[1] = (excl + packed) >> 16;                      // all ties
-    }
-    uint32_t tie_ord = excl >> 16;
-    uint32_t pos = (excl & 0xFFFFu) + min(tie_ord, need_ties);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        bool win = key[j] > kstar;
-        if (kstar != 0u && key[j] == kstar) win = tie_ord++ < need_ties;
-        if (win) {
-            const uint32_t col = LIST ? colv[j] : (uint32_t)(col0 + i0 + j);
-            const uint32_t o = pos++;
-            if (a.out_list) {
-                a.out_list[((int64_t)b * a.parts + part) * k + o] = make_uint2(key[j], col);
-            } else {
-                int32_t e = (int32_t)col;
-                if (a.chunk_ids) {
-                    const int32_t beta = a.chunk_ids[(int64_t)b * a.max_chunks + (int32_t)col / kBlock];
-                    e = beta * kBlock + (int32_t)col % kBlock;
-                }
-                a.out_idx[(int64_t)b * k + o] = e;
-                if (a.out_val) a.out_val[(int64_t)b * k + o] = key_value(key[j]);
-            }
-        }
-    }
-    __syncthreads();
-    const uint32_t count = min(sh_cut[0] + min(sh_cut[1], need_ties), (uint32_t)k);
-    if (a.out_list) {
-        if (tid == 0) a.out_cnt[(int64_t)b * a.parts + part] = count;
-    } else {
-        for (int i = (int)count + tid; i < k; i += NT) {
-            a.out_idx[(int64_t)b * k + i] = -1;
-            if (a.out_val) a.out_val[(int64_t)b * k + i] = -__builtin_inff();
-        }
+        if (!sh.flag) return;                         // uniform
+        sel_reset(sh);
+        uint32_t mkey[kMPer], mcol[kMPer];
+        load_items<kMPer, true>(a.out_list + (int64_t)b * a.parts * lcap, a.parts * (int)lcap, tid * kMPer, mkey,
+                                mcol);
+        find_cut<NT, kMPer>(mkey, k, sh, kstar, need_ties, total);
+        scan_winners<NT, kMPer>(mkey, kstar, need_ties, sh, cur);
+        write_final<NT, kMPer>(a, b, cur, mkey, [&](int j) { return mcol[j]; }, min(total, k));
+        if (tid == 0) a.row_done[b] = 0u;             // ready for the next call
     }
 }
 
-template <int CAP, bool LIST, int NT>
+template <int CAP, bool LIST, int NT, int MMUL = 0>
 hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
     const int64_t grid = (int64_t)a.B * a.parts;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((topk_segment_kernel<CAP, LIST, NT>), dim3((unsigned)grid), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((topk_segment_kernel<CAP, LIST, NT, MMUL>), dim3((unsigned)grid), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-// Capacities (items per workgroup / threads): logits 4096/256, 8192/512,
-// 16384/1024, 32768/1024; lists 4096/256, 16384/1024.
-hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, hipStream_t s) {
-    if (list) return cap <= 4096 ? launch_seg<4096, true, 256>(a, s) : launch_seg<kSegListCap, true, 1024>(a, s);
+// Capacities (items per workgroup / threads): logits 4096/512, 8192/1024,
+// 16384/1024, 32768/1024; lists 4096/512, 16384/1024.  `fused` (logits with
+// several parts per row whose lists, parts * (k rounded up to even) items,
+// fit in 2 * cap; row_done zeroed) merges in the same launch.
+hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused, hipStream_t s) {
+    if (list) return cap <= 4096 ? launch_seg<4096, true, 512>(a, s) : launch_seg<kSegListCap, true, 1024>(a, s);
+    if (fused) {
+        const bool one = (int64_t)a.parts * list_cap((uint32_t)a.k) <= cap;
+        switch (cap) {
+        case 4096: return one ? launch_seg<4096, false, 512, 1>(a, s) : launch_seg<4096, false, 512, 2>(a, s);
+        case 8192: return one ? launch_seg<8192, false, 1024, 1>(a, s) : launch_seg<8192, false, 1024, 2>(a, s);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (cap) {
-    case 4096: return launch_seg<4096, false, 256>(a, s);
-    case 8192: return launch_seg<8192, false, 512>(a, s);
+    case 4096: return launch_seg<4096, false, 512>(a, s);
+    case 8192: return launch_seg<8192, false, 1024>(a, s);
     case 16384: return launch_seg<16384, false, 1024>(a, s);
     default: return launch_seg<kSegLogitCap, false, 1024>(a, s);
     }

@@ -51,8 +51,8 @@ def test_workspace_bytes(lib):
     # rows that fit one top-k workgroup need no scratch of their own
     assert L.workspace_bytes(L.IDX_OP_TOPK, 4, 1000, 512) == 0
     # score_topk holds the logits (4 rows x 1024 padded columns x 4 B) and
-    # one column count per row, each piece 256-byte aligned
-    assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 4, 1000, 512) == 4 * 1024 * 4 + 256
+    # per-row column counts and merge counters, each piece 256-byte aligned
+    assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 4, 1000, 512) == 4 * 1024 * 4 + 2 * 256
     # long rows: per-part (key, column) lists of k items and their counts
     parts = -(-262144 // 32768)
     need = L.workspace_bytes(L.IDX_OP_TOPK, 8, 262144, 512)

@@ -217,6 +217,23 @@ def test_k_values(k):
     _check_workload(wl, tag=f"k{k}")
 
 
+@pytest.mark.parametrize("k", [1, 7, 512, 1500, 2048])
+def test_multi_part_rows_k_values(k):
+    """Rows of up to 20000 entries, each split over 5 top-k workgroups: for
+    k <= 1638 the row's last part merges the parts' lists in the same launch,
+    k = 2048 takes a separate merge launch."""
+    wl = W.paged_decode([20000, 9000, 300, 16000], seed=11, k=k, name="multi-part")
+    _check_workload(wl, tag=f"multipart-k{k}")
+
+
+@pytest.mark.parametrize("k", [7, 512])
+def test_multi_part_rows_with_chunk_lists(k):
+    """Chunk-list rows over 4 top-k parts: the in-launch merge resolves the
+    winners' columns to logical entries."""
+    wl = W.resident(3, 512, 200, seed=12, k=k, name="multi-part-chunks")
+    _check_workload(wl, tag=f"multipart-chunks-k{k}")
+
+
 def test_negative_and_zero_scales():
     wl = W.small_config(0)
     sc = wl.pool[:, 128:].copy().view("<f4")
