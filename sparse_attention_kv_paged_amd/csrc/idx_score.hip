@@ -46,10 +46,27 @@ struct RowCtx {
     int32_t limit;    // bound on logical entry ids, clamped to capacity
 };
 
-__device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, int b, uint32_t &st) {
+// A row's inputs (request, bound, chunk count), read without branches so
+// that they are in flight together: absent arrays get empty descriptors,
+// which read 0, and so do rows >= B.
+struct RowRaw {
+    int32_t qreq, limit, nchunks;
+};
+
+__device__ __forceinline__ RowRaw row_raw(const ScoreArgs &a, int b) {
+    const uint32_t nb = (uint32_t)a.B * 4u, off = (uint32_t)b * 4u;
+    RowRaw r;
+    r.qreq = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.q_req, a.q_req ? nb : 0u), off, 0, 0);
+    r.limit = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.limits, nb), off, 0, 0);
+    r.nchunks = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.n_chunks, a.chunk_ids ? nb : 0u), off, 0, 0);
+    if (!a.q_req) r.qreq = b;
+    return r;
+}
+
+__device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, const RowRaw &raw, uint32_t &st) {
     RowCtx r;
-    r.req = a.q_req ? a.q_req[b] : b;
-    r.limit = a.limits[b];
+    r.req = raw.qreq;
+    r.limit = raw.limit;
     r.nslots = 0;
     if (r.req >= 0 && a.block_table && r.req >= a.n_req) {
         st |= 0x4u;                                   // IDX_STATUS_BAD_REQUEST
@@ -63,7 +80,7 @@ __device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, int b, uint32_
     }
     if (r.limit < 0) r.limit = 0;
     if (a.chunk_ids) {
-        int32_t nc = a.n_chunks[b];
+        int32_t nc = raw.nchunks;
         if (nc > a.max_chunks) {
             st |= 0x8u;                               // IDX_STATUS_BAD_CHUNK
             nc = a.max_chunks;
@@ -75,19 +92,35 @@ __device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, int b, uint32_
     return r;
 }
 
-// The table reads of slot j, issued under bounds the host guarantees (j <
-// max_chunks, beta < max_blocks, req < n_req) and before the row's bound is
-// known, so they overlap the bound's own load.
+constexpr uint32_t kDrop = 0x7FFFFFF0u;               // a byte offset every descriptor rejects
+
+// The table reads of slot j (lane_ok: the lane holds a slot), issued under
+// bounds the host guarantees (j < max_chunks, beta < max_blocks,
+// req < n_req) through buffer descriptors, without branches, so that later
+// loads go out before these are waited on.  CHUNKED: the slot's logical
+// block comes from the row's chunk list, a read the table read depends on.
 struct SlotRaw {
-    int64_t beta;   // logical block (chunk id), -1 if none
-    int64_t pblk;   // pool block from the table, -1 if none
+    int32_t beta;   // logical block (chunk id), -1 if none
+    int32_t p;      // the table's entry, valid when tok
+    bool tok;       // the table was read (else: no pool block)
 };
 
-__device__ __forceinline__ SlotRaw slot_raw(const ScoreArgs &a, int req, int b, int j) {
-    SlotRaw s{j, -1};
-    if (a.chunk_ids) s.beta = j < a.max_chunks ? a.chunk_ids[(int64_t)b * a.max_chunks + j] : -1;
-    if (a.block_table && req >= 0 && req < a.n_req && s.beta >= 0 && s.beta < a.max_blocks)
-        s.pblk = a.block_table[(int64_t)req * a.max_blocks + s.beta];
+template <bool CHUNKED>
+__device__ __forceinline__ SlotRaw slot_raw(const ScoreArgs &a, int req, int b, int j, bool lane_ok) {
+    SlotRaw s{j, -1, false};
+    if (CHUNKED) {
+        const bool ok = lane_ok && j < a.max_chunks;
+        const __amdgpu_buffer_rsrc_t cr =
+            make_rsrc(a.chunk_ids + (int64_t)b * a.max_chunks, (uint32_t)a.max_chunks * 4u);
+        const int32_t c = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(cr, ok ? (uint32_t)j * 4u : kDrop, 0, 0);
+        s.beta = ok ? c : -1;
+    }
+    s.tok = lane_ok && a.block_table && req >= 0 && req < a.n_req && s.beta >= 0 && s.beta < a.max_blocks;
+    const __amdgpu_buffer_rsrc_t tr =
+        make_rsrc(a.block_table + (int64_t)max(req, 0) * a.max_blocks, a.block_table ? (uint32_t)a.max_blocks * 4u : 0u);
+    // the value is only looked at in resolve_slot, so this read stays in
+    // flight across whatever the caller issues in between
+    s.p = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(tr, s.tok ? (uint32_t)s.beta * 4u : kDrop, 0, 0);
     return s;
 }
 
@@ -111,7 +144,7 @@ __device__ __forceinline__ int64_t resolve_slot(const ScoreArgs &a, const RowCtx
     ebase = (int32_t)(beta * kBlock);
     if (ebase >= r.limit) return -1;
     if (!a.block_table) return beta * kBlock;
-    const int64_t pblk = raw.pblk;
+    const int64_t pblk = raw.tok ? raw.p : -1;
     if (pblk < 0) {
         if (pblk != -1) st |= 0x2u;                       // IDX_STATUS_BAD_BLOCK
         return -1;
@@ -213,7 +246,7 @@ constexpr int kRing = 2;
 constexpr int kFlatRows = 512;  // rows up to which waves share work evenly
 
 __device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_t &st) {
-    RowCtx r = row_context(a, b, st);
+    RowCtx r = row_context(a, row_raw(a, b), st);
     // wave-uniform values stay in scalar registers, so the tile loop is
     // uniform control flow and its loads stay in flight across iterations
     r.req = __builtin_amdgcn_readfirstlane(r.req);
@@ -222,11 +255,44 @@ __device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_
     return r;
 }
 
+// q[b] staged in LDS for the waves of a workgroup: 64 heads of 128 bf16,
+// rows padded to 136 elements so that the 32 heads a half-wave reads sit in
+// different banks.
+constexpr int kQPad = kHeadDim + 8;
+constexpr int kQStage = kHeads * kQPad;                 // elements per staged row
+
+// The lane's MFMA A operands of q[b]: head 32*hb + (lane & 31), dims
+// 64*(lane >> 5) + 8*kk .. +7, from global memory or from a staged row.
+__device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, bf16x8 (&qa)[2][8]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+            a.q + ((int64_t)b * kHeads + 32 * hb + (lane & 31)) * kHeadDim + 64 * (lane >> 5));
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+    }
+}
+
+__device__ __forceinline__ void load_q_staged(const uint16_t *row, bf16x8 (&qa)[2][8]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(row + (32 * hb + (lane & 31)) * kQPad + 64 * (lane >> 5));
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+    }
+}
+
 // Score slots [j0, j1) of row b with the calling wave.  sh_w is the wave's
 // own 64-float LDS slot for w[b].  Columns >= col_end are not written.
-template <bool OWN_COLS>
+// USE_PRE: pre holds the first group's table reads, already issued by the
+// caller, and pre_q the MFMA operands of q[b], already loaded.
+template <bool OWN_COLS, bool CHUNKED, bool USE_PRE = false>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
-                                           int col_end, float *sh_w, uint32_t &st) {
+                                           int col_end, float *sh_w, uint32_t &st,
+                                           const SlotRaw &pre = SlotRaw{-1, -1, false},
+                                           const bf16x8 (*pre_q)[8] = nullptr) {
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int n32 = lane & 31;
@@ -235,21 +301,23 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     float *score_row = a.scores ? a.scores + (int64_t)b * a.ld : nullptr;
 
     // Start-up reads, issued back to back in the order they are needed (the
-    // vector memory counter retires in order): w[b], the first group's
-    // block-table entries, then q[b] -- resolving the table then leaves q in
-    // flight, and the first ring of key loads goes out before q is waited on.
+    // vector memory counter retires in order) and none behind a branch:
+    // w[b], the first group's block-table entries, then q[b] -- resolving
+    // the table then leaves q in flight, and the first ring of key loads goes
+    // out before q is waited on.
     float w_lane = 0.f;
-    SlotRaw raw0{-1, -1};
+    SlotRaw raw0{-1, -1, false};
     bf16x8 qa[2][8];
     if (live) {
         w_lane = a.w[(int64_t)b * kHeads + lane];
-        if (lane < min(64, j1 - j0)) raw0 = slot_raw(a, r.req, b, j0 + lane);
+        raw0 = USE_PRE ? pre : slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));
+        if (USE_PRE) {
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const u32x4 *qp = reinterpret_cast<const u32x4 *>(
-                a.q + ((int64_t)b * kHeads + 32 * hb + n32) * kHeadDim + 64 * hf);
+            for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+                for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = pre_q[hb][kk];
+        } else {
+            load_q_global(a, b, qa);
         }
     }
 
@@ -261,14 +329,15 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     const __amdgpu_buffer_rsrc_t sc_r =
         make_rsrc(score_row ? score_row : out_row, score_row ? (uint32_t)col_end * 4u : 0u);
     const uint32_t lane_row = (uint32_t)n32 * kRowBytes;
-    constexpr uint32_t kDrop = 0x7FFFFFF0u;            // an offset every descriptor rejects
+    SlotRaw graw = raw0;
     for (int g0 = j0; g0 < j1; g0 += 64) {
         const int gn = min(64, j1 - g0);
         int32_t lane_ebase = 0;
         int64_t lane_prow0 = -1;
-        if (live && lane < gn)
-            lane_prow0 = resolve_slot(a, r, g0 == j0 ? raw0 : slot_raw(a, r.req, b, g0 + lane), g0 + lane,
-                                      lane_ebase, st);
+        if (live && lane < gn) lane_prow0 = resolve_slot(a, r, graw, g0 + lane, lane_ebase, st);
+        // the next group's table reads, in flight during this group's ring
+        // (no traffic when there is no next group)
+        graw = slot_raw<CHUNKED>(a, r.req, b, g0 + 64 + lane, live && lane < min(64, j1 - g0 - 64));
         const int ntiles = 2 * gn;
         KeyHalf kv[kRing];
         int64_t prow_t[kRing];
@@ -318,12 +387,13 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // FLAT: the (row, slot) work of all rows is flattened and split evenly over
 // every wave of the grid (rows of very different lengths); otherwise each
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
-template <bool OWN_COLS, bool FLAT>
+template <bool OWN_COLS, bool FLAT, bool CHUNKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
     __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
     __shared__ int32_t sh_rreq[FLAT ? kFlatRows : 1], sh_rlim[FLAT ? kFlatRows : 1], sh_rslots[FLAT ? kFlatRows : 1];
     __shared__ uint32_t sh_scan[kWaves];
+    __shared__ __attribute__((aligned(16))) uint16_t sh_q[FLAT ? 2 : 1][FLAT ? kQStage : 8];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
     const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
@@ -341,15 +411,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         const int j0 = (split * kWaves + wave) * a.slots_per_wave;
         const int j1 = min(j0 + a.slots_per_wave, slot_stop);
-        if (j0 < j1) score_span<OWN_COLS>(a, b, j0, j1, r, col_end, sh_w[wave], st);
+        if (j0 < j1) score_span<OWN_COLS, CHUNKED>(a, b, j0, j1, r, col_end, sh_w[wave], st);
     } else {
         // per-row work (slots) and its prefix over rows, in LDS
         uint32_t st_rows = 0;
         int32_t cnt[2] = {0, 0};
+        RowRaw raw[2];
+        for (int k2 = 0; k2 < 2; ++k2) raw[k2] = row_raw(a, 2 * threadIdx.x + k2);    // all in flight
         for (int k2 = 0; k2 < 2; ++k2) {
             const int row = 2 * threadIdx.x + k2;
             if (row < a.B) {
-                const RowCtx rr = row_context(a, row, st_rows);
+                const RowCtx rr = row_context(a, raw[k2], st_rows);
                 sh_rreq[row] = rr.req;
                 sh_rlim[row] = rr.limit;
                 sh_rslots[row] = rr.nslots;
@@ -362,13 +434,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         if (blockIdx.x == 0) st |= st_rows;
         // block exclusive scan of the pairs
-        uint32_t v = (uint32_t)(cnt[0] + cnt[1]);
-        uint32_t incl = v;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const uint32_t o = __shfl_up(incl, d, 64);
-            if (lane >= d) incl += o;
-        }
+        const uint32_t v = (uint32_t)(cnt[0] + cnt[1]);
+        const uint32_t incl = wave_scan(v);
         if (lane == 63) sh_scan[wave] = incl;
         __syncthreads();
         uint32_t add = 0;
@@ -382,29 +449,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int total = __builtin_amdgcn_readfirstlane(sh_pre[a.B]);
         const int nw = (int)gridDim.x * kWaves;
         const int chunk = (total + nw - 1) / nw;
-        int f = ((int)blockIdx.x * kWaves + wave) * chunk;
-        const int fend = min(f + chunk, total);
-        if (f < fend) {
-            // first row whose work range contains f
+        // the row whose work range holds flattened item x (x < total)
+        const auto row_of = [&](int x) {
             int lo = 0, hi = a.B - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (sh_pre[mid] <= f) lo = mid; else hi = mid - 1;
+                if (sh_pre[mid] <= x) lo = mid; else hi = mid - 1;
             }
-            int b = __builtin_amdgcn_readfirstlane(lo);
-            while (f < fend) {
-                const int pb = __builtin_amdgcn_readfirstlane(sh_pre[b]);
-                const int pe = __builtin_amdgcn_readfirstlane(sh_pre[b + 1]);
-                if (pe > f) {
-                    RowCtx r;
-                    r.req = __builtin_amdgcn_readfirstlane(sh_rreq[b]);
-                    r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
-                    r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
-                    const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                    score_span<OWN_COLS>(a, b, f - pb, min(fend, pe) - pb, r, col_end, sh_w[wave], st);
-                    f = min(fend, pe);
+            return __builtin_amdgcn_readfirstlane(lo);
+        };
+        int f = ((int)blockIdx.x * kWaves + wave) * chunk;
+        const int fend = min(f + chunk, total);
+
+        // The wave's first span, and its table reads issued before the q
+        // staging reads below.
+        int b = row_of(min(f, max(total - 1, 0)));
+        int pb = __builtin_amdgcn_readfirstlane(sh_pre[b]);
+        int pe = __builtin_amdgcn_readfirstlane(sh_pre[b + 1]);
+        RowCtx r0;
+        r0.req = __builtin_amdgcn_readfirstlane(sh_rreq[b]);
+        r0.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
+        r0.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
+        const SlotRaw raw0 = slot_raw<CHUNKED>(a, r0.req, b, f - pb + lane, lane < min(64, min(fend, pe) - f));
+        // q of the workgroup's first two rows, staged in LDS once for its
+        // four waves (most workgroups lie within one or two rows)
+        const int fw = (int)blockIdx.x * kWaves * chunk;
+        const int rb = fw < total ? row_of(fw) : a.B;
+        {
+            u32x4 qv[2][4];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                if (rb + rr < a.B) {
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + (int64_t)(rb + rr) * kHeads * kHeadDim);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) qv[rr][i] = src[threadIdx.x + 256 * i];
                 }
-                ++b;
+            }
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                if (rb + rr < a.B) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = threadIdx.x + 256 * i;             // 16-byte chunk: head c / 16, dims 8 (c % 16)
+                        *reinterpret_cast<u32x4 *>(&sh_q[rr][(c >> 4) * kQPad + 8 * (c & 15)]) = qv[rr][i];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        if (f < fend) {
+            const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
+            bf16x8 qa0[2][8];
+            if (b == rb || b == rb + 1)
+                load_q_staged(sh_q[b - rb], qa0);
+            else
+                load_q_global(a, b, qa0);
+            score_span<OWN_COLS, CHUNKED, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], st, raw0,
+                                                qa0);
+            f = min(fend, pe);
+            for (++b; f < fend; ++b) {
+                pb = __builtin_amdgcn_readfirstlane(sh_pre[b]);
+                pe = __builtin_amdgcn_readfirstlane(sh_pre[b + 1]);
+                if (pe <= f) continue;
+                RowCtx r;
+                r.req = __builtin_amdgcn_readfirstlane(sh_rreq[b]);
+                r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
+                r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
+                const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
+                score_span<OWN_COLS, CHUNKED>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], st);
+                f = min(fend, pe);
             }
         }
     }
@@ -412,6 +526,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 }  // namespace
+
+template <bool OWN_COLS, bool FLAT>
+void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s) {
+    if (a.chunk_ids)
+        hipLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+}
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
     if (a.B <= 0) return hipSuccess;
@@ -422,15 +544,15 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
         const int64_t slots = (a.n_cols + kBlock - 1) / kBlock;
         const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(512, ((int64_t)a.B * slots + kWaves - 1) / kWaves));
         if (own)
-            hipLaunchKernelGGL((score_kernel<true, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+            launch_score_as<true, true>(a, grid, s);
         else
-            hipLaunchKernelGGL((score_kernel<false, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+            launch_score_as<false, true>(a, grid, s);
     } else {
         const int64_t grid = (int64_t)a.B * a.splits;
         if (own)
-            hipLaunchKernelGGL((score_kernel<true, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+            launch_score_as<true, false>(a, grid, s);
         else
-            hipLaunchKernelGGL((score_kernel<false, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+            launch_score_as<false, false>(a, grid, s);
     }
     return hipGetLastError();
 }

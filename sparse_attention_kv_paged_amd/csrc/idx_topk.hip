@@ -33,25 +33,6 @@ namespace {
 
 constexpr int kBins = 2048;
 
-// DPP controls (GFX9): row_shr:n = 0x110 + n, row_bcast:15, row_bcast:31.
-// Lanes the control leaves without a source keep `old`.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint32_t dpp(uint32_t v, uint32_t old = 0u) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP row shifts and
-// row broadcasts (no LDS round trips).
-__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
-    v += dpp<0x111, 0xF>(v);
-    v += dpp<0x112, 0xF>(v);
-    v += dpp<0x114, 0xF>(v);
-    v += dpp<0x118, 0xF>(v);
-    v += dpp<0x142, 0xA>(v);
-    v += dpp<0x143, 0xC>(v);
-    return v;
-}
-
 // Same pattern for max and min: lane 63 ends with the wave's result.
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
     v = max(v, dpp<0x111, 0xF>(v));
