@@ -179,10 +179,11 @@ const char *idx_last_error(void);
 
 /*
  * idx_profile_events: measurement hook for benchmark harnesses.  When both
- * are non-NULL (hipEvent_t handles created by the caller), every later
- * idx_score / idx_score_topk call on this thread records `before` right
- * before its score kernel and `after` right after it, on the call's stream,
- * so hipEventElapsedTime(before, after) is that kernel's duration.  Pass
+ * are non-NULL (hipEvent_t handles created by the caller, with timing), every
+ * later idx_score / idx_score_topk call on this thread launches its score
+ * kernel so that the dispatch itself stamps `before` with the kernel's start
+ * and `after` with its end (hipExtLaunchKernelGGL), so
+ * hipEventElapsedTime(before, after) is that kernel's execution time.  Pass
  * NULL, NULL to stop.  Returns IDX_OK.
  */
 int idx_profile_events(void *before, void *after);

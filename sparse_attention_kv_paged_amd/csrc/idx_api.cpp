@@ -16,13 +16,9 @@ thread_local char g_last_error[512] = "";
 thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
 
 hipError_t launch_score_timed(const idx::ScoreArgs &a, hipStream_t s) {
-    if (g_ev_before && g_ev_after) {
-        hipError_t e = hipEventRecord(g_ev_before, s);
-        if (e != hipSuccess) return e;
-        if ((e = idx::launch_score(a, s)) != hipSuccess) return e;
-        return hipEventRecord(g_ev_after, s);
-    }
-    return idx::launch_score(a, s);
+    // with the profiling hook set, the dispatch stamps the events with the
+    // kernel's own start and end
+    return idx::launch_score(a, s, g_ev_before, g_ev_after);
 }
 
 int fail(int code, const char *fmt, ...) {

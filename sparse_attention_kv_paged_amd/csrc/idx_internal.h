@@ -72,7 +72,10 @@ struct SegArgs {
     int32_t max_chunks;
 };
 
-hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
+// ev_start / ev_stop (optional): events the dispatch itself stamps with the
+// kernel's start and end time (hipExtLaunchKernelGGL).
+hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t ev_start = nullptr,
+                        hipEvent_t ev_stop = nullptr);
 hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused, hipStream_t s);
 
 }  // namespace idx

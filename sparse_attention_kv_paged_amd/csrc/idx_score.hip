@@ -29,6 +29,8 @@
 // before conversion (exact).
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "idx_device.h"
 #include "idx_internal.h"
 
@@ -363,8 +365,10 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
             if (prow0 >= 0) logit = score_tile(src, qa, sh_w, hf, ebase + 32 * t + n32, r.limit);
             const uint32_t off = (tau < ntiles && hf == 0) ? (uint32_t)col * 4u : kDrop;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, 0);
-            const float score = score_row ? 1.0f / (1.0f + expf(-logit)) : 0.f;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), sc_r, off, 0, 0);
+            if (score_row) {                          // uniform: scores requested
+                const float score = 1.0f / (1.0f + expf(-logit));
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), sc_r, off, 0, 0);
+            }
         };
 #pragma unroll
         for (int i = 0; i < kRing; ++i) issue(i, kv[i], prow_t[i], ebase_t[i]);
@@ -528,14 +532,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }  // namespace
 
 template <bool OWN_COLS, bool FLAT>
-void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s) {
+void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    const dim3 g((unsigned)grid), blk(256);
     if (a.chunk_ids)
-        hipLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, true>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, true>), g, blk, 0, s, e0, e1, 0, a);
     else
-        hipLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, false>), dim3((unsigned)grid), dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, false>), g, blk, 0, s, e0, e1, 0, a);
 }
 
-hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
+hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.B <= 0) return hipSuccess;
     const bool own = a.row_cols != nullptr;
     if (a.B <= kFlatRows) {
@@ -544,15 +549,15 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
         const int64_t slots = (a.n_cols + kBlock - 1) / kBlock;
         const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(512, ((int64_t)a.B * slots + kWaves - 1) / kWaves));
         if (own)
-            launch_score_as<true, true>(a, grid, s);
+            launch_score_as<true, true>(a, grid, s, e0, e1);
         else
-            launch_score_as<false, true>(a, grid, s);
+            launch_score_as<false, true>(a, grid, s, e0, e1);
     } else {
         const int64_t grid = (int64_t)a.B * a.splits;
         if (own)
-            launch_score_as<true, false>(a, grid, s);
+            launch_score_as<true, false>(a, grid, s, e0, e1);
         else
-            launch_score_as<false, false>(a, grid, s);
+            launch_score_as<false, false>(a, grid, s, e0, e1);
     }
     return hipGetLastError();
 }

@@ -101,12 +101,12 @@ __device__ void find_from_top(const uint32_t *h, int nbins, uint32_t need, int32
     __syncthreads();
 }
 
-// LDS scratch of one selection by NT threads over at most CAND items.  The
-// histogram has 32 extra bins past kBins that absorb non-selectable items,
-// so the histogram's atomics need no branch.
+// LDS scratch of one selection by NT threads.  The histogram has 32 extra
+// bins past kBins that absorb non-selectable items, so the histogram's
+// atomics need no branch.
 template <int NT, int CAND>
 struct SelScratch {
-    uint32_t cand[CAND];          // keys of the cut bin's members
+    uint32_t cand[CAND];          // keys of the cut bin's members, when <= 64
     uint32_t hist[kBins + 32];
     uint32_t scan_a[NT / 64], scan_b[NT / 64];
     uint32_t kmin[NT / 64], kmax[NT / 64];
@@ -195,12 +195,14 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     const uint32_t cbin = (uint32_t)sh.res[0];
     uint32_t rem = k - (uint32_t)sh.res[1];
     const uint32_t n_in_bin = sh.hist[cbin];
-    // 4. the members' keys, in any order
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-        if ((kKeep ? bins[kKeep ? j : 0] : bin_of(key[j])) == cbin) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
-    __syncthreads();
+    // 4. few members: their keys go to LDS (in any order) and one wave
+    // ranks them against each other
+    const auto in_cut_bin = [&](int j) { return (kKeep ? bins[kKeep ? j : 0] : bin_of(key[j])) == cbin; };
     if (n_in_bin <= 64u) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if (in_cut_bin(j)) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
+        __syncthreads();
         if (wave == 0) {
             const uint32_t my = lane < (int)n_in_bin ? sh.cand[lane] : 0u;
             uint32_t greater = 0, equal = 0;
@@ -219,6 +221,8 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
         need_ties = sh.cut[1];
         return;
     }
+    // many members: radix passes over the keys of the cut bin, straight from
+    // registers (bits 31:21, 20:10, 9:0)
     uint32_t prefix = 0u;
     for (int stage = 0; stage < 3; ++stage) {
         const int hi = stage == 0 ? 32 : (stage == 1 ? 21 : 10);
@@ -227,9 +231,10 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
         for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
         __syncthreads();
         const uint32_t mask = (1u << (hi - lo)) - 1u;
-        for (uint32_t c = tid; c < n_in_bin; c += NT) {
-            const uint32_t kk = sh.cand[c];
-            if (hi == 32 || (kk >> hi) == prefix) atomicAdd(&sh.hist[(kk >> lo) & mask], 1u);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const uint32_t kk = key[j];
+            if (in_cut_bin(j) && (hi == 32 || (kk >> hi) == prefix)) atomicAdd(&sh.hist[(kk >> lo) & mask], 1u);
         }
         __syncthreads();
         find_from_top<NT>(sh.hist, kBins, rem, sh.res, sh.scan_a);
@@ -376,7 +381,7 @@ __global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
     constexpr bool kFused = MMUL > 0;
     constexpr int kPer = CAP / NT;                    // items per thread
     constexpr int kMPer = kFused ? MMUL * kPer : kPer;    // merge items per thread
-    __shared__ SelScratch<NT, NT * kMPer> sh;
+    __shared__ SelScratch<NT, 64> sh;
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x / a.parts;

@@ -120,6 +120,10 @@ class Workload:
         """Scored (query row, entry) pairs."""
         return int(self.valid_mask().sum())
 
+    def pairs_per_row(self) -> np.ndarray:
+        """Scored entries of each query row."""
+        return self.valid_mask().sum(axis=1)
+
 
 # ----------------------------------------------------------------------------
 # value helpers (library casts only)
