@@ -126,36 +126,32 @@ __device__ __forceinline__ SlotRaw slot_raw(const ScoreArgs &a, int req, int b, 
     return s;
 }
 
-// First pool row of slot j of row b, or -1 when the slot's block is absent.
-// *ebase receives the logical entry id of the slot's first entry.
+// First pool row of slot j of row b, or -1 when the slot's block is absent
+// (or !ok: the lane holds no slot).  *ebase receives the logical entry id of
+// the slot's first entry.  Straight-line selects, no branches, so the wait
+// for the table read is the only one the compiler needs here.
 __device__ __forceinline__ int64_t resolve_slot(const ScoreArgs &a, const RowCtx &r, const SlotRaw &raw,
-                                                int j, int32_t &ebase, uint32_t &st) {
+                                                int j, bool ok, int32_t &ebase, uint32_t &st) {
     const int64_t beta = raw.beta;
-    ebase = 0;
-    if (r.req < 0 || j >= r.nslots) return -1;
+    ok = ok && r.req >= 0 && j < r.nslots;
+    uint32_t bad = 0;
     if (a.chunk_ids) {
-        if (beta < 0) {
-            if (beta != -1) st |= 0x8u;                   // IDX_STATUS_BAD_CHUNK
-            return -1;
-        }
-        if (a.block_table ? beta >= a.max_blocks : beta * kBlock >= a.n_pool_rows) {
-            st |= 0x8u;
-            return -1;
-        }
+        const bool beyond = a.block_table ? beta >= a.max_blocks : beta * kBlock >= a.n_pool_rows;
+        bad |= (ok && (beta < -1 || (beta >= 0 && beyond))) ? 0x8u : 0u;        // IDX_STATUS_BAD_CHUNK
+        ok = ok && beta >= 0 && !beyond;
     }
     ebase = (int32_t)(beta * kBlock);
-    if (ebase >= r.limit) return -1;
-    if (!a.block_table) return beta * kBlock;
-    const int64_t pblk = raw.tok ? raw.p : -1;
-    if (pblk < 0) {
-        if (pblk != -1) st |= 0x2u;                       // IDX_STATUS_BAD_BLOCK
-        return -1;
+    ok = ok && ebase < r.limit;
+    int64_t prow = beta * kBlock;
+    if (a.block_table) {
+        const int64_t pblk = raw.tok ? raw.p : -1;
+        const bool past = (pblk + 1) * kBlock > a.n_pool_rows;
+        bad |= (ok && (pblk < -1 || (pblk >= 0 && past))) ? 0x2u : 0u;         // IDX_STATUS_BAD_BLOCK
+        ok = ok && pblk >= 0 && !past;
+        prow = pblk * kBlock;
     }
-    if ((pblk + 1) * kBlock > a.n_pool_rows) {
-        st |= 0x2u;
-        return -1;
-    }
-    return pblk * kBlock;
+    st |= bad;
+    return ok ? prow : -1;
 }
 
 struct KeyHalf {
@@ -276,6 +272,39 @@ __device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, bf16x8 
     }
 }
 
+// q of rows rb .. rb + NR - 1 (those below B) for padded LDS rows, read by
+// all 256 threads of the workgroup: fetch_q_rows issues the reads,
+// put_q_rows (after other loads have been issued) stores them to LDS; the
+// caller synchronises before the rows are read.
+template <int NR>
+__device__ __forceinline__ void fetch_q_rows(const ScoreArgs &a, int rb, u32x4 (&qv)[NR][4]) {
+    // rows past B read row B - 1 instead (not stored): the reads are
+    // unconditional so the compiler can count them when waiting for
+    // earlier ones
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+        const int row = min(rb + rr, a.B - 1);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + (int64_t)row * kHeads * kHeadDim);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[rr][i] = src[threadIdx.x + 256 * i];
+    }
+}
+
+template <int NR>
+__device__ __forceinline__ void put_q_rows(const ScoreArgs &a, int rb, const u32x4 (&qv)[NR][4],
+                                           uint16_t (*sq)[kQStage]) {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+        if (rb + rr < a.B) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = threadIdx.x + 256 * i;             // 16-byte chunk: head c / 16, dims 8 (c % 16)
+                *reinterpret_cast<u32x4 *>(&sq[rr][(c >> 4) * kQPad + 8 * (c & 15)]) = qv[rr][i];
+            }
+        }
+    }
+}
+
 __device__ __forceinline__ void load_q_staged(const uint16_t *row, bf16x8 (&qa)[2][8]) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -286,15 +315,20 @@ __device__ __forceinline__ void load_q_staged(const uint16_t *row, bf16x8 (&qa)[
     }
 }
 
+struct NoQ {
+    __device__ void operator()(bf16x8 (&)[2][8]) const {}
+};
+
 // Score slots [j0, j1) of row b with the calling wave.  sh_w is the wave's
 // own 64-float LDS slot for w[b].  Columns >= col_end are not written.
 // USE_PRE: pre holds the first group's table reads, already issued by the
-// caller, and pre_q the MFMA operands of q[b], already loaded.
-template <bool OWN_COLS, bool CHUNKED, bool USE_PRE = false>
+// caller, and qfin(qa) -- called once, right after the first ring of key
+// loads has been issued, by every wave of the workgroup (it synchronises
+// the workgroup) -- delivers the MFMA operands of q[b].
+template <bool OWN_COLS, bool CHUNKED, bool USE_PRE = false, class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint32_t &st,
-                                           const SlotRaw &pre = SlotRaw{-1, -1, false},
-                                           const bf16x8 (*pre_q)[8] = nullptr) {
+                                           const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{}) {
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int n32 = lane & 31;
@@ -313,14 +347,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     if (live) {
         w_lane = a.w[(int64_t)b * kHeads + lane];
         raw0 = USE_PRE ? pre : slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));
-        if (USE_PRE) {
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = pre_q[hb][kk];
-        } else {
-            load_q_global(a, b, qa);
-        }
+        if (!USE_PRE) load_q_global(a, b, qa);
     }
 
     // Slots go in groups of up to 64: lane j resolves slot j of the group
@@ -336,7 +363,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         const int gn = min(64, j1 - g0);
         int32_t lane_ebase = 0;
         int64_t lane_prow0 = -1;
-        if (live && lane < gn) lane_prow0 = resolve_slot(a, r, graw, g0 + lane, lane_ebase, st);
+        lane_prow0 = resolve_slot(a, r, graw, g0 + lane, live && lane < gn, lane_ebase, st);
         // the next group's table reads, in flight during this group's ring
         // (no traffic when there is no next group)
         graw = slot_raw<CHUNKED>(a, r.req, b, g0 + 64 + lane, live && lane < min(64, j1 - g0 - 64));
@@ -372,6 +399,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         };
 #pragma unroll
         for (int i = 0; i < kRing; ++i) issue(i, kv[i], prow_t[i], ebase_t[i]);
+        if (USE_PRE && g0 == j0) qfin(qa);            // q arrives while the ring is in flight
         if (g0 == j0) {
             sh_w[lane] = w_lane;                        // w[b] into the wave's LDS slot
             __builtin_amdgcn_wave_barrier();
@@ -397,7 +425,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
     __shared__ int32_t sh_rreq[FLAT ? kFlatRows : 1], sh_rlim[FLAT ? kFlatRows : 1], sh_rslots[FLAT ? kFlatRows : 1];
     __shared__ uint32_t sh_scan[kWaves];
-    __shared__ __attribute__((aligned(16))) uint16_t sh_q[FLAT ? 2 : 1][FLAT ? kQStage : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sh_q[FLAT ? 2 : 1][kQStage];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
     const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
@@ -415,7 +443,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         const int j0 = (split * kWaves + wave) * a.slots_per_wave;
         const int j1 = min(j0 + a.slots_per_wave, slot_stop);
-        if (j0 < j1) score_span<OWN_COLS, CHUNKED>(a, b, j0, j1, r, col_end, sh_w[wave], st);
+        // the first group's table reads, then q[b] staged in LDS once for
+        // the four waves
+        const SlotRaw raw0 = slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));
+        u32x4 qv[1][4];
+        fetch_q_rows<1>(a, b, qv);
+        const auto qfin = [&](bf16x8 (&qa)[2][8]) {
+            put_q_rows<1>(a, b, qv, sh_q);
+            __syncthreads();
+            load_q_staged(sh_q[0], qa);
+        };
+        if (j0 < j1) {
+            score_span<OWN_COLS, CHUNKED, true>(a, b, j0, j1, r, col_end, sh_w[wave], st, raw0, qfin);
+        } else {
+            put_q_rows<1>(a, b, qv, sh_q);            // the workgroup's one barrier
+            __syncthreads();
+        }
     } else {
         // per-row work (slots) and its prefix over rows, in LDS
         uint32_t st_rows = 0;
@@ -479,38 +522,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // four waves (most workgroups lie within one or two rows)
         const int fw = (int)blockIdx.x * kWaves * chunk;
         const int rb = fw < total ? row_of(fw) : a.B;
-        {
-            u32x4 qv[2][4];
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                if (rb + rr < a.B) {
-                    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + (int64_t)(rb + rr) * kHeads * kHeadDim);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) qv[rr][i] = src[threadIdx.x + 256 * i];
-                }
-            }
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                if (rb + rr < a.B) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int c = threadIdx.x + 256 * i;             // 16-byte chunk: head c / 16, dims 8 (c % 16)
-                        *reinterpret_cast<u32x4 *>(&sh_q[rr][(c >> 4) * kQPad + 8 * (c & 15)]) = qv[rr][i];
-                    }
-                }
-            }
-        }
-        __syncthreads();
-
-        if (f < fend) {
-            const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            bf16x8 qa0[2][8];
+        u32x4 qv[2][4];
+        fetch_q_rows<2>(a, rb, qv);
+        const auto qfin = [&](bf16x8 (&qa)[2][8]) {
+            put_q_rows<2>(a, rb, qv, sh_q);
+            __syncthreads();
             if (b == rb || b == rb + 1)
-                load_q_staged(sh_q[b - rb], qa0);
+                load_q_staged(sh_q[b - rb], qa);
             else
-                load_q_global(a, b, qa0);
+                load_q_global(a, b, qa);
+        };
+
+        if (!(f < fend)) {
+            put_q_rows<2>(a, rb, qv, sh_q);           // the workgroup's one barrier
+            __syncthreads();
+        } else {
+            const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
             score_span<OWN_COLS, CHUNKED, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], st, raw0,
-                                                qa0);
+                                                qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
                 pb = __builtin_amdgcn_readfirstlane(sh_pre[b]);
