@@ -153,6 +153,17 @@ def test_full_size_prefill_sampled_rows():
     _check_workload(wl, rows=rows, tag="full3")
 
 
+def test_many_rows_sharing_a_request():
+    """More than 512 rows of one request take the path where four rows share
+    each key tile; a padding row, an out-of-range request id and a partial
+    last group of rows fall back to one row per wave."""
+    wl = W.prefill(8192, 603, seed=13, name="shared-rows")
+    wl.q_req = wl.q_req.copy()
+    wl.q_req[301] = -1                                         # padding row inside a group
+    wl.q_req[450] = 5                                          # no such request: absent, flagged
+    _check_workload(wl, tag="shared-rows")
+
+
 # --------------------------------------------------------------- edge cases
 
 def _small_paged(seed=7, entries=(700, 64, 1, 129, 2048)):
