@@ -194,10 +194,11 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
 
 // One 32-entry tile: MFMA contraction, relu / head-weight / head-sum epilogue,
 // scale and bound.  Returns the logit of entry (lane & 31) on every lane.
-// sh_w holds w[b]; accumulator register i of head block hb is head
-// 32*hb + 8*(i/4) + 4*hf + i%4, so lanes of one half read the same weights.
+// Accumulator register i of head block hb is head 32*hb + 8*(i/4) + 4*hf +
+// i%4; wr[hb][g][i%4] holds that head's weight w[b] (g = i/4), loaded once
+// per span.
 __device__ __forceinline__ float score_tile(KeyHalf &k, const bf16x8 (&qa)[2][8],
-                                            const float *sh_w, int hf, int e, int limit) {
+                                            const float (&wr)[2][4][4], int hf, int e, int limit) {
     // relu(s x) = |s| relu(sign(s) x): flip the fp8 signs of rows with s < 0
     if (__any(k.s < 0.f)) {
         const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
@@ -215,15 +216,13 @@ __device__ __forceinline__ float score_tile(KeyHalf &k, const bf16x8 (&qa)[2][8]
     // relu as a signed-integer max on the float's bits (negative floats,
     // -0.0 included, have the sign bit set and become +0.0): one VALU op with
     // no NaN canonicalisation; four partial sums break the FMA chain
-    const float4 *w4 = reinterpret_cast<const float4 *>(sh_w);
     float Tp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const f32x16 &acc = hb ? acc1 : acc0;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const float4 wv = w4[8 * hb + 2 * g + hf];
-            const float wg[4] = {wv.x, wv.y, wv.z, wv.w};
+            const float *wg = wr[hb][g];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float x = __int_as_float(max(__float_as_int(acc[4 * g + e]), 0));
@@ -359,6 +358,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         make_rsrc(score_row ? score_row : out_row, score_row ? (uint32_t)col_end * 4u : 0u);
     const uint32_t lane_row = (uint32_t)n32 * kRowBytes;
     SlotRaw graw = raw0;
+    float wr[2][4][4];                                // the lane's 32 head weights
     for (int g0 = j0; g0 < j1; g0 += 64) {
         const int gn = min(64, j1 - g0);
         int32_t lane_ebase = 0;
@@ -389,7 +389,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
             const int t = tau & 1;
             const int col = (g0 + (tau >> 1)) * kBlock + 32 * t + n32;
             float logit = -__builtin_inff();
-            if (prow0 >= 0) logit = score_tile(src, qa, sh_w, hf, ebase + 32 * t + n32, r.limit);
+            if (prow0 >= 0) logit = score_tile(src, qa, wr, hf, ebase + 32 * t + n32, r.limit);
             const uint32_t off = (tau < ntiles && hf == 0) ? (uint32_t)col * 4u : kDrop;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, 0);
             if (score_row) {                          // uniform: scores requested
@@ -403,6 +403,17 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         if (g0 == j0) {
             sh_w[lane] = w_lane;                        // w[b] into the wave's LDS slot
             __builtin_amdgcn_wave_barrier();
+            const float4 *w4 = reinterpret_cast<const float4 *>(sh_w);
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 wv = w4[8 * hb + 2 * g + hf];
+                    wr[hb][g][0] = wv.x;
+                    wr[hb][g][1] = wv.y;
+                    wr[hb][g][2] = wv.z;
+                    wr[hb][g][3] = wv.w;
+                }
         }
         for (int base = 0; base < ntiles; base += kRing) {
 #pragma unroll
