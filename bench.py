@@ -212,7 +212,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              f"this build has no multi-GPU path", file=sys.stderr)
+              f"the library runs on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
