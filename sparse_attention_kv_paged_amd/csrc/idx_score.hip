@@ -19,14 +19,18 @@
 //                             bf16 in registers (v_cvt_scalef32_pk_bf16_fp8,
 //                             scale 1.0)
 // The reduction index d is permuted identically in A and B: k-step kk, lane
-// half hf covers d = 64*hf + 8*kk + 0..7, so each lane streams one contiguous
-// 64-byte half row with four 16-byte loads and never re-reads it.
+// half hf covers d = 64*hf + 8*kk + 0..7.  Key tiles reach LDS by
+// buffer-to-LDS loads that each read eight whole consecutive rows (a per-wave
+// two-slot ring), and each lane then reads its 64-byte half row from LDS.
 // The accumulator gives each lane 16 heads x 1 entry per head block, so the
 // relu / head-weight / head-sum epilogue is 32 in-register FMAs plus one
 // cross-half add.  The row scale s is applied after the head sum as
 // |s| * sum_h relu(x_h) w_h, which equals the definition because
 // relu(s x) = |s| relu(sign(s) x); for s < 0 the fp8 sign bits are flipped
-// before conversion (exact).
+// before conversion (exact).  The tile loop is a two-stage pipeline: tile
+// t's MFMAs are interleaved with tile t-1's epilogue, because the VALU work
+// per tile (conversion + epilogue) is close to the MFMA time and the two
+// only overlap when they sit in one straight-line stretch of code.
 #include <algorithm>
 
 #include <hip/hip_ext.h>
@@ -159,18 +163,53 @@ struct KeyHalf {
     float s;      // the row's scale
 };
 
-// Every load and store of the tile loop goes through a buffer descriptor
-// (make_rsrc), so none of them sits behind a branch and the compiler's wait
-// counts stay exact across the ring.
+// Key tiles travel from memory straight into a per-wave LDS ring
+// (buffer_load ... lds: lane l of a load lands at byte 16*l -- or 4*l for a
+// 4-byte load -- of the destination, no registers involved).  Load i of a
+// 32-row tile brings rows 8*i .. 8*i + 7 whole, so every load instruction
+// reads ~1 KB of consecutive bytes; lane l takes 16-byte chunk
+// c = (l & 7) ^ (l >> 3) of row 8*i + (l >> 3).  In LDS, chunk c of tile
+// row n is granule 8*n + (c ^ (n & 7)): the eight rows that eight
+// consecutive lanes read back sit in eight different bank groups.  A fifth
+// load puts the 32 row scales (twice: lanes 32-63 repeat lanes 0-31) after
+// the fp8 bytes.
+constexpr int kTileFp8 = 32 * kHeadDim;                // one tile's fp8 bytes in LDS
+constexpr int kTileBytes = kTileFp8 + 64 * 4;          // + the scales
 
-// The lane's half row: 64 fp8 bytes at voff (row * 132 + 64 * hf) and the
-// scale at soff (row * 132 + 128) of the block described by r.
-__device__ __forceinline__ void load_key_half(KeyHalf &k, __amdgpu_buffer_rsrc_t r, uint32_t voff,
-                                              uint32_t soff) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) k.v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, 0, 0);
-    k.s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, soff, 0, 0));
+// The lane's byte offset (within a tile) of the chunk it loads with load 0.
+__device__ __forceinline__ uint32_t tile_load_offset(int lane) {
+    return (uint32_t)(lane >> 3) * kRowBytes + 16u * (uint32_t)((lane & 7) ^ (lane >> 3));
 }
+
+// Issue the five loads of the tile whose first row is at byte t0 of the
+// block described by r into the LDS slot dst.
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, uint32_t t0, uint32_t lo, uint8_t *dst) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 1024 * i), 16,
+                                                 t0 + lo + 8u * kRowBytes * i, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + kTileFp8), 4,
+                                             t0 + (uint32_t)(threadIdx.x & 31) * kRowBytes + kHeadDim, 0, 0, 0);
+}
+
+// The lane's half row (lane >> 5) of tile row (lane & 31), and that row's
+// scale, from an LDS slot.
+__device__ __forceinline__ void read_tile(const uint8_t *slot, KeyHalf &k) {
+    const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        k.v[j] = *reinterpret_cast<const u32x4 *>(slot + 128 * n + 16 * ((4 * hf + j) ^ (n & 7)));
+    k.s = *reinterpret_cast<const float *>(slot + kTileFp8 + 4 * lane);
+}
+
+// The compiler does not see that an LDS read depends on a buffer-to-LDS
+// load, so the ring's waits are explicit, and each is also a compiler
+// barrier for memory operations.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // fp8 bytes [2*HI, 2*HI+1] of x -> two bf16 in one dword, exact (scale 1).
 template <bool HI>
@@ -192,54 +231,65 @@ __device__ __forceinline__ int64_t readlane64(int64_t v, int lane) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// One 32-entry tile: MFMA contraction, relu / head-weight / head-sum epilogue,
-// scale and bound.  Returns the logit of entry (lane & 31) on every lane.
-// Accumulator register i of head block hb is head 32*hb + 8*(i/4) + 4*hf +
-// i%4; wr[hb][g][i%4] holds that head's weight w[b] (g = i/4), loaded once
-// per span.
-__device__ __forceinline__ float score_tile(KeyHalf &k, const bf16x8 (&qa)[2][8],
-                                            const float (&wr)[2][4][4], int hf, int e, int limit) {
+// A tile's contraction result: for head block hb, accumulator register i
+// of lane (hf, n) is head 32*hb + 8*(i/4) + 4*hf + i%4 against entry n.
+struct TileAcc {
+    f32x16 h0, h1;
+};
+
+// MFMA half of one 32-entry tile: exact fp8 -> bf16 widening and the
+// contraction over the 128 dims, for both head blocks.
+__device__ __forceinline__ void tile_mma(KeyHalf &k, const bf16x8 (&qa)[2][8], TileAcc &acc) {
     // relu(s x) = |s| relu(sign(s) x): flip the fp8 signs of rows with s < 0
     if (__any(k.s < 0.f)) {
         const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) k.v[i] ^= u32x4{m, m, m, m};
     }
-    f32x16 acc0 = {}, acc1 = {};
+    acc.h0 = f32x16{};
+    acc.h1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
         const u32x4 &v = k.v[kk >> 1];
         const bf16x8 kb = (kk & 1) ? fp8x8_to_bf16x8(v.z, v.w) : fp8x8_to_bf16x8(v.x, v.y);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kk], kb, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kk], kb, acc1, 0, 0, 0);
+        acc.h0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kk], kb, acc.h0, 0, 0, 0);
+        acc.h1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kk], kb, acc.h1, 0, 0, 0);
     }
+}
+
+// Epilogue half: relu, head weights and head sum, then the row scale.
+// wr[hb][g][i%4] holds the weight w[b] of the head that accumulator
+// register i = 4*g + i%4 of head block hb carries on this lane.  Returns the
+// logit of entry (lane & 31) on every lane, or -inf when !keep.
+__device__ __forceinline__ float tile_logit(const TileAcc &acc, const float (&wr)[2][4][4], float s, bool keep) {
     // relu as a signed-integer max on the float's bits (negative floats,
     // -0.0 included, have the sign bit set and become +0.0): one VALU op with
     // no NaN canonicalisation; four partial sums break the FMA chain
     float Tp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-        const f32x16 &acc = hb ? acc1 : acc0;
+        const f32x16 &h = hb ? acc.h1 : acc.h0;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const float *wg = wr[hb][g];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float x = __int_as_float(max(__float_as_int(acc[4 * g + e]), 0));
-                Tp[e] = fmaf(x, wg[e], Tp[e]);
+                const float x = __int_as_float(max(__float_as_int(h[4 * g + e]), 0));
+                Tp[e] = fmaf(x, wr[hb][g][e], Tp[e]);
             }
         }
     }
-    float T = (Tp[0] + Tp[1]) + (Tp[2] + Tp[3]);
-    T += __shfl_xor(T, 32, 64);
-    return e < limit ? fabsf(k.s) * T : -__builtin_inff();
+    const float T = (Tp[0] + Tp[1]) + (Tp[2] + Tp[3]);
+    // the two lane halves hold the two halves of the head sum: swapping
+    // them across lanes 0-31 / 32-63 gives both halves the same total
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(T), __float_as_uint(T), false, false);
+    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    return keep ? fabsf(s) * tot : -__builtin_inff();
 }
 
-// Key tiles in flight per wave.  Two per wave over the whole grid already
-// keep more bytes in flight than HBM needs at its loaded latency; deeper
-// rings only lengthen the memory queues, which delays the dependent
-// block-table reads of the waves that start last.
-constexpr int kRing = 2;
+// Key tiles in flight per wave: two (the LDS ring's slots).  Two per wave
+// over the whole grid already keep more bytes in flight than HBM needs at
+// its loaded latency; deeper rings only lengthen the memory queues, which
+// delays the dependent block-table reads of the waves that start last.
 constexpr int kFlatRows = 512;  // rows up to which waves share work evenly
 
 __device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_t &st) {
@@ -324,16 +374,16 @@ struct NoQ {
 // caller, and qfin(qa) -- called once, right after the first ring of key
 // loads has been issued, by every wave of the workgroup (it synchronises
 // the workgroup) -- delivers the MFMA operands of q[b].
-template <bool OWN_COLS, bool CHUNKED, bool USE_PRE = false, class QFin = NoQ>
+template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool USE_PRE = false, class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
-                                           int col_end, float *sh_w, uint32_t &st,
+                                           int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
                                            const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{}) {
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int n32 = lane & 31;
     const bool live = r.req >= 0 && j0 < r.nslots;
     float *out_row = a.logits + (int64_t)b * a.ld;
-    float *score_row = a.scores ? a.scores + (int64_t)b * a.ld : nullptr;
+    float *score_row = SCORES ? a.scores + (int64_t)b * a.ld : nullptr;
 
     // Start-up reads, issued back to back in the order they are needed (the
     // vector memory counter retires in order) and none behind a branch:
@@ -351,12 +401,12 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 
     // Slots go in groups of up to 64: lane j resolves slot j of the group
     // (one vector load per table level), then the group's tiles stream
-    // through a ring of kRing tiles in flight.  Tiles of absent blocks and
+    // through the wave's two-slot LDS ring.  Tiles of absent blocks and
     // ring slots past the group's end get an empty descriptor (no traffic).
     const __amdgpu_buffer_rsrc_t out_r = make_rsrc(out_row, (uint32_t)col_end * 4u);
     const __amdgpu_buffer_rsrc_t sc_r =
         make_rsrc(score_row ? score_row : out_row, score_row ? (uint32_t)col_end * 4u : 0u);
-    const uint32_t lane_row = (uint32_t)n32 * kRowBytes;
+    const uint32_t lane_lo = tile_load_offset(lane);
     SlotRaw graw = raw0;
     float wr[2][4][4];                                // the lane's 32 head weights
     for (int g0 = j0; g0 < j1; g0 += 64) {
@@ -368,37 +418,61 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         // (no traffic when there is no next group)
         graw = slot_raw<CHUNKED>(a, r.req, b, g0 + 64 + lane, live && lane < min(64, j1 - g0 - 64));
         const int ntiles = 2 * gn;
-        KeyHalf kv[kRing];
-        int64_t prow_t[kRing];
-        int32_t ebase_t[kRing];
-        auto issue = [&](int tau, KeyHalf &dst, int64_t &prow0, int32_t &ebase) {
+        int64_t prow_t[2];
+        int32_t ebase_t[2];
+        // tile tau of the group: rows 32*(tau & 1) .. +31 of slot tau >> 1,
+        // into ring slot tau & 1; tiles past the group's end and tiles of
+        // absent blocks get an empty descriptor (no traffic).  Selects, no
+        // branches, so the loop body stays one block for the scheduler.
+        auto issue = [&](int tau) {
             const int j = min(tau >> 1, gn - 1);
-            prow0 = tau < ntiles ? readlane64(lane_prow0, j) : -1;
-            ebase = __builtin_amdgcn_readlane(lane_ebase, j);
-            uint32_t bytes = 0;
-            const uint8_t *base = a.pool;
-            if (prow0 >= 0) {
-                base = a.pool + prow0 * kRowBytes;
-                bytes = (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - prow0) * kRowBytes;
-            }
-            const __amdgpu_buffer_rsrc_t kr = make_rsrc(base, bytes);
-            const uint32_t row = (uint32_t)(32 * (tau & 1)) * kRowBytes + lane_row;
-            load_key_half(dst, kr, row + 64u * (uint32_t)hf, row + (uint32_t)kHeadDim);
+            const int64_t pr = readlane64(lane_prow0, j);
+            const int64_t prow0 = tau < ntiles ? pr : -1;
+            prow_t[tau & 1] = prow0;
+            ebase_t[tau & 1] = __builtin_amdgcn_readlane(lane_ebase, j) + 32 * (tau & 1);
+            const bool ok = prow0 >= 0;
+            const int64_t p0 = ok ? prow0 : 0;
+            const uint32_t bytes = ok ? (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - p0) * kRowBytes : 0u;
+            load_tile(make_rsrc(a.pool + p0 * kRowBytes, bytes), (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo,
+                      ring + (tau & 1) * kTileBytes);
         };
-        auto consume = [&](int tau, KeyHalf &src, int64_t prow0, int32_t ebase) {
-            const int t = tau & 1;
-            const int col = (g0 + (tau >> 1)) * kBlock + 32 * t + n32;
-            float logit = -__builtin_inff();
-            if (prow0 >= 0) logit = score_tile(src, qa, wr, hf, ebase + 32 * t + n32, r.limit);
-            const uint32_t off = (tau < ntiles && hf == 0) ? (uint32_t)col * 4u : kDrop;
+        // a tile's epilogue inputs, kept with its accumulators because the
+        // ring slot is reloaded before the epilogue runs
+        struct Stage {
+            TileAcc acc;
+            float s;
+            bool keep;
+        };
+        // tile tau's contraction.  Its ring slot is free for tile tau + 2 as
+        // soon as the lane has read it, and that reload goes out before the
+        // MFMAs, so the contraction and the caller's next epilogue form one
+        // straight-line stretch for the scheduler to interleave.  The wait
+        // for the tile's loads counts only the five loads of tile tau + 1 as
+        // later: vector memory loads complete in order, so this holds
+        // whatever order stores take.
+        auto mma = [&](int tau, Stage &st_) {
+            const int k = tau & 1;
+            wait_vmem<5>();
+            KeyHalf kh;
+            read_tile(ring + k * kTileBytes, kh);
+            wait_lds();
+            st_.keep = prow_t[k] >= 0 && ebase_t[k] + n32 < r.limit;
+            issue(tau + 2);
+            tile_mma(kh, qa, st_.acc);
+            st_.s = kh.s;
+        };
+        auto finish = [&](int tau, const Stage &st_) {
+            const float logit = tile_logit(st_.acc, wr, st_.s, st_.keep);
+            const int col = (g0 + (tau >> 1)) * kBlock + 32 * (tau & 1) + n32;
+            const uint32_t off = hf == 0 ? (uint32_t)col * 4u : kDrop;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, 0);
-            if (score_row) {                          // uniform: scores requested
+            if (SCORES) {
                 const float score = 1.0f / (1.0f + expf(-logit));
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), sc_r, off, 0, 0);
             }
         };
-#pragma unroll
-        for (int i = 0; i < kRing; ++i) issue(i, kv[i], prow_t[i], ebase_t[i]);
+        issue(0);
+        issue(1);
         if (USE_PRE && g0 == j0) qfin(qa);            // q arrives while the ring is in flight
         if (g0 == j0) {
             sh_w[lane] = w_lane;                        // w[b] into the wave's LDS slot
@@ -415,12 +489,20 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
                     wr[hb][g][3] = wv.w;
                 }
         }
-        for (int base = 0; base < ntiles; base += kRing) {
-#pragma unroll
-            for (int i = 0; i < kRing; ++i) {
-                consume(base + i, kv[i], prow_t[i], ebase_t[i]);
-                issue(base + i + kRing, kv[i], prow_t[i], ebase_t[i]);
+        // Two-stage pipeline over the ring: the contraction of tile tau is
+        // issued before the epilogue of tile tau - 1, so the MFMA chain of
+        // one tile runs under the other's VALU work.  ntiles is even.
+        Stage sa, sb;
+        mma(0, sa);
+        for (int tau = 1;; tau += 2) {
+            mma(tau, sb);
+            finish(tau - 1, sa);
+            if (tau + 1 >= ntiles) {
+                finish(tau, sb);
+                break;
             }
+            mma(tau + 1, sa);
+            finish(tau, sb);
         }
     }
 }
@@ -430,13 +512,14 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // FLAT: the (row, slot) work of all rows is flattened and split evenly over
 // every wave of the grid (rows of very different lengths); otherwise each
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
-template <bool OWN_COLS, bool FLAT, bool CHUNKED>
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
     __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
     __shared__ int32_t sh_rreq[FLAT ? kFlatRows : 1], sh_rlim[FLAT ? kFlatRows : 1], sh_rslots[FLAT ? kFlatRows : 1];
     __shared__ uint32_t sh_scan[kWaves];
     __shared__ __attribute__((aligned(16))) uint16_t sh_q[FLAT ? 2 : 1][kQStage];
+    __shared__ __attribute__((aligned(16))) uint8_t sh_ring[kWaves][2 * kTileBytes];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
     const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
@@ -465,7 +548,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
-            score_span<OWN_COLS, CHUNKED, true>(a, b, j0, j1, r, col_end, sh_w[wave], st, raw0, qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put_q_rows<1>(a, b, qv, sh_q);            // the workgroup's one barrier
             __syncthreads();
@@ -549,7 +632,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, CHUNKED, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], st, raw0,
+            score_span<OWN_COLS, SCORES, CHUNKED, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
                                                 qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
@@ -561,43 +644,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
                 r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, CHUNKED>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], st);
+                score_span<OWN_COLS, SCORES, CHUNKED>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
                 f = min(fend, pe);
             }
         }
     }
+    wait_vmem<0>();     // no buffer-to-LDS load outlives the workgroup
     if (st && a.status) atomicOr(a.status, st);
 }
 
 }  // namespace
 
-template <bool OWN_COLS, bool FLAT>
+template <bool OWN_COLS, bool SCORES, bool FLAT>
 void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 g((unsigned)grid), blk(256);
     if (a.chunk_ids)
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, true>), g, blk, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true>), g, blk, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, FLAT, false>), g, blk, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false>), g, blk, 0, s, e0, e1, 0, a);
 }
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.B <= 0) return hipSuccess;
+    // the top-k feed (row_cols) never asks for scores
     const bool own = a.row_cols != nullptr;
-    if (a.B <= kFlatRows) {
+    const bool scores = !own && a.scores != nullptr;
+    const bool flat = a.B <= kFlatRows;
+    int64_t grid;
+    if (flat) {
         // one resident round: up to 2 workgroups per CU, never more waves
         // than (row, slot) pairs
         const int64_t slots = (a.n_cols + kBlock - 1) / kBlock;
-        const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(512, ((int64_t)a.B * slots + kWaves - 1) / kWaves));
-        if (own)
-            launch_score_as<true, true>(a, grid, s, e0, e1);
-        else
-            launch_score_as<false, true>(a, grid, s, e0, e1);
+        grid = std::max<int64_t>(1, std::min<int64_t>(512, ((int64_t)a.B * slots + kWaves - 1) / kWaves));
     } else {
-        const int64_t grid = (int64_t)a.B * a.splits;
-        if (own)
-            launch_score_as<true, false>(a, grid, s, e0, e1);
-        else
-            launch_score_as<false, false>(a, grid, s, e0, e1);
+        grid = (int64_t)a.B * a.splits;
+    }
+    if (own) {
+        if (flat) launch_score_as<true, false, true>(a, grid, s, e0, e1);
+        else launch_score_as<true, false, false>(a, grid, s, e0, e1);
+    } else if (scores) {
+        if (flat) launch_score_as<false, true, true>(a, grid, s, e0, e1);
+        else launch_score_as<false, true, false>(a, grid, s, e0, e1);
+    } else {
+        if (flat) launch_score_as<false, false, true>(a, grid, s, e0, e1);
+        else launch_score_as<false, false, false>(a, grid, s, e0, e1);
     }
     return hipGetLastError();
 }
