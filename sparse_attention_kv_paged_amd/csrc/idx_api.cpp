@@ -49,7 +49,7 @@ struct TopkPlan {
 int list_cap(int32_t k) { return (k + 1) & ~1; }
 
 int seg_cap_for(int64_t cols) {
-    for (int c : {4096, 8192, 16384})
+    for (int c : {4096, 8192, 16384, 20480, 24576})
         if (cols <= c) return c;
     return idx::kSegLogitCap;
 }

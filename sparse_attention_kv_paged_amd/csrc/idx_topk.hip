@@ -297,8 +297,10 @@ __device__ __forceinline__ void write_final(const SegArgs &a, int b, WinCursor c
     float *ov = a.out_val ? a.out_val + (int64_t)b * k : nullptr;
     const __amdgpu_buffer_rsrc_t ir = make_rsrc(oi, k * 4u);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(ov ? (void *)ov : (void *)oi, ov ? k * 4u : 0u);
-    // groups of 8 slots: their chunk lookups are in flight together
-    constexpr int kG = PER < 8 ? PER : 8;
+    // groups of up to 8 slots (a divisor of PER): their chunk lookups are in
+    // flight together
+    constexpr int kG = PER % 8 == 0 ? 8 : (PER % 4 == 0 ? 4 : (PER % 2 == 0 ? 2 : 1));
+    static_assert(PER % kG == 0, "slot groups must tile the thread's slots");
 #pragma unroll
     for (int g = 0; g < PER; g += kG) {
         uint32_t e[kG], pos[kG];
@@ -471,7 +473,9 @@ hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
 }  // namespace
 
 // Capacities (items per workgroup / threads): logits 4096/512, 8192/1024,
-// 16384/1024, 32768/1024; lists 4096/512, 16384/1024.  `fused` (logits with
+// 16384/1024, 20480/1024, 24576/1024, 32768/1024 (the smallest that holds a
+// part: every slot costs work whether it holds a column or not); lists
+// 4096/512, 16384/1024.  `fused` (logits with
 // several parts per row whose lists, parts * (k rounded up to even) items,
 // fit in 2 * cap; row_done zeroed) merges in the same launch.
 hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused, hipStream_t s) {
@@ -488,6 +492,8 @@ hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused,
     case 4096: return launch_seg<4096, false, 512>(a, s);
     case 8192: return launch_seg<8192, false, 1024>(a, s);
     case 16384: return launch_seg<16384, false, 1024>(a, s);
+    case 20480: return launch_seg<20480, false, 1024>(a, s);
+    case 24576: return launch_seg<24576, false, 1024>(a, s);
     default: return launch_seg<kSegLogitCap, false, 1024>(a, s);
     }
 }

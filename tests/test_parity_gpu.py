@@ -318,3 +318,21 @@ def test_topk_standalone_multilevel(n, k):
     ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
     assert np.array_equal(cols.cpu().numpy(), ref_cols)
     assert np.array_equal(v.cpu().numpy(), ref_v.astype(np.float32))
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n,k", [(17408, 512), (20000, 512), (24000, 2048), (24576, 7)])
+def test_topk_standalone_one_segment_per_row(n, k):
+    """Many rows (one top-k workgroup per row) whose segment sizes are not a
+    multiple of the write-out's 8-slot groups (20 and 24 slots per thread)."""
+    rng = np.random.default_rng(n + 7 * k)
+    B = 256
+    vals = rng.standard_normal((B, n)).astype(np.float32)
+    vals[1, ::3] = -np.inf
+    vals[2, :] = np.round(vals[2, :] * 4) / 4                 # many exact ties
+    vals[3, n // 2:] = -np.inf                                # half the row not selectable
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    assert np.array_equal(cols.cpu().numpy(), ref_cols)
+    assert np.array_equal(v.cpu().numpy(), ref_v.astype(np.float32))
+
