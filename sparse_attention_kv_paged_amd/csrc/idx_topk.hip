@@ -181,12 +181,19 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
         const int x = __float2int_rz((key_value(kj) - vmin) * scale);        // >= 0 (NaN -> 0)
         return kj ? min((uint32_t)x, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (lane & 31));
     };
-    constexpr bool kKeep = PER <= 16;                 // else recomputed (registers)
-    uint32_t bins[kKeep ? PER : 1];
+    // the bins are kept for step 4: one per register up to 16 slots, else
+    // two 16-bit bins per register (bins < 2080)
+    constexpr bool kWide = PER <= 16;
+    uint32_t bins[kWide ? PER : (PER + 1) / 2];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const uint32_t bn = bin_of(key[j]);
-        if (kKeep) bins[kKeep ? j : 0] = bn;
+        if (kWide)
+            bins[j] = bn;
+        else if (j & 1)
+            bins[j >> 1] |= bn << 16;
+        else
+            bins[j >> 1] = bn;
         atomicAdd(&sh.hist[bn], 1u);
     }
     __syncthreads();
@@ -197,7 +204,10 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     const uint32_t n_in_bin = sh.hist[cbin];
     // 4. few members: their keys go to LDS (in any order) and one wave
     // ranks them against each other
-    const auto in_cut_bin = [&](int j) { return (kKeep ? bins[kKeep ? j : 0] : bin_of(key[j])) == cbin; };
+    const auto in_cut_bin = [&](int j) {
+        if (kWide) return bins[j] == cbin;
+        return ((j & 1) ? bins[j >> 1] >> 16 : bins[j >> 1] & 0xFFFFu) == cbin;
+    };
     if (n_in_bin <= 64u) {
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -314,15 +324,23 @@ __device__ __forceinline__ void write_final(const SegArgs &a, int b, WinCursor c
                 const uint32_t off = pos[j] == kLoses ? kDrop : (col(g + j) / kBlock) * 4u;
                 e[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, off, 0, 0) * kBlock + col(g + j) % kBlock;
             }
+#pragma unroll
+            for (int j = 0; j < kG; ++j) {
+                const uint32_t off = byte_off(pos[j], 4u);
+                __builtin_amdgcn_raw_buffer_store_b32(e[j], ir, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key[g + j])), vr, off, 0, 0);
+            }
         } else {
+            // few slots hold a winner: a slot no lane of the wave wins
+            // issues no stores
 #pragma unroll
-            for (int j = 0; j < kG; ++j) e[j] = col(g + j);
-        }
-#pragma unroll
-        for (int j = 0; j < kG; ++j) {
-            const uint32_t off = byte_off(pos[j], 4u);
-            __builtin_amdgcn_raw_buffer_store_b32(e[j], ir, off, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key[g + j])), vr, off, 0, 0);
+            for (int j = 0; j < kG; ++j) {
+                if (__any(pos[j] != kLoses)) {
+                    const uint32_t off = byte_off(pos[j], 4u);
+                    __builtin_amdgcn_raw_buffer_store_b32(col(g + j), ir, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(key_value(key[g + j])), vr, off, 0, 0);
+                }
+            }
         }
     }
     for (uint32_t i = count + threadIdx.x; i < k; i += NT) {
@@ -349,10 +367,13 @@ __device__ __forceinline__ void write_list(uint2 *dst, uint32_t lcap, WinCursor 
     const __amdgpu_buffer_rsrc_t r = make_rsrc(dst, lcap * 8u);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        u32x2 v;
-        v.x = key[j];
-        v.y = col(j);
-        __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off(cur.next(key[j]), 8u), 0, aux);
+        const uint32_t pos = cur.next(key[j]);
+        if (__any(pos != kLoses)) {                   // a slot no lane wins issues no store
+            u32x2 v;
+            v.x = key[j];
+            v.y = col(j);
+            __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off(pos, 8u), 0, aux);
+        }
     }
     const u32x2 zero = {0u, 0u};
     for (uint32_t i = count + threadIdx.x; i < lcap; i += NT) __builtin_amdgcn_raw_buffer_store_b64(zero, r, i * 8u, 0, aux);
