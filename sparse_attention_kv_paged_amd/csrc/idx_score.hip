@@ -535,8 +535,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             a.row_cols[b] = (uint32_t)col_end;
             if (a.row_done) a.row_done[b] = 0u;
         }
-        const int j0 = (split * kWaves + wave) * a.slots_per_wave;
-        const int j1 = min(j0 + a.slots_per_wave, slot_stop);
+        // a row that one workgroup covers is split evenly over its four
+        // waves by the row's own length (rows of one launch differ in length)
+        const int spw = a.splits == 1 ? (slot_stop + kWaves - 1) / kWaves : a.slots_per_wave;
+        const int j0 = (split * kWaves + wave) * spw;
+        const int j1 = min(j0 + spw, slot_stop);
         // the first group's table reads, then q[b] staged in LDS once for
         // the four waves
         const SlotRaw raw0 = slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));

@@ -493,7 +493,9 @@ hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
 
 }  // namespace
 
-// Capacities (items per workgroup / threads): logits 4096/512, 8192/1024,
+// Capacities (items per workgroup / threads): logits 4096/512 (4096/1024 when
+// the row's last part merges: the latency-bound phases run faster on more
+// waves), 8192/1024,
 // 16384/1024, 20480/1024, 24576/1024, 32768/1024 (the smallest that holds a
 // part: every slot costs work whether it holds a column or not); lists
 // 4096/512, 16384/1024.  `fused` (logits with
@@ -504,7 +506,7 @@ hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused,
     if (fused) {
         const bool one = (int64_t)a.parts * list_cap((uint32_t)a.k) <= cap;
         switch (cap) {
-        case 4096: return one ? launch_seg<4096, false, 512, 1>(a, s) : launch_seg<4096, false, 512, 2>(a, s);
+        case 4096: return one ? launch_seg<4096, false, 1024, 1>(a, s) : launch_seg<4096, false, 1024, 2>(a, s);
         case 8192: return one ? launch_seg<8192, false, 1024, 1>(a, s) : launch_seg<8192, false, 1024, 2>(a, s);
         default: return hipErrorInvalidValue;
         }
