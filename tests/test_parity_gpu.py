@@ -154,9 +154,9 @@ def test_full_size_prefill_sampled_rows():
 
 
 def test_many_rows_sharing_a_request():
-    """More than 512 rows of one request take the path where four rows share
-    each key tile; a padding row, an out-of-range request id and a partial
-    last group of rows fall back to one row per wave."""
+    """More than 512 rows of one request take the per-row path (one
+    workgroup per row, its four waves splitting the row's blocks); a padding
+    row and an out-of-range request id among them."""
     wl = W.prefill(8192, 603, seed=13, name="shared-rows")
     wl.q_req = wl.q_req.copy()
     wl.q_req[301] = -1                                         # padding row inside a group
@@ -253,6 +253,29 @@ def test_negative_and_zero_scales():
     sc[rng.random(len(sc)) < 0.05] = 0.0
     wl.pool[:, 128:] = sc.view(np.uint8)
     _check_workload(wl, tag="edge-scales")
+
+
+def _flip_some_scales(wl, seed):
+    sc = wl.pool[:, 128:].copy().view("<f4")
+    rng = np.random.default_rng(seed)
+    sc[rng.random(len(sc)) < 0.3] *= -1
+    sc[rng.random(len(sc)) < 0.05] = 0.0
+    wl.pool[:, 128:] = sc.view(np.uint8)
+
+
+def test_per_row_path_negative_and_zero_scales():
+    """Over 512 rows (one workgroup per row): negative and zero scales reach
+    the sign flip inside the pipelined tile loop; logits, scores and top-k."""
+    wl = W.prefill(4096, 600, seed=21, name="per-row-edge-scales")
+    _flip_some_scales(wl, 22)
+    _check_workload(wl, tag="per-row-edge-scales")
+
+
+def test_per_row_path_chunk_lists_negative_scales():
+    """Over 512 rows with chunk lists (per-row path, chunked kernel)."""
+    wl = W.resident(B=520, chunks_per_req=64, n_resident=20, seed=23, name="per-row-chunks")
+    _flip_some_scales(wl, 24)
+    _check_workload(wl, tag="per-row-chunks")
 
 
 def test_contiguous_chunk_list():
