@@ -288,8 +288,9 @@ __device__ __forceinline__ float tile_logit(const TileAcc &acc, const float (&wr
 
 // Key tiles in flight per wave: two (the LDS ring's slots).  Two per wave
 // over the whole grid already keep more bytes in flight than HBM needs at
-// its loaded latency; deeper rings only lengthen the memory queues, which
-// delays the dependent block-table reads of the waves that start last.
+// its loaded latency; deeper rings (three slots measured on every workload)
+// only lengthen the memory queues, which delays the dependent block-table
+// reads of the waves that start last.
 constexpr int kFlatRows = 512;  // rows up to which waves share work evenly
 
 __device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_t &st) {
@@ -422,8 +423,9 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         int32_t ebase_t[2];
         // tile tau of the group: rows 32*(tau & 1) .. +31 of slot tau >> 1,
         // into ring slot tau & 1; tiles past the group's end and tiles of
-        // absent blocks get an empty descriptor (no traffic).  Selects, no
-        // branches, so the loop body stays one block for the scheduler.
+        // absent blocks get an empty descriptor (no traffic).  It runs
+        // before a tile's MFMAs, so the scalar descriptor arithmetic never
+        // splits the stretch where MFMAs and the epilogue interleave.
         auto issue = [&](int tau) {
             const int j = min(tau >> 1, gn - 1);
             const int64_t pr = readlane64(lane_prow0, j);
