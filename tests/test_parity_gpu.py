@@ -255,6 +255,21 @@ def test_negative_and_zero_scales():
     _check_workload(wl, tag="edge-scales")
 
 
+@pytest.mark.parametrize("B", [601, 602, 603, 300])
+def test_no_writes_past_the_last_row(B):
+    """The last workgroup of the per-row path may hold fewer than four rows;
+    nothing may be written below row B of the logits or scores."""
+    wl = W.prefill(4096, B, seed=25, name="tail-rows")
+    d = L.to_device(wl)
+    guard = 8
+    big_l = torch.full((B + guard, d.n_cols), 7.0, dtype=torch.float32, device="cuda")
+    big_s = torch.full((B + guard, d.n_cols), 7.0, dtype=torch.float32, device="cuda")
+    L.idx_score(d.q, d.w, d.keys, d.n_cols, with_scores=True, logits=big_l[:B], scores=big_s[:B])
+    torch.cuda.synchronize()
+    assert torch.all(big_l[B:] == 7.0) and torch.all(big_s[B:] == 7.0)
+    assert bool(torch.all(big_l[:B] != 7.0))
+
+
 def _flip_some_scales(wl, seed):
     sc = wl.pool[:, 128:].copy().view("<f4")
     rng = np.random.default_rng(seed)
