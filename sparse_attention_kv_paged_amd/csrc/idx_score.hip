@@ -375,7 +375,7 @@ struct NoQ {
 // caller, and qfin(qa) -- called once, right after the first ring of key
 // loads has been issued, by every wave of the workgroup (it synchronises
 // the workgroup) -- delivers the MFMA operands of q[b].
-template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool USE_PRE = false, class QFin = NoQ>
+template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool USE_PRE = false, class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
                                            const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{}) {
@@ -408,6 +408,10 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     const __amdgpu_buffer_rsrc_t sc_r =
         make_rsrc(score_row ? score_row : out_row, score_row ? (uint32_t)col_end * 4u : 0u);
     const uint32_t lane_lo = tile_load_offset(lane);
+    // the lane's logit store offset within a tile (the upper half's lanes
+    // hold the same entries and store nothing: kDrop plus any column stays
+    // past every descriptor's end)
+    const uint32_t lane_off = LEAN && hf == 0 ? (uint32_t)n32 * 4u : kDrop;
     SlotRaw graw = raw0;
     float wr[2][4][4];                                // the lane's 32 head weights
     for (int g0 = j0; g0 < j1; g0 += 64) {
@@ -419,24 +423,34 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         // (no traffic when there is no next group)
         graw = slot_raw<CHUNKED>(a, r.req, b, g0 + 64 + lane, live && lane < min(64, j1 - g0 - 64));
         const int ntiles = 2 * gn;
-        int64_t prow_t[2];
-        int32_t ebase_t[2];
         // tile tau of the group: rows 32*(tau & 1) .. +31 of slot tau >> 1,
         // into ring slot tau & 1; tiles past the group's end and tiles of
-        // absent blocks get an empty descriptor (no traffic).  It runs
-        // before a tile's MFMAs, so the scalar descriptor arithmetic never
-        // splits the stretch where MFMAs and the epilogue interleave.
+        // absent blocks get an empty descriptor (no traffic).  The slot's
+        // descriptor and bound are worked out at its first tile and reused
+        // for its second (tiles are issued in order).  It runs before a
+        // tile's MFMAs, so the scalar descriptor arithmetic never splits the
+        // stretch where MFMAs and the epilogue interleave.
+        int32_t lim_t[2];                               // entries of the tile below the bound
+        __amdgpu_buffer_rsrc_t slot_r = make_rsrc(a.pool, 0u);
+        int32_t slot_lim = 0;
         auto issue = [&](int tau) {
-            const int j = min(tau >> 1, gn - 1);
-            const int64_t pr = readlane64(lane_prow0, j);
-            const int64_t prow0 = tau < ntiles ? pr : -1;
-            prow_t[tau & 1] = prow0;
-            ebase_t[tau & 1] = __builtin_amdgcn_readlane(lane_ebase, j) + 32 * (tau & 1);
-            const bool ok = prow0 >= 0;
-            const int64_t p0 = ok ? prow0 : 0;
-            const uint32_t bytes = ok ? (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - p0) * kRowBytes : 0u;
-            load_tile(make_rsrc(a.pool + p0 * kRowBytes, bytes), (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo,
-                      ring + (tau & 1) * kTileBytes);
+            if (!LEAN || (tau & 1) == 0) {
+                const int j = min(tau >> 1, gn - 1);
+                const int64_t pr = readlane64(lane_prow0, j);
+                const int64_t prow0 = tau < ntiles ? pr : -1;
+                const bool ok = prow0 >= 0;
+                const int64_t p0 = ok ? prow0 : 0;
+                const uint32_t bytes = ok ? (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - p0) * kRowBytes : 0u;
+                slot_r = make_rsrc(a.pool + p0 * kRowBytes, bytes);
+                slot_lim = ok ? r.limit - __builtin_amdgcn_readlane(lane_ebase, j) - (LEAN ? 0 : 32 * (tau & 1)) : 0;
+                if (!LEAN) {
+                    lim_t[tau & 1] = slot_lim;
+                    load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * kTileBytes);
+                    return;
+                }
+            }
+            lim_t[tau & 1] = slot_lim - 32 * (tau & 1);
+            load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * kTileBytes);
         };
         // a tile's epilogue inputs, kept with its accumulators because the
         // ring slot is reloaded before the epilogue runs
@@ -458,15 +472,15 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
             KeyHalf kh;
             read_tile(ring + k * kTileBytes, kh);
             wait_lds();
-            st_.keep = prow_t[k] >= 0 && ebase_t[k] + n32 < r.limit;
+            st_.keep = n32 < lim_t[k];
             issue(tau + 2);
             tile_mma(kh, qa, st_.acc);
             st_.s = kh.s;
         };
         auto finish = [&](int tau, const Stage &st_) {
             const float logit = tile_logit(st_.acc, wr, st_.s, st_.keep);
-            const int col = (g0 + (tau >> 1)) * kBlock + 32 * (tau & 1) + n32;
-            const uint32_t off = hf == 0 ? (uint32_t)col * 4u : kDrop;
+            const uint32_t col0 = (uint32_t)((g0 + (tau >> 1)) * kBlock + 32 * (tau & 1));
+            const uint32_t off = LEAN ? lane_off + col0 * 4u : (hf == 0 ? (col0 + (uint32_t)n32) * 4u : kDrop);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, 0);
             if (SCORES) {
                 const float score = 1.0f / (1.0f + expf(-logit));
@@ -553,7 +567,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
-            score_span<OWN_COLS, SCORES, CHUNKED, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put_q_rows<1>(a, b, qv, sh_q);            // the workgroup's one barrier
             __syncthreads();
@@ -637,7 +651,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, SCORES, CHUNKED, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
                                                 qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
@@ -649,7 +663,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
                 r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, SCORES, CHUNKED>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
                 f = min(fend, pe);
             }
         }
