@@ -61,7 +61,11 @@ TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
     P.ld = round_up(std::max<int64_t>(n_cols, 1), 64);
     const int64_t want = std::max<int64_t>(1, (256 + std::max(B, 1) - 1) / std::max(B, 1));
     const int64_t most = std::max<int64_t>(1, ((int64_t)n_cols + 4095) / 4096);
-    const int64_t parts = std::min(want, most);
+    int64_t parts = std::min(want, most);
+    // few long rows: at most 16 parts of up to 16384 columns, merged in the
+    // same launch -- the merge of 16 short lists beats a part-selection of
+    // 8192 columns followed by a merge of 32 lists
+    if (B <= 16 && parts > 16 && ((int64_t)n_cols + 15) / 16 <= 16384) parts = 16;
     P.cap0 = seg_cap_for(((int64_t)n_cols + parts - 1) / parts);
     P.parts0 = (int)std::max<int64_t>(1, ((int64_t)n_cols + P.cap0 - 1) / P.cap0);
     size_t off = 0;
@@ -75,7 +79,8 @@ TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
         P.row_cols = take((size_t)B * sizeof(uint32_t));
         P.row_done = take((size_t)B * sizeof(uint32_t));
         // the score kernel zeroes row_done, so score_topk can merge in place
-        P.fused = P.parts0 > 1 && P.cap0 <= 8192 && (int64_t)P.parts0 * list_cap(k) <= 2 * (int64_t)P.cap0;
+        P.fused = P.parts0 > 1 && P.cap0 <= 16384 &&
+                  (int64_t)P.parts0 * list_cap(k) <= (P.cap0 <= 8192 ? 2 : 1) * (int64_t)P.cap0;
     }
     if (P.parts0 > 1) {
         const int per = idx::kSegListCap / list_cap(k);

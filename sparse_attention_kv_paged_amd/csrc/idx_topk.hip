@@ -500,7 +500,8 @@ hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
 // part: every slot costs work whether it holds a column or not); lists
 // 4096/512, 16384/1024.  `fused` (logits with
 // several parts per row whose lists, parts * (k rounded up to even) items,
-// fit in 2 * cap; row_done zeroed) merges in the same launch.
+// fit in 2 * cap for caps up to 8192 or in cap for 16384; row_done zeroed)
+// merges in the same launch.
 hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused, hipStream_t s) {
     if (list) return cap <= 4096 ? launch_seg<4096, true, 512>(a, s) : launch_seg<kSegListCap, true, 1024>(a, s);
     if (fused) {
@@ -508,6 +509,7 @@ hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused,
         switch (cap) {
         case 4096: return one ? launch_seg<4096, false, 1024, 1>(a, s) : launch_seg<4096, false, 1024, 2>(a, s);
         case 8192: return one ? launch_seg<8192, false, 1024, 1>(a, s) : launch_seg<8192, false, 1024, 2>(a, s);
+        case 16384: return one ? launch_seg<16384, false, 1024, 1>(a, s) : hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
         }
     }
