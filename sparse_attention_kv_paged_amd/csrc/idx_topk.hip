@@ -7,12 +7,11 @@
 // registers for the whole kernel, so after the single global read the passes
 // below are register work plus a few LDS histograms and block scans; nothing
 // needs a global atomic or a zeroed workspace:
-//   1. load the keys and reduce the count, min and max of the selectable
-//      values;
+//   1. load the keys and reduce the min and max of the selectable values;
 //   2. histogram the values into 2048 bins LINEAR in value between min and
 //      max (few LDS atomic collisions, unlike bins of the float's top bits,
 //      which put most logits of a row into a handful of bins), and find the
-//      bin t holding the k-th largest value;
+//      bin t holding the k-th largest value and the selectable count;
 //   3. copy bin t's members to LDS (positions from a block scan) and find the
 //      exact k-th largest key among them: one wave ranks up to 64 members
 //      against each other; larger bins take radix passes over their keys
@@ -70,7 +69,8 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *sh) {
 
 // Bin t of an LDS histogram `h` (nbins a multiple of NT) with
 // count(bins > t) < need <= count(bins >= t).  res[0] = t (-1 if the total is
-// below need), res[1] = count(bins > t).  All NT threads call it.
+// below need), res[1] = count(bins > t), res[2] = the total.  All NT threads
+// call it.
 template <int NT>
 __device__ void find_from_top(const uint32_t *h, int nbins, uint32_t need, int32_t *res,
                               uint32_t *scan_sh) {
@@ -85,7 +85,10 @@ __device__ void find_from_top(const uint32_t *h, int nbins, uint32_t need, int32
     }
     const uint32_t incl = block_scan<NT>(local, scan_sh);
     const uint32_t excl = incl - local;
-    if (tid == NT - 1 && incl < need) res[1] = incl;
+    if (tid == NT - 1) {
+        res[2] = (int32_t)incl;                       // the histogram's total
+        if (incl < need) res[1] = incl;
+    }
     if (excl < need && need <= incl) {
         uint32_t c = excl;
         for (int i = bpt - 1; i >= 0; --i) {
@@ -110,8 +113,7 @@ struct SelScratch {
     uint32_t hist[kBins + 32];
     uint32_t scan_a[NT / 64], scan_b[NT / 64];
     uint32_t kmin[NT / 64], kmax[NT / 64];
-    uint32_t cnt[NT / 64];
-    int32_t res[2];
+    int32_t res[3];
     uint32_t cut[2];
     uint32_t ncand;
     uint32_t flag;
@@ -129,46 +131,44 @@ __device__ __forceinline__ void sel_reset(SelScratch<NT, CAND> &sh) {
 // registers (thread t: key[0..PER) of a column-ordered sequence; key 0 = not
 // selectable), how many of its copies win (need_ties, lowest columns first)
 // and the number of selectable items (total).  kstar = 0 when every
-// selectable item wins.  All threads call it, after sel_reset.
-//   1. count and key range of the selectable items;
+// selectable item wins.  All threads call it, after sel_reset.  With
+// HAVE_V, val[j] is the float whose order key is key[j] (saves decoding it).
+//   1. key range of the selectable items;
 //   2. histogram of 2048 bins linear in value between min and max;
-//   3. the bin t holding the k-th largest value;
+//   3. the bin t holding the k-th largest value (and the selectable count);
 //   4. t's members go to LDS; one wave ranks up to 64 of them against each
 //      other, larger bins take radix passes over their keys (bits 31:21,
 //      20:10, 9:0).
-template <int NT, int PER, int CAND>
+template <int NT, int PER, int CAND, bool HAVE_V = false>
 __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k, SelScratch<NT, CAND> &sh,
-                                         uint32_t &kstar, uint32_t &need_ties, uint32_t &total) {
+                                         uint32_t &kstar, uint32_t &need_ties, uint32_t &total,
+                                         const float *val = nullptr) {
     constexpr int kW = NT / 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // 1. integer min/max of the order-preserving keys
-    uint32_t n_valid = 0, kmn = 0xFFFFFFFFu, kmx = 0u;
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        n_valid += key[j] != 0u;
         kmn = min(kmn, key[j] ? key[j] : 0xFFFFFFFFu);
         kmx = max(kmx, key[j]);
     }
-    n_valid = wave_scan(n_valid);
     kmn = wave_min(kmn);
     kmx = wave_max(kmx);
     if (lane == 63) {
-        sh.cnt[wave] = n_valid;
         sh.kmin[wave] = kmn;
         sh.kmax[wave] = kmx;
     }
     __syncthreads();
-    total = 0;
     kmn = 0xFFFFFFFFu;
     kmx = 0u;
     for (int w = 0; w < kW; ++w) {
-        total += sh.cnt[w];
         kmn = min(kmn, sh.kmin[w]);
         kmx = max(kmx, sh.kmax[w]);
     }
     kstar = 0u;
     need_ties = 0u;
-    if (total <= k) return;                           // uniform
+    total = 0u;
+    if (kmx == 0u) return;                            // uniform: nothing selectable
 
     // 2. value-linear bins (monotone in value); other items go to the extra
     // bins, 32 of them so that a wave's lanes hit distinct LDS banks
@@ -177,8 +177,13 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     const float range = vmax - vmin;
     if (range > 0.f && range < __builtin_inff()) scale = (float)kBins / range;
     if (!(scale < __builtin_inff())) scale = 0.f;
-    const auto bin_of = [&](uint32_t kj) {
-        const int x = __float2int_rz((key_value(kj) - vmin) * scale);        // >= 0 (NaN -> 0)
+    const float off = -vmin * scale;
+    const auto bin_of = [&](int j) {
+        const uint32_t kj = key[j];
+        // fma(v, scale, -vmin*scale) is monotone in v like (v - vmin)*scale;
+        // it only has to be the same function in every pass
+        const float v = HAVE_V ? val[j] : key_value(kj);
+        const int x = __float2int_rz(fmaf(v, scale, off));                // >= 0 (NaN -> 0)
         return kj ? min((uint32_t)x, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (lane & 31));
     };
     // the bins are kept for step 4: one per register up to 16 slots, else
@@ -187,7 +192,7 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     uint32_t bins[kWide ? PER : (PER + 1) / 2];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const uint32_t bn = bin_of(key[j]);
+        const uint32_t bn = bin_of(j);
         if (kWide)
             bins[j] = bn;
         else if (j & 1)
@@ -199,15 +204,17 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     __syncthreads();
     // 3.
     find_from_top<NT>(sh.hist, kBins, k, sh.res, sh.scan_a);
+    total = (uint32_t)sh.res[2];
+    if (total <= k) return;                           // uniform: every selectable item wins
     const uint32_t cbin = (uint32_t)sh.res[0];
     uint32_t rem = k - (uint32_t)sh.res[1];
     const uint32_t n_in_bin = sh.hist[cbin];
-    // 4. few members: their keys go to LDS (in any order) and one wave
-    // ranks them against each other
     const auto in_cut_bin = [&](int j) {
         if (kWide) return bins[j] == cbin;
         return ((j & 1) ? bins[j >> 1] >> 16 : bins[j >> 1] & 0xFFFFu) == cbin;
     };
+    // 4. few members: their keys go to LDS (in any order) and one wave
+    // ranks them against each other
     if (n_in_bin <= 64u) {
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -417,12 +424,12 @@ __global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
     // logits input: slot j holds column col0 + i0 + j; list input: col[j]
     uint32_t key[kPer];
     uint32_t col[LIST ? kPer : 1];
+    float v[LIST ? 1 : kPer];                         // logits input: the loaded values
     const int64_t col0 = (int64_t)part * CAP;
     if constexpr (!LIST) {
         const int ncols = a.row_cols ? min((int)a.row_cols[b], a.n_cols) : a.n_cols;
         const int n = (int)max<int64_t>(0, min<int64_t>(CAP, ncols - col0));
         const float *src = a.logits + (int64_t)b * a.ld + col0 + i0;
-        float v[kPer];
         if ((a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && i0 + kPer <= n) {
 #pragma unroll
             for (int j = 0; j < kPer; j += 4) {
@@ -455,7 +462,7 @@ __global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
 
     uint32_t kstar, need_ties, total;
     WinCursor cur;
-    find_cut<NT, kPer>(key, k, sh, kstar, need_ties, total);
+    find_cut<NT, kPer, 64, !LIST>(key, k, sh, kstar, need_ties, total, v);
     scan_winners<NT, kPer>(key, kstar, need_ties, sh, cur);
     uint32_t count = min(total, k);
     if (a.out_list)
