@@ -237,6 +237,15 @@ def test_multi_part_rows_k_values(k):
     _check_workload(wl, tag=f"multipart-k{k}")
 
 
+@pytest.mark.parametrize("k", [1, 512, 1024, 2048])
+def test_few_long_rows_sixteen_parts(k):
+    """Three rows of ~250000 entries: 16 top-k parts of up to 16384 columns
+    per row, merged by the row's last part in the same launch while the lists
+    fit one segment (k <= 1024), else by a separate merge launch."""
+    wl = W.paged_decode([250000, 180001, 249999], seed=27, k=k, name="long-rows")
+    _check_workload(wl, tag=f"long-rows-k{k}")
+
+
 @pytest.mark.parametrize("k", [7, 512])
 def test_multi_part_rows_with_chunk_lists(k):
     """Chunk-list rows over 4 top-k parts: the in-launch merge resolves the
