@@ -424,12 +424,13 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         const int ntiles = 2 * gn;
         // tile tau of the group: rows 32*(tau & 1) .. +31 of slot tau >> 1,
         // into ring slot tau & 1; tiles past the group's end and tiles of
-        // absent blocks get an empty descriptor (no traffic).  The slot's
-        // descriptor and bound are worked out at its first tile and reused
-        // for its second (tiles are issued in order).  It runs before a
-        // tile's MFMAs, so the scalar descriptor arithmetic never splits the
-        // stretch where MFMAs and the epilogue interleave.
-        int32_t lim_t[2];                               // entries of the tile below the bound
+        // absent blocks get an empty descriptor (no traffic).  lim_t: how
+        // many of the tile's entries lie below the bound (<= 0 when absent).
+        // LEAN works out a slot's descriptor and bound at its first tile and
+        // reuses them for its second (tiles are issued in order).  It runs
+        // before a tile's MFMAs, so the scalar descriptor arithmetic never
+        // splits the stretch where MFMAs and the epilogue interleave.
+        int32_t lim_t[2];
         __amdgpu_buffer_rsrc_t slot_r = make_rsrc(a.pool, 0u);
         int32_t slot_lim = 0;
         auto issue = [&](int tau) {
@@ -441,12 +442,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
                 const int64_t p0 = ok ? prow0 : 0;
                 const uint32_t bytes = ok ? (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - p0) * kRowBytes : 0u;
                 slot_r = make_rsrc(a.pool + p0 * kRowBytes, bytes);
-                slot_lim = ok ? r.limit - __builtin_amdgcn_readlane(lane_ebase, j) - (LEAN ? 0 : 32 * (tau & 1)) : 0;
-                if (!LEAN) {
-                    lim_t[tau & 1] = slot_lim;
-                    load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * kTileBytes);
-                    return;
-                }
+                slot_lim = ok ? r.limit - __builtin_amdgcn_readlane(lane_ebase, j) : 0;
             }
             lim_t[tau & 1] = slot_lim - 32 * (tau & 1);
             load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * kTileBytes);
