@@ -160,7 +160,10 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld,
  *          logits at the cut the lower columns win; -1 pads.
  * out_val  fp32 [B, k] out or NULL: their logits.
  * workspace / ws_bytes: at least
- *          idx_workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k) bytes.
+ *          idx_workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k) bytes,
+ *          256-byte aligned; contents on entry do not matter (the score
+ *          kernel clears the per-row counters the top-k's in-launch merge
+ *          uses).  Calls that share one workspace must not overlap.
  */
 int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H,
                    int32_t D, const idx_keys *keys, int32_t n_cols, int32_t k,
