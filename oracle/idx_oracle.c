@@ -37,6 +37,9 @@
  *  - top-k keeps the k largest logits; equal logits go to the lower column;
  *    -inf (masked) and NaN entries are never selected; rows with fewer than k
  *    selectable entries are padded with column -1.
+ *  - index-plane writer: scale = amax / 448 per row, values rounded to the
+ *    nearest e4m3 value (ties to even, saturating), zero rows stored as
+ *    zeros with scale 0 (see the writer section below).
  *
  * Build: plain C99, `gcc -O2 -fopenmp -shared -fPIC` (no -ffast-math).
  */
@@ -346,6 +349,83 @@ int oracle_cols_to_entries(const int32_t *cols, int32_t B, int32_t k,
         }
     }
     return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Index-plane writer: a new compressed key (HEAD_DIM values) becomes one pool
+ * row in the [FM] "compressed_k format" layout, the inverse of the dequant
+ * above ([BG]: the fp8 indexer-pool insert kernel writes rows of that same
+ * layout).  The pages do not state the scale rule; the reading taken here is
+ * the per-row absolute maximum over the largest finite e4m3 value:
+ *     s = amax / 448,  byte d = e4m3(k[d] / s)
+ * with s and each quotient rounded to binary32 (IEEE division) and e4m3
+ * rounding to the nearest value, ties to the even code, saturating at
+ * +-448.  A row of zeros gets bytes 0 and scale 0.  Keys arrive as bf16.
+ * ------------------------------------------------------------------------- */
+
+/* Nearest finite e4m3fn value to y, by search over every finite magnitude
+ * code (0x00 .. 0x7E, increasing in value); on an exact tie the even code
+ * wins, which is round-half-to-even on the 3-bit mantissa.  Magnitudes past
+ * 448 give 448.  The sign bit is y's own (so -0.0 and small negatives give
+ * 0x80).  NaN input is not defined. */
+uint8_t oracle_e4m3_encode(float y)
+{
+    double a = fabs((double)y);
+    double best_d = INFINITY;
+    int best = 0, c;
+    for (c = 0; c <= 0x7E; ++c) {
+        double d = fabs(oracle_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(best | (signbit(y) ? 0x80 : 0));
+}
+
+/* One key row: k bf16 [head_dim] -> row [head_dim + 4]. */
+void oracle_quantize_row(const uint16_t *k, int32_t head_dim, uint8_t *row)
+{
+    float amax = 0.0f, scale;
+    uint32_t bits;
+    int32_t d;
+    for (d = 0; d < head_dim; ++d) {
+        float v = (float)bf16_value(k[d]);
+        if (fabsf(v) > amax)
+            amax = fabsf(v);
+    }
+    scale = amax / 448.0f;
+    for (d = 0; d < head_dim; ++d) {
+        float v = (float)bf16_value(k[d]);
+        row[d] = amax == 0.0f ? 0 : oracle_e4m3_encode(v / scale);
+    }
+    memcpy(&bits, &scale, sizeof bits);
+    row[head_dim + 0] = (uint8_t)(bits & 0xFF);
+    row[head_dim + 1] = (uint8_t)((bits >> 8) & 0xFF);
+    row[head_dim + 2] = (uint8_t)((bits >> 16) & 0xFF);
+    row[head_dim + 3] = (uint8_t)(bits >> 24);
+}
+
+/* Write n keys k [n, head_dim] into pool rows slots[i] ([AT]: -1 is the
+ * padding id and writes nothing).  A slot outside [0, n_pool_rows) writes
+ * nothing either and is counted.  Returns the count of such slots. */
+int64_t oracle_write_keys(const uint16_t *k, int64_t n, int32_t head_dim,
+                          const int64_t *slots, uint8_t *pool,
+                          int64_t n_pool_rows)
+{
+    int64_t i, bad = 0;
+    for (i = 0; i < n; ++i) {
+        int64_t r = slots[i];
+        if (r == -1)
+            continue;
+        if (r < 0 || r >= n_pool_rows) {
+            ++bad;
+            continue;
+        }
+        oracle_quantize_row(k + i * head_dim, head_dim,
+                            pool + r * (int64_t)(head_dim + 4));
+    }
+    return bad;
 }
 
 int oracle_max_threads(void)

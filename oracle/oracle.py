@@ -66,6 +66,13 @@ def _load():
     lib.oracle_cols_to_entries.restype = ctypes.c_int
     lib.oracle_cols_to_entries.argtypes = [_c_i32p, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, _c_i32p, ctypes.c_int32, _c_i32p]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.oracle_quantize_row.restype = None
+    lib.oracle_quantize_row.argtypes = [_c_u16p, ctypes.c_int32, _c_u8p]
+    lib.oracle_write_keys.restype = ctypes.c_int64
+    lib.oracle_write_keys.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int64), _c_u8p, ctypes.c_int64]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     _lib = lib
@@ -189,3 +196,38 @@ def score_topk(wl, rows=None, n_threads: int = 0):
     lg = score(wl, rows=rows, n_threads=n_threads)
     cols, vals = topk(lg, wl.k, n_threads=n_threads)
     return cols_to_entries(wl, cols, rows=rows), vals, lg
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """float8_e4m3fn byte of each float32 value: nearest value, ties to the
+    even code, saturating at +-448 (the writer's rounding)."""
+    lib = _load()
+    y = np.asarray(y, dtype=np.float32)
+    flat = y.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    for i, v in enumerate(flat.tolist()):
+        out[i] = lib.oracle_e4m3_encode(ctypes.c_float(v))
+    return out.reshape(y.shape)
+
+
+def quantize_row(k_row: np.ndarray) -> np.ndarray:
+    """One pool row (uint8 [D + 4]) from a key of D bf16 bit patterns."""
+    k_row = np.ascontiguousarray(k_row, dtype=np.uint16)
+    (D,) = k_row.shape
+    row = np.empty(D + 4, dtype=np.uint8)
+    _load().oracle_quantize_row(_ptr(k_row, ctypes.c_uint16), D, _ptr(row, ctypes.c_uint8))
+    return row
+
+
+def write_keys(k: np.ndarray, slots: np.ndarray, pool: np.ndarray) -> int:
+    """Quantise keys k (uint16 [n, D], bf16 bits) into pool rows slots[i]
+    (int64 [n]; -1 = none) in place.  Returns the count of slots outside the
+    pool (those write nothing)."""
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    assert pool.flags["C_CONTIGUOUS"] and pool.dtype == np.uint8
+    n, D = k.shape
+    assert slots.shape == (n,) and pool.shape[1] == D + 4
+    return int(_load().oracle_write_keys(_ptr(k, ctypes.c_uint16), n, D,
+                                         _ptr(slots, ctypes.c_int64),
+                                         _ptr(pool, ctypes.c_uint8), pool.shape[0]))

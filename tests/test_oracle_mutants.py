@@ -34,6 +34,16 @@ MUTANTS = {
     "nan-selectable": ("if (isnan(v) || v == -INFINITY)", "if (v == -INFINITY)"),
     "weights-dropped": ("logit += (dot > 0.0 ? dot : 0.0) * (double)w_row[h];",
                         "logit += (dot > 0.0 ? dot : 0.0);"),
+    "encode-ties-to-lower": ("if (d < best_d || (d == best_d && (c & 1) == 0)) {",
+                             "if (d < best_d) {"),
+    "encode-sign-dropped": ("return (uint8_t)(best | (signbit(y) ? 0x80 : 0));",
+                            "return (uint8_t)best;"),
+    "encode-truncates": ("double d = fabs(oracle_e4m3_value((uint8_t)c) - a);",
+                         "double d = oracle_e4m3_value((uint8_t)c) <= a ? a - oracle_e4m3_value((uint8_t)c) : INFINITY;"),
+    "writer-scale-447": ("scale = amax / 448.0f;", "scale = amax / 447.0f;"),
+    "writer-amax-ignores-negatives": ("if (fabsf(v) > amax)\n            amax = fabsf(v);",
+                                      "if (v > amax)\n            amax = v;"),
+    "writer-bad-slot-not-counted": ("            ++bad;\n", ""),
 }
 
 PIN_TESTS = [
@@ -47,6 +57,11 @@ PIN_TESTS = [
     lambda: pins.test_integer_case_matches_numpy_matmul(0),
     pins.test_limits_mask_exactly_and_poison_never_leaks,
     lambda: pins.test_topk_matches_brute_force_with_ties(0),
+    pins.test_e4m3_encode_matches_torch_cast_at_values_and_midpoints,
+    pins.test_e4m3_encode_ties_and_saturation_closed_form,
+    pins.test_quantize_row_with_amax_448_is_the_plain_cast,
+    lambda: pins.test_quantize_row_scale_is_rounded_amax_over_448_and_error_is_half_a_step(0),
+    pins.test_write_keys_places_rows_and_skips_padding_and_bad_slots,
 ]
 
 

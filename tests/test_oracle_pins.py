@@ -349,3 +349,148 @@ def test_generator_is_deterministic():
     a, b = W.small_config(1), W.small_config(1)
     assert np.array_equal(a.pool, b.pool) and np.array_equal(a.q, b.q)
     assert np.array_equal(a.block_table, b.block_table)
+
+
+# ------------------------------------------------------ index-plane writer
+
+def _e4m3_finite_magnitudes():
+    """The 127 finite non-negative e4m3fn values, ascending (from torch)."""
+    v = torch.arange(0x7F, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.all(np.diff(v) > 0)
+    return v
+
+
+def _torch_e4m3(y):
+    return W.e4m3_bytes(np.asarray(y, dtype=np.float32))
+
+
+def test_e4m3_encode_matches_torch_cast_at_values_and_midpoints():
+    """Encoder == torch's float8_e4m3fn cast (round to nearest even) at every
+    finite value, every midpoint between neighbours (the ties), one fp32 ulp
+    either side of each midpoint, and both signs."""
+    v = _e4m3_finite_magnitudes()
+    mids = (v[:-1] + v[1:]) / 2.0                      # exact in fp32 (4 significant bits)
+    pts = np.concatenate([v, mids, v[-1:] + 8.0])      # 456: between 448 and the 464 overflow point
+    f = pts.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), pts)
+    f = np.concatenate([f, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+                        np.nextafter(mids.astype(np.float32), np.float32(0))])
+    f = np.concatenate([f, -f])
+    assert np.array_equal(oracle.e4m3_encode(f), _torch_e4m3(f))
+
+
+def test_e4m3_encode_matches_torch_cast_on_random_values():
+    rng = np.random.default_rng(7)
+    mag = np.exp2(rng.uniform(-14.0, np.log2(448.0), 20000)).astype(np.float32)
+    lin = rng.uniform(-448.0, 448.0, 20000).astype(np.float32)
+    f = np.concatenate([mag * rng.choice([-1, 1], mag.size).astype(np.float32), lin])
+    assert np.array_equal(oracle.e4m3_encode(f), _torch_e4m3(f))
+
+
+def test_e4m3_encode_ties_and_saturation_closed_form():
+    # ties go to the even mantissa: 1 + 1/16 -> 1.0 (0x38); 1 + 3/16 -> 1.25 (0x3A);
+    # 17 -> 16 (0x58); 2^-10 -> 0; 3 * 2^-10 -> 2^-8 (0x02); 15 * 2^-10 -> 2^-6 (0x08)
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 17.0: 0x58, 2.0 ** -10: 0x00,
+             3 * 2.0 ** -10: 0x02, 15 * 2.0 ** -10: 0x08, 460.0: 0x7E,
+             464.0: 0x7E, 1.0e6: 0x7E, 3.0e38: 0x7E, -500.0: 0xFE, -1e-9: 0x80, 0.0: 0x00}
+    for y, code in cases.items():
+        assert int(oracle.e4m3_encode([y])[0]) == code, y
+
+
+def test_e4m3_encode_inverts_decode():
+    for u in range(256):
+        if u in (0x7F, 0xFF):
+            continue
+        assert int(oracle.e4m3_encode([oracle.e4m3_value(u)])[0]) == u
+
+
+def _scale_of(row):
+    return float(row[-4:].view("<f4")[0])
+
+
+def test_quantize_row_with_amax_448_is_the_plain_cast():
+    """amax = 448 gives scale exactly 1, so the bytes are the cast of the values;
+    amax = 448 * 2^j gives scale 2^j and the same bytes; a negated row flips
+    only sign bits; a zero row is all zeros with scale 0."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(128).astype(np.float32) * 40
+    x[17] = -448.0
+    kb = _bf16(x)
+    xb = (kb.astype(np.uint32) << 16).view(np.float32)
+    row = oracle.quantize_row(kb)
+    assert list(row[-4:]) == [0x00, 0x00, 0x80, 0x3F]
+    assert np.array_equal(row[:-4], _torch_e4m3(xb))
+    for j in (-20, -3, 5, 30):
+        rj = oracle.quantize_row(_bf16(xb * np.float32(2.0 ** j)))
+        assert _scale_of(rj) == 2.0 ** j and np.array_equal(rj[:-4], row[:-4])
+    rn = oracle.quantize_row(_bf16(-xb))
+    assert np.array_equal(rn[:-4], row[:-4] ^ 0x80) and _scale_of(rn) == 1.0
+    r0 = oracle.quantize_row(np.zeros(128, dtype=np.uint16))
+    assert not r0.any()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_quantize_row_scale_is_rounded_amax_over_448_and_error_is_half_a_step(seed):
+    """Random rows: the scale is the binary32 nearest amax/448 (checked with
+    exact rationals), the largest element lands on +-448, and every value is
+    recovered within half an e4m3 step (times the scale, plus the quotient's
+    own rounding)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    v = _e4m3_finite_magnitudes()
+    for _ in range(20):
+        x = (rng.standard_normal(128) * np.exp2(rng.uniform(-30, 30))).astype(np.float32)
+        kb = _bf16(x)
+        xb = (kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        row = oracle.quantize_row(kb)
+        s = _scale_of(row)
+        amax = float(np.abs(xb).max())
+        exact = Fraction(amax) / 448
+        s32 = np.float32(s)
+        for nb in (np.nextafter(s32, np.float32(0)), np.nextafter(s32, np.float32(np.inf))):
+            assert abs(Fraction(s) - exact) <= abs(Fraction(float(nb)) - exact)
+        i = int(np.abs(xb).argmax())
+        assert row[i] & 0x7F == 0x7E and (row[i] >> 7) == (xb[i] < 0)
+        dec = np.array([oracle.e4m3_value(u) for u in row[:-4]])
+        y = np.abs(xb) / s
+        pos = np.clip(np.searchsorted(v, y), 1, len(v) - 1)
+        half_step = (v[pos] - v[pos - 1]) / 2
+        assert np.all(np.abs(np.abs(dec) - y) <= half_step * (1 + 2.0 ** -20) + 2.0 ** -40)
+        assert np.all((np.signbit(dec) == np.signbit(xb)) | (dec == 0))
+
+
+def test_write_keys_places_rows_and_skips_padding_and_bad_slots():
+    rng = np.random.default_rng(5)
+    n, rows = 12, 40
+    k = _bf16(rng.standard_normal((n, 128)).astype(np.float32))
+    slots = rng.permutation(rows)[:n].astype(np.int64)
+    slots[3] = -1
+    slots[7] = rows            # one past the end
+    slots[9] = -5
+    pool = np.full((rows, 132), 0xA5, dtype=np.uint8)
+    before = pool.copy()
+    assert oracle.write_keys(k, slots, pool) == 2
+    written = set()
+    for i, r in enumerate(slots):
+        if 0 <= r < rows:
+            assert np.array_equal(pool[r], oracle.quantize_row(k[i]))
+            written.add(int(r))
+    untouched = [r for r in range(rows) if r not in written]
+    assert np.array_equal(pool[untouched], before[untouched])
+
+
+def test_written_rows_score_like_their_dequantised_keys():
+    """Write keys, then score them: the logit equals the definition applied to
+    the dequantised values (decode(byte) * scale) in double."""
+    rng = np.random.default_rng(9)
+    n = 64
+    k = _bf16(rng.standard_normal((n, 128)).astype(np.float32))
+    pool = np.zeros((n, 132), dtype=np.uint8)
+    oracle.write_keys(k, np.arange(n, dtype=np.int64), pool)
+    q = _bf16(rng.standard_normal((64, 128)).astype(np.float32))
+    w = rng.standard_normal(64).astype(np.float32)
+    qd = (q.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    for e in range(0, n, 9):
+        kd = np.array([oracle.e4m3_value(u) for u in pool[e, :128]]) * _scale_of(pool[e])
+        want = float(np.maximum(qd @ kd, 0.0) @ w.astype(np.float64))
+        assert oracle.logit(q, w, pool[e]) == pytest.approx(want, rel=1e-12, abs=1e-12)
