@@ -12,6 +12,11 @@ Prints ONE JSON line.  `value` is scored (query, entry) pairs per second of
 the whole path; `roofline` covers the score kernel (the dominant kernel),
 timed live with HIP events that each launch's dispatch stamps with the
 kernel's start and end on the stream it runs on.
+
+`--workload index-fill` measures the index-plane writer instead: one step is
+one idx_write_keys call that quantises the 262,144 compressed keys of one
+1M-token request into a shuffled paged pool; `value` is keys written per
+second and `roofline` covers the writer kernel.
 """
 from __future__ import annotations
 
@@ -32,13 +37,25 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 SCORE_SOURCES = ["sparse_attention_kv_paged_amd/csrc/idx_score.hip",
                  "sparse_attention_kv_paged_amd/csrc/idx_device.h",
                  "sparse_attention_kv_paged_amd/csrc/idx_internal.h"]
+WRITE_SOURCES = ["sparse_attention_kv_paged_amd/csrc/idx_write.hip",
+                 "sparse_attention_kv_paged_amd/csrc/idx_write.h",
+                 "sparse_attention_kv_paged_amd/csrc/idx_internal.h"]
 WORKLOADS = {"tiny-decode": 0, "decode-batch": 1, "long-decode": 2,
              "chunked-prefill": 3, "resident-subset": 4}
+WRITE_WORKLOAD = "index-fill"
+WRITE_BYTES_PER_KEY = 128 * 2 + 8 + 132      # bf16 key in, int64 slot, pool row out
 
 
-def score_source_hash() -> str:
+def kernel_of(workload: str):
+    """(kernel name, its sources, profile file prefix) measured for a workload."""
+    if workload == WRITE_WORKLOAD:
+        return "write_keys_kernel", WRITE_SOURCES, "write_keys"
+    return "score_kernel", SCORE_SOURCES, "score_kernel"
+
+
+def score_source_hash(sources=SCORE_SOURCES) -> str:
     h = hashlib.sha256()
-    for p in SCORE_SOURCES:
+    for p in sources:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -72,11 +89,12 @@ def _read_kv(path):
 def read_traffic(workload: str):
     """HBM bytes per score-kernel launch from the committed rocprofv3 counter
     summary, or None if absent or taken on a different kernel source."""
-    path = os.path.join(PROFILE_DIR, f"score_kernel_{workload}_pmc.txt")
+    _, sources, prefix = kernel_of(workload)
+    path = os.path.join(PROFILE_DIR, f"{prefix}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     kv = _read_kv(path)
-    if kv.get("score_source_hash") != score_source_hash():
+    if kv.get("source_hash", kv.get("score_source_hash")) != score_source_hash(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -102,9 +120,10 @@ def summarize_trace(trace_dir, workload, command, out):
     """Kernel-time summary of a `rocprofv3 --kernel-trace --stats
     --output-format csv` run, as text for profiles/."""
     rows = _csv_rows(_find(trace_dir, "kernel_stats.csv"))
+    _, sources, _ = kernel_of(workload)
     lines = [f"# rocprofv3 kernel statistics, workload {workload}",
              f"# command: {command}",
-             f"score_source_hash = {score_source_hash()}",
+             f"source_hash = {score_source_hash(sources)}",
              f"{'kernel':72s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share':>6s}"]
     for r in rows:
         lines.append(f"{r['Name'][:72]:72s} {int(r['Calls']):6d} {float(r['AverageNs'])/1e3:10.3f} "
@@ -115,10 +134,12 @@ def summarize_trace(trace_dir, workload, command, out):
 
 
 def summarize_pmc(fetch_dir, write_dir, workload, command, out):
-    """HBM traffic per score-kernel launch from two counter runs (FETCH_SIZE,
-    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
-    for the 1 GiB device copy that `--copy-calibration` runs (1 GiB read and
-    1 GiB written per dispatch)."""
+    """HBM traffic per launch of the workload's measured kernel from two
+    counter runs (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by
+    what the same counter reads for the 1 GiB device copy that
+    `--copy-calibration` runs (1 GiB read and 1 GiB written per dispatch)."""
+    kname, sources, _ = kernel_of(workload)
+
     def per_kernel(dirpath, counter):
         vals = {}
         for r in _csv_rows(_find(dirpath, "counter_collection.csv")):
@@ -126,7 +147,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, command, out):
                 continue
             key = (r["Kernel_Name"], r["Dispatch_Id"])
             vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
-        score = [v for (n, _), v in vals.items() if "score_kernel" in n]
+        score = [v for (n, _), v in vals.items() if kname in n]
         copy = [v for (n, _), v in vals.items() if "copy" in n.lower() and v > 5e5]
         return score, copy
     import statistics
@@ -137,12 +158,12 @@ def summarize_pmc(fetch_dir, write_dir, workload, command, out):
     write_scale = gib_kib / statistics.median(wc)
     fetch_b = statistics.median(fs) * 1024 * fetch_scale
     write_b = statistics.median(ws) * 1024 * write_scale
-    lines = [f"# rocprofv3 HBM counters for the score kernel, workload {workload}",
+    lines = [f"# rocprofv3 HBM counters for {kname}, workload {workload}",
              f"# command: {command}",
              f"# FETCH_SIZE and WRITE_SIZE are KiB per dispatch; each is scaled by the same",
              f"# counter's reading for a 1 GiB device copy (1 GiB read, 1 GiB written).",
-             f"score_source_hash = {score_source_hash()}",
-             f"score_dispatches = {len(fs)}",
+             f"source_hash = {score_source_hash(sources)}",
+             f"dispatches = {len(fs)}",
              f"fetch_kib_per_launch_raw = {statistics.median(fs):.1f}",
              f"write_kib_per_launch_raw = {statistics.median(ws):.1f}",
              f"copy_fetch_kib_raw = {statistics.median(fc):.1f}",
@@ -183,12 +204,161 @@ def cpu_baseline(wl, pairs: int, min_seconds: float, max_sample_pairs: int = 4_0
             "sample": f"{reps} {what} ({sample_pairs} pairs, score + top-{wl.k}) in {el:.1f} s"}
 
 
+def run_steps(step, K, R, use_graph):
+    """K timed steps (replays of captured graphs of up to R steps, or eager
+    launches), bracketed by synchronisations; returns ms per step."""
+    import torch
+    graphs = []
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        per = min(R, K)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per):
+                step(i)
+        graphs = [g] * (K // per)
+        if K % per:
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2):
+                for i in range(K % per):
+                    step(i)
+            graphs.append(g2)
+        for g_ in set(graphs):
+            g_.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    if graphs:
+        for g_ in graphs:
+            g_.replay()
+    else:
+        for i in range(K):
+            step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(wall * 1e3, gpu_ms) / K
+    print(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall * 1e3:.3f} ms, "
+          f"events {gpu_ms:.3f} ms)", file=sys.stderr, flush=True)
+    return ms_per_step
+
+
+def kernel_ms_live(step, n):
+    """Average duration of the measured kernel over n eager steps: each
+    launch's dispatch stamps a pair of events with the kernel's start and end
+    on its own stream; the steps queue behind a busy wait so the queue never
+    drains while the host enqueues."""
+    import numpy as np
+    import torch
+    from sparse_attention_kv_paged_amd import lib
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:            # create the hipEvents; the library re-records them
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(5e7))
+    for i in range(n):
+        lib.idx_profile_events(*evs[i])
+        step(i)
+    lib.idx_profile_events(None, None)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def copy_calibration(n):
+    """n plain device copies of 1 GiB (the reference reading for HBM counters)."""
+    import torch
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def bench_writer(args):
+    """One step = one idx_write_keys of the index-fill workload (262,144 keys
+    of one 1M-token request into a shuffled paged pool)."""
+    import numpy as np
+    import torch
+    from oracle import oracle
+    from sparse_attention_kv_paged_amd import lib, workloads
+
+    torch.cuda.set_device(0)
+    wr = workloads.index_fill()
+    n = wr.n
+    print(f"[bench] workload {wr.name}: {wr.description}", file=sys.stderr, flush=True)
+    k = torch.from_numpy(wr.k.view(np.int16)).cuda()
+    slots = torch.from_numpy(wr.slots).cuda()
+    pool = torch.from_numpy(wr.pool).cuda()
+    per_copy = k.numel() * 2 + pool.numel()
+    R = args.replicas or max(4, min(64, math.ceil(1.0e9 / per_copy)))
+    ks = [k] + [k.clone() for _ in range(R - 1)]
+    pools = [pool] + [pool.clone() for _ in range(R - 1)]
+
+    def step(i):
+        lib.idx_write_keys(ks[i % R], slots, pools[i % R])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ms_per_step = run_steps(step, args.steps, R, not args.no_graph)
+    kern_ms = kernel_ms_live(step, args.steps)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+
+    algo = n * WRITE_BYTES_PER_KEY
+    roofline = {"kernel": "write_keys_kernel", "bound": "hbm",
+                "achieved": algo / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "traffic": read_traffic(WRITE_WORKLOAD), "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+    roofline["frac"] = roofline["achieved"] / roofline["peak"]
+    out = {
+        "metric": "index-plane writer keys quantised and stored/s; % of HBM peak, 1 MI355X",
+        "value": n / (ms_per_step * 1e-3),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wr.name, "keys": n, "head_dim": 128, "block": 64,
+                   "description": wr.description, "replicas": R, "graph": not args.no_graph},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle writer (one thread) on leading slices of the keys
+        sample = min(n, 4096)
+        out_pool = wr.pool.copy()
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.write_keys(wr.k[:sample], wr.slots[:sample], out_pool)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        out["cpu_baseline"] = {"value": sample * reps / el, "unit": "keys/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{reps} passes over the first {sample} keys of {wr.name} in {el:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=96)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode-batch", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode-batch", choices=sorted(WORKLOADS) + [WRITE_WORKLOAD])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for >= 1 GB)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -201,19 +371,24 @@ def main():
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
 
+    trace_prefix = "write_keys" if args.workload == WRITE_WORKLOAD else "score_topk"
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.workload, args.command,
-                        os.path.join(PROFILE_DIR, f"score_topk_{args.workload}_trace.txt"))
+                        os.path.join(PROFILE_DIR, f"{trace_prefix}_{args.workload}_trace.txt"))
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.command,
-                      os.path.join(PROFILE_DIR, f"score_kernel_{args.workload}_pmc.txt"))
+                      os.path.join(PROFILE_DIR, f"{kernel_of(args.workload)[2]}_{args.workload}_pmc.txt"))
         return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               f"the library runs on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == WRITE_WORKLOAD:
+        bench_writer(args)
+        return
 
     import numpy as np
     import torch

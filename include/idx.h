@@ -67,6 +67,7 @@ enum idx_op { IDX_OP_SCORE = 0, IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
 #define IDX_STATUS_BAD_BLOCK 0x2u      /* a block-table entry < -1 or past the pool's end */
 #define IDX_STATUS_BAD_REQUEST 0x4u    /* q_req[b] >= n_req (row treated as padding) */
 #define IDX_STATUS_BAD_CHUNK 0x8u      /* chunk id < 0 or >= max_blocks, or n_chunks[b] > max_chunks */
+#define IDX_STATUS_BAD_SLOT 0x10u      /* idx_write_keys: a slot < -1 or >= n_pool_rows (nothing written) */
 
 #define IDX_HEADS 64
 #define IDX_HEAD_DIM 128
@@ -170,6 +171,43 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H,
                    int32_t *out_idx, float *out_val, void *workspace,
                    size_t ws_bytes, void *stream);
 
+/*
+ * idx_write_keys: the index-plane writer -- quantise new compressed keys and
+ * store them as pool rows in the layout idx_score reads ("FlashMemory-
+ * DeepSeek-V4" README, section "compressed_k format": D float8_e4m3 bytes
+ * then the fp32 scale; the batchgen pull request's fp8 indexer-pool insert
+ * fills rows of that layout).  The pages do not state the scale rule; this
+ * library takes the per-key absolute maximum over e4m3's largest finite
+ * value:
+ *
+ *     s       = amax_d |k[d]| / 448          (binary32 division, nearest)
+ *     byte d  = e4m3fn( k[d] / s )           (binary32 division, nearest;
+ *                                             then the nearest e4m3 value,
+ *                                             ties to the even code,
+ *                                             saturating at +-448)
+ *
+ * so the largest element is stored as +-448 and every element is recovered
+ * as e4m3(byte) * s within half an e4m3 step.  A key of zeros (either sign)
+ * is stored as zero bytes and scale 0.
+ *
+ * k        bf16 bit patterns [n, D], 16-byte aligned; values must be finite.
+ * n        number of keys (0 = nothing to do).
+ * D        head dimension; must be 128.
+ * slots    int64 [n]: pool row that receives key i.  -1 writes nothing (the
+ *          padding id of "DeepSeek-V4.1 native paged runtime"); any other
+ *          value outside [0, n_pool_rows) writes nothing and, when status is
+ *          given, ORs IDX_STATUS_BAD_SLOT into *status.  Two keys naming the
+ *          same slot leave that row unspecified.
+ * pool     uint8 [n_pool_rows, D + 4] in/out, 4-byte aligned; only the named
+ *          rows are written (each whole: D bytes and the scale).
+ * status   optional uint32 device word (bits OR-ed in, never cleared).
+ * The write is ordered on `stream` like every call: a later idx_score on the
+ * same stream sees the new rows.
+ */
+int idx_write_keys(const uint16_t *k, int64_t n, int32_t D,
+                   const int64_t *slots, uint8_t *pool, int64_t n_pool_rows,
+                   uint32_t *status, void *stream);
+
 /* Workspace bytes an op needs for B rows of n_cols columns and top-k
  * (0 for IDX_OP_SCORE); (size_t)-1 for invalid arguments. */
 size_t idx_workspace_bytes(int32_t op, int32_t B, int32_t n_cols, int32_t k);
@@ -184,10 +222,10 @@ const char *idx_last_error(void);
  * idx_profile_events: measurement hook for benchmark harnesses.  When both
  * are non-NULL (hipEvent_t handles created by the caller, with timing), every
  * later idx_score / idx_score_topk call on this thread launches its score
- * kernel so that the dispatch itself stamps `before` with the kernel's start
- * and `after` with its end (hipExtLaunchKernelGGL), so
- * hipEventElapsedTime(before, after) is that kernel's execution time.  Pass
- * NULL, NULL to stop.  Returns IDX_OK.
+ * kernel, and every idx_write_keys call its writer kernel, so that the
+ * dispatch itself stamps `before` with the kernel's start and `after` with
+ * its end (hipExtLaunchKernelGGL), so hipEventElapsedTime(before, after) is
+ * that kernel's execution time.  Pass NULL, NULL to stop.  Returns IDX_OK.
  */
 int idx_profile_events(void *before, void *after);
 

@@ -9,6 +9,7 @@
 
 #include "../../include/idx.h"
 #include "idx_internal.h"
+#include "idx_write.h"
 
 namespace {
 
@@ -281,6 +282,30 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t
     hipError_t e = enqueue_topk(P, static_cast<char *>(workspace), logits, ld, nullptr, B, n_cols, k,
                                 out_col, out_val, nullptr, 0, (hipStream_t)stream);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
+}
+
+int idx_write_keys(const uint16_t *k, int64_t n, int32_t D, const int64_t *slots, uint8_t *pool,
+                   int64_t n_pool_rows, uint32_t *status, void *stream) {
+    g_last_error[0] = 0;
+    if (n < 0 || n_pool_rows < 0) return fail(IDX_E_ARG, "n and n_pool_rows must be >= 0");
+    if (D != idx::kHeadDim) return fail(IDX_E_SHAPE, "only D=128 is supported (got D=%d)", D);
+    // one workgroup per 16 keys: the grid's x extent bounds n
+    if (n > (int64_t)INT32_MAX * 16) return fail(IDX_E_SHAPE, "too many keys in one call (%lld)", (long long)n);
+    if (n == 0) return IDX_OK;
+    if (!k || !slots) return fail(IDX_E_ARG, "k and slots must be non-null");
+    if (n_pool_rows > 0 && !pool) return fail(IDX_E_ARG, "pool is null");
+    if (!aligned(k, 16)) return fail(IDX_E_ALIGN, "k must be 16-byte aligned");
+    if (!aligned(slots, 8) || !aligned(pool, 4) || !aligned(status, 4))
+        return fail(IDX_E_ALIGN, "slots must be 8-byte aligned, pool and status 4-byte aligned");
+    idx::WriteArgs a{};
+    a.k = k;
+    a.n = n;
+    a.slots = slots;
+    a.pool = pool;
+    a.n_pool_rows = n_pool_rows;
+    a.status = status;
+    hipError_t e = idx::launch_write_keys(a, (hipStream_t)stream, g_ev_before, g_ev_after);
+    return e == hipSuccess ? IDX_OK : hip_fail(e, "writer kernel");
 }
 
 int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D,

@@ -21,8 +21,9 @@ LIB_PATH = os.path.join(_PKG, "libidx.so")
 IDX_OK, IDX_E_ARG, IDX_E_SHAPE, IDX_E_ALIGN, IDX_E_WORKSPACE, IDX_E_HIP = range(6)
 IDX_OP_SCORE, IDX_OP_TOPK, IDX_OP_SCORE_TOPK = range(3)
 STATUS_LIMIT_CLAMPED, STATUS_BAD_BLOCK, STATUS_BAD_REQUEST, STATUS_BAD_CHUNK = 1, 2, 4, 8
+STATUS_BAD_SLOT = 16
 
-EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_workspace_bytes",
+EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_write_keys", "idx_workspace_bytes",
            "idx_error_string", "idx_last_error", "idx_profile_events", "idx_abi_version")
 
 
@@ -69,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.idx_topk.restype = ctypes.c_int
     lib.idx_score_topk.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
     lib.idx_score_topk.restype = ctypes.c_int
+    lib.idx_write_keys.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp]
+    lib.idx_write_keys.restype = ctypes.c_int
     lib.idx_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.idx_workspace_bytes.restype = sz
     lib.idx_error_string.argtypes = [i32]
@@ -142,7 +145,7 @@ class Keys:
 
 def idx_profile_events(before, after) -> None:
     """Record hipEvents (torch.cuda.Event objects, or None to stop) around
-    every later score-kernel launch on this thread."""
+    every later score-kernel or writer-kernel launch on this thread."""
     bp = None if before is None else ctypes.c_void_p(before.cuda_event)
     ap = None if after is None else ctypes.c_void_p(after.cuda_event)
     _check(load().idx_profile_events(bp, ap))
@@ -228,6 +231,23 @@ def idx_score_topk(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=
                                  _ptr(out_idx), _ptr(out_val), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
     return out_idx, out_val
+
+
+def idx_write_keys(k: torch.Tensor, slots: torch.Tensor, pool: torch.Tensor,
+                   status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Quantise keys k [n, 128] (bf16) into pool rows slots[i] (int64 [n],
+    -1 = none) of pool (uint8 [n_pool_rows, 132]) in place; returns pool."""
+    if k.dtype == torch.bfloat16:
+        k = k.view(torch.int16)
+    k = _dev(k, torch.int16, "k (bf16 bits)")
+    slots = _dev(slots, torch.int64, "slots")
+    pool = _dev(pool, torch.uint8, "pool")
+    _dev(status, torch.int32, "status")
+    if k.dim() != 2 or slots.shape != (k.shape[0],) or pool.dim() != 2 or pool.shape[1] != k.shape[1] + 4:
+        raise ValueError("k must be [n, D], slots [n] and pool [n_pool_rows, D + 4]")
+    _check(load().idx_write_keys(_ptr(k), k.shape[0], k.shape[1], _ptr(slots), _ptr(pool),
+                                 pool.shape[0], _ptr(status), _stream(stream)))
+    return pool
 
 
 # ---------------------------------------------------------------------------

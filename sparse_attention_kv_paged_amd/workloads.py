@@ -315,6 +315,51 @@ def resident(B=40, chunks_per_req=4096, n_resident=384, seed=4, H=HEADS,
                     description=f"B={B}, {n_resident}/{chunks_per_req} resident chunks, seed {seed}")
 
 
+@dataclasses.dataclass
+class WriteLoad:
+    """Host arrays of one index-plane write: keys k [n, D] (bf16 bits) go to
+    pool rows slots [n] (int64, -1 = none) of a pool whose rows start out as
+    poison."""
+
+    name: str
+    k: np.ndarray                       # uint16 [n, D]
+    slots: np.ndarray                   # int64 [n]
+    pool: np.ndarray                    # uint8 [n_pool_rows, D + 4] (before the write)
+    block_table: np.ndarray             # int32 [1, n_blocks]: the request's blocks
+    description: str = ""
+
+    @property
+    def n(self) -> int:
+        return int(self.k.shape[0])
+
+
+def index_fill(n_keys=262144, seed=5, D=HEAD_DIM, poison_frac=0.01,
+               name="index-fill") -> WriteLoad:
+    """The compressed keys of one request (n_keys entries, 262,144 = one
+    1M-token context at C4) written into a shuffled paged pool of 64-entry
+    blocks: entry e goes to row 64 * table[e // 64] + e % 64.  Key values are
+    bf16(N(0, 1) * m) with a per-key magnitude m ~ U(1, 6), so the scales the
+    writer derives (amax / 448) fall in about the range the scoring workloads
+    draw theirs from.  Unreferenced blocks (1 %) and the tail of the last
+    block keep their poison rows.  Draw order: permutation -> magnitudes ->
+    values."""
+    rng = np.random.default_rng(seed)
+    nblk = _ceil_div(n_keys, BLOCK)
+    n_blocks = nblk + _ceil_div(nblk * int(round(poison_frac * 1000)), 1000)
+    perm = rng.permutation(n_blocks).astype(np.int32)
+    table = perm[:nblk].reshape(1, nblk).copy()
+    m = rng.uniform(1.0, 6.0, size=n_keys).astype(np.float32)
+    x = rng.standard_normal((n_keys, D), dtype=np.float32)
+    x *= m[:, None]
+    k = bf16_bits(x)
+    e = np.arange(n_keys, dtype=np.int64)
+    slots = table[0, e // BLOCK].astype(np.int64) * BLOCK + e % BLOCK
+    pool = np.empty((n_blocks * BLOCK, D + 4), dtype=np.uint8)
+    poison_rows(pool, slice(None))
+    return WriteLoad(name=name, k=k, slots=slots, pool=pool, block_table=table,
+                     description=f"{n_keys} keys into {nblk} shuffled blocks (+{n_blocks - nblk} unreferenced), seed {seed}")
+
+
 # ----------------------------------------------------------------------------
 # the five named workloads at full size, and small variants of each
 

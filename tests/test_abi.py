@@ -141,3 +141,29 @@ def test_score_topk_rejects_small_workspace(lib):
     rc = lib.idx_score_topk(0x1000, 0x1000, 1, 64, 128, ctypes.byref(keys), 64, 4096, 0x2000, None,
                             0x10000, need, None)
     assert rc == L.IDX_E_SHAPE
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), L.IDX_E_SHAPE),
+    (dict(n=-1), L.IDX_E_ARG),
+    (dict(n_pool_rows=-1), L.IDX_E_ARG),
+    (dict(k=None), L.IDX_E_ARG),
+    (dict(slots=None), L.IDX_E_ARG),
+    (dict(pool=None), L.IDX_E_ARG),
+    (dict(k=0x1008), L.IDX_E_ALIGN),
+    (dict(slots=0x2004), L.IDX_E_ALIGN),
+    (dict(pool=0x3002), L.IDX_E_ALIGN),
+    (dict(status=0x4001), L.IDX_E_ALIGN),
+    (dict(n=(1 << 31) * 16), L.IDX_E_SHAPE),
+])
+def test_write_keys_rejects_bad_arguments(lib, kw, code):
+    a = dict(k=0x1000, n=10, D=128, slots=0x2000, pool=0x3000, n_pool_rows=64, status=None)
+    a.update(kw)
+    rc = lib.idx_write_keys(a["k"], a["n"], a["D"], a["slots"], a["pool"], a["n_pool_rows"],
+                            a["status"], None)
+    assert rc == code
+    assert lib.idx_last_error() != b""
+
+
+def test_write_keys_with_no_keys_is_a_no_op(lib):
+    assert lib.idx_write_keys(None, 0, 128, None, None, 0, None, None) == L.IDX_OK
