@@ -40,6 +40,9 @@
  *  - index-plane writer: scale = amax / 448 per row, values rounded to the
  *    nearest e4m3 value (ties to even, saturating), zero rows stored as
  *    zeros with scale 0 (see the writer section below).
+ *  - Level-1 resident-set selection: per-entry ensemble (max or mean) of the
+ *    layers' sigmoid scores, threshold, page density, sink and recent pages,
+ *    the densest pages up to KMAX (see the Level-1 section below).
  *
  * Build: plain C99, `gcc -O2 -fopenmp -shared -fPIC` (no -ffast-math).
  */
@@ -426,6 +429,117 @@ int64_t oracle_write_keys(const uint16_t *k, int64_t n, int32_t head_dim,
                             pool + r * (int64_t)(head_dim + 4));
     }
     return bad;
+}
+
+/* ---------------------------------------------------------------------------
+ * Level 1 of [FM] "Two-level recall algorithm" (the Memory Indexer): the
+ * retriever scores a row's whole history at several layers ([FM] "Joint
+ * checkpoint + ensemble": three layers, each with its own weights), the
+ * per-layer sigmoid scores of each compressed entry are ensembled (max, the
+ * default, or mean), a threshold picks the query-critical entries, and the
+ * recency tail and the attention sink are kept; pages are recalled whole,
+ * the densest KMAX per request ([FM] "Quick start": KMAX pages of 64
+ * entries).  Readings taken where the pages give no detail:
+ *  - entry e of row b (e < limits[b], clamped to n_cols) is selected iff its
+ *    ensemble score s >= threshold;
+ *  - page p holds entries 64p .. 64p+63; its density is its count of
+ *    selected entries; the row's history has P = ceil(limit / 64) pages;
+ *  - pages p < n_sink and p >= P - n_recent are always resident ("forced");
+ *  - the other pages with density > 0 follow in order of density (higher
+ *    first), equal densities to the lower page; the first kmax pages of
+ *    (forced pages, then that order) are the resident set, listed in
+ *    ascending page order and padded with -1; out_count[b] is their number;
+ *  - the scores given are the binary32 sigmoid values the scorer reports;
+ *    the ensemble is taken in binary32 too, so that the threshold decision
+ *    (an integer outcome) is made in the scorer's precision: max is exact,
+ *    mean is the binary32 sum in layer order divided by L in binary32.
+ * scores is [L][B][ld].  Returns 0, or -1 on bad sizes / allocation failure.
+ * ------------------------------------------------------------------------- */
+enum { ORACLE_ENSEMBLE_MAX = 0, ORACLE_ENSEMBLE_MEAN = 1 };
+
+typedef struct {
+    int32_t rank;   /* 2: forced, 1: density > 0, 0: not resident */
+    int32_t density;
+    int32_t page;
+} page_rank;
+
+/* Forced pages first, then higher density, then the lower page. */
+static int cmp_page(const void *pa, const void *pb)
+{
+    const page_rank *a = (const page_rank *)pa, *b = (const page_rank *)pb;
+    if (a->rank != b->rank)
+        return a->rank > b->rank ? -1 : 1;
+    if (a->density != b->density)
+        return a->density > b->density ? -1 : 1;
+    return (a->page > b->page) - (a->page < b->page);
+}
+
+static int cmp_int(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+int oracle_level1_select(const float *scores, int32_t L, int32_t B,
+                         int32_t n_cols, int64_t ld, const int32_t *limits,
+                         int32_t ensemble, float threshold, int32_t n_sink,
+                         int32_t n_recent, int32_t kmax, int32_t *out_pages,
+                         int32_t *out_count)
+{
+    int32_t b;
+    if (L < 1 || B < 0 || n_cols < 0 || ld < n_cols || kmax < 1 ||
+        n_sink < 0 || n_recent < 0 ||
+        (ensemble != ORACLE_ENSEMBLE_MAX && ensemble != ORACLE_ENSEMBLE_MEAN))
+        return -1;
+    for (b = 0; b < B; ++b) {
+        int32_t hist = limits[b] < 0 ? 0 : (limits[b] > n_cols ? n_cols : limits[b]);
+        int32_t P = (hist + 63) / 64, p, e, l, n = 0, i;
+        page_rank *pr = (page_rank *)calloc((size_t)P + 1, sizeof(page_rank));
+        int32_t *chosen = (int32_t *)malloc(sizeof(int32_t) * ((size_t)P + 1));
+        if (!pr || !chosen) {
+            free(pr);
+            free(chosen);
+            return -1;
+        }
+        for (p = 0; p < P; ++p)
+            pr[p].page = p;
+        for (e = 0; e < hist; ++e) {
+            float s;
+            if (ensemble == ORACLE_ENSEMBLE_MAX) {
+                s = scores[(int64_t)b * ld + e];
+                for (l = 1; l < L; ++l) {
+                    float x = scores[((int64_t)l * B + b) * ld + e];
+                    if (x > s)
+                        s = x;
+                }
+            } else {
+                float sum = 0.0f;
+                for (l = 0; l < L; ++l)
+                    sum += scores[((int64_t)l * B + b) * ld + e];
+                s = sum / (float)L;
+            }
+            if (s >= threshold)
+                pr[e / 64].density += 1;
+        }
+        for (p = 0; p < P; ++p) {
+            if (p < n_sink || p >= P - n_recent)
+                pr[p].rank = 2;
+            else
+                pr[p].rank = pr[p].density > 0 ? 1 : 0;
+        }
+        qsort(pr, (size_t)P, sizeof(page_rank), cmp_page);
+        for (i = 0; i < P && n < kmax; ++i)
+            if (pr[i].rank > 0)
+                chosen[n++] = pr[i].page;
+        qsort(chosen, (size_t)n, sizeof(int32_t), cmp_int);
+        for (i = 0; i < kmax; ++i)
+            out_pages[(int64_t)b * kmax + i] = i < n ? chosen[i] : -1;
+        if (out_count)
+            out_count[b] = n;
+        free(pr);
+        free(chosen);
+    }
+    return 0;
 }
 
 int oracle_max_threads(void)

@@ -73,6 +73,10 @@ def _load():
     lib.oracle_write_keys.restype = ctypes.c_int64
     lib.oracle_write_keys.argtypes = [_c_u16p, ctypes.c_int64, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_int64), _c_u8p, ctypes.c_int64]
+    lib.oracle_level1_select.restype = ctypes.c_int
+    lib.oracle_level1_select.argtypes = [_c_f32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int64, _c_i32p, ctypes.c_int32, ctypes.c_float,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _c_i32p, _c_i32p]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     _lib = lib
@@ -231,3 +235,36 @@ def write_keys(k: np.ndarray, slots: np.ndarray, pool: np.ndarray) -> int:
     return int(_load().oracle_write_keys(_ptr(k, ctypes.c_uint16), n, D,
                                          _ptr(slots, ctypes.c_int64),
                                          _ptr(pool, ctypes.c_uint8), pool.shape[0]))
+
+
+ENSEMBLE_MAX, ENSEMBLE_MEAN = 0, 1
+
+
+def level1_select(scores: np.ndarray, limits, ensemble: int, threshold: float, n_sink: int,
+                  n_recent: int, kmax: int):
+    """Level-1 resident pages from per-layer binary32 sigmoid scores
+    [L, B, n_cols]: (pages int32 [B, kmax] ascending, -1 padded; count [B])."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    L, B, n = scores.shape
+    limits = np.ascontiguousarray(limits, dtype=np.int32)
+    pages = np.empty((B, kmax), dtype=np.int32)
+    count = np.empty(B, dtype=np.int32)
+    rc = _load().oracle_level1_select(_ptr(scores, ctypes.c_float), L, B, n, n,
+                                      _ptr(limits, ctypes.c_int32), ensemble,
+                                      ctypes.c_float(threshold), n_sink, n_recent, kmax,
+                                      _ptr(pages, ctypes.c_int32), _ptr(count, ctypes.c_int32))
+    if rc != 0:
+        raise RuntimeError(f"oracle_level1_select failed ({rc})")
+    return pages, count
+
+
+def level1_scores(layers, rows=None, n_threads: int = 0) -> np.ndarray:
+    """The oracle's own per-layer scores [L, B, n_cols]: sigmoid of the double
+    logits of each layer's workload, rounded to binary32 (0 where unscored)."""
+    out = []
+    for wl in layers:
+        lg = score(wl, rows=rows, n_threads=n_threads)
+        with np.errstate(over="ignore"):
+            s = 1.0 / (1.0 + np.exp(-lg))
+        out.append(s.astype(np.float32))
+    return np.stack(out)

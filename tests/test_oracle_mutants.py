@@ -44,6 +44,15 @@ MUTANTS = {
     "writer-amax-ignores-negatives": ("if (fabsf(v) > amax)\n            amax = fabsf(v);",
                                       "if (v > amax)\n            amax = v;"),
     "writer-bad-slot-not-counted": ("            ++bad;\n", ""),
+    "level1-max-is-min": ("                    if (x > s)\n", "                    if (x < s)\n"),
+    "level1-mean-not-divided": ("s = sum / (float)L;", "s = sum;"),
+    "level1-threshold-exclusive": ("if (s >= threshold)", "if (s > threshold)"),
+    "level1-ties-to-higher-page": ("return (a->page > b->page) - (a->page < b->page);",
+                                   "return (a->page < b->page) - (a->page > b->page);"),
+    "level1-recent-off-by-one": ("if (p < n_sink || p >= P - n_recent)", "if (p < n_sink || p > P - n_recent)"),
+    "level1-entries-past-limit": ("for (e = 0; e < hist; ++e) {", "for (e = 0; e < P * 64 && e < n_cols; ++e) {"),
+    "level1-nothing-forced": ("                pr[p].rank = 2;\n", "                pr[p].rank = pr[p].density > 0;\n"),
+    "level1-empty-pages-eligible": ("pr[p].rank = pr[p].density > 0 ? 1 : 0;", "pr[p].rank = 1;"),
 }
 
 PIN_TESTS = [
@@ -62,6 +71,11 @@ PIN_TESTS = [
     pins.test_quantize_row_with_amax_448_is_the_plain_cast,
     lambda: pins.test_quantize_row_scale_is_rounded_amax_over_448_and_error_is_half_a_step(0),
     pins.test_write_keys_places_rows_and_skips_padding_and_bad_slots,
+    pins.test_level1_densest_pages_closed_form,
+    pins.test_level1_threshold_is_inclusive_and_mean_rounds_in_binary32,
+    pins.test_level1_history_bounds,
+    lambda: pins.test_level1_matches_brute_force(0),
+    pins.test_level1_layer_order_and_single_layer,
 ]
 
 

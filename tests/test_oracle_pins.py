@@ -494,3 +494,136 @@ def test_written_rows_score_like_their_dequantised_keys():
         kd = np.array([oracle.e4m3_value(u) for u in pool[e, :128]]) * _scale_of(pool[e])
         want = float(np.maximum(qd @ kd, 0.0) @ w.astype(np.float64))
         assert oracle.logit(q, w, pool[e]) == pytest.approx(want, rel=1e-12, abs=1e-12)
+
+
+# ------------------------------------------------- Level-1 resident selection
+
+def _constructed_scores(densities, limit, hi=0.9, lo=0.2, n_cols=None):
+    """One row whose page p holds exactly densities[p] entries scoring `hi`
+    (the rest `lo`), over `limit` entries."""
+    n_cols = n_cols or 64 * len(densities)
+    s = np.full((1, 1, n_cols), lo, dtype=np.float32)
+    for p, d in enumerate(densities):
+        room = min(64, limit - 64 * p)
+        assert d <= room
+        s[0, 0, 64 * p + np.arange(d)[::-1] * (room // max(d, 1)) if d else []] = hi
+    return s
+
+
+def test_level1_densest_pages_closed_form():
+    """Densities fixed by construction: forced sink and recent pages, then
+    the densest others, equal densities to the lower page, pages of density
+    0 only when forced, ascending output with -1 padding."""
+    d = [3, 0, 7, 7, 1, 5, 0, 2]
+    s = _constructed_scores(d, limit=500)               # 8 pages, the last one partial
+    lim = [500]
+    M = oracle.ENSEMBLE_MAX
+    pages, cnt = oracle.level1_select(s, lim, M, 0.5, 1, 1, 4)
+    assert pages.tolist() == [[0, 2, 3, 7]] and cnt.tolist() == [4]
+    pages, cnt = oracle.level1_select(s, lim, M, 0.5, 1, 1, 5)
+    assert pages.tolist() == [[0, 2, 3, 5, 7]]
+    pages, cnt = oracle.level1_select(s, lim, M, 0.5, 1, 1, 8)
+    assert pages.tolist() == [[0, 2, 3, 4, 5, 7, -1, -1]] and cnt.tolist() == [6]
+    pages, _ = oracle.level1_select(s, lim, M, 0.5, 0, 0, 3)
+    assert pages.tolist() == [[2, 3, 5]]
+    pages, _ = oracle.level1_select(s, lim, M, 0.5, 2, 3, 6)       # sink {0,1}, recent {5,6,7}
+    assert pages.tolist() == [[0, 1, 2, 5, 6, 7]]
+    pages, cnt = oracle.level1_select(s, lim, M, 2.0, 1, 1, 4)      # nothing passes: forced only
+    assert pages.tolist() == [[0, 7, -1, -1]] and cnt.tolist() == [2]
+
+
+def test_level1_threshold_is_inclusive_and_mean_rounds_in_binary32():
+    s = np.zeros((2, 1, 64), np.float32)
+    s[0, 0, :5] = 0.25
+    s[1, 0, :5] = 0.75                                  # mean exactly 0.5, max 0.75
+    lim = [64]
+    for ens, tau, want in [(oracle.ENSEMBLE_MEAN, 0.5, 1), (oracle.ENSEMBLE_MEAN, np.nextafter(np.float32(0.5), 1), 0),
+                           (oracle.ENSEMBLE_MAX, 0.75, 1), (oracle.ENSEMBLE_MAX, 0.76, 0),
+                           (oracle.ENSEMBLE_MEAN, 0.6, 0), (oracle.ENSEMBLE_MAX, 0.6, 1)]:
+        _, cnt = oracle.level1_select(s, lim, ens, float(tau), 0, 0, 1)
+        assert cnt.tolist() == [want], (ens, tau)
+    # binary32 mean: 0.1 + 0.2 + 0.3 in float is 0.6000000238..., / 3 rounds to 0.2 (binary32)
+    t = np.zeros((3, 1, 64), np.float32)
+    t[:, 0, 0] = np.float32([0.1, 0.2, 0.3])
+    m32 = (np.float32(0.1) + np.float32(0.2) + np.float32(0.3)) / np.float32(3)
+    _, cnt = oracle.level1_select(t, lim, oracle.ENSEMBLE_MEAN, float(m32), 0, 0, 1)
+    assert cnt.tolist() == [1]
+    _, cnt = oracle.level1_select(t, lim, oracle.ENSEMBLE_MEAN, float(np.nextafter(m32, np.float32(1))), 0, 0, 1)
+    assert cnt.tolist() == [0]
+
+
+def test_level1_history_bounds():
+    """Entries at or past the limit never count; the recent pages end at the
+    row's last page; empty and one-page histories."""
+    s = np.full((1, 3, 64 * 6), 0.9, np.float32)
+    pages, cnt = oracle.level1_select(s, [130, 0, 64], oracle.ENSEMBLE_MAX, 0.5, 0, 1, 6)
+    assert pages[0].tolist() == [0, 1, 2, -1, -1, -1] and cnt[0] == 3    # 130 entries: 3 pages
+    assert pages[1].tolist() == [-1] * 6 and cnt[1] == 0
+    assert pages[2].tolist() == [0, -1, -1, -1, -1, -1]
+    # the limit's partial page: only its first 2 entries count, so it is the least dense
+    s2 = np.full((1, 1, 64 * 3), 0.9, np.float32)
+    pages, _ = oracle.level1_select(s2, [130], oracle.ENSEMBLE_MAX, 0.5, 0, 0, 2)
+    assert pages[0].tolist() == [0, 1]
+    # limits past n_cols are clamped to it
+    pages, cnt = oracle.level1_select(s2, [10 ** 6], oracle.ENSEMBLE_MAX, 0.5, 0, 1, 3)
+    assert cnt.tolist() == [3]
+
+
+def _level1_brute(scores, limits, ens, tau, n_sink, n_recent, kmax):
+    """Independent numpy version: page densities by reduceat, ranking by lexsort."""
+    L, B, n = scores.shape
+    out = np.full((B, kmax), -1, np.int32)
+    cnt = np.zeros(B, np.int32)
+    for b in range(B):
+        hist = int(min(max(limits[b], 0), n))
+        P = -(-hist // 64)
+        if P == 0:
+            continue
+        if ens == oracle.ENSEMBLE_MAX:
+            s = scores[:, b, :hist].max(axis=0)
+        else:
+            s = scores[0, b, :hist].copy()
+            for l in range(1, L):
+                s = (s + scores[l, b, :hist]).astype(np.float32)
+            s = (s / np.float32(L)).astype(np.float32)
+        dens = np.add.reduceat((s >= np.float32(tau)).astype(np.int64), np.arange(0, hist, 64))
+        p = np.arange(P)
+        forced = (p < n_sink) | (p >= P - n_recent)
+        elig = forced | (dens > 0)
+        order = np.lexsort((p, -dens, ~forced))
+        chosen = np.sort([q for q in order if elig[q]][:kmax])
+        out[b, :len(chosen)] = chosen
+        cnt[b] = len(chosen)
+    return out, cnt
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_level1_matches_brute_force(seed):
+    rng = np.random.default_rng(200 + seed)
+    L, B, n = 3, 5, 64 * 40
+    # scores on a coarse grid so many entries tie with each other and the threshold
+    s = (rng.integers(0, 20, size=(L, B, n)) / np.float32(20)).astype(np.float32)
+    limits = np.array([n, n - 17, 64 * 7 + 1, 33, 0], np.int32)
+    for ens in (oracle.ENSEMBLE_MAX, oracle.ENSEMBLE_MEAN):
+        for tau, ns, nr, km in [(0.8, 1, 1, 8), (0.95, 2, 2, 6), (0.5, 0, 0, 40), (0.9, 1, 3, 4)]:
+            got = oracle.level1_select(s, limits, ens, tau, ns, nr, km)
+            want = _level1_brute(s, limits, ens, tau, ns, nr, km)
+            assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1]), (ens, tau, ns, nr, km)
+
+
+def test_level1_layer_order_and_single_layer():
+    rng = np.random.default_rng(5)
+    s = rng.random((3, 4, 64 * 12)).astype(np.float32)
+    lim = [768, 700, 300, 64]
+    a = oracle.level1_select(s, lim, oracle.ENSEMBLE_MAX, 0.9, 1, 1, 5)
+    b = oracle.level1_select(s[::-1].copy(), lim, oracle.ENSEMBLE_MAX, 0.9, 1, 1, 5)
+    assert np.array_equal(a[0], b[0])
+    one = s[:1].copy()
+    c = oracle.level1_select(one, lim, oracle.ENSEMBLE_MAX, 0.7, 1, 1, 5)
+    d = oracle.level1_select(one, lim, oracle.ENSEMBLE_MEAN, 0.7, 1, 1, 5)
+    assert np.array_equal(c[0], d[0])
+    # max over layers selects at least what each layer alone selects: raise one layer to 1
+    s2 = s.copy()
+    s2[1] = 1.0
+    e, cnt = oracle.level1_select(s2, lim, oracle.ENSEMBLE_MAX, 0.99, 0, 0, 12)
+    assert cnt.tolist() == [12, 11, 5, 1]
