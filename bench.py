@@ -17,6 +17,11 @@ kernel's start and end on the stream it runs on.
 one idx_write_keys call that quantises the 262,144 compressed keys of one
 1M-token request into a shuffled paged pool; `value` is keys written per
 second and `roofline` covers the writer kernel.
+
+`--workload memory-indexer` measures the Level-1 resident-set selection: one
+step is one idx_select_resident call over 8 requests at 1M tokens (262,144
+entries each) scored at 3 layers, KMAX 384 pages; `value` is scored pairs per
+second over all layers and `roofline` covers one layer's score-kernel launch.
 """
 from __future__ import annotations
 
@@ -43,12 +48,13 @@ WRITE_SOURCES = ["sparse_attention_kv_paged_amd/csrc/idx_write.hip",
 WORKLOADS = {"tiny-decode": 0, "decode-batch": 1, "long-decode": 2,
              "chunked-prefill": 3, "resident-subset": 4}
 WRITE_WORKLOAD = "index-fill"
+RESIDENT_WORKLOAD = "memory-indexer"
 WRITE_BYTES_PER_KEY = 128 * 2 + 8 + 132      # bf16 key in, int64 slot, pool row out
 
 
 def kernel_of(workload: str):
     """(kernel name, its sources, profile file prefix) measured for a workload."""
-    if workload == WRITE_WORKLOAD:
+    if workload == "index-fill":
         return "write_keys_kernel", WRITE_SOURCES, "write_keys"
     return "score_kernel", SCORE_SOURCES, "score_kernel"
 
@@ -353,12 +359,93 @@ def bench_writer(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_resident(args):
+    """One step = one idx_select_resident of the memory-indexer workload."""
+    import numpy as np
+    import torch
+    from oracle import oracle
+    from sparse_attention_kv_paged_amd import lib, workloads
+
+    torch.cuda.set_device(0)
+    rl = workloads.memory_indexer()
+    print(f"[bench] workload {rl.name}: {rl.description}", file=sys.stderr, flush=True)
+    dls = [lib.to_device(wl) for wl in rl.layers]
+    pairs_layer = [wl.pairs() for wl in rl.layers]
+    pairs = int(sum(pairs_layer))
+    out_pages = torch.empty((rl.B, rl.kmax), dtype=torch.int32, device="cuda")
+    out_count = torch.empty(rl.B, dtype=torch.int32, device="cuda")
+    ws = torch.empty(lib.resident_workspace_bytes(len(dls), rl.B, rl.n_cols, rl.kmax), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(i):
+        lib.idx_select_resident([d.q for d in dls], [d.w for d in dls], [d.keys for d in dls], rl.n_cols,
+                                rl.kmax, ensemble=rl.ensemble, threshold=rl.threshold, n_sink=rl.n_sink,
+                                n_recent=rl.n_recent, out_pages=out_pages, out_count=out_count, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # the three layers' pools (830 MB) exceed the 256 MB MALL: no replicas needed
+    ms_per_step = run_steps(step, args.steps, 1, not args.no_graph)
+    # the hook stamps every score launch of a step; the events keep the last
+    # layer's launch, whose bytes are one layer's
+    kern_ms = kernel_ms_live(step, args.steps)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+    wl = rl.layers[-1]
+    algo = algorithmic_bytes(wl, pairs_layer[-1]) + pairs_layer[-1] * 4     # + the scores written
+    roofline = {"kernel": "score_kernel", "bound": "hbm", "achieved": algo / (kern_ms * 1e-3) / 1e9,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": read_traffic(RESIDENT_WORKLOAD),
+                "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+    roofline["frac"] = roofline["achieved"] / roofline["peak"]
+    step_bytes = sum(algorithmic_bytes(w_, p_) + p_ * 4 for w_, p_ in zip(rl.layers, pairs_layer))
+    out = {
+        "metric": "Level-1 resident-set selection: scored pairs/s over all layers; % of HBM peak, 1 MI355X",
+        "value": pairs / (ms_per_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": rl.name, "queries": rl.B, "layers": len(rl.layers), "n_cols": rl.n_cols,
+                   "kmax": rl.kmax, "threshold": rl.threshold, "n_sink": rl.n_sink, "n_recent": rl.n_recent,
+                   "ensemble": "max" if rl.ensemble == 0 else "mean", "pairs": pairs,
+                   "description": rl.description, "graph": not args.no_graph},
+        "requests_per_s": rl.B / (ms_per_step * 1e-3),
+        "path_hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on one request: three layers' double scores, then the selection
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            sc = oracle.level1_scores(rl.layers, rows=[reps % rl.B])
+            oracle.level1_select(sc, rl.limits[[reps % rl.B]], rl.ensemble, rl.threshold, rl.n_sink,
+                                 rl.n_recent, rl.kmax)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        per_row = pairs / rl.B
+        out["cpu_baseline"] = {"value": per_row * reps / el, "unit": "pairs/s", "cores": oracle.max_threads(),
+                               "kind": "oracle",
+                               "sample": f"{reps} requests of {rl.name} (3 layers x {rl.n_cols} entries, "
+                                         f"score + selection) in {el:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=96)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode-batch", choices=sorted(WORKLOADS) + [WRITE_WORKLOAD])
+    ap.add_argument("--workload", default="decode-batch",
+                    choices=sorted(WORKLOADS) + [WRITE_WORKLOAD, RESIDENT_WORKLOAD])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for >= 1 GB)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -371,7 +458,8 @@ def main():
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
 
-    trace_prefix = "write_keys" if args.workload == WRITE_WORKLOAD else "score_topk"
+    trace_prefix = {WRITE_WORKLOAD: "write_keys", RESIDENT_WORKLOAD: "select_resident"}.get(args.workload,
+                                                                                          "score_topk")
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.workload, args.command,
                         os.path.join(PROFILE_DIR, f"{trace_prefix}_{args.workload}_trace.txt"))
@@ -388,6 +476,9 @@ def main():
 
     if args.workload == WRITE_WORKLOAD:
         bench_writer(args)
+        return
+    if args.workload == RESIDENT_WORKLOAD:
+        bench_resident(args)
         return
 
     import numpy as np

@@ -208,6 +208,67 @@ int idx_write_keys(const uint16_t *k, int64_t n, int32_t D,
                    const int64_t *slots, uint8_t *pool, int64_t n_pool_rows,
                    uint32_t *status, void *stream);
 
+/*
+ * idx_select_resident: Level 1 of the two-level recall ("FlashMemory-
+ * DeepSeek-V4" README, sections "Two-level recall algorithm" and "Joint
+ * checkpoint + ensemble"; KMAX in section "Quick start"): score each row's
+ * whole history at n_layers retriever layers, each with its own q, w and
+ * index plane, ensemble the layers' sigmoid scores per entry, threshold them,
+ * and choose the pages (64-entry blocks) to keep resident.  The pages give
+ * the steps but not their details; this library takes:
+ *   - entry e of row b (e < keys[0].limits[b], clamped to n_cols) is
+ *     selected iff its ensemble score s >= cfg->threshold, where s is the
+ *     maximum of the layers' binary32 sigmoid scores (IDX_ENSEMBLE_MAX, the
+ *     pages' default) or their binary32 sum in layer order divided by
+ *     n_layers (IDX_ENSEMBLE_MEAN);
+ *   - a page's density is its number of selected entries; the row's history
+ *     has P = ceil(limit / 64) pages;
+ *   - pages p < n_sink (the attention sink) and p >= P - n_recent (the
+ *     recency tail) are always resident; the others with density > 0 follow,
+ *     densest first, equal densities to the lower page, up to kmax pages.
+ *
+ * n_layers  1 .. IDX_MAX_LAYERS (the pages' checkpoint has 3).
+ * q, w      host arrays of n_layers device pointers: layer l's q [B, H, D]
+ *           (bf16, 16-byte aligned) and fused weights [B, H].
+ * keys      host array of n_layers structs: layer l's index plane and tile
+ *           lists, as for idx_score, without chunk lists (the whole history
+ *           is scored).  keys[0].limits also bounds the selection.
+ * n_cols    columns per row (logical entries), >= 1.
+ * cfg       ensemble, threshold, n_sink, n_recent >= 0, 1 <= kmax <= 2048,
+ *           n_sink + n_recent <= kmax.
+ * out_pages int32 [B, kmax] out: resident pages in ascending order, -1 after
+ *           the last.  Usable as chunk_ids (max_chunks = kmax) of a later
+ *           idx_score / idx_score_topk on the same rows.
+ * out_count int32 [B] out, or NULL: resident pages per row (usable as
+ *           n_chunks).
+ * workspace / ws_bytes: at least idx_resident_workspace_bytes(n_layers, B,
+ *           n_cols, kmax) bytes, 256-byte aligned; contents on entry do not
+ *           matter.  Calls that share one workspace must not overlap.
+ */
+#define IDX_ENSEMBLE_MAX 0
+#define IDX_ENSEMBLE_MEAN 1
+#define IDX_MAX_LAYERS 8
+
+typedef struct idx_resident_cfg {
+    int32_t ensemble;
+    float threshold;
+    int32_t n_sink;
+    int32_t n_recent;
+    int32_t kmax;
+} idx_resident_cfg;
+
+int idx_select_resident(int32_t n_layers, const uint16_t *const *q,
+                        const float *const *w, int32_t B, int32_t H, int32_t D,
+                        const idx_keys *keys, int32_t n_cols,
+                        const idx_resident_cfg *cfg, int32_t *out_pages,
+                        int32_t *out_count, void *workspace, size_t ws_bytes,
+                        void *stream);
+
+/* Workspace bytes idx_select_resident needs; (size_t)-1 for invalid
+ * arguments. */
+size_t idx_resident_workspace_bytes(int32_t n_layers, int32_t B, int32_t n_cols,
+                                    int32_t kmax);
+
 /* Workspace bytes an op needs for B rows of n_cols columns and top-k
  * (0 for IDX_OP_SCORE); (size_t)-1 for invalid arguments. */
 size_t idx_workspace_bytes(int32_t op, int32_t B, int32_t n_cols, int32_t k);

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libidx.so")
-SOURCES = ["idx_api.cpp", "idx_score.hip", "idx_topk.hip", "idx_write.hip"]
+SOURCES = ["idx_api.cpp", "idx_score.hip", "idx_topk.hip", "idx_write.hip", "idx_level1.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

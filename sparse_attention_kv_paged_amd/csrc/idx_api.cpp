@@ -9,6 +9,7 @@
 
 #include "../../include/idx.h"
 #include "idx_internal.h"
+#include "idx_level1.h"
 #include "idx_write.h"
 
 namespace {
@@ -97,8 +98,9 @@ TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
 hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_t ld,
                         const uint32_t *row_cols, int32_t B, int32_t n_cols, int32_t k,
                         int32_t *out_idx, float *out_val, const int32_t *chunk_ids,
-                        int32_t max_chunks, hipStream_t s) {
+                        int32_t max_chunks, hipStream_t s, int32_t *out_count = nullptr) {
     idx::SegArgs a{};
+    a.out_count = out_count;
     a.B = B;
     a.k = k;
     a.logits = logits;
@@ -140,6 +142,36 @@ hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_
         in_parts = m.parts;
         cur ^= 1;
     }
+}
+
+// Level-1 workspace: one logits scratch row block (written by every layer's
+// score launch, never read), the layers' scores, the page keys, then the
+// page top-k's own pieces; each piece 256-byte aligned.
+struct ResidentPlan {
+    int64_t ld = 0, ldp = 0;
+    int32_t n_pages = 0;
+    size_t logits = 0, scores = 0, page_keys = 0, topk = 0, total = 0;
+    TopkPlan top;
+};
+
+ResidentPlan resident_plan(int32_t L, int32_t B, int32_t n_cols, int32_t kmax) {
+    ResidentPlan R;
+    R.ld = round_up(std::max<int64_t>(n_cols, 1), 64);
+    R.n_pages = (int32_t)(R.ld / 64);
+    R.ldp = round_up(R.n_pages, 64);
+    R.top = topk_plan(false, B, R.n_pages, kmax);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += (size_t)round_up((int64_t)std::max<size_t>(bytes, 1), 256);
+        return at;
+    };
+    R.logits = take((size_t)B * R.ld * sizeof(float));
+    R.scores = take((size_t)L * B * R.ld * sizeof(float));
+    R.page_keys = take((size_t)B * R.ldp * sizeof(float));
+    R.topk = take(R.top.total);
+    R.total = off;
+    return R;
 }
 
 int check_qw(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D) {
@@ -282,6 +314,71 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t
     hipError_t e = enqueue_topk(P, static_cast<char *>(workspace), logits, ld, nullptr, B, n_cols, k,
                                 out_col, out_val, nullptr, 0, (hipStream_t)stream);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
+}
+
+size_t idx_resident_workspace_bytes(int32_t n_layers, int32_t B, int32_t n_cols, int32_t kmax) {
+    if (n_layers < 1 || n_layers > IDX_MAX_LAYERS || B < 0 || n_cols < 1 || kmax < 1 || kmax > idx::kMaxK)
+        return (size_t)-1;
+    return resident_plan(n_layers, B, n_cols, kmax).total;
+}
+
+int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float *const *w, int32_t B, int32_t H,
+                        int32_t D, const idx_keys *keys, int32_t n_cols, const idx_resident_cfg *cfg,
+                        int32_t *out_pages, int32_t *out_count, void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    if (n_layers < 1 || n_layers > IDX_MAX_LAYERS)
+        return fail(IDX_E_SHAPE, "n_layers must be in [1, %d] (got %d)", IDX_MAX_LAYERS, n_layers);
+    if (!q || !w || !keys || !cfg) return fail(IDX_E_ARG, "q, w, keys and cfg must be non-null");
+    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if (cfg->ensemble != IDX_ENSEMBLE_MAX && cfg->ensemble != IDX_ENSEMBLE_MEAN)
+        return fail(IDX_E_ARG, "ensemble must be IDX_ENSEMBLE_MAX or IDX_ENSEMBLE_MEAN");
+    if (!(cfg->threshold == cfg->threshold)) return fail(IDX_E_ARG, "threshold is NaN");
+    if (cfg->kmax < 1 || cfg->kmax > idx::kMaxK) return fail(IDX_E_SHAPE, "kmax must be in [1, 2048]");
+    if (cfg->n_sink < 0 || cfg->n_recent < 0 || (int64_t)cfg->n_sink + cfg->n_recent > cfg->kmax)
+        return fail(IDX_E_SHAPE, "need n_sink, n_recent >= 0 and n_sink + n_recent <= kmax");
+    int rc;
+    for (int l = 0; l < n_layers; ++l) {
+        if ((rc = check_qw(q[l], w[l], B, H, D))) return rc;
+        if ((rc = check_keys(&keys[l], B))) return rc;
+        if (keys[l].chunk_ids) return fail(IDX_E_ARG, "Level-1 scoring takes no chunk lists (layer %d)", l);
+    }
+    if (B == 0) return IDX_OK;
+    if (!out_pages) return fail(IDX_E_ARG, "out_pages must be non-null");
+    if (!aligned(out_pages, 4) || !aligned(out_count, 4)) return fail(IDX_E_ALIGN, "outputs must be 4-byte aligned");
+    const ResidentPlan R = resident_plan(n_layers, B, n_cols, cfg->kmax);
+    if (!workspace || ws_bytes < R.total)
+        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", R.total, ws_bytes);
+    if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+    float *scores = reinterpret_cast<float *>(ws + R.scores);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    for (int l = 0; l < n_layers; ++l) {
+        idx::ScoreArgs a = score_args(q[l], w[l], B, &keys[l], n_cols);
+        a.ld = R.ld;
+        a.logits = reinterpret_cast<float *>(ws + R.logits);
+        a.scores = scores + (int64_t)l * B * R.ld;
+        if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
+    }
+    idx::PageArgs pa{};
+    pa.scores = scores;
+    pa.L = n_layers;
+    pa.B = B;
+    pa.ld = R.ld;
+    pa.layer_stride = (int64_t)B * R.ld;
+    pa.n_cols = n_cols;
+    pa.limits = keys[0].limits;
+    pa.ensemble = cfg->ensemble;
+    pa.threshold = cfg->threshold;
+    pa.n_sink = cfg->n_sink;
+    pa.n_recent = cfg->n_recent;
+    pa.page_keys = reinterpret_cast<float *>(ws + R.page_keys);
+    pa.ldp = R.ldp;
+    pa.n_pages = R.n_pages;
+    if ((e = idx::launch_pages(pa, s)) != hipSuccess) return hip_fail(e, "page kernel");
+    e = enqueue_topk(R.top, ws + R.topk, pa.page_keys, R.ldp, nullptr, B, R.n_pages, cfg->kmax, out_pages,
+                     nullptr, nullptr, 0, s, out_count);
+    return e == hipSuccess ? IDX_OK : hip_fail(e, "page top-k");
 }
 
 int idx_write_keys(const uint16_t *k, int64_t n, int32_t D, const int64_t *slots, uint8_t *pool,

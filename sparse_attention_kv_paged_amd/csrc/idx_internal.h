@@ -68,6 +68,7 @@ struct SegArgs {
     // final output
     int32_t *out_idx;           // [B, k]
     float *out_val;             // [B, k] or null
+    int32_t *out_count;         // [B] number of winners per row, or null
     const int32_t *chunk_ids;   // columns -> logical entries, or null
     int32_t max_chunks;
 };

@@ -1,0 +1,29 @@
+// Internal launch interface of the Level-1 page pass (idx_level1.hip), used
+// by the C-ABI layer (idx_api.cpp).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace idx {
+
+struct PageArgs {
+    const float *scores;        // [L][B][ld] binary32 sigmoid scores
+    int32_t L;
+    int32_t B;
+    int64_t ld;                 // row stride of one layer's scores
+    int64_t layer_stride;       // B * ld
+    int32_t n_cols;             // scored columns (logical entries) per row
+    const int32_t *limits;      // [B] history length of each row
+    int32_t ensemble;           // IDX_ENSEMBLE_MAX or IDX_ENSEMBLE_MEAN
+    float threshold;
+    int32_t n_sink;
+    int32_t n_recent;
+    float *page_keys;           // [B, ldp] out
+    int64_t ldp;
+    int32_t n_pages;            // ceil(n_cols / 64)
+};
+
+hipError_t launch_pages(const PageArgs &a, hipStream_t s);
+
+}  // namespace idx

@@ -304,8 +304,9 @@ __device__ __forceinline__ void scan_winners(const uint32_t (&key)[PER], uint32_
 
 // Final output of row b: the winners' logical entry ids (a column's chunk
 // resolved through chunk_ids) and values at their positions, -1 / -inf in
-// [count, k).  Every load and store goes through a buffer descriptor, none
-// behind a branch.
+// [count, k), and count itself when out_count is given.  The chunk loads and
+// the id and value stores go through buffer descriptors, none behind a
+// branch.
 template <int NT, int PER, class ColOf>
 __device__ __forceinline__ void write_final(const SegArgs &a, int b, WinCursor cur, const uint32_t (&key)[PER],
                                             ColOf col, uint32_t count) {
@@ -354,6 +355,7 @@ __device__ __forceinline__ void write_final(const SegArgs &a, int b, WinCursor c
         __builtin_amdgcn_raw_buffer_store_b32(0xFFFFFFFFu, ir, i * 4u, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(-__builtin_inff()), vr, i * 4u, 0, 0);
     }
+    if (a.out_count && threadIdx.x == 0) a.out_count[b] = (int32_t)count;
 }
 
 // Merge lists: every list holds exactly lcap = k rounded up to even items,

@@ -22,8 +22,11 @@ IDX_OK, IDX_E_ARG, IDX_E_SHAPE, IDX_E_ALIGN, IDX_E_WORKSPACE, IDX_E_HIP = range(
 IDX_OP_SCORE, IDX_OP_TOPK, IDX_OP_SCORE_TOPK = range(3)
 STATUS_LIMIT_CLAMPED, STATUS_BAD_BLOCK, STATUS_BAD_REQUEST, STATUS_BAD_CHUNK = 1, 2, 4, 8
 STATUS_BAD_SLOT = 16
+ENSEMBLE_MAX, ENSEMBLE_MEAN = 0, 1
+MAX_LAYERS = 8
 
-EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_write_keys", "idx_workspace_bytes",
+EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_write_keys", "idx_select_resident",
+           "idx_resident_workspace_bytes", "idx_workspace_bytes",
            "idx_error_string", "idx_last_error", "idx_profile_events", "idx_abi_version")
 
 
@@ -42,6 +45,17 @@ class IdxKeys(ctypes.Structure):
         ("n_chunks", ctypes.c_void_p),
         ("limits", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+    ]
+
+
+class ResidentCfg(ctypes.Structure):
+    """Mirror of `struct idx_resident_cfg`."""
+    _fields_ = [
+        ("ensemble", ctypes.c_int32),
+        ("threshold", ctypes.c_float),
+        ("n_sink", ctypes.c_int32),
+        ("n_recent", ctypes.c_int32),
+        ("kmax", ctypes.c_int32),
     ]
 
 
@@ -72,6 +86,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.idx_score_topk.restype = ctypes.c_int
     lib.idx_write_keys.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp]
     lib.idx_write_keys.restype = ctypes.c_int
+    lib.idx_select_resident.argtypes = [i32, vp, vp, i32, i32, i32, kp, i32, ctypes.POINTER(ResidentCfg),
+                                        vp, vp, vp, sz, vp]
+    lib.idx_select_resident.restype = ctypes.c_int
+    lib.idx_resident_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.idx_resident_workspace_bytes.restype = sz
     lib.idx_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.idx_workspace_bytes.restype = sz
     lib.idx_error_string.argtypes = [i32]
@@ -248,6 +267,48 @@ def idx_write_keys(k: torch.Tensor, slots: torch.Tensor, pool: torch.Tensor,
     _check(load().idx_write_keys(_ptr(k), k.shape[0], k.shape[1], _ptr(slots), _ptr(pool),
                                  pool.shape[0], _ptr(status), _stream(stream)))
     return pool
+
+
+def resident_workspace_bytes(n_layers: int, B: int, n_cols: int, kmax: int) -> int:
+    n = load().idx_resident_workspace_bytes(n_layers, B, n_cols, kmax)
+    if n == ctypes.c_size_t(-1).value:
+        raise IdxError(IDX_E_ARG, "invalid workspace request")
+    return int(n)
+
+
+def idx_resident_workspace_bytes(n_layers: int, B: int, n_cols: int, kmax: int) -> int:
+    return resident_workspace_bytes(n_layers, B, n_cols, kmax)
+
+
+def idx_select_resident(qs, ws, keys_list, n_cols: int, kmax: int, ensemble: int = ENSEMBLE_MAX,
+                        threshold: float = 0.5, n_sink: int = 1, n_recent: int = 1, out_pages=None,
+                        out_count=None, workspace=None, stream=None):
+    """Level-1 resident pages [B, kmax] (int32, ascending, -1 padded) and
+    their count [B] from per-layer q, w and Keys (lists of equal length)."""
+    L = len(qs)
+    if not (len(ws) == len(keys_list) == L) or L < 1 or L > MAX_LAYERS:
+        raise ValueError(f"need 1..{MAX_LAYERS} layers with one q, w and Keys each")
+    pairs = [_qw(q, w) for q, w in zip(qs, ws)]
+    B, H, D = pairs[0][0].shape
+    if any(q.shape != (B, H, D) for q, _ in pairs):
+        raise ValueError("every layer's q must have the same shape")
+    dev = pairs[0][0].device
+    if out_pages is None:
+        out_pages = torch.empty((B, kmax), dtype=torch.int32, device=dev)
+    if out_count is None:
+        out_count = torch.empty(B, dtype=torch.int32, device=dev)
+    _dev(out_pages, torch.int32, "out_pages")
+    _dev(out_count, torch.int32, "out_count")
+    need = resident_workspace_bytes(L, B, n_cols, kmax)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    qa = (ctypes.c_void_p * L)(*[q.data_ptr() for q, _ in pairs])
+    wa = (ctypes.c_void_p * L)(*[w.data_ptr() for _, w in pairs])
+    ka = (IdxKeys * L)(*[k.struct() for k in keys_list])
+    cfg = ResidentCfg(ensemble, threshold, n_sink, n_recent, kmax)
+    _check(load().idx_select_resident(L, qa, wa, B, H, D, ka, n_cols, ctypes.byref(cfg), _ptr(out_pages),
+                                      _ptr(out_count), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out_pages, out_count
 
 
 # ---------------------------------------------------------------------------

@@ -360,6 +360,55 @@ def index_fill(n_keys=262144, seed=5, D=HEAD_DIM, poison_frac=0.01,
                      description=f"{n_keys} keys into {nblk} shuffled blocks (+{n_blocks - nblk} unreferenced), seed {seed}")
 
 
+@dataclasses.dataclass
+class ResidentLoad:
+    """One Level-1 selection problem: per-layer scoring workloads (same rows,
+    same limits, each layer its own q, w and paged index plane) and the
+    selection settings."""
+
+    name: str
+    layers: list                        # [Workload] * n_layers
+    kmax: int = 384
+    threshold: float = 0.76
+    n_sink: int = 1
+    n_recent: int = 1
+    ensemble: int = 0                   # 0 = max, 1 = mean
+    description: str = ""
+
+    @property
+    def B(self) -> int:
+        return self.layers[0].B
+
+    @property
+    def n_cols(self) -> int:
+        return self.layers[0].n_cols
+
+    @property
+    def limits(self) -> np.ndarray:
+        return self.layers[0].limits
+
+
+def memory_indexer(entries=(262144,) * 8, n_layers=3, seed=6, kmax=384, threshold=0.76,
+                   n_sink=1, n_recent=1, ensemble=0, name="memory-indexer") -> ResidentLoad:
+    """Level 1 over each request's whole history: layer l is a paged decode
+    workload of the given per-request entry counts drawn from seed
+    16 * seed + l (its own q, w, keys and block table, the same limits).
+    Defaults: 8 requests at 1M tokens (262,144 entries), 3 layers, KMAX 384
+    pages, one sink page and one recent page, threshold 0.76 (the maximum of
+    three layers' synthetic scores passes it for about 12 % of the entries,
+    inside the 10-15 % resident share the pages report)."""
+    entries = np.asarray(entries, dtype=np.int64)
+    mb = _ceil_div(int(entries.max()), BLOCK)
+    layers = [_paged_decode_from(np.random.default_rng(16 * seed + l), entries, HEADS, HEAD_DIM, TOPK,
+                                 mb, 0.01, f"{name}-layer{l}", f"seed {16 * seed + l}")
+              for l in range(n_layers)]
+    return ResidentLoad(name=name, layers=layers, kmax=kmax, threshold=threshold, n_sink=n_sink,
+                        n_recent=n_recent, ensemble=ensemble,
+                        description=(f"B={len(entries)}, {n_layers} layers, entries {int(entries.min())}.."
+                                     f"{int(entries.max())}, KMAX {kmax}, threshold {threshold}, "
+                                     f"sink {n_sink}, recent {n_recent}, seed {seed}"))
+
+
 # ----------------------------------------------------------------------------
 # the five named workloads at full size, and small variants of each
 

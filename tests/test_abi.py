@@ -167,3 +167,48 @@ def test_write_keys_rejects_bad_arguments(lib, kw, code):
 
 def test_write_keys_with_no_keys_is_a_no_op(lib):
     assert lib.idx_write_keys(None, 0, 128, None, None, 0, None, None) == L.IDX_OK
+
+
+def _resident(lib, n_layers=3, B=2, n_cols=640, cfg=None, out_pages=0x7000, ws=0x10000, ws_bytes=None,
+              keys=None, q=0x1000):
+    cfg = cfg or L.ResidentCfg(L.ENSEMBLE_MAX, 0.7, 1, 1, 8)
+    need = L.resident_workspace_bytes(max(n_layers, 1), max(B, 0), max(n_cols, 1), max(cfg.kmax, 1)) \
+        if 1 <= n_layers <= L.MAX_LAYERS and 1 <= cfg.kmax <= 2048 and n_cols >= 1 else 0
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    n = max(n_layers, 1)
+    qa = (ctypes.c_void_p * n)(*([q] * n))
+    wa = (ctypes.c_void_p * n)(*([0x2000] * n))
+    ka = (L.IdxKeys * n)(*([keys or _keys()] * n))
+    return lib.idx_select_resident(n_layers, qa, wa, B, 64, 128, ka, n_cols, ctypes.byref(cfg), out_pages,
+                                   None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_layers=0), L.IDX_E_SHAPE),
+    (dict(n_layers=9), L.IDX_E_SHAPE),
+    (dict(n_cols=0), L.IDX_E_SHAPE),
+    (dict(cfg=L.ResidentCfg(7, 0.7, 1, 1, 8)), L.IDX_E_ARG),
+    (dict(cfg=L.ResidentCfg(0, float("nan"), 1, 1, 8)), L.IDX_E_ARG),
+    (dict(cfg=L.ResidentCfg(0, 0.7, 1, 1, 0)), L.IDX_E_SHAPE),
+    (dict(cfg=L.ResidentCfg(0, 0.7, 1, 1, 2049)), L.IDX_E_SHAPE),
+    (dict(cfg=L.ResidentCfg(0, 0.7, 5, 4, 8)), L.IDX_E_SHAPE),
+    (dict(cfg=L.ResidentCfg(0, 0.7, -1, 0, 8)), L.IDX_E_SHAPE),
+    (dict(q=0x1008), L.IDX_E_ALIGN),
+    (dict(keys=_keys(chunk_ids=0x5000, n_chunks=0x6000, max_chunks=4)), L.IDX_E_ARG),
+    (dict(out_pages=None), L.IDX_E_ARG),
+    (dict(ws_bytes=256), L.IDX_E_WORKSPACE),
+    (dict(ws=0x10010), L.IDX_E_ALIGN),
+])
+def test_select_resident_rejects_bad_arguments(lib, kw, code):
+    assert _resident(lib, **kw) == code
+    assert lib.idx_last_error() != b""
+
+
+def test_resident_workspace_bytes(lib):
+    # logits [B, ld] + scores [L, B, ld] + page keys [B, ldp] (ld = n_cols rounded to 64,
+    # ldp = pages rounded to 64), each piece 256-byte aligned, no top-k lists for short rows
+    n = L.resident_workspace_bytes(3, 2, 640, 8)
+    assert n == 2 * 640 * 4 + 3 * 2 * 640 * 4 + 2 * 64 * 4 + 256
+    assert lib.idx_resident_workspace_bytes(0, 2, 640, 8) == ctypes.c_size_t(-1).value
+    assert lib.idx_resident_workspace_bytes(3, 2, 640, 0) == ctypes.c_size_t(-1).value
+    assert _resident(lib, B=0, out_pages=None) == L.IDX_OK
