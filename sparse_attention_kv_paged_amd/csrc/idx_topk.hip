@@ -104,6 +104,13 @@ __device__ void find_from_top(const uint32_t *h, int nbins, uint32_t need, int32
     __syncthreads();
 }
 
+// The next binary32 value above a finite x.
+__device__ __forceinline__ float next_up(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) == 0u) return __uint_as_float(1u);          // +-0 -> smallest positive
+    return __uint_as_float(x > 0.f ? u + 1u : u - 1u);
+}
+
 // LDS scratch of one selection by NT threads.  The histogram has 32 extra
 // bins past kBins that absorb non-selectable items, so the histogram's
 // atomics need no branch.
@@ -177,11 +184,18 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     const float range = vmax - vmin;
     if (range > 0.f && range < __builtin_inff()) scale = (float)kBins / range;
     if (!(scale < __builtin_inff())) scale = 0.f;
-    const float off = -vmin * scale;
+    float off = -vmin * scale;
+    // off is -vmin*scale rounded, so fma(vmin, scale, off) is that rounding's
+    // error (exact, at most half an ulp of off); when it is negative, off
+    // moves up one ulp so that no item's bin is negative -- with values far
+    // from 0 in a narrow range the error exceeds 1, and a negative bin would
+    // wrap past the top bin below
+    if (fmaf(vmin, scale, off) < 0.f) off = next_up(off);
     const auto bin_of = [&](int j) {
         const uint32_t kj = key[j];
-        // fma(v, scale, -vmin*scale) is monotone in v like (v - vmin)*scale;
-        // it only has to be the same function in every pass
+        // fma(v, scale, off) is monotone in v like (v - vmin)*scale and at
+        // least fma(vmin, scale, off) >= 0; it only has to be the same
+        // function in every pass
         const float v = HAVE_V ? val[j] : key_value(kj);
         const int x = __float2int_rz(fmaf(v, scale, off));                // >= 0 (NaN -> 0)
         return kj ? min((uint32_t)x, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (lane & 31));

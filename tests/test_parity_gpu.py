@@ -383,3 +383,25 @@ def test_topk_standalone_one_segment_per_row(n, k):
     assert np.array_equal(cols.cpu().numpy(), ref_cols)
     assert np.array_equal(v.cpu().numpy(), ref_v.astype(np.float32))
 
+
+
+@pytest.mark.parametrize("n,k", [(100, 4), (4096, 384), (70000, 512)])
+def test_topk_standalone_values_far_from_zero_in_a_narrow_range(n, k):
+    """Values whose magnitude is large against their spread (|min| / range
+    well past 8192): the histogram's bin offset rounds by more than one bin,
+    and the lowest values must still rank lowest.  Distinct integers near
+    2^23, near -2^23, and fractions just above 1e6, with ties at the cut."""
+    rng = np.random.default_rng(n + k + 5)
+    B = 4
+    base = np.arange(n, dtype=np.float64)
+    vals = np.empty((B, n), np.float32)
+    vals[0] = (2.0 ** 23 + 131071 - base).astype(np.float32)          # decreasing: the first k win
+    vals[1] = (-(2.0 ** 23) + rng.permutation(n)).astype(np.float32)
+    vals[2] = (1.0e6 + np.round(rng.random(n) * 64) / 64).astype(np.float32)
+    vals[3] = (3.0e7 + rng.integers(0, 3, n) * 2.0).astype(np.float32)  # three values, heavy ties
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    assert np.array_equal(cols.cpu().numpy(), ref_cols)
+    assert np.array_equal(v.cpu().numpy(), ref_v.astype(np.float32))
+    assert cols.cpu().numpy()[0].tolist() == list(range(k))
