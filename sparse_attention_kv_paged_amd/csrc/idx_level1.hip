@@ -4,15 +4,19 @@
 // sections "Two-level recall algorithm" and "Joint checkpoint + ensemble";
 // KMAX pages of 64 entries per request, section "Quick start").
 //
-// One wave per 64-entry page: lane e reads entry 64p + e of every layer's
-// score row (one 256-byte coalesced load per layer), ensembles them (max, or
-// the binary32 sum in layer order divided by L), compares with the threshold,
-// and the ballot's popcount is the page's density.  The page's key for the
-// selection is +inf for a sink or recent page (always resident), the density
-// for another page with at least one selected entry, and -inf otherwise (past
-// the row's history too); the top-k over these keys then keeps the forced
-// pages, then the densest, equal densities to the lower page, in ascending
-// page order.
+// A wave takes four consecutive 64-entry pages: lane l reads entries
+// 4l .. 4l + 3 of the 256 (one 16-byte load per layer), ensembles them (max,
+// or the binary32 sum in layer order divided by L) and counts those at or
+// above the threshold; a DPP row (16 lanes) covers one page, so four row
+// rotations sum the page's density.  The page's key for the selection orders
+// pages by (forced, density, lower page first) and is exact in binary32:
+//     forced (sink or recent page)       (kMaxDensity + 1) * 2^17 + (2^17 - 1 - p)
+//     density d > 0                      d * 2^17 + (2^17 - 1 - p)
+//     otherwise (or past the history)    -inf
+// so that every key of a row is distinct and the top-k's value-linear
+// histogram separates them (a +inf or integer-only key would put whole tie
+// groups in one bin).  Rows of more than 2^17 pages use keys d and +inf
+// instead, which select the same pages through the top-k's own tie rule.
 #include <hip/hip_runtime.h>
 
 #include "../../include/idx.h"
@@ -23,37 +27,64 @@ namespace idx {
 namespace {
 
 constexpr int kPageWaves = 4;
+constexpr int kPagesPerWave = 4;
+constexpr int kPageBits = 17;
+
+// The value of the lane N places further along this lane's 16-lane DPP row.
+template <int N>
+__device__ __forceinline__ int row_ror(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, 0x120 + N, 0xF, 0xF, false);
+}
 
 __global__ __launch_bounds__(64 * kPageWaves) void page_kernel(PageArgs a) {
     const int b = blockIdx.y;
-    const int p = blockIdx.x * kPageWaves + threadIdx.x / 64;
     const int lane = threadIdx.x % 64;
-    if (p >= a.n_pages) return;                       // uniform per wave
+    const int p0 = (blockIdx.x * kPageWaves + threadIdx.x / 64) * kPagesPerWave;
+    if (p0 >= a.n_pages) return;                      // uniform per wave
     const int hist = max(0, min(a.limits[b], a.n_cols));
     const int P = (hist + kBlock - 1) / kBlock;
-    const int e = p * kBlock + lane;
-    const bool valid = e < hist;
-    float s = 0.0f;
-    if (valid) {
-        const float *row = a.scores + (int64_t)b * a.ld + e;
-        if (a.ensemble == IDX_ENSEMBLE_MAX) {
-            s = row[0];
-            for (int l = 1; l < a.L; ++l) {
-                const float x = row[(int64_t)l * a.layer_stride];
-                s = x > s ? x : s;
+    const int p = p0 + lane / 16;                      // this lane's page
+    const int e0 = p0 * kBlock + 4 * lane;             // its first entry
+    int count = 0;
+    if (e0 < hist) {
+        const float *row = a.scores + (int64_t)b * a.ld + e0;
+        float s[4];
+        // the four entries are in bounds of the row stride (ld is a multiple
+        // of 64); entries past hist are not counted
+        float4 x = *reinterpret_cast<const float4 *>(row);
+        s[0] = x.x; s[1] = x.y; s[2] = x.z; s[3] = x.w;
+        for (int l = 1; l < a.L; ++l) {
+            x = *reinterpret_cast<const float4 *>(row + (int64_t)l * a.layer_stride);
+            const float y[4] = {x.x, x.y, x.z, x.w};
+            if (a.ensemble == IDX_ENSEMBLE_MAX) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] = y[i] > s[i] ? y[i] : s[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[i] += y[i];
             }
-        } else {
-            float sum = 0.0f;
-            for (int l = 0; l < a.L; ++l) sum += row[(int64_t)l * a.layer_stride];
-            s = sum / (float)a.L;
         }
+        if (a.ensemble == IDX_ENSEMBLE_MEAN) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[i] = s[i] / (float)a.L;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) count += (e0 + i < hist && s[i] >= a.threshold) ? 1 : 0;
     }
-    const int density = __popcll(__ballot(valid && s >= a.threshold));
-    if (lane == 0) {
+    count += row_ror<8>(count);
+    count += row_ror<4>(count);
+    count += row_ror<2>(count);
+    count += row_ror<1>(count);
+    if (lane % 16 == 0 && p < a.n_pages) {
+        const bool forced = p < P && (p < a.n_sink || p >= P - a.n_recent);
         float key = -__builtin_inff();
-        if (p < P) {
-            if (p < a.n_sink || p >= P - a.n_recent) key = __builtin_inff();
-            else if (density > 0) key = (float)density;
+        if (a.n_pages <= (1 << kPageBits)) {
+            const int tie = (1 << kPageBits) - 1 - p;
+            if (forced) key = (float)((kBlock + 1) * (1 << kPageBits) + tie);
+            else if (p < P && count > 0) key = (float)(count * (1 << kPageBits) + tie);
+        } else {
+            if (forced) key = __builtin_inff();
+            else if (p < P && count > 0) key = (float)count;
         }
         a.page_keys[(int64_t)b * a.ldp + p] = key;
     }
@@ -63,7 +94,8 @@ __global__ __launch_bounds__(64 * kPageWaves) void page_kernel(PageArgs a) {
 
 hipError_t launch_pages(const PageArgs &a, hipStream_t s) {
     if (a.B <= 0 || a.n_pages <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((a.n_pages + kPageWaves - 1) / kPageWaves), (unsigned)a.B);
+    const int per_group = kPageWaves * kPagesPerWave;
+    const dim3 grid((unsigned)((a.n_pages + per_group - 1) / per_group), (unsigned)a.B);
     hipLaunchKernelGGL(page_kernel, grid, dim3(64 * kPageWaves), 0, s, a);
     return hipGetLastError();
 }

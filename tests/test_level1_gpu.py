@@ -194,3 +194,28 @@ def test_resident_full_size_sampled_rows():
     amb = (np.abs(e - tau) <= 2 * (ATOL + RTOL * tau)).astype(np.int64)
     near = np.add.reduceat(amb, np.arange(0, e.shape[1], 64), axis=1)
     assert np.all(np.abs(dg - do) <= near)
+
+
+def test_resident_rows_beyond_the_exact_key_range():
+    """A row of more than 2^17 pages (8.4M entries; one layer over a
+    contiguous pool) takes the other page-key form: the pages still equal
+    the oracle's selection on the GPU's scores."""
+    rng = np.random.default_rng(70)
+    n = (1 << 17) * 64 + 640
+    pool = np.empty((n, 132), np.uint8)
+    # any finite e4m3 byte (0x00..0x7E with either sign), fp32 scales as in the other workloads
+    pool[:, :128] = rng.integers(0, 0x7F, size=(n, 128), dtype=np.uint8) | \
+        (rng.integers(0, 2, size=(n, 128), dtype=np.uint8) << 7)
+    pool[:, 128:] = rng.uniform(0.005, 0.05, n).astype("<f4").view(np.uint8).reshape(n, 4)
+    q = W.bf16_bits(rng.standard_normal((1, 64, 128), dtype=np.float32))
+    w = (rng.standard_normal((1, 64), dtype=np.float32) * np.float32(128 ** -0.5 * 64 ** -0.5)).astype(np.float32)
+    wl = W.Workload(name="huge-row", q=q, w=w, pool=pool, limits=np.array([n - 5], np.int32), n_cols=n,
+                    description="one row of 8.4M entries, contiguous pool")
+    rl = W.ResidentLoad(name="huge-row", layers=[wl], kmax=300, threshold=0.6, n_sink=2, n_recent=2)
+    _log(f"[level1] {n} entries in one row ({-(-n // 64)} pages)")
+    dls = _device_layers(rl)
+    g = _gpu_scores(dls, rl.n_cols)
+    pages, count = _check(rl, dls, g, None)
+    assert count.tolist() == [300]
+    del dls
+    torch.cuda.empty_cache()
