@@ -260,6 +260,28 @@ def decode_batch(B=32, min_tokens=32768, max_tokens=131072, seed=1, **kw):
                               f"L~U[{min_tokens},{max_tokens}], seed {seed}")
 
 
+def speculative_decode(n_req=16, draft=4, min_tokens=4096, max_tokens=16384, seed=8, k=TOPK,
+                       name="speculative-decode") -> Workload:
+    """Several query rows per request in one call (the draft tokens of
+    speculative decoding): request r has L_r ~ integers U[min_tokens,
+    max_tokens] tokens; its draft row i (0-based) scores entries
+    < (L_r + i + 1) // 4, and all rows of a request share its shuffled block
+    table through q_req.  Draw order: lengths, then the paged pool as in
+    paged_decode, then the B = n_req * draft query rows."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(min_tokens, max_tokens, size=n_req, endpoint=True)
+    entries = (L + draft) // COMPRESS
+    base = _paged_decode_from(rng, entries, HEADS, HEAD_DIM, k, None, 0.01, name, f"seed {seed}")
+    B = n_req * draft
+    q, w = _draw_queries(rng, B, HEADS, HEAD_DIM)
+    q_req = np.repeat(np.arange(n_req, dtype=np.int32), draft)
+    i = np.tile(np.arange(draft, dtype=np.int64), n_req)
+    limits = ((L[q_req] + i + 1) // COMPRESS).astype(np.int32)
+    return Workload(name=name, q=q, w=w, pool=base.pool, limits=limits, n_cols=base.n_cols, k=k,
+                    block_table=base.block_table, q_req=q_req,
+                    description=f"{n_req} requests x {draft} draft rows, L~U[{min_tokens},{max_tokens}], seed {seed}")
+
+
 def prefill(prefix_tokens=65536, n_queries=4096, seed=3, H=HEADS, D=HEAD_DIM,
             k=TOPK, name="chunked-prefill") -> Workload:
     """One request: query i (0-based) of the new chunk scores entries

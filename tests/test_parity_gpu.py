@@ -164,6 +164,15 @@ def test_many_rows_sharing_a_request():
     _check_workload(wl, tag="shared-rows")
 
 
+@pytest.mark.parametrize("n_req,draft", [(16, 4), (130, 4)])
+def test_speculative_draft_rows(n_req, draft):
+    """Several query rows per request in one call, each with its own bound
+    (draft tokens of speculative decoding): 64 rows take the flattened split,
+    520 rows (130 requests) the per-row path."""
+    wl = W.speculative_decode(n_req=n_req, draft=draft, seed=80 + n_req)
+    _check_workload(wl, tag="speculative")
+
+
 # --------------------------------------------------------------- edge cases
 
 def _small_paged(seed=7, entries=(700, 64, 1, 129, 2048)):
