@@ -200,15 +200,19 @@ double oracle_logit(const uint16_t *q_row, const float *w_row, int32_t H,
 }
 
 /* Logits of every (row, column); unscored columns hold -inf ([FM] "Two-level
- * recall algorithm": masked logits are -inf).  Returns 0, or -1 on bad sizes
- * or allocation failure. */
-int oracle_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
-                 int32_t D, const uint8_t *pool, int64_t n_pool_rows,
-                 int32_t block_size, const int32_t *block_table, int32_t n_req,
-                 int32_t max_blocks, const int32_t *q_req,
-                 const int32_t *chunk_ids, const int32_t *n_chunks,
-                 int32_t max_chunks, const int32_t *limits, int32_t n_cols,
-                 double *logits, int32_t n_threads)
+ * recall algorithm": masked logits are -inf).  The query is q (bf16 bits
+ * [B, H, D], widened exactly) or, when q8 is given instead, quantised rows
+ * [B, H, D + 4] in the index-plane layout (e4m3 bytes, then the head's fp32
+ * scale), dequantised exactly as e4m3(byte) * scale -- the quantised-query
+ * variant.  Returns 0, or -1 on bad sizes or allocation failure. */
+static int score_rows(const uint16_t *q, const uint8_t *q8, const float *w,
+                      int32_t B, int32_t H, int32_t D, const uint8_t *pool,
+                      int64_t n_pool_rows, int32_t block_size,
+                      const int32_t *block_table, int32_t n_req,
+                      int32_t max_blocks, const int32_t *q_req,
+                      const int32_t *chunk_ids, const int32_t *n_chunks,
+                      int32_t max_chunks, const int32_t *limits, int32_t n_cols,
+                      double *logits, int32_t n_threads)
 {
     int64_t row_bytes = (int64_t)D + 4;
     int32_t b;
@@ -234,8 +238,18 @@ int oracle_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
             failed = 1;
             continue;
         }
-        for (i = 0; i < (int64_t)H * D; ++i)
-            qd[i] = bf16_value(q[(int64_t)b * H * D + i]);
+        if (q8) {
+            int32_t h, d;
+            for (h = 0; h < H; ++h) {
+                const uint8_t *qrow = q8 + ((int64_t)b * H + h) * row_bytes;
+                double qs = le_f32_value(qrow + D);
+                for (d = 0; d < D; ++d)
+                    qd[(int64_t)h * D + d] = oracle_e4m3_value(qrow[d]) * qs;
+            }
+        } else {
+            for (i = 0; i < (int64_t)H * D; ++i)
+                qd[i] = bf16_value(q[(int64_t)b * H * D + i]);
+        }
         for (c = 0; c < n_cols; ++c) {
             int64_t entry;
             int64_t prow = oracle_resolve(b, c, n_pool_rows, block_size,
@@ -254,8 +268,34 @@ int oracle_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
     return failed ? -1 : 0;
 }
 
-/* [FM] "Retriever architecture": score = sigmoid(logit), the logistic
- * function; a masked logit (-inf) gives score 0. */
+int oracle_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
+                 int32_t D, const uint8_t *pool, int64_t n_pool_rows,
+                 int32_t block_size, const int32_t *block_table, int32_t n_req,
+                 int32_t max_blocks, const int32_t *q_req,
+                 const int32_t *chunk_ids, const int32_t *n_chunks,
+                 int32_t max_chunks, const int32_t *limits, int32_t n_cols,
+                 double *logits, int32_t n_threads)
+{
+    return score_rows(q, NULL, w, B, H, D, pool, n_pool_rows, block_size,
+                      block_table, n_req, max_blocks, q_req, chunk_ids,
+                      n_chunks, max_chunks, limits, n_cols, logits, n_threads);
+}
+
+int oracle_score_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H,
+                    int32_t D, const uint8_t *pool, int64_t n_pool_rows,
+                    int32_t block_size, const int32_t *block_table,
+                    int32_t n_req, int32_t max_blocks, const int32_t *q_req,
+                    const int32_t *chunk_ids, const int32_t *n_chunks,
+                    int32_t max_chunks, const int32_t *limits, int32_t n_cols,
+                    double *logits, int32_t n_threads)
+{
+    if (!q8)
+        return -1;
+    return score_rows(NULL, q8, w, B, H, D, pool, n_pool_rows, block_size,
+                      block_table, n_req, max_blocks, q_req, chunk_ids,
+                      n_chunks, max_chunks, limits, n_cols, logits, n_threads);
+}
+
 double oracle_sigmoid(double x)
 {
     return 1.0 / (1.0 + exp(-x));

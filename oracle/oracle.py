@@ -60,6 +60,8 @@ def _load():
         _c_i32p, ctypes.c_int32, ctypes.c_int32, _c_i32p,
         _c_i32p, _c_i32p, ctypes.c_int32, _c_i32p, ctypes.c_int32,
         _c_f64p, ctypes.c_int32]
+    lib.oracle_score_q8.restype = ctypes.c_int
+    lib.oracle_score_q8.argtypes = [_c_u8p] + lib.oracle_score.argtypes[1:]
     lib.oracle_topk.restype = ctypes.c_int
     lib.oracle_topk.argtypes = [_c_f64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                 ctypes.c_int32, _c_i32p, _c_f64p, ctypes.c_int32]
@@ -125,10 +127,16 @@ def _i32(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
 
 
-def score(wl, rows=None, n_threads: int = 0) -> np.ndarray:
+def score(wl, rows=None, n_threads: int = 0, q8=None) -> np.ndarray:
     """Double logits [B, n_cols] (or [len(rows), n_cols] for a row subset);
-    unscored columns are -inf."""
+    unscored columns are -inf.  With q8 (uint8 [B, H, D + 4] quantised query
+    rows, see quantize_q) the query is q8's dequantised values instead of
+    wl.q."""
     q = np.ascontiguousarray(wl.q, dtype=np.uint16)
+    if q8 is not None:
+        q8 = np.ascontiguousarray(q8, dtype=np.uint8)
+        if rows is not None:
+            q8 = np.ascontiguousarray(q8[np.asarray(rows, dtype=np.int64)])
     w = np.ascontiguousarray(wl.w, dtype=np.float32)
     limits = _i32(wl.limits)
     q_req = _i32(wl.q_req)
@@ -154,8 +162,10 @@ def score(wl, rows=None, n_threads: int = 0) -> np.ndarray:
     pool = np.ascontiguousarray(wl.pool, dtype=np.uint8)
     assert pool.shape[1] == D + 4
     out = np.empty((B, wl.n_cols), dtype=np.float64)
-    rc = _load().oracle_score(
-        _ptr(q, ctypes.c_uint16), _ptr(w, ctypes.c_float), B, H, D,
+    fn, qp = ((_load().oracle_score, _ptr(q, ctypes.c_uint16)) if q8 is None
+              else (_load().oracle_score_q8, _ptr(q8, ctypes.c_uint8)))
+    rc = fn(
+        qp, _ptr(w, ctypes.c_float), B, H, D,
         _ptr(pool, ctypes.c_uint8), pool.shape[0], wl.block_size,
         _ptr(table, ctypes.c_int32), n_req, max_blocks, _ptr(q_req, ctypes.c_int32),
         _ptr(chunk_ids, ctypes.c_int32), _ptr(n_chunks, ctypes.c_int32), max_chunks,
@@ -268,3 +278,13 @@ def level1_scores(layers, rows=None, n_threads: int = 0) -> np.ndarray:
             s = 1.0 / (1.0 + np.exp(-lg))
         out.append(s.astype(np.float32))
     return np.stack(out)
+
+
+def quantize_q(q: np.ndarray) -> np.ndarray:
+    """Quantised query rows uint8 [B, H, D + 4] from q (bf16 bits [B, H, D]):
+    each head through the index-plane writer's rule (amax / 448 scale)."""
+    q = np.ascontiguousarray(q, dtype=np.uint16)
+    B, H, D = q.shape
+    out = np.zeros((B * H, D + 4), dtype=np.uint8)
+    write_keys(q.reshape(B * H, D), np.arange(B * H, dtype=np.int64), out)
+    return out.reshape(B, H, D + 4)

@@ -52,6 +52,10 @@ MUTANTS = {
     "level1-recent-off-by-one": ("if (p < n_sink || p >= P - n_recent)", "if (p < n_sink || p > P - n_recent)"),
     "level1-entries-past-limit": ("for (e = 0; e < hist; ++e) {", "for (e = 0; e < P * 64 && e < n_cols; ++e) {"),
     "level1-nothing-forced": ("                pr[p].rank = 2;\n", "                pr[p].rank = pr[p].density > 0;\n"),
+    "q8-scale-ignored": ("qd[(int64_t)h * D + d] = oracle_e4m3_value(qrow[d]) * qs;",
+                         "qd[(int64_t)h * D + d] = oracle_e4m3_value(qrow[d]);"),
+    "q8-head-stride-wrong": ("const uint8_t *qrow = q8 + ((int64_t)b * H + h) * row_bytes;",
+                             "const uint8_t *qrow = q8 + ((int64_t)b * H + h) * D;"),
     "level1-empty-pages-eligible": ("pr[p].rank = pr[p].density > 0 ? 1 : 0;", "pr[p].rank = 1;"),
 }
 
@@ -76,6 +80,8 @@ PIN_TESTS = [
     pins.test_level1_history_bounds,
     lambda: pins.test_level1_matches_brute_force(0),
     pins.test_level1_layer_order_and_single_layer,
+    pins.test_quantised_query_equals_plain_query_when_quantisation_is_exact,
+    pins.test_quantised_query_closed_form,
 ]
 
 

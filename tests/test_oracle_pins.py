@@ -627,3 +627,51 @@ def test_level1_layer_order_and_single_layer():
     s2[1] = 1.0
     e, cnt = oracle.level1_select(s2, lim, oracle.ENSEMBLE_MAX, 0.99, 0, 0, 12)
     assert cnt.tolist() == [12, 11, 5, 1]
+
+
+# ------------------------------------------------------ quantised query
+
+def _e4m3_grid_q(rng, B, H, D, js):
+    """bf16 queries whose every head is exactly representable after the
+    writer's quantisation: values on the e4m3 grid times 2^j, with one
+    element at +-448 * 2^j (so the head's scale is exactly 2^j)."""
+    v = torch.arange(0x7F, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    codes = rng.integers(0, 0x7F, size=(B, H, D))
+    x = v[codes] * np.where(rng.random((B, H, D)) < 0.5, -1.0, 1.0)
+    x[:, :, 0] = 448.0 * np.where(rng.random((B, H)) < 0.5, -1.0, 1.0)
+    x *= np.exp2(np.asarray(js, dtype=np.float64))[None, :, None]
+    return _bf16(x.astype(np.float32))
+
+
+def test_quantised_query_equals_plain_query_when_quantisation_is_exact():
+    """Heads on the e4m3 grid times 2^j (j from -20 to 20) quantise without
+    error, so the quantised-query logits equal the plain ones bit for bit."""
+    rng = np.random.default_rng(17)
+    wl = W.small_config(1)
+    js = rng.integers(-20, 21, size=wl.H)
+    wl.q = _e4m3_grid_q(rng, wl.B, wl.H, wl.D, js)
+    q8 = oracle.quantize_q(wl.q)
+    scales = q8[:, :, -4:].copy().view("<f4")[..., 0]
+    assert np.array_equal(scales, np.broadcast_to(np.exp2(js).astype(np.float32), scales.shape))
+    a = oracle.score(wl)
+    b = oracle.score(wl, q8=q8)
+    assert np.array_equal(a, b)
+
+
+def test_quantised_query_closed_form():
+    """One head with one nonzero element: logit = relu(k_d * e4m3(byte) * s_q) * w_h
+    for a key row of all ones at scale 0.5."""
+    H, D = 64, 128
+    q8 = np.zeros((1, H, D + 4), np.uint8)
+    q8[0, 5, 17] = 0x3C                                 # 1.5
+    q8[0, 5, -4:] = np.array([0.25], "<f4").view(np.uint8)
+    q8[0, 9, 3] = 0xB8                                  # -1.0 (relu removes it)
+    q8[0, 9, -4:] = np.array([4.0], "<f4").view(np.uint8)
+    row = np.full(D + 4, 0x38, np.uint8)                # e4m3 1.0
+    row[-4:] = np.array([0.5], "<f4").view(np.uint8)
+    w = np.zeros((1, H), np.float32)
+    w[0, 5], w[0, 9] = 3.0, 7.0
+    wl = W.Workload(name="q8-one-hot", q=np.zeros((1, H, D), np.uint16), w=w, pool=row[None].copy(),
+                    limits=np.array([1], np.int32), n_cols=1)
+    got = oracle.score(wl, q8=q8)[0, 0]
+    assert got == 1.0 * 0.5 * 1.5 * 0.25 * 3.0
