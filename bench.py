@@ -18,6 +18,10 @@ one idx_write_keys call that quantises the 262,144 compressed keys of one
 1M-token request into a shuffled paged pool; `value` is keys written per
 second and `roofline` covers the writer kernel.
 
+`--q8` measures the quantised-query variant on any scoring workload: each
+step quantises q per head (the writer kernel) and runs idx_score_topk_q8; the
+prefill roofline is then priced at the fp8 MFMA peak.
+
 `--workload memory-indexer` measures the Level-1 resident-set selection: one
 step is one idx_select_resident call over 8 requests at 1M tokens (262,144
 entries each) scored at 3 layers, KMAX 384 pages; `value` is scored pairs per
@@ -38,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, TFLOP/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 SCORE_SOURCES = ["sparse_attention_kv_paged_amd/csrc/idx_score.hip",
                  "sparse_attention_kv_paged_amd/csrc/idx_device.h",
@@ -67,16 +72,18 @@ def score_source_hash(sources=SCORE_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(wl, pairs: int) -> int:
+def algorithmic_bytes(wl, pairs: int, q8: bool = False) -> int:
     """Bytes the score kernel must move at minimum: one 132-byte key row per
     scored (query, entry) pair for decode shapes (rows shared by every query
     of a prefill request are counted once), one 4-byte logit written per
-    pair, plus q, w, bounds and tables."""
+    pair, plus q (bf16, or 132-byte quantised rows per head), w, bounds and
+    tables."""
     if wl.q_req is not None and wl.block_table is not None and wl.block_table.shape[0] == 1:
         keys = int((wl.block_table >= 0).sum()) * 64 * 132          # one request
     else:
         keys = pairs * 132
-    extra = pairs * 4 + wl.q.nbytes + wl.w.nbytes + wl.limits.nbytes
+    q_bytes = wl.B * wl.H * (wl.D + 4) if q8 else wl.q.nbytes
+    extra = pairs * 4 + q_bytes + wl.w.nbytes + wl.limits.nbytes
     for a in (wl.block_table, wl.q_req, wl.chunk_ids, wl.n_chunks):
         if a is not None:
             extra += a.nbytes
@@ -448,6 +455,9 @@ def main():
                     choices=sorted(WORKLOADS) + [WRITE_WORKLOAD, RESIDENT_WORKLOAD])
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for >= 1 GB)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--q8", action="store_true",
+                    help="quantised-query variant: each step quantises q per head (writer kernel) and scores "
+                         "with idx_score_topk_q8 on fp8 MFMA")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -460,13 +470,14 @@ def main():
 
     trace_prefix = {WRITE_WORKLOAD: "write_keys", RESIDENT_WORKLOAD: "select_resident"}.get(args.workload,
                                                                                           "score_topk")
+    prof_name = args.workload + ("-q8" if args.q8 else "")
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.workload, args.command,
-                        os.path.join(PROFILE_DIR, f"{trace_prefix}_{args.workload}_trace.txt"))
+        summarize_trace(args.summarize_trace, prof_name, args.command,
+                        os.path.join(PROFILE_DIR, f"{trace_prefix}_{prof_name}_trace.txt"))
         return
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload, args.command,
-                      os.path.join(PROFILE_DIR, f"{kernel_of(args.workload)[2]}_{args.workload}_pmc.txt"))
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], prof_name, args.command,
+                      os.path.join(PROFILE_DIR, f"{kernel_of(args.workload)[2]}_{prof_name}_pmc.txt"))
         return
 
     if args.gpus != 1:
@@ -504,9 +515,18 @@ def main():
     ws = torch.empty(lib.workspace_bytes(lib.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, k),
                      dtype=torch.uint8, device="cuda")
 
-    def step(i):
-        lib.idx_score_topk(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
-                           out_idx=out_idx, out_val=out_val, workspace=ws)
+    if args.q8:
+        q8 = torch.empty((wl.B, wl.H, wl.D + 4), dtype=torch.uint8, device="cuda")
+        q8_slots = torch.arange(wl.B * wl.H, dtype=torch.int64, device="cuda")
+
+        def step(i):
+            lib.quantize_q(qs[i % R], out=q8, slots=q8_slots)
+            lib.idx_score_topk_q8(q8, d.w, keys[i % R], wl.n_cols, k,
+                                  out_idx=out_idx, out_val=out_val, workspace=ws)
+    else:
+        def step(i):
+            lib.idx_score_topk(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
+                               out_idx=out_idx, out_val=out_val, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -581,13 +601,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
 
-    algo = algorithmic_bytes(wl, pairs)
-    traffic = read_traffic(args.workload)
+    algo = algorithmic_bytes(wl, pairs, q8=args.q8)
+    traffic = read_traffic(args.workload + ("-q8" if args.q8 else ""))
     if args.workload == "chunked-prefill":
         # one request's keys are shared by every query: the contraction bounds it
         flop = 2.0 * wl.H * wl.D * pairs
         roofline = {"kernel": "score_kernel", "bound": "mfma",
-                    "achieved": flop / (kern_ms * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "achieved": flop / (kern_ms * 1e-3) / 1e12,
+                    "peak": MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "traffic": traffic, "algorithmic_flop": flop,
                     "algorithmic_bytes": algo, "kernel_ms": kern_ms}
     else:
@@ -606,9 +627,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if args.q8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "queries": wl.B, "heads": wl.H, "head_dim": wl.D,
+                   "query": "e4m3, quantised per head each step" if args.q8 else "bf16",
                    "block": wl.block_size, "k": k, "n_cols": wl.n_cols, "pairs": pairs,
                    "description": wl.description, "replicas": R, "graph": bool(graphs)},
         "queries_per_s": wl.B / (ms_per_step * 1e-3),

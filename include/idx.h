@@ -172,6 +172,31 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H,
                    size_t ws_bytes, void *stream);
 
 /*
+ * idx_score_q8 / idx_score_topk_q8: the same path with the query quantised
+ * to e4m3 as well, so that the contraction runs on fp8 MFMA with both
+ * operands taken as stored (the pages' deployed indexer quantises its query
+ * too: the batchgen pull request's fp8 indexer path).  q8 holds, for each
+ * row b and head h, one 132-byte row in the index-plane layout: 128 e4m3
+ * bytes then the head's fp32 scale s_q[b,h] -- exactly what idx_write_keys
+ * writes from q viewed as B*H keys of D values (slot b*H + h), i.e. the
+ * amax/448 rule per head.  The logit is the definition above with q replaced
+ * by its dequantised values:
+ *
+ *     logit = sum_h relu( sum_d k[d] * e4m3(q8[b,h,d]) * s_q[b,h] ) * w[b,h]
+ *
+ * (s_q >= 0, so relu(s_q x) = s_q relu(x) and the kernel folds s_q into w).
+ * q8 is [B, H, D + 4] bytes, 4-byte aligned; every other argument, output
+ * and rule is as for idx_score / idx_score_topk.
+ */
+int idx_score_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H,
+                 int32_t D, const idx_keys *keys, int32_t n_cols, float *logits,
+                 float *scores, void *stream);
+int idx_score_topk_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H,
+                      int32_t D, const idx_keys *keys, int32_t n_cols,
+                      int32_t k, int32_t *out_idx, float *out_val,
+                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * idx_write_keys: the index-plane writer -- quantise new compressed keys and
  * store them as pool rows in the layout idx_score reads ("FlashMemory-
  * DeepSeek-V4" README, section "compressed_k format": D float8_e4m3 bytes

@@ -244,6 +244,71 @@ int hip_fail(hipError_t e, const char *what) {
     return fail(IDX_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// q (bf16 [B, H, D], 16-byte aligned) or q8 (quantised rows [B, H, D + 4],
+// 4-byte aligned): exactly one is used.
+int check_qw8(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D) {
+    if (!q8) return check_qw(q, w, B, H, D);
+    if (B < 0) return fail(IDX_E_ARG, "B must be >= 0 (got %d)", B);
+    if (H != idx::kHeads || D != idx::kHeadDim)
+        return fail(IDX_E_SHAPE, "only H=64, D=128 are supported (got H=%d, D=%d)", H, D);
+    if (B > 0 && !w) return fail(IDX_E_ARG, "w must be non-null");
+    if (!aligned(q8, 4) || !aligned(w, 16)) return fail(IDX_E_ALIGN, "q8 must be 4-byte and w 16-byte aligned");
+    return IDX_OK;
+}
+
+int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
+               const idx_keys *keys, int32_t n_cols, float *logits, float *scores, void *stream) {
+    g_last_error[0] = 0;
+    int rc = check_qw8(q, q8, w, B, H, D);
+    if (rc) return rc;
+    if ((rc = check_keys(keys, B))) return rc;
+    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if (B == 0) return IDX_OK;
+    if (q8 == nullptr && q == nullptr) return fail(IDX_E_ARG, "q must be non-null");
+    if (!logits) return fail(IDX_E_ARG, "logits must be non-null");
+    if (!aligned(logits, 16) || !aligned(scores, 4)) return fail(IDX_E_ALIGN, "logits must be 16-byte aligned");
+    idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
+    a.q8 = q8;
+    a.ld = n_cols;
+    a.logits = logits;
+    a.scores = scores;
+    hipError_t e = launch_score_timed(a, (hipStream_t)stream);
+    return e == hipSuccess ? IDX_OK : hip_fail(e, "score kernel");
+}
+
+int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
+                    const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
+                    void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    int rc = check_qw8(q, q8, w, B, H, D);
+    if (rc) return rc;
+    if ((rc = check_keys(keys, B))) return rc;
+    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if (k < 1 || k > idx::kMaxK) return fail(IDX_E_SHAPE, "k must be in [1, 2048] (got %d)", k);
+    if (B == 0) return IDX_OK;
+    if (q8 == nullptr && q == nullptr) return fail(IDX_E_ARG, "q must be non-null");
+    if (!out_idx) return fail(IDX_E_ARG, "out_idx must be non-null");
+    if (!aligned(out_idx, 4) || !aligned(out_val, 4)) return fail(IDX_E_ALIGN, "outputs must be 4-byte aligned");
+    const TopkPlan P = topk_plan(true, B, n_cols, k);
+    if (P.total > 0 && (!workspace || ws_bytes < P.total))
+        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
+    if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+    idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
+    a.q8 = q8;
+    a.ld = P.ld;
+    a.logits = reinterpret_cast<float *>(ws + P.logits);
+    a.scores = nullptr;
+    a.row_cols = reinterpret_cast<uint32_t *>(ws + P.row_cols);
+    a.row_done = reinterpret_cast<uint32_t *>(ws + P.row_done);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
+    e = enqueue_topk(P, ws, a.logits, P.ld, a.row_cols, B, n_cols, k, out_idx, out_val,
+                     keys->chunk_ids, keys->max_chunks, s);
+    return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,20 +347,12 @@ size_t idx_workspace_bytes(int32_t op, int32_t B, int32_t n_cols, int32_t k) {
 
 int idx_score(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D,
               const idx_keys *keys, int32_t n_cols, float *logits, float *scores, void *stream) {
-    g_last_error[0] = 0;
-    int rc = check_qw(q, w, B, H, D);
-    if (rc) return rc;
-    if ((rc = check_keys(keys, B))) return rc;
-    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
-    if (B == 0) return IDX_OK;
-    if (!logits) return fail(IDX_E_ARG, "logits must be non-null");
-    if (!aligned(logits, 16) || !aligned(scores, 4)) return fail(IDX_E_ALIGN, "logits must be 16-byte aligned");
-    idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
-    a.ld = n_cols;
-    a.logits = logits;
-    a.scores = scores;
-    hipError_t e = launch_score_timed(a, (hipStream_t)stream);
-    return e == hipSuccess ? IDX_OK : hip_fail(e, "score kernel");
+    return score_impl(q, nullptr, w, B, H, D, keys, n_cols, logits, scores, stream);
+}
+
+int idx_score_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,
+                 int32_t n_cols, float *logits, float *scores, void *stream) {
+    return score_impl(nullptr, q8, w, B, H, D, keys, n_cols, logits, scores, stream);
 }
 
 int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t k, int32_t *out_col,
@@ -408,32 +465,15 @@ int idx_write_keys(const uint16_t *k, int64_t n, int32_t D, const int64_t *slots
 int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D,
                    const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
                    void *workspace, size_t ws_bytes, void *stream) {
-    g_last_error[0] = 0;
-    int rc = check_qw(q, w, B, H, D);
-    if (rc) return rc;
-    if ((rc = check_keys(keys, B))) return rc;
-    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
-    if (k < 1 || k > idx::kMaxK) return fail(IDX_E_SHAPE, "k must be in [1, 2048] (got %d)", k);
-    if (B == 0) return IDX_OK;
-    if (!out_idx) return fail(IDX_E_ARG, "out_idx must be non-null");
-    if (!aligned(out_idx, 4) || !aligned(out_val, 4)) return fail(IDX_E_ALIGN, "outputs must be 4-byte aligned");
-    const TopkPlan P = topk_plan(true, B, n_cols, k);
-    if (P.total > 0 && (!workspace || ws_bytes < P.total))
-        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
-    if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
-    char *ws = static_cast<char *>(workspace);
-    idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
-    a.ld = P.ld;
-    a.logits = reinterpret_cast<float *>(ws + P.logits);
-    a.scores = nullptr;
-    a.row_cols = reinterpret_cast<uint32_t *>(ws + P.row_cols);
-    a.row_done = reinterpret_cast<uint32_t *>(ws + P.row_done);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e;
-    if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
-    e = enqueue_topk(P, ws, a.logits, P.ld, a.row_cols, B, n_cols, k, out_idx, out_val,
-                     keys->chunk_ids, keys->max_chunks, s);
-    return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
+    return score_topk_impl(q, nullptr, w, B, H, D, keys, n_cols, k, out_idx, out_val, workspace, ws_bytes,
+                           stream);
+}
+
+int idx_score_topk_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,
+                      int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val, void *workspace,
+                      size_t ws_bytes, void *stream) {
+    return score_topk_impl(nullptr, q8, w, B, H, D, keys, n_cols, k, out_idx, out_val, workspace, ws_bytes,
+                           stream);
 }
 
 }  // extern "C"

@@ -18,7 +18,8 @@ constexpr int kSegLogitCap = 32768;          // logits per top-k workgroup
 constexpr int kSegListCap = 16384;           // (key, column) items per merge workgroup
 
 struct ScoreArgs {
-    const uint16_t *q;          // [B, 64, 128] bf16
+    const uint16_t *q;          // [B, 64, 128] bf16 (unused when q8 is set)
+    const uint8_t *q8;          // [B, 64, 132] quantised q rows (e4m3 bytes, then the head's scale), or null
     const float *w;             // [B, 64]
     int32_t B;
     const uint8_t *pool;        // [n_pool_rows, 132]

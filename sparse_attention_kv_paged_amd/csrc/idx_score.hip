@@ -44,6 +44,25 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+// 16 bytes at a 4-byte aligned address (q8 rows are 132 bytes apart)
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// q[b] as the MFMA's A operand.  bf16 path: 2 head blocks x 8 k-steps of 8
+// bf16 (v_mfma_f32_32x32x16_bf16).  fp8 path (quantised q): 2 head blocks x
+// 2 k-steps of 32 e4m3 bytes (v_mfma_scale_f32_32x32x64_f8f6f4, scales 1).
+struct QBf16 {
+    bf16x8 v[2][8];
+};
+struct QFp8 {
+    v8i v[2][2];
+};
+template <bool Q8> struct QSel {
+    using Op = QBf16;
+};
+template <> struct QSel<true> {
+    using Op = QFp8;
+};
 
 struct RowCtx {
     int32_t req;      // request row, -1 = padding
@@ -238,7 +257,7 @@ struct TileAcc {
 
 // MFMA half of one 32-entry tile: exact fp8 -> bf16 widening and the
 // contraction over the 128 dims, for both head blocks.
-__device__ __forceinline__ void tile_mma(KeyHalf &k, const bf16x8 (&qa)[2][8], TileAcc &acc) {
+__device__ __forceinline__ void tile_mma(KeyHalf &k, const QBf16 &qa, TileAcc &acc) {
     // relu(s x) = |s| relu(sign(s) x): flip the fp8 signs of rows with s < 0
     if (__any(k.s < 0.f)) {
         const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
@@ -251,9 +270,30 @@ __device__ __forceinline__ void tile_mma(KeyHalf &k, const bf16x8 (&qa)[2][8], T
     for (int kk = 0; kk < 8; ++kk) {
         const u32x4 &v = k.v[kk >> 1];
         const bf16x8 kb = (kk & 1) ? fp8x8_to_bf16x8(v.z, v.w) : fp8x8_to_bf16x8(v.x, v.y);
-        acc.h0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][kk], kb, acc.h0, 0, 0, 0);
-        acc.h1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][kk], kb, acc.h1, 0, 0, 0);
+        acc.h0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.v[0][kk], kb, acc.h0, 0, 0, 0);
+        acc.h1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa.v[1][kk], kb, acc.h1, 0, 0, 0);
     }
+}
+
+// The same with quantised q: both operands e4m3, so the key bytes feed the
+// MFMA as they are (no widening); k-step kk covers d = 64*hf + 32*kk + 0..31
+// in q and keys alike.  Products of two e4m3 values are exact in fp32.
+__device__ __forceinline__ void tile_mma(KeyHalf &k, const QFp8 &qa, TileAcc &acc) {
+    if (__any(k.s < 0.f)) {
+        const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k.v[i] ^= u32x4{m, m, m, m};
+    }
+    const v8i b0 = {(int)k.v[0].x, (int)k.v[0].y, (int)k.v[0].z, (int)k.v[0].w,
+                    (int)k.v[1].x, (int)k.v[1].y, (int)k.v[1].z, (int)k.v[1].w};
+    const v8i b1 = {(int)k.v[2].x, (int)k.v[2].y, (int)k.v[2].z, (int)k.v[2].w,
+                    (int)k.v[3].x, (int)k.v[3].y, (int)k.v[3].z, (int)k.v[3].w};
+    const f32x16 z = {};
+    // format 0 = e4m3 for both operands; E8M0 scales 127 = 1.0
+    acc.h0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa.v[0][0], b0, z, 0, 0, 0, 127, 0, 127);
+    acc.h1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa.v[1][0], b0, z, 0, 0, 0, 127, 0, 127);
+    acc.h0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa.v[0][1], b1, acc.h0, 0, 0, 0, 127, 0, 127);
+    acc.h1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa.v[1][1], b1, acc.h1, 0, 0, 0, 127, 0, 127);
 }
 
 // Epilogue half: relu, head weights and head sum, then the row scale.
@@ -310,23 +350,56 @@ constexpr int kQStage = kHeads * kQPad;                 // elements per staged r
 
 // The lane's MFMA A operands of q[b]: head 32*hb + (lane & 31), dims
 // 64*(lane >> 5) + 8*kk .. +7, from global memory or from a staged row.
-__device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, bf16x8 (&qa)[2][8]) {
+__device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QBf16 &qa) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const u32x4 *qp = reinterpret_cast<const u32x4 *>(
             a.q + ((int64_t)b * kHeads + 32 * hb + (lane & 31)) * kHeadDim + 64 * (lane >> 5));
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+        for (int kk = 0; kk < 8; ++kk) qa.v[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
     }
+}
+
+// Quantised q: rows of 132 bytes (128 e4m3 bytes, then the head's scale).
+constexpr int kQ8Row = kHeadDim + 4;
+
+__device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QFp8 &qa) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const u32x4a4 *qp = reinterpret_cast<const u32x4a4 *>(
+            a.q8 + ((int64_t)b * kHeads + 32 * hb + (lane & 31)) * kQ8Row + 64 * (lane >> 5));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const u32x4a4 x = qp[2 * kk], y = qp[2 * kk + 1];
+            qa.v[hb][kk] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        }
+    }
+}
+
+// The scale of head `lane` of quantised q[b] (0 for the bf16 path).
+__device__ __forceinline__ float q8_scale(const ScoreArgs &a, int b, int lane) {
+    return *reinterpret_cast<const float *>(a.q8 + ((int64_t)b * kHeads + lane) * kQ8Row + kHeadDim);
 }
 
 // q of rows rb .. rb + NR - 1 (those below B) for padded LDS rows, read by
 // all 256 threads of the workgroup: fetch_q_rows issues the reads,
 // put_q_rows (after other loads have been issued) stores them to LDS; the
-// caller synchronises before the rows are read.
+// caller synchronises before the rows are read.  bf16 rows: 64 heads of 128
+// elements padded to 136; quantised rows (132 bytes a head) go to 144-byte
+// LDS rows, so each lane's 64-byte half row starts 16-byte aligned.
+template <bool Q8, int NR> struct QRows {
+    u32x4 v[NR][4];
+};
+template <int NR> struct QRows<true, NR> {
+    uint32_t v[NR][9];                                   // 2112 dwords per row over 256 threads
+};
+constexpr int kQ8Dwords = kHeads * kQ8Row / 4;           // 2112
+constexpr int kQ8Stage = 144;                            // LDS bytes per staged head row
+
 template <int NR>
-__device__ __forceinline__ void fetch_q_rows(const ScoreArgs &a, int rb, u32x4 (&qv)[NR][4]) {
+__device__ __forceinline__ void fetch_q_rows(const ScoreArgs &a, int rb, QRows<false, NR> &qv) {
     // rows past B read row B - 1 instead (not stored): the reads are
     // unconditional so the compiler can count them when waiting for
     // earlier ones
@@ -335,12 +408,26 @@ __device__ __forceinline__ void fetch_q_rows(const ScoreArgs &a, int rb, u32x4 (
         const int row = min(rb + rr, a.B - 1);
         const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + (int64_t)row * kHeads * kHeadDim);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qv[rr][i] = src[threadIdx.x + 256 * i];
+        for (int i = 0; i < 4; ++i) qv.v[rr][i] = src[threadIdx.x + 256 * i];
     }
 }
 
 template <int NR>
-__device__ __forceinline__ void put_q_rows(const ScoreArgs &a, int rb, const u32x4 (&qv)[NR][4],
+__device__ __forceinline__ void fetch_q_rows(const ScoreArgs &a, int rb, QRows<true, NR> &qv) {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+        const int row = min(rb + rr, a.B - 1);
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.q8 + (int64_t)row * kHeads * kQ8Row);
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            const int j = min((int)threadIdx.x + 256 * i, kQ8Dwords - 1);
+            qv.v[rr][i] = src[j];
+        }
+    }
+}
+
+template <int NR>
+__device__ __forceinline__ void put_q_rows(const ScoreArgs &a, int rb, const QRows<false, NR> &qv,
                                            uint16_t (*sq)[kQStage]) {
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
@@ -348,24 +435,56 @@ __device__ __forceinline__ void put_q_rows(const ScoreArgs &a, int rb, const u32
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = threadIdx.x + 256 * i;             // 16-byte chunk: head c / 16, dims 8 (c % 16)
-                *reinterpret_cast<u32x4 *>(&sq[rr][(c >> 4) * kQPad + 8 * (c & 15)]) = qv[rr][i];
+                *reinterpret_cast<u32x4 *>(&sq[rr][(c >> 4) * kQPad + 8 * (c & 15)]) = qv.v[rr][i];
             }
         }
     }
 }
 
-__device__ __forceinline__ void load_q_staged(const uint16_t *row, bf16x8 (&qa)[2][8]) {
+template <int NR>
+__device__ __forceinline__ void put_q_rows(const ScoreArgs &a, int rb, const QRows<true, NR> &qv,
+                                           uint16_t (*sq)[kQStage]) {
+#pragma unroll
+    for (int rr = 0; rr < NR; ++rr) {
+        if (rb + rr < a.B) {
+            uint8_t *dst = reinterpret_cast<uint8_t *>(sq[rr]);
+#pragma unroll
+            for (int i = 0; i < 9; ++i) {
+                const int j = (int)threadIdx.x + 256 * i;        // dword j: head j / 33, dword j % 33
+                if (j < kQ8Dwords)
+                    *reinterpret_cast<uint32_t *>(dst + (j / 33) * kQ8Stage + 4 * (j % 33)) = qv.v[rr][i];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void load_q_staged(const uint16_t *row, QBf16 &qa) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const u32x4 *qp = reinterpret_cast<const u32x4 *>(row + (32 * hb + (lane & 31)) * kQPad + 64 * (lane >> 5));
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) qa[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+        for (int kk = 0; kk < 8; ++kk) qa.v[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
+    }
+}
+
+__device__ __forceinline__ void load_q_staged(const uint16_t *row, QFp8 &qa) {
+    const int lane = threadIdx.x & 63;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(row);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(base + (32 * hb + (lane & 31)) * kQ8Stage + 64 * (lane >> 5));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const u32x4 x = qp[2 * kk], y = qp[2 * kk + 1];
+            qa.v[hb][kk] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+        }
     }
 }
 
 struct NoQ {
-    __device__ void operator()(bf16x8 (&)[2][8]) const {}
+    template <class Op>
+    __device__ void operator()(Op &) const {}
 };
 
 // Score slots [j0, j1) of row b with the calling wave.  sh_w is the wave's
@@ -374,7 +493,7 @@ struct NoQ {
 // caller, and qfin(qa) -- called once, right after the first ring of key
 // loads has been issued, by every wave of the workgroup (it synchronises
 // the workgroup) -- delivers the MFMA operands of q[b].
-template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool USE_PRE = false, class QFin = NoQ>
+template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool USE_PRE = false, class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
                                            const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{}) {
@@ -392,9 +511,12 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     // out before q is waited on.
     float w_lane = 0.f;
     SlotRaw raw0{-1, -1, false};
-    bf16x8 qa[2][8];
+    typename QSel<Q8>::Op qa;
     if (live) {
         w_lane = a.w[(int64_t)b * kHeads + lane];
+        // quantised q: relu(s_q x) = s_q relu(x) for s_q >= 0, so each head's
+        // q scale joins its weight
+        if (Q8) w_lane *= q8_scale(a, b, lane);
         raw0 = USE_PRE ? pre : slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));
         if (!USE_PRE) load_q_global(a, b, qa);
     }
@@ -523,7 +645,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // FLAT: the (row, slot) work of all rows is flattened and split evenly over
 // every wave of the grid (rows of very different lengths); otherwise each
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED>
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
     __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
@@ -554,15 +676,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // the first group's table reads, then q[b] staged in LDS once for
         // the four waves
         const SlotRaw raw0 = slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));
-        u32x4 qv[1][4];
+        QRows<Q8, 1> qv;
         fetch_q_rows<1>(a, b, qv);
-        const auto qfin = [&](bf16x8 (&qa)[2][8]) {
+        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
             put_q_rows<1>(a, b, qv, sh_q);
             __syncthreads();
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put_q_rows<1>(a, b, qv, sh_q);            // the workgroup's one barrier
             __syncthreads();
@@ -630,9 +752,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // four waves (most workgroups lie within one or two rows)
         const int fw = (int)blockIdx.x * kWaves * chunk;
         const int rb = fw < total ? row_of(fw) : a.B;
-        u32x4 qv[2][4];
+        QRows<Q8, 2> qv;
         fetch_q_rows<2>(a, rb, qv);
-        const auto qfin = [&](bf16x8 (&qa)[2][8]) {
+        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
             put_q_rows<2>(a, rb, qv, sh_q);
             __syncthreads();
             if (b == rb || b == rb + 1)
@@ -646,8 +768,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
-                                                qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
+                                                    qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
                 pb = __builtin_amdgcn_readfirstlane(sh_pre[b]);
@@ -658,7 +780,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
                 r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
                 f = min(fend, pe);
             }
         }
@@ -669,13 +791,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-template <bool OWN_COLS, bool SCORES, bool FLAT>
-void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8>
+void launch_score_q(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 g((unsigned)grid), blk(256);
     if (a.chunk_ids)
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true>), g, blk, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8>), g, blk, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false>), g, blk, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8>), g, blk, 0, s, e0, e1, 0, a);
+}
+
+template <bool OWN_COLS, bool SCORES, bool FLAT>
+void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (a.q8)
+        launch_score_q<OWN_COLS, SCORES, FLAT, true>(a, grid, s, e0, e1);
+    else
+        launch_score_q<OWN_COLS, SCORES, FLAT, false>(a, grid, s, e0, e1);
 }
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {

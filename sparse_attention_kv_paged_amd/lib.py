@@ -25,7 +25,8 @@ STATUS_BAD_SLOT = 16
 ENSEMBLE_MAX, ENSEMBLE_MEAN = 0, 1
 MAX_LAYERS = 8
 
-EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_write_keys", "idx_select_resident",
+EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_score_q8", "idx_score_topk_q8",
+           "idx_write_keys", "idx_select_resident",
            "idx_resident_workspace_bytes", "idx_workspace_bytes",
            "idx_error_string", "idx_last_error", "idx_profile_events", "idx_abi_version")
 
@@ -84,6 +85,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.idx_topk.restype = ctypes.c_int
     lib.idx_score_topk.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
     lib.idx_score_topk.restype = ctypes.c_int
+    lib.idx_score_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, vp, vp, vp]
+    lib.idx_score_q8.restype = ctypes.c_int
+    lib.idx_score_topk_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
+    lib.idx_score_topk_q8.restype = ctypes.c_int
     lib.idx_write_keys.argtypes = [vp, i64, i32, vp, vp, i64, vp, vp]
     lib.idx_write_keys.restype = ctypes.c_int
     lib.idx_select_resident.argtypes = [i32, vp, vp, i32, i32, i32, kp, i32, ctypes.POINTER(ResidentCfg),
@@ -249,6 +254,63 @@ def idx_score_topk(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=
     _check(load().idx_score_topk(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
                                  _ptr(out_idx), _ptr(out_val), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
+    return out_idx, out_val
+
+
+def quantize_q(q: torch.Tensor, out: Optional[torch.Tensor] = None, slots: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Quantised query rows [B, H, D + 4] (uint8) from q [B, H, D] (bf16):
+    each head quantised by idx_write_keys (amax / 448 scale).  out and slots
+    (arange(B * H), int64) may be passed in to avoid allocations."""
+    B, H, D = q.shape
+    q8 = torch.empty((B * H, D + 4), dtype=torch.uint8, device=q.device) if out is None else out.view(B * H, D + 4)
+    if slots is None:
+        slots = torch.arange(B * H, dtype=torch.int64, device=q.device)
+    idx_write_keys(q.reshape(B * H, D), slots, q8, stream=stream)
+    return q8.view(B, H, D + 4)
+
+
+def _q8w(q8, w):
+    q8 = _dev(q8, torch.uint8, "q8")
+    w = _dev(w, torch.float32, "w")
+    if q8.dim() != 3 or w.dim() != 2 or w.shape != q8.shape[:2]:
+        raise ValueError("q8 must be [B, H, D + 4] and w [B, H]")
+    return q8, w
+
+
+def idx_score_q8(q8, w, keys: Keys, n_cols: int, with_scores: bool = False,
+                 logits: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None, stream=None):
+    """idx_score with quantised query rows (see quantize_q)."""
+    q8, w = _q8w(q8, w)
+    B, H, D4 = q8.shape
+    if logits is None:
+        logits = torch.empty((B, n_cols), dtype=torch.float32, device=q8.device)
+    if with_scores and scores is None:
+        scores = torch.empty((B, n_cols), dtype=torch.float32, device=q8.device)
+    _dev(logits, torch.float32, "logits")
+    _dev(scores, torch.float32, "scores")
+    ks = keys.struct()
+    _check(load().idx_score_q8(_ptr(q8), _ptr(w), B, H, D4 - 4, ctypes.byref(ks), n_cols,
+                               _ptr(logits), _ptr(scores), _stream(stream)))
+    return (logits, scores) if with_scores else logits
+
+
+def idx_score_topk_q8(q8, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=None,
+                      workspace=None, stream=None):
+    """idx_score_topk with quantised query rows (see quantize_q)."""
+    q8, w = _q8w(q8, w)
+    B, H, D4 = q8.shape
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=q8.device)
+    if out_val is None:
+        out_val = torch.empty((B, k), dtype=torch.float32, device=q8.device)
+    need = workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k)
+    if workspace is None:
+        workspace = _workspace(need, q8.device)
+    ks = keys.struct()
+    _check(load().idx_score_topk_q8(_ptr(q8), _ptr(w), B, H, D4 - 4, ctypes.byref(ks), n_cols, k,
+                                    _ptr(out_idx), _ptr(out_val), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
     return out_idx, out_val
 
 

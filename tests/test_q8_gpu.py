@@ -1,0 +1,119 @@
+"""GPU parity of the quantised-query path (idx_score_q8, idx_score_topk_q8,
+through the C ABI) against the CPU oracle's quantised-query scoring.
+
+The query heads are quantised on the GPU by the index-plane writer
+(idx_write_keys) and must equal the oracle writer's bytes exactly; the
+logits then follow the same tolerance as the plain path (products of two
+e4m3 values are exact, accumulation is fp32); top-k as for the plain path.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle
+from sparse_attention_kv_paged_amd import lib as L
+from sparse_attention_kv_paged_amd import workloads as W
+from tests.parity import assert_logits_close, assert_topk_near_tie, column_order
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _check_q8(wl, rows=None, tag=""):
+    _log(f"[q8] {tag} {wl.name}: {wl.description} rows={'all' if rows is None else len(rows)}")
+    d = L.to_device(wl)
+    q8 = L.quantize_q(d.q)
+    torch.cuda.synchronize()
+    q8_host = q8.cpu().numpy()
+    want_q8 = oracle.quantize_q(wl.q if rows is None else wl.q[np.asarray(rows)])
+    sel = slice(None) if rows is None else np.asarray(rows)
+    assert np.array_equal(q8_host[sel], want_q8), f"{tag}: quantised query differs from the oracle writer's"
+    lg, sc = L.idx_score_q8(q8, d.w, d.keys, d.n_cols, with_scores=True)
+    torch.cuda.synchronize()
+    g_logits, g_scores = lg.cpu().numpy(), sc.cpu().numpy()
+    ref = oracle.score(wl, rows=rows, q8=q8_host)
+    assert_logits_close(g_logits[sel], ref, f"{tag} q8 logits")
+    ref_sc = np.where(ref == -np.inf, 0.0, 1.0 / (1.0 + np.exp(-np.where(ref == -np.inf, 0, ref))))
+    err = np.abs(g_scores[sel] - ref_sc)
+    assert np.all(err <= 1e-4 + 2e-3 * ref_sc), f"{tag} q8 scores: worst {err.max():.3e}"
+    g_idx, g_val = L.idx_score_topk_q8(q8, d.w, d.keys, d.n_cols, wl.k)
+    torch.cuda.synchronize()
+    g_idx, g_val = g_idx.cpu().numpy(), g_val.cpu().numpy()
+    own_cols, own_vals = column_order(*oracle.topk(g_logits.astype(np.float64), wl.k))
+    own_ids = oracle.cols_to_entries(wl, own_cols)
+    assert np.array_equal(g_idx, own_ids), f"{tag}: q8 score_topk != top-k of its own logits"
+    ok = own_cols >= 0
+    assert np.array_equal(g_val[ok], own_vals[ok].astype(np.float32))
+    ref_cols, _ = oracle.topk(ref, wl.k)
+    ref_ids = oracle.cols_to_entries(wl, ref_cols, rows=rows)
+
+    def logit_of(b, ids):
+        ids = np.asarray(ids, dtype=np.int64)
+        if wl.chunk_ids is None:
+            return ref[b, ids]
+        row = b if rows is None else rows[b]
+        pos = {int(c): j for j, c in enumerate(wl.chunk_ids[row])}
+        return ref[b, np.array([pos[int(e) // 64] * 64 + int(e) % 64 for e in ids])]
+    assert_topk_near_tie(g_idx[sel], ref_ids, logit_of, wl.k, f"{tag} q8")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_q8_integer_case_is_bit_exact(seed):
+    """Query heads of small integers with one element at 448 (scale exactly
+    1), integer keys, power-of-two scales and weights: every product and
+    partial sum is exact, so the GPU equals the oracle bit for bit."""
+    rng = np.random.default_rng(50 + seed)
+    n, B = 64 * 5 + 17, 3
+    kv = rng.integers(-4, 5, size=(n, 128)).astype(np.float32)
+    scales = np.ldexp(1.0, rng.integers(-2, 3, size=n)).astype(np.float32)
+    scales[rng.random(n) < 0.2] *= -1
+    pool = np.zeros((n, 132), dtype=np.uint8)
+    pool[:, :128] = W.e4m3_bytes(kv)
+    pool[:, 128:] = scales.astype("<f4").view(np.uint8).reshape(n, 4)
+    q = rng.integers(-3, 4, size=(B, 64, 128)).astype(np.float32)
+    q[:, :, 7] = 448.0
+    # 8 weighted heads: every dot product is a multiple of 2^-2 below 2^14
+    # and every weighted partial sum a multiple of 2^-5 below 2^17
+    w = (rng.choice([-1.0, 1.0], size=(B, 64)) * np.ldexp(1.0, rng.integers(-3, 1, size=(B, 64)))).astype(np.float32)
+    w[:, 8:] = 0.0
+    wl = W.Workload(name="q8-int", q=W.bf16_bits(q), w=w, pool=pool,
+                    limits=np.array([n, n - 40, 70], np.int32), n_cols=n + 30)
+    d = L.to_device(wl)
+    q8 = L.quantize_q(d.q)
+    g = L.idx_score_q8(q8, d.w, d.keys, d.n_cols).cpu().numpy()
+    ref = oracle.score(wl, q8=q8.cpu().numpy())
+    assert np.array_equal(g.astype(np.float64), ref)
+    # here the quantisation is exact, so the plain path gives the same logits
+    assert np.array_equal(ref, oracle.score(wl))
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_q8_small_workloads(cfg):
+    _check_q8(W.small_config(cfg), tag=f"small{cfg}")
+
+
+def test_q8_rows_sharing_a_request_per_row_path():
+    wl = W.prefill(8192, 603, seed=14, name="q8-shared-rows")
+    _check_q8(wl, tag="shared-rows")
+
+
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_q8_full_size_workloads(cfg):
+    _check_q8(W.config(cfg), tag=f"full{cfg}")
+
+
+def test_q8_full_size_prefill_sampled_rows():
+    wl = W.config(3)
+    rows = sorted({0, 1, 63, 64, 255, 256, 2047, 2048, 4094, 4095}
+                  | set(np.random.default_rng(33).integers(0, 4096, 10).tolist()))
+    _check_q8(wl, rows=rows, tag="full3")
