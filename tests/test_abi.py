@@ -212,3 +212,35 @@ def test_resident_workspace_bytes(lib):
     assert lib.idx_resident_workspace_bytes(0, 2, 640, 8) == ctypes.c_size_t(-1).value
     assert lib.idx_resident_workspace_bytes(3, 2, 640, 0) == ctypes.c_size_t(-1).value
     assert _resident(lib, B=0, out_pages=None) == L.IDX_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=32), L.IDX_E_SHAPE),
+    (dict(D=64), L.IDX_E_SHAPE),
+    (dict(B=-1), L.IDX_E_ARG),
+    (dict(q8=None), L.IDX_E_ARG),
+    (dict(w=None), L.IDX_E_ARG),
+    (dict(q8=0x1002), L.IDX_E_ALIGN),
+    (dict(w=0x2004), L.IDX_E_ALIGN),
+    (dict(n_cols=0), L.IDX_E_SHAPE),
+    (dict(logits=None), L.IDX_E_ARG),
+])
+def test_score_q8_rejects_bad_arguments(lib, kw, code):
+    a = dict(q8=0x1004, w=0x2000, B=1, H=64, D=128, n_cols=64, logits=0x3000)   # q8 needs only 4-byte alignment
+    a.update(kw)
+    keys = _keys()
+    rc = lib.idx_score_q8(a["q8"], a["w"], a["B"], a["H"], a["D"], ctypes.byref(keys), a["n_cols"], a["logits"],
+                          None, None)
+    assert rc == code
+    assert lib.idx_last_error() != b""
+
+
+def test_score_topk_q8_rejects_bad_arguments_and_accepts_empty(lib):
+    keys = _keys()
+    need = L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 1, 64, 16)
+    assert lib.idx_score_topk_q8(0x1004, 0x2000, 1, 64, 128, ctypes.byref(keys), 64, 4096, 0x3000, None,
+                                 0x10000, need, None) == L.IDX_E_SHAPE
+    assert lib.idx_score_topk_q8(0x1004, 0x2000, 1, 64, 128, ctypes.byref(keys), 64, 16, 0x3000, None,
+                                 0x10000, need - 256, None) == L.IDX_E_WORKSPACE
+    assert lib.idx_score_topk_q8(None, None, 0, 64, 128, ctypes.byref(keys), 64, 16, None, None,
+                                 None, 0, None) == L.IDX_OK

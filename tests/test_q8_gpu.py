@@ -117,3 +117,23 @@ def test_q8_full_size_prefill_sampled_rows():
     rows = sorted({0, 1, 63, 64, 255, 256, 2047, 2048, 4094, 4095}
                   | set(np.random.default_rng(33).integers(0, 4096, 10).tolist()))
     _check_q8(wl, rows=rows, tag="full3")
+
+
+def test_q8_zero_heads_negative_scales_and_padding_rows():
+    """All-zero query heads (scale 0: they add nothing), keys with negative
+    and zero scales, a padding row (q_req = -1) and an absent block."""
+    wl = W.paged_decode([700, 64, 1, 129, 2048], seed=91, max_blocks=40, k=64, name="q8-edge")
+    wl.q = wl.q.copy()
+    wl.q[0, 3:9] = 0                                   # six zero heads in row 0
+    wl.q[2] = 0                                        # a row whose every head is zero
+    pool = wl.pool.copy()
+    s = pool[:, 128:].copy().view("<f4")[:, 0]
+    s[::5] *= -1.0                                     # negative scales
+    s[1::7] = 0.0                                      # zero scales
+    pool[:, 128:] = s.astype("<f4").view(np.uint8).reshape(-1, 4)
+    wl.pool = pool
+    wl.q_req = np.arange(wl.B, dtype=np.int32)
+    wl.q_req[1] = -1                                   # padding row
+    wl.block_table = wl.block_table.copy()
+    wl.block_table[3, 1] = -1                          # absent block
+    _check_q8(wl, tag="edge")
