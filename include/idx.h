@@ -174,8 +174,13 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H,
 /*
  * idx_score_q8 / idx_score_topk_q8: the same path with the query quantised
  * to e4m3 as well, so that the contraction runs on fp8 MFMA with both
- * operands taken as stored (the pages' deployed indexer quantises its query
- * too: the batchgen pull request's fp8 indexer path).  q8 holds, for each
+ * operands taken as stored.  The pages' deployed indexers quantise the
+ * query too (the batchgen pull request: fp4 where the hardware has it, an
+ * e4m3 fallback with one scale per 32 values elsewhere; the ATOM runtime
+ * page: the published model rounds query and key to fp4); this variant
+ * gives the query the index plane's own row format instead, one e4m3 scale
+ * per head, which is what lets the scale fold exactly into the head weight
+ * below.  q8 holds, for each
  * row b and head h, one 132-byte row in the index-plane layout: 128 e4m3
  * bytes then the head's fp32 scale s_q[b,h] -- exactly what idx_write_keys
  * writes from q viewed as B*H keys of D values (slot b*H + h), i.e. the
