@@ -485,6 +485,9 @@ def main():
               f"the library runs on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
+    if args.q8 and args.workload in (WRITE_WORKLOAD, RESIDENT_WORKLOAD):
+        print(f"--q8 applies to the scoring workloads, not {args.workload}", file=sys.stderr)
+        sys.exit(2)
     if args.workload == WRITE_WORKLOAD:
         bench_writer(args)
         return
