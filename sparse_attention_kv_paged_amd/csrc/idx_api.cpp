@@ -176,8 +176,8 @@ ResidentPlan resident_plan(int32_t L, int32_t B, int32_t n_cols, int32_t kmax) {
 
 int check_qw(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D) {
     if (B < 0) return fail(IDX_E_ARG, "B must be >= 0 (got %d)", B);
-    if (H != idx::kHeads || D != idx::kHeadDim)
-        return fail(IDX_E_SHAPE, "only H=64, D=128 are supported (got H=%d, D=%d)", H, D);
+    if ((H != idx::kHeads && H != 2 * idx::kHeads) || D != idx::kHeadDim)
+        return fail(IDX_E_SHAPE, "only H=64 or 128 and D=128 are supported (got H=%d, D=%d)", H, D);
     if (B > 0 && (!q || !w)) return fail(IDX_E_ARG, "q and w must be non-null");
     if (!aligned(q, 16) || !aligned(w, 16)) return fail(IDX_E_ALIGN, "q and w must be 16-byte aligned");
     return IDX_OK;
@@ -227,6 +227,9 @@ idx::ScoreArgs score_args(const uint16_t *q, const float *w, int32_t B, const id
     a.limits = keys->limits;
     a.status = keys->status;
     a.n_cols = n_cols;
+    a.q_row = (int64_t)idx::kHeads * idx::kHeadDim;
+    a.w_row = idx::kHeads;
+    a.accum = false;
     // Launch shape: about one resident round of waves (256 CUs x 8 waves)
     // over the whole problem, at most one workgroup per row, so each wave
     // pays its start-up latency (bound, table, q) once and then streams
@@ -242,6 +245,25 @@ idx::ScoreArgs score_args(const uint16_t *q, const float *w, int32_t B, const id
 
 int hip_fail(hipError_t e, const char *what) {
     return fail(IDX_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// The score kernel for H = 64 heads, or for H = 128 as two launches over the
+// two halves of the heads: relu is per head, so the logit is the sum of the
+// halves' weighted sums -- the first launch writes its logits (no scores),
+// the second adds its own to them and writes the scores when asked.
+hipError_t launch_heads(idx::ScoreArgs a, int32_t H, hipStream_t s) {
+    if (H == idx::kHeads) return launch_score_timed(a, s);
+    float *scores = a.scores;
+    a.q_row = (int64_t)H * idx::kHeadDim;
+    a.w_row = H;
+    a.scores = nullptr;
+    hipError_t e = launch_score_timed(a, s);
+    if (e != hipSuccess) return e;
+    a.q += (int64_t)idx::kHeads * idx::kHeadDim;
+    a.w += idx::kHeads;
+    a.accum = true;
+    a.scores = scores;
+    return launch_score_timed(a, s);
 }
 
 // q (bf16 [B, H, D], 16-byte aligned) or q8 (quantised rows [B, H, D + 4],
@@ -272,7 +294,7 @@ int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, 
     a.ld = n_cols;
     a.logits = logits;
     a.scores = scores;
-    hipError_t e = launch_score_timed(a, (hipStream_t)stream);
+    hipError_t e = launch_heads(a, H, (hipStream_t)stream);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "score kernel");
 }
 
@@ -303,7 +325,7 @@ int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_
     a.row_done = reinterpret_cast<uint32_t *>(ws + P.row_done);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
+    if ((e = launch_heads(a, H, s)) != hipSuccess) return hip_fail(e, "score kernel");
     e = enqueue_topk(P, ws, a.logits, P.ld, a.row_cols, B, n_cols, k, out_idx, out_val,
                      keys->chunk_ids, keys->max_chunks, s);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
@@ -415,7 +437,7 @@ int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float 
         a.ld = R.ld;
         a.logits = reinterpret_cast<float *>(ws + R.logits);
         a.scores = scores + (int64_t)l * B * R.ld;
-        if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
+        if ((e = launch_heads(a, H, s)) != hipSuccess) return hip_fail(e, "score kernel");
     }
     idx::PageArgs pa{};
     pa.scores = scores;

@@ -20,6 +20,9 @@ constexpr int kSegListCap = 16384;           // (key, column) items per merge wo
 struct ScoreArgs {
     const uint16_t *q;          // [B, 64, 128] bf16 (unused when q8 is set)
     const uint8_t *q8;          // [B, 64, 132] quantised q rows (e4m3 bytes, then the head's scale), or null
+    int64_t q_row;              // elements from one q row to the next (64 * 128, or 128 * 128 for a head half)
+    int32_t w_row;              // floats from one w row to the next (64, or 128)
+    bool accum;                 // add to the logits already in the output (the second head half)
     const float *w;             // [B, 64]
     int32_t B;
     const uint8_t *pool;        // [n_pool_rows, 132]

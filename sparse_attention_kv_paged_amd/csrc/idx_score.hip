@@ -355,7 +355,7 @@ __device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QBf16 &
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const u32x4 *qp = reinterpret_cast<const u32x4 *>(
-            a.q + ((int64_t)b * kHeads + 32 * hb + (lane & 31)) * kHeadDim + 64 * (lane >> 5));
+            a.q + (int64_t)b * a.q_row + (int64_t)(32 * hb + (lane & 31)) * kHeadDim + 64 * (lane >> 5));
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) qa.v[hb][kk] = __builtin_bit_cast(bf16x8, qp[kk]);
     }
@@ -406,7 +406,7 @@ __device__ __forceinline__ void fetch_q_rows(const ScoreArgs &a, int rb, QRows<f
 #pragma unroll
     for (int rr = 0; rr < NR; ++rr) {
         const int row = min(rb + rr, a.B - 1);
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + (int64_t)row * kHeads * kHeadDim);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q + (int64_t)row * a.q_row);
 #pragma unroll
         for (int i = 0; i < 4; ++i) qv.v[rr][i] = src[threadIdx.x + 256 * i];
     }
@@ -493,7 +493,8 @@ struct NoQ {
 // caller, and qfin(qa) -- called once, right after the first ring of key
 // loads has been issued, by every wave of the workgroup (it synchronises
 // the workgroup) -- delivers the MFMA operands of q[b].
-template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool USE_PRE = false, class QFin = NoQ>
+template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, bool USE_PRE = false,
+          class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
                                            const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{}) {
@@ -513,7 +514,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     SlotRaw raw0{-1, -1, false};
     typename QSel<Q8>::Op qa;
     if (live) {
-        w_lane = a.w[(int64_t)b * kHeads + lane];
+        w_lane = a.w[(int64_t)b * a.w_row + lane];
         // quantised q: relu(s_q x) = s_q relu(x) for s_q >= 0, so each head's
         // q scale joins its weight
         if (Q8) w_lane *= q8_scale(a, b, lane);
@@ -575,6 +576,12 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
             TileAcc acc;
             float s;
             bool keep;
+            float prev;     // ACCUM: the logit already in the output
+        };
+        // the lane's logit offset of tile tau (kDrop for lanes that store nothing)
+        const auto out_off = [&](int tau) {
+            const uint32_t col0 = (uint32_t)((g0 + (tau >> 1)) * kBlock + 32 * (tau & 1));
+            return LEAN ? lane_off + col0 * 4u : (hf == 0 ? (col0 + (uint32_t)n32) * 4u : kDrop);
         };
         // tile tau's contraction.  Its ring slot is free for tile tau + 2 as
         // soon as the lane has read it, and that reload goes out before the
@@ -590,14 +597,17 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
             read_tile(ring + k * kTileBytes, kh);
             wait_lds();
             st_.keep = n32 < lim_t[k];
+            // ACCUM: the earlier logit is read before the next tile's loads
+            // go out, so the ring's in-order wait still counts only those
+            if (ACCUM) st_.prev = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(out_r, out_off(tau), 0, 0));
             issue(tau + 2);
             tile_mma(kh, qa, st_.acc);
             st_.s = kh.s;
         };
         auto finish = [&](int tau, const Stage &st_) {
-            const float logit = tile_logit(st_.acc, wr, st_.s, st_.keep);
-            const uint32_t col0 = (uint32_t)((g0 + (tau >> 1)) * kBlock + 32 * (tau & 1));
-            const uint32_t off = LEAN ? lane_off + col0 * 4u : (hf == 0 ? (col0 + (uint32_t)n32) * 4u : kDrop);
+            float logit = tile_logit(st_.acc, wr, st_.s, st_.keep);
+            if (ACCUM) logit += st_.prev;             // -inf stays -inf: both halves mask alike
+            const uint32_t off = out_off(tau);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, 0);
             if (SCORES) {
                 const float score = 1.0f / (1.0f + expf(-logit));
@@ -645,7 +655,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // FLAT: the (row, slot) work of all rows is flattened and split evenly over
 // every wave of the grid (rows of very different lengths); otherwise each
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8>
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
     __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
@@ -684,7 +694,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put_q_rows<1>(a, b, qv, sh_q);            // the workgroup's one barrier
             __syncthreads();
@@ -768,7 +778,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
                                                     qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
@@ -780,7 +790,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
                 r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
                 f = min(fend, pe);
             }
         }
@@ -791,13 +801,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8>
-void launch_score_q(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8, bool ACCUM>
+void launch_score_qa(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 g((unsigned)grid), blk(256);
     if (a.chunk_ids)
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8>), g, blk, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM>), g, blk, 0, s, e0, e1, 0, a);
     else
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8>), g, blk, 0, s, e0, e1, 0, a);
+        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM>), g, blk, 0, s, e0, e1, 0, a);
+}
+
+// The accumulating second head half exists for bf16 queries only.
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8>
+void launch_score_q(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if constexpr (!Q8) {
+        if (a.accum) return launch_score_qa<OWN_COLS, SCORES, FLAT, false, true>(a, grid, s, e0, e1);
+    }
+    launch_score_qa<OWN_COLS, SCORES, FLAT, Q8, false>(a, grid, s, e0, e1);
 }
 
 template <bool OWN_COLS, bool SCORES, bool FLAT>
@@ -810,6 +829,7 @@ void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.B <= 0) return hipSuccess;
+    if (a.accum && a.q8) return hipErrorInvalidValue;
     // the top-k feed (row_cols) never asks for scores
     const bool own = a.row_cols != nullptr;
     const bool scores = !own && a.scores != nullptr;

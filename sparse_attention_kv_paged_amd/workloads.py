@@ -411,17 +411,18 @@ class ResidentLoad:
 
 
 def memory_indexer(entries=(262144,) * 8, n_layers=3, seed=6, kmax=384, threshold=0.76,
-                   n_sink=1, n_recent=1, ensemble=0, name="memory-indexer") -> ResidentLoad:
+                   n_sink=1, n_recent=1, ensemble=0, H=HEADS, name="memory-indexer") -> ResidentLoad:
     """Level 1 over each request's whole history: layer l is a paged decode
     workload of the given per-request entry counts drawn from seed
     16 * seed + l (its own q, w, keys and block table, the same limits).
     Defaults: 8 requests at 1M tokens (262,144 entries), 3 layers, KMAX 384
     pages, one sink page and one recent page, threshold 0.76 (the maximum of
     three layers' synthetic scores passes it for about 12 % of the entries,
-    inside the 10-15 % resident share the pages report)."""
+    inside the 10-15 % resident share the pages report).  H = 128 gives the
+    trained retriever's head count."""
     entries = np.asarray(entries, dtype=np.int64)
     mb = _ceil_div(int(entries.max()), BLOCK)
-    layers = [_paged_decode_from(np.random.default_rng(16 * seed + l), entries, HEADS, HEAD_DIM, TOPK,
+    layers = [_paged_decode_from(np.random.default_rng(16 * seed + l), entries, H, HEAD_DIM, TOPK,
                                  mb, 0.01, f"{name}-layer{l}", f"seed {16 * seed + l}")
               for l in range(n_layers)]
     return ResidentLoad(name=name, layers=layers, kmax=kmax, threshold=threshold, n_sink=n_sink,

@@ -244,3 +244,12 @@ def test_score_topk_q8_rejects_bad_arguments_and_accepts_empty(lib):
                                  0x10000, need - 256, None) == L.IDX_E_WORKSPACE
     assert lib.idx_score_topk_q8(None, None, 0, 64, 128, ctypes.byref(keys), 64, 16, None, None,
                                  None, 0, None) == L.IDX_OK
+
+
+def test_h128_accepted_for_bf16_rejected_for_q8(lib):
+    keys = _keys()
+    # 96 heads: rejected on every path; 128: rejected for the quantised query only
+    assert _score(lib, H=96) == L.IDX_E_SHAPE
+    assert lib.idx_score_q8(0x1004, 0x2000, 1, 128, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_SHAPE
+    # 128 heads pass every host check (B = 0 returns before any launch)
+    assert _score(lib, H=128, B=0, q=None, w=None, logits=None) == L.IDX_OK

@@ -219,3 +219,19 @@ def test_resident_rows_beyond_the_exact_key_range():
     assert count.tolist() == [300]
     del dls
     torch.cuda.empty_cache()
+
+
+def test_resident_selection_with_128_head_layers():
+    """The trained retriever's 128 heads: every layer scored as two head
+    halves; pages exact given the GPU's scores and densities consistent with
+    the oracle's."""
+    rl = W.memory_indexer(entries=[12000, 5000, 300], n_layers=3, seed=75, kmax=24, threshold=0.76, H=128,
+                          name="memory-indexer-h128")
+    _log(f"[level1] {rl.description} H=128")
+    dls = _device_layers(rl)
+    g = _gpu_scores(dls, rl.n_cols)
+    ref = oracle.level1_scores(rl.layers)
+    for l in range(3):
+        assert_logits_close(g[l], ref[l], f"h128 layer {l} scores")
+    for over in [dict(), dict(ensemble=L.ENSEMBLE_MEAN, threshold=0.6), dict(kmax=4, n_sink=1, n_recent=2)]:
+        _check(rl, dls, g, ref, **over)

@@ -173,6 +173,47 @@ def test_speculative_draft_rows(n_req, draft):
     _check_workload(wl, tag="speculative")
 
 
+# ------------------------------------------------------------ 128 heads
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_h128_integer_case_is_bit_exact(seed):
+    """128 heads (two launches over the head halves, the second adding to the
+    first's logits): integer data keeps every partial sum exact, so the GPU
+    equals the oracle bit for bit."""
+    rng = np.random.default_rng(60 + seed)
+    n, B = 64 * 5 + 17, 3
+    kv = rng.integers(-4, 5, size=(n, 128)).astype(np.float32)
+    scales = np.ldexp(1.0, rng.integers(-2, 3, size=n)).astype(np.float32)
+    scales[rng.random(n) < 0.2] *= -1
+    pool = np.zeros((n, 132), dtype=np.uint8)
+    pool[:, :128] = W.e4m3_bytes(kv)
+    pool[:, 128:] = scales.astype("<f4").view(np.uint8).reshape(n, 4)
+    q = rng.integers(-2, 3, size=(B, 128, 128)).astype(np.float32)
+    w = (rng.choice([-1.0, 1.0], size=(B, 128)) * np.ldexp(1.0, rng.integers(-3, 4, size=(B, 128)))).astype(np.float32)
+    wl = W.Workload(name="int-h128", q=W.bf16_bits(q), w=w, pool=pool,
+                    limits=np.array([n, n - 40, 70], np.int32), n_cols=n + 30)
+    g = _gpu_logits(L.to_device(wl))
+    ref = oracle.score(wl)
+    assert np.array_equal(g.astype(np.float64), ref)
+
+
+def test_h128_paged_rows():
+    """128 heads on the flattened split: ragged paged rows, scores, top-k."""
+    wl = W.paged_decode([9000, 64, 1, 4097, 16384], seed=61, max_blocks=256, H=128, k=512, name="h128-paged")
+    _check_workload(wl, tag="h128")
+
+
+def test_h128_chunk_lists():
+    wl = W.resident(5, 256, 24, seed=62, H=128, name="h128-resident")
+    _check_workload(wl, tag="h128-chunks")
+
+
+def test_h128_per_row_path():
+    """More than 512 rows of one request with 128 heads (per-row path)."""
+    wl = W.prefill(4096, 520, seed=63, H=128, name="h128-rows")
+    _check_workload(wl, tag="h128-rows")
+
+
 # --------------------------------------------------------------- edge cases
 
 def _small_paged(seed=7, entries=(700, 64, 1, 129, 2048)):
