@@ -191,6 +191,48 @@ def summarize_pmc(fetch_dir, write_dir, workload, command, out):
     print("\n".join(lines))
 
 
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                 "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+SIMDS = 256 * 4
+
+
+def summarize_mfma(pmc_dir, workload, command, out):
+    """MFMA utilisation of the score kernel from one counter run of
+    MFMA_COUNTERS.  The profiler's CSV holds each counter summed over its
+    instances, so GRBM_GUI_ACTIVE is the sum over the 8 XCDs: busy =
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (GRBM_GUI_ACTIVE / 8 x
+    1024 SIMDs), the profiler's MfmaUtil ratio; the clock the kernel ran at
+    is GRBM_GUI_ACTIVE / 8 over the dispatch's duration.  Plus the
+    instruction mix."""
+    import statistics
+    kname, sources, _ = kernel_of(workload.replace("-q8", ""))
+    per = {}
+    for r in _csv_rows(_find(pmc_dir, "counter_collection.csv")):
+        if kname not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    rows = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS)]
+    med = {c: statistics.median(d[c] for d in rows) for c in MFMA_COUNTERS + ["ns"]}
+    active = med["GRBM_GUI_ACTIVE"] / 8
+    busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * SIMDS)
+    lines = [f"# rocprofv3 MFMA counters for {kname}, workload {workload}",
+             f"# command: {command}",
+             f"# medians over dispatches; busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x {SIMDS} SIMDs)",
+             f"source_hash = {score_source_hash(sources)}",
+             f"dispatches = {len(rows)}"]
+    lines += [f"{c.lower()} = {med[c]:.0f}" for c in MFMA_COUNTERS]
+    lines += [f"dispatch_ns = {med['ns']:.0f}",
+              f"clock_ghz = {active / med['ns']:.3f}",
+              f"mfma_busy_frac = {busy:.4f}",
+              f"coexec_frac_of_mfma_busy = {med['SQ_VALU_MFMA_COEXEC_CYCLES'] / med['SQ_VALU_MFMA_BUSY_CYCLES']:.4f}",
+              f"valu_insts_per_mfma_inst = {med['SQ_INSTS_VALU'] / med['SQ_INSTS_MFMA']:.2f}"]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(wl, pairs: int, min_seconds: float, max_sample_pairs: int = 4_000_000):
     """The oracle as it stands on the host cores, timed on a bounded sample:
     full passes of the workload until `min_seconds` of wall time, or, when one
@@ -465,6 +507,7 @@ def main():
     ap.add_argument("--summarize-trace", metavar="DIR", help="write profiles/ summary of a kernel-trace run")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summary of FETCH_SIZE / WRITE_SIZE runs")
+    ap.add_argument("--summarize-mfma", metavar="DIR", help="write profiles/ summary of an MFMA counter run")
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
 
@@ -474,6 +517,10 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, prof_name, args.command,
                         os.path.join(PROFILE_DIR, f"{trace_prefix}_{prof_name}_trace.txt"))
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, prof_name, args.command,
+                       os.path.join(PROFILE_DIR, f"score_kernel_{prof_name}_mfma.txt"))
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], prof_name, args.command,
