@@ -115,6 +115,21 @@ def read_traffic(workload: str):
         return None
 
 
+def read_mfma(name: str):
+    """(MFMA busy fraction, clock GHz) of the score kernel from the committed
+    counter summary, or (None, None) if absent or taken on other sources."""
+    path = os.path.join(PROFILE_DIR, f"score_kernel_{name}_mfma.txt")
+    if not os.path.exists(path):
+        return None, None
+    kv = _read_kv(path)
+    if kv.get("source_hash") != score_source_hash(SCORE_SOURCES):
+        return None, None
+    try:
+        return float(kv["mfma_busy_frac"]), float(kv["clock_ghz"])
+    except (KeyError, ValueError):
+        return None, None
+
+
 def _csv_rows(path):
     import csv
     with open(path) as f:
@@ -661,6 +676,10 @@ def main():
                     "peak": MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "traffic": traffic, "algorithmic_flop": flop,
                     "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+        # counters: the MFMA pipe's busy fraction and the clock the chip held
+        busy, clock = read_mfma(args.workload + ("-q8" if args.q8 else ""))
+        roofline["mfma_busy_frac"] = busy
+        roofline["clock_ghz"] = clock
     else:
         roofline = {"kernel": "score_kernel", "bound": "hbm",
                     "achieved": algo / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
