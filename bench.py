@@ -340,7 +340,16 @@ def kernel_ms_live(step, n):
         step(i)
     lib.idx_profile_events(None, None)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def spread(ms):
+    """Mean (what `achieved` divides by) and p10 / p50 / p90 of per-launch
+    kernel times, in ms."""
+    import numpy as np
+    p10, p50, p90 = np.percentile(ms, [10, 50, 90])
+    return float(np.mean(ms)), {"kernel_ms_p10": float(p10), "kernel_ms_p50": float(p50),
+                                "kernel_ms_p90": float(p90), "launches": len(ms)}
 
 
 def copy_calibration(n):
@@ -380,14 +389,15 @@ def bench_writer(args):
         step(i)
     torch.cuda.synchronize()
     ms_per_step = run_steps(step, args.steps, R, not args.no_graph)
-    kern_ms = kernel_ms_live(step, args.steps)
+    kern_ms, kern_spread = spread(kernel_ms_live(step, args.steps))
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
     algo = n * WRITE_BYTES_PER_KEY
     roofline = {"kernel": "write_keys_kernel", "bound": "hbm",
                 "achieved": algo / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "traffic": read_traffic(WRITE_WORKLOAD), "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+                "traffic": read_traffic(WRITE_WORKLOAD), "algorithmic_bytes": algo, "kernel_ms": kern_ms,
+                **kern_spread}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
     out = {
         "metric": "index-plane writer keys quantised and stored/s; % of HBM peak, 1 MI355X",
@@ -453,14 +463,14 @@ def bench_resident(args):
     ms_per_step = run_steps(step, args.steps, 1, not args.no_graph)
     # the hook stamps every score launch of a step; the events keep the last
     # layer's launch, whose bytes are one layer's
-    kern_ms = kernel_ms_live(step, args.steps)
+    kern_ms, kern_spread = spread(kernel_ms_live(step, args.steps))
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
     wl = rl.layers[-1]
     algo = algorithmic_bytes(wl, pairs_layer[-1]) + pairs_layer[-1] * 4     # + the scores written
     roofline = {"kernel": "score_kernel", "bound": "hbm", "achieved": algo / (kern_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": read_traffic(RESIDENT_WORKLOAD),
-                "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+                "algorithmic_bytes": algo, "kernel_ms": kern_ms, **kern_spread}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
     step_bytes = sum(algorithmic_bytes(w_, p_) + p_ * 4 for w_, p_ in zip(rl.layers, pairs_layer))
     out = {
@@ -598,73 +608,12 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    graphs = []
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step(0)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        per = min(R, K)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(per):
-                step(i)
-        graphs = [g] * (K // per)
-        if K % per:
-            g2 = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g2):
-                for i in range(K % per):
-                    step(i)
-            graphs.append(g2)
-        for g_ in set(graphs):
-            g_.replay()
-        torch.cuda.synchronize()
-
-    # ---- timed region: K steps
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record()
-    if graphs:
-        for g_ in graphs:
-            g_.replay()
-    else:
-        for i in range(K):
-            step(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = max(wall * 1e3, gpu_ms) / K
-    print(f"[bench] {K} steps: {ms_per_step * 1e3:.2f} us/step (wall {wall * 1e3:.3f} ms, "
-          f"events {gpu_ms:.3f} ms)", file=sys.stderr, flush=True)
-
-    # ---- score kernel duration, live: every score-kernel launch of K eager
-    # steps stamps a pair of events with its start and end (the dispatch does,
-    # on the launch stream), queued behind a busy wait so the queue never
-    # drains while the host enqueues
-    n_ev = K
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-    for a, b in evs:            # create the hipEvents; the library re-records them
-        a.record()
-        b.record()
-    torch.cuda.synchronize()
-    torch.cuda._sleep(int(5e7))
-    for i in range(n_ev):
-        lib.idx_profile_events(*evs[i])
-        step(i)
-    lib.idx_profile_events(None, None)
-    torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-
+    # ---- timed region: K steps (graph replays), then the score kernel's own
+    # duration from dispatch-stamped events over K eager steps
+    ms_per_step = run_steps(step, K, R, not args.no_graph)
+    kern_ms, kern_spread = spread(kernel_ms_live(step, K))
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(args.copy_calibration):
-            dst.copy_(src)
-        torch.cuda.synchronize()
+        copy_calibration(args.copy_calibration)
 
     algo = algorithmic_bytes(wl, pairs, q8=args.q8)
     traffic = read_traffic(args.workload + ("-q8" if args.q8 else ""))
@@ -675,7 +624,7 @@ def main():
                     "achieved": flop / (kern_ms * 1e-3) / 1e12,
                     "peak": MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "traffic": traffic, "algorithmic_flop": flop,
-                    "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+                    "algorithmic_bytes": algo, "kernel_ms": kern_ms, **kern_spread}
         # counters: the MFMA pipe's busy fraction and the clock the chip held
         busy, clock = read_mfma(args.workload + ("-q8" if args.q8 else ""))
         roofline["mfma_busy_frac"] = busy
@@ -683,7 +632,8 @@ def main():
     else:
         roofline = {"kernel": "score_kernel", "bound": "hbm",
                     "achieved": algo / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "traffic": traffic, "algorithmic_bytes": algo, "kernel_ms": kern_ms}
+                    "unit": "GB/s", "traffic": traffic, "algorithmic_bytes": algo, "kernel_ms": kern_ms,
+                    **kern_spread}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
     out = {
         "metric": "indexer scored pairs/s + top-512 queries/s; % of HBM/MFMA peak, 1 MI355X",
@@ -701,7 +651,7 @@ def main():
         "config": {"workload": wl.name, "queries": wl.B, "heads": wl.H, "head_dim": wl.D,
                    "query": "e4m3, quantised per head each step" if args.q8 else "bf16",
                    "block": wl.block_size, "k": k, "n_cols": wl.n_cols, "pairs": pairs,
-                   "description": wl.description, "replicas": R, "graph": bool(graphs)},
+                   "description": wl.description, "replicas": R, "graph": not args.no_graph},
         "queries_per_s": wl.B / (ms_per_step * 1e-3),
         "path_hbm_frac": algo / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": roofline,
