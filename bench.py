@@ -22,6 +22,10 @@ second and `roofline` covers the writer kernel.
 step quantises q per head (the writer kernel) and runs idx_score_topk_q8; the
 prefill roofline is then priced at the fp8 MFMA peak.
 
+`--block-size 16` re-lays a scoring workload's pool into 16-row blocks, each
+placed on its own (the block table grows fourfold, chunk lists are cut into
+small blocks), and measures the same step over that layout.
+
 `--workload memory-indexer` measures the Level-1 resident-set selection: one
 step is one idx_select_resident call over 8 requests at 1M tokens (262,144
 entries each) scored at 3 layers, KMAX 384 pages; `value` is scored pairs per
@@ -79,7 +83,7 @@ def algorithmic_bytes(wl, pairs: int, q8: bool = False) -> int:
     pair, plus q (bf16, or 132-byte quantised rows per head), w, bounds and
     tables."""
     if wl.q_req is not None and wl.block_table is not None and wl.block_table.shape[0] == 1:
-        keys = int((wl.block_table >= 0).sum()) * 64 * 132          # one request
+        keys = int((wl.block_table >= 0).sum()) * wl.block_size * 132   # one request
     else:
         keys = pairs * 132
     q_bytes = wl.B * wl.H * (wl.D + 4) if q8 else wl.q.nbytes
@@ -525,6 +529,8 @@ def main():
     ap.add_argument("--q8", action="store_true",
                     help="quantised-query variant: each step quantises q per head (writer kernel) and scores "
                          "with idx_score_topk_q8 on fp8 MFMA")
+    ap.add_argument("--block-size", type=int, default=64, choices=(64, 16),
+                    help="pool block rows of the scoring workloads (16: the same keys re-laid in 16-row blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -538,7 +544,7 @@ def main():
 
     trace_prefix = {WRITE_WORKLOAD: "write_keys", RESIDENT_WORKLOAD: "select_resident"}.get(args.workload,
                                                                                           "score_topk")
-    prof_name = args.workload + ("-q8" if args.q8 else "")
+    prof_name = args.workload + ("-b16" if args.block_size == 16 else "") + ("-q8" if args.q8 else "")
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, prof_name, args.command,
                         os.path.join(PROFILE_DIR, f"{trace_prefix}_{prof_name}_trace.txt"))
@@ -557,8 +563,8 @@ def main():
               f"the library runs on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
-    if args.q8 and args.workload in (WRITE_WORKLOAD, RESIDENT_WORKLOAD):
-        print(f"--q8 applies to the scoring workloads, not {args.workload}", file=sys.stderr)
+    if (args.q8 or args.block_size != 64) and args.workload in (WRITE_WORKLOAD, RESIDENT_WORKLOAD):
+        print(f"--q8 and --block-size apply to the scoring workloads, not {args.workload}", file=sys.stderr)
         sys.exit(2)
     if args.workload == WRITE_WORKLOAD:
         bench_writer(args)
@@ -574,6 +580,8 @@ def main():
     torch.cuda.set_device(0)
     cfg = WORKLOADS[args.workload]
     wl = workloads.config(cfg)
+    if args.block_size != 64:
+        wl = workloads.reblock(wl, seed=50 + cfg, block_size=args.block_size, name=f"{wl.name}-b{args.block_size}")
     pairs = wl.pairs()
     print(f"[bench] workload {wl.name}: {wl.description}; pairs {pairs}", file=sys.stderr, flush=True)
     d = lib.to_device(wl)
@@ -582,7 +590,8 @@ def main():
     pools = [d.keys.pool] + [d.keys.pool.clone() for _ in range(R - 1)]
     qs = [d.q] + [d.q.clone() for _ in range(R - 1)]
     keys = [lib.Keys(pool=p, limits=d.keys.limits, block_table=d.keys.block_table,
-                     q_req=d.keys.q_req, chunk_ids=d.keys.chunk_ids, n_chunks=d.keys.n_chunks)
+                     q_req=d.keys.q_req, chunk_ids=d.keys.chunk_ids, n_chunks=d.keys.n_chunks,
+                     block_size=wl.block_size)
             for p in pools]
     k = wl.k
     out_idx = torch.empty((wl.B, k), dtype=torch.int32, device="cuda")
@@ -616,7 +625,7 @@ def main():
         copy_calibration(args.copy_calibration)
 
     algo = algorithmic_bytes(wl, pairs, q8=args.q8)
-    traffic = read_traffic(args.workload + ("-q8" if args.q8 else ""))
+    traffic = read_traffic(prof_name)
     if args.workload == "chunked-prefill":
         # one request's keys are shared by every query: the contraction bounds it
         flop = 2.0 * wl.H * wl.D * pairs
@@ -626,7 +635,7 @@ def main():
                     "unit": "TFLOP/s", "traffic": traffic, "algorithmic_flop": flop,
                     "algorithmic_bytes": algo, "kernel_ms": kern_ms, **kern_spread}
         # counters: the MFMA pipe's busy fraction and the clock the chip held
-        busy, clock = read_mfma(args.workload + ("-q8" if args.q8 else ""))
+        busy, clock = read_mfma(prof_name)
         roofline["mfma_busy_frac"] = busy
         roofline["clock_ghz"] = clock
     else:

@@ -19,7 +19,7 @@
  * Tile lists ("DeepSeek-V4.1 native paged runtime", section "Current
  * execution scope"): every query row carries its own bound (limits[b], the
  * compressed length seq_len // 4 per the c4 fix in the batchgen pull request)
- * and its own list of 64-entry blocks read in place from the paged pool; a
+ * and its own list of blocks read in place from the paged pool; a
  * prefill token, a decode token and a ragged batch are all the same shape.
  *
  * Conventions for every entry point:
@@ -28,7 +28,8 @@
  *    host.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream) and returns before it finishes.  Bounds, block ids and chunk
  *    lists stay on the device, so calls can be captured in a HIP graph.
- *  - Supported shapes: H = 64 heads, D = 128, block_size = 64, 1 <= k <= 2048.
+ *  - Supported shapes: H = 64 or 128 heads, D = 128, block_size = 64 or 16,
+ *    1 <= k <= 2048.
  *  - The return value is IDX_OK (0) or an IDX_E_* code; nothing is launched
  *    when a host-side check fails.  idx_last_error() gives a message for the
  *    calling thread's last failure.
@@ -81,9 +82,12 @@ enum idx_op { IDX_OP_SCORE = 0, IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
  *
  * pool         uint8 [n_pool_rows, D + 4]: row r = D e4m3fn bytes, then the
  *              fp32 scale (little-endian).  16-byte aligned.  Rows of one
- *              64-entry block are contiguous (a block is 8448 bytes).
- * n_pool_rows  rows in the pool (with a block table: a multiple of 64).
- * block_size   entries per block; must be 64.
+ *              block are contiguous (8448 bytes for 64 rows).
+ * n_pool_rows  rows in the pool (with a block table: a multiple of
+ *              block_size).
+ * block_size   entries (rows) per block: 64, or 16 ("DeepSeek-V4.1 native
+ *              paged runtime": one block id names 16 index rows).  Block
+ *              table entries and chunk ids count blocks of this size.
  * block_table  int32 [n_req, max_blocks]: logical block -> pool block, -1 =
  *              absent.  NULL = contiguous: logical entry e is pool row e for
  *              every request.
@@ -99,8 +103,9 @@ enum idx_op { IDX_OP_SCORE = 0, IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
  *
  * Column c of row b (the logits' second index):
  *   without chunk_ids: c is the logical entry id;
- *   with chunk_ids:    c = 64*j + s is entry s of block chunk_ids[b][j],
- *                      i.e. logical entry chunk_ids[b][j]*64 + s.
+ *   with chunk_ids:    c = block_size*j + s is entry s of block
+ *                      chunk_ids[b][j], i.e. logical entry
+ *                      chunk_ids[b][j]*block_size + s.
  * A column is scored iff it maps to an entry below limits[b] whose block is
  * present; every other column is -inf.
  */
@@ -267,8 +272,10 @@ int idx_write_keys(const uint16_t *k, int64_t n, int32_t D,
  * cfg       ensemble, threshold, n_sink, n_recent >= 0, 1 <= kmax <= 2048,
  *           n_sink + n_recent <= kmax.
  * out_pages int32 [B, kmax] out: resident pages in ascending order, -1 after
- *           the last.  Usable as chunk_ids (max_chunks = kmax) of a later
- *           idx_score / idx_score_topk on the same rows.
+ *           the last.  Pages are 64 entries whatever keys' block_size.
+ *           Usable as chunk_ids (max_chunks = kmax) of a later idx_score /
+ *           idx_score_topk on the same rows over 64-row blocks; over 16-row
+ *           blocks page p is the chunks 4p .. 4p + 3.
  * out_count int32 [B] out, or NULL: resident pages per row (usable as
  *           n_chunks).
  * workspace / ws_bytes: at least idx_resident_workspace_bytes(n_layers, B,

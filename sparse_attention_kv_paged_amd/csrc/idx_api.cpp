@@ -98,7 +98,8 @@ TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
 hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_t ld,
                         const uint32_t *row_cols, int32_t B, int32_t n_cols, int32_t k,
                         int32_t *out_idx, float *out_val, const int32_t *chunk_ids,
-                        int32_t max_chunks, hipStream_t s, int32_t *out_count = nullptr) {
+                        int32_t max_chunks, int32_t chunk_shift, hipStream_t s,
+                        int32_t *out_count = nullptr) {
     idx::SegArgs a{};
     a.out_count = out_count;
     a.B = B;
@@ -112,6 +113,7 @@ hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_
     a.out_val = out_val;
     a.chunk_ids = chunk_ids;
     a.max_chunks = max_chunks;
+    a.chunk_shift = chunk_shift;
     if (P.parts0 == 1) return idx::launch_topk_segment(a, false, P.cap0, false, s);
     a.out_list = reinterpret_cast<uint2 *>(ws + P.list[0]);
     if (P.fused) {
@@ -185,8 +187,9 @@ int check_qw(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D)
 
 int check_keys(const idx_keys *keys, int32_t B) {
     if (!keys) return fail(IDX_E_ARG, "keys must be non-null");
-    if (keys->block_size != idx::kBlock)
-        return fail(IDX_E_SHAPE, "block_size must be 64 (got %d)", keys->block_size);
+    const int32_t bs = keys->block_size;
+    if (bs != idx::kBlock && bs != idx::kSmallBlock)
+        return fail(IDX_E_SHAPE, "block_size must be 64 or 16 (got %d)", bs);
     if (keys->n_pool_rows < 0) return fail(IDX_E_ARG, "n_pool_rows must be >= 0");
     if (keys->n_pool_rows > 0 && !keys->pool) return fail(IDX_E_ARG, "pool is null");
     if (!aligned(keys->pool, 16)) return fail(IDX_E_ALIGN, "pool must be 16-byte aligned");
@@ -194,9 +197,9 @@ int check_keys(const idx_keys *keys, int32_t B) {
     if (keys->block_table) {
         if (keys->n_req <= 0 || keys->max_blocks <= 0)
             return fail(IDX_E_SHAPE, "a block table needs n_req >= 1 and max_blocks >= 1");
-        if (keys->n_pool_rows % idx::kBlock)
-            return fail(IDX_E_SHAPE, "with a block table, n_pool_rows must be a multiple of 64");
-        if ((int64_t)keys->max_blocks * idx::kBlock > INT32_MAX)
+        if (keys->n_pool_rows % bs)
+            return fail(IDX_E_SHAPE, "with a block table, n_pool_rows must be a multiple of block_size");
+        if ((int64_t)keys->max_blocks * bs > INT32_MAX)
             return fail(IDX_E_SHAPE, "max_blocks too large");
     } else if (!keys->q_req && B > 0) {
         // contiguous pool: every row reads the same rows; nothing else to check
@@ -217,6 +220,7 @@ idx::ScoreArgs score_args(const uint16_t *q, const float *w, int32_t B, const id
     a.B = B;
     a.pool = keys->pool;
     a.n_pool_rows = keys->n_pool_rows;
+    a.block_size = keys->block_size;
     a.block_table = keys->block_table;
     a.n_req = keys->n_req;
     a.max_blocks = keys->max_blocks;
@@ -327,7 +331,7 @@ int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_
     hipError_t e;
     if ((e = launch_heads(a, H, s)) != hipSuccess) return hip_fail(e, "score kernel");
     e = enqueue_topk(P, ws, a.logits, P.ld, a.row_cols, B, n_cols, k, out_idx, out_val,
-                     keys->chunk_ids, keys->max_chunks, s);
+                     keys->chunk_ids, keys->max_chunks, keys->block_size == idx::kSmallBlock ? 4 : 6, s);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
 }
 
@@ -391,7 +395,7 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t
         return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
     if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
     hipError_t e = enqueue_topk(P, static_cast<char *>(workspace), logits, ld, nullptr, B, n_cols, k,
-                                out_col, out_val, nullptr, 0, (hipStream_t)stream);
+                                out_col, out_val, nullptr, 0, 6, (hipStream_t)stream);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
 }
 
@@ -456,7 +460,7 @@ int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float 
     pa.n_pages = R.n_pages;
     if ((e = idx::launch_pages(pa, s)) != hipSuccess) return hip_fail(e, "page kernel");
     e = enqueue_topk(R.top, ws + R.topk, pa.page_keys, R.ldp, nullptr, B, R.n_pages, cfg->kmax, out_pages,
-                     nullptr, nullptr, 0, s, out_count);
+                     nullptr, nullptr, 0, 6, s, out_count);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "page top-k");
 }
 

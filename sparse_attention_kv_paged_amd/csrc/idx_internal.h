@@ -10,7 +10,8 @@ namespace idx {
 
 constexpr int kHeads = 64;
 constexpr int kHeadDim = 128;
-constexpr int kBlock = 64;                   // entries per paged block
+constexpr int kBlock = 64;                   // entries per slot (and per paged block by default)
+constexpr int kSmallBlock = 16;              // the other supported pool block size
 constexpr int kRowBytes = kHeadDim + 4;      // 128 e4m3 bytes + fp32 scale
 constexpr int kWaves = 4;                    // waves per score workgroup
 constexpr int kMaxK = 2048;
@@ -27,6 +28,7 @@ struct ScoreArgs {
     int32_t B;
     const uint8_t *pool;        // [n_pool_rows, 132]
     int64_t n_pool_rows;
+    int32_t block_size;         // rows per pool block: 64, or 16 (four blocks per 64-column slot)
     const int32_t *block_table; // [n_req, max_blocks] or null
     int32_t n_req;
     int32_t max_blocks;
@@ -75,6 +77,7 @@ struct SegArgs {
     int32_t *out_count;         // [B] number of winners per row, or null
     const int32_t *chunk_ids;   // columns -> logical entries, or null
     int32_t max_chunks;
+    int32_t chunk_shift;        // log2 of the entries one chunk id names (6, or 4 for 16-row blocks)
 };
 
 // ev_start / ev_stop (optional): events the dispatch itself stamps with the

@@ -66,7 +66,8 @@ template <> struct QSel<true> {
 
 struct RowCtx {
     int32_t req;      // request row, -1 = padding
-    int32_t nslots;   // slots of the tile list that may hold scored entries
+    int32_t nslots;   // 64-column slots of the tile list that may hold scored entries
+    int32_t nunits;   // pool blocks of the tile list (= nslots for 64-row blocks)
     int32_t limit;    // bound on logical entry ids, clamped to capacity
 };
 
@@ -87,17 +88,21 @@ __device__ __forceinline__ RowRaw row_raw(const ScoreArgs &a, int b) {
     return r;
 }
 
+// BS: rows per pool block (64, or 16: four blocks make one 64-column slot).
+template <int BS>
 __device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, const RowRaw &raw, uint32_t &st) {
+    constexpr int U = kBlock / BS;
     RowCtx r;
     r.req = raw.qreq;
     r.limit = raw.limit;
     r.nslots = 0;
+    r.nunits = 0;
     if (r.req >= 0 && a.block_table && r.req >= a.n_req) {
         st |= 0x4u;                                   // IDX_STATUS_BAD_REQUEST
         r.req = -1;
     }
     if (r.req < 0) return r;
-    const int64_t cap = a.block_table ? (int64_t)a.max_blocks * kBlock : a.n_pool_rows;
+    const int64_t cap = a.block_table ? (int64_t)a.max_blocks * BS : a.n_pool_rows;
     if ((int64_t)r.limit > cap) {
         st |= 0x1u;                                   // IDX_STATUS_LIMIT_CLAMPED
         r.limit = (int32_t)cap;
@@ -109,10 +114,11 @@ __device__ __forceinline__ RowCtx row_context(const ScoreArgs &a, const RowRaw &
             st |= 0x8u;                               // IDX_STATUS_BAD_CHUNK
             nc = a.max_chunks;
         }
-        r.nslots = nc < 0 ? 0 : nc;
+        r.nunits = nc < 0 ? 0 : nc;
     } else {
-        r.nslots = (r.limit + kBlock - 1) / kBlock;
+        r.nunits = (int32_t)(((int64_t)r.limit + BS - 1) / BS);
     }
+    r.nslots = (r.nunits + U - 1) / U;
     return r;
 }
 
@@ -148,29 +154,31 @@ __device__ __forceinline__ SlotRaw slot_raw(const ScoreArgs &a, int req, int b, 
     return s;
 }
 
-// First pool row of slot j of row b, or -1 when the slot's block is absent
-// (or !ok: the lane holds no slot).  *ebase receives the logical entry id of
-// the slot's first entry.  Straight-line selects, no branches, so the wait
-// for the table read is the only one the compiler needs here.
+// First pool row of pool block j (of BS rows) of row b's tile list, or -1
+// when the block is absent (or !ok: the lane holds no block).  *ebase
+// receives the logical entry id of the block's first entry.  Straight-line
+// selects, no branches, so the wait for the table read is the only one the
+// compiler needs here.
+template <int BS>
 __device__ __forceinline__ int64_t resolve_slot(const ScoreArgs &a, const RowCtx &r, const SlotRaw &raw,
                                                 int j, bool ok, int32_t &ebase, uint32_t &st) {
     const int64_t beta = raw.beta;
-    ok = ok && r.req >= 0 && j < r.nslots;
+    ok = ok && r.req >= 0 && j < r.nunits;
     uint32_t bad = 0;
     if (a.chunk_ids) {
-        const bool beyond = a.block_table ? beta >= a.max_blocks : beta * kBlock >= a.n_pool_rows;
+        const bool beyond = a.block_table ? beta >= a.max_blocks : beta * BS >= a.n_pool_rows;
         bad |= (ok && (beta < -1 || (beta >= 0 && beyond))) ? 0x8u : 0u;        // IDX_STATUS_BAD_CHUNK
         ok = ok && beta >= 0 && !beyond;
     }
-    ebase = (int32_t)(beta * kBlock);
+    ebase = (int32_t)(beta * BS);
     ok = ok && ebase < r.limit;
-    int64_t prow = beta * kBlock;
+    int64_t prow = beta * BS;
     if (a.block_table) {
         const int64_t pblk = raw.tok ? raw.p : -1;
-        const bool past = (pblk + 1) * kBlock > a.n_pool_rows;
+        const bool past = (pblk + 1) * BS > a.n_pool_rows;
         bad |= (ok && (pblk < -1 || (pblk >= 0 && past))) ? 0x2u : 0u;         // IDX_STATUS_BAD_BLOCK
         ok = ok && pblk >= 0 && !past;
-        prow = pblk * kBlock;
+        prow = pblk * BS;
     }
     st |= bad;
     return ok ? prow : -1;
@@ -190,9 +198,15 @@ struct KeyHalf {
 // row n is granule 8*n + (c ^ (n & 7)): the eight rows that eight
 // consecutive lanes read back sit in eight different bank groups.  A fifth
 // load puts the 32 row scales (twice: lanes 32-63 repeat lanes 0-31) after
-// the fp8 bytes.
+// the fp8 bytes.  With 16-row pool blocks a tile spans two blocks, each
+// with a descriptor of its own: loads 0-1 read the first, loads 2-3 the
+// second, and each block's 16 scales come with a load of their own (64
+// lanes, rows repeated four times), the second block's 256 bytes further on.
 constexpr int kTileFp8 = 32 * kHeadDim;                // one tile's fp8 bytes in LDS
-constexpr int kTileBytes = kTileFp8 + 64 * 4;          // + the scales
+template <int BS> constexpr int tile_bytes() {         // + the scales
+    return kTileFp8 + (BS == kBlock ? 64 : 128) * 4;
+}
+template <int BS> constexpr int loads_per_tile() { return BS == kBlock ? 5 : 6; }
 
 // The lane's byte offset (within a tile) of the chunk it loads with load 0.
 __device__ __forceinline__ uint32_t tile_load_offset(int lane) {
@@ -210,14 +224,35 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t r, uint32_t t0,
                                              t0 + (uint32_t)(threadIdx.x & 31) * kRowBytes + kHeadDim, 0, 0, 0);
 }
 
+// The six loads of a tile made of two 16-row pool blocks (ra: tile rows
+// 0-15, rb: rows 16-31); lo as for load_tile.
+__device__ __forceinline__ void load_tile16(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb, uint32_t lo,
+                                            uint8_t *dst) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void *)(dst + 1024 * i), 16,
+                                                 lo + 8u * kRowBytes * i, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void *)(dst + 1024 * (i + 2)),
+                                                 16, lo + 8u * kRowBytes * i, 0, 0, 0);
+    const uint32_t so = (uint32_t)(threadIdx.x & 15) * kRowBytes + kHeadDim;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void *)(dst + kTileFp8), 4, so, 0,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void *)(dst + kTileFp8 + 256), 4,
+                                             so, 0, 0, 0);
+}
+
 // The lane's half row (lane >> 5) of tile row (lane & 31), and that row's
 // scale, from an LDS slot.
+template <int BS>
 __device__ __forceinline__ void read_tile(const uint8_t *slot, KeyHalf &k) {
     const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         k.v[j] = *reinterpret_cast<const u32x4 *>(slot + 128 * n + 16 * ((4 * hf + j) ^ (n & 7)));
-    k.s = *reinterpret_cast<const float *>(slot + kTileFp8 + 4 * lane);
+    const int si = BS == kBlock ? lane : (n & 15) + 64 * (n >> 4);
+    k.s = *reinterpret_cast<const float *>(slot + kTileFp8 + 4 * si);
 }
 
 // The compiler does not see that an LDS read depends on a buffer-to-LDS
@@ -332,12 +367,14 @@ __device__ __forceinline__ float tile_logit(const TileAcc &acc, const float (&wr
 // reads of the waves that start last.
 constexpr int kFlatRows = 512;  // rows up to which waves share work evenly
 
+template <int BS>
 __device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_t &st) {
-    RowCtx r = row_context(a, row_raw(a, b), st);
+    RowCtx r = row_context<BS>(a, row_raw(a, b), st);
     // wave-uniform values stay in scalar registers, so the tile loop is
     // uniform control flow and its loads stay in flight across iterations
     r.req = __builtin_amdgcn_readfirstlane(r.req);
     r.nslots = __builtin_amdgcn_readfirstlane(r.nslots);
+    r.nunits = __builtin_amdgcn_readfirstlane(r.nunits);
     r.limit = __builtin_amdgcn_readfirstlane(r.limit);
     return r;
 }
@@ -489,11 +526,12 @@ struct NoQ {
 
 // Score slots [j0, j1) of row b with the calling wave.  sh_w is the wave's
 // own 64-float LDS slot for w[b].  Columns >= col_end are not written.
+// BS: rows per pool block; a 64-column slot is 64 / BS pool blocks.
 // USE_PRE: pre holds the first group's table reads, already issued by the
 // caller, and qfin(qa) -- called once, right after the first ring of key
 // loads has been issued, by every wave of the workgroup (it synchronises
 // the workgroup) -- delivers the MFMA operands of q[b].
-template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, bool USE_PRE = false,
+template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, int BS, bool USE_PRE = false,
           class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
@@ -501,6 +539,9 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int n32 = lane & 31;
+    constexpr int U = kBlock / BS;                    // pool blocks per slot
+    constexpr int GS = 64 / U;                        // slots per group: one block per lane
+    constexpr int TB = tile_bytes<BS>();
     const bool live = r.req >= 0 && j0 < r.nslots;
     float *out_row = a.logits + (int64_t)b * a.ld;
     float *score_row = SCORES ? a.scores + (int64_t)b * a.ld : nullptr;
@@ -518,12 +559,12 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         // quantised q: relu(s_q x) = s_q relu(x) for s_q >= 0, so each head's
         // q scale joins its weight
         if (Q8) w_lane *= q8_scale(a, b, lane);
-        raw0 = USE_PRE ? pre : slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));
+        raw0 = USE_PRE ? pre : slot_raw<CHUNKED>(a, r.req, b, U * j0 + lane, lane < min(64, U * (j1 - j0)));
         if (!USE_PRE) load_q_global(a, b, qa);
     }
 
-    // Slots go in groups of up to 64: lane j resolves slot j of the group
-    // (one vector load per table level), then the group's tiles stream
+    // Slots go in groups of up to GS (64 pool blocks): lane j resolves block
+    // j of the group (one vector load per table level), then its tiles stream
     // through the wave's two-slot LDS ring.  Tiles of absent blocks and
     // ring slots past the group's end get an empty descriptor (no traffic).
     const __amdgpu_buffer_rsrc_t out_r = make_rsrc(out_row, (uint32_t)col_end * 4u);
@@ -536,14 +577,14 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     const uint32_t lane_off = LEAN && hf == 0 ? (uint32_t)n32 * 4u : kDrop;
     SlotRaw graw = raw0;
     float wr[2][4][4];                                // the lane's 32 head weights
-    for (int g0 = j0; g0 < j1; g0 += 64) {
-        const int gn = min(64, j1 - g0);
+    for (int g0 = j0; g0 < j1; g0 += GS) {
+        const int gn = min(GS, j1 - g0);
         int32_t lane_ebase = 0;
         int64_t lane_prow0 = -1;
-        lane_prow0 = resolve_slot(a, r, graw, g0 + lane, live && lane < gn, lane_ebase, st);
+        lane_prow0 = resolve_slot<BS>(a, r, graw, U * g0 + lane, live && lane < U * gn, lane_ebase, st);
         // the next group's table reads, in flight during this group's ring
         // (no traffic when there is no next group)
-        graw = slot_raw<CHUNKED>(a, r.req, b, g0 + 64 + lane, live && lane < min(64, j1 - g0 - 64));
+        graw = slot_raw<CHUNKED>(a, r.req, b, U * (g0 + GS) + lane, live && lane < min(64, U * (j1 - g0 - GS)));
         const int ntiles = 2 * gn;
         // tile tau of the group: rows 32*(tau & 1) .. +31 of slot tau >> 1,
         // into ring slot tau & 1; tiles past the group's end and tiles of
@@ -553,22 +594,42 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         // reuses them for its second (tiles are issued in order).  It runs
         // before a tile's MFMAs, so the scalar descriptor arithmetic never
         // splits the stretch where MFMAs and the epilogue interleave.
+        // With 16-row blocks each tile has two blocks of its own: the lane's
+        // bound is its block's, shifted by 16 for rows 16-31.
         int32_t lim_t[2];
         __amdgpu_buffer_rsrc_t slot_r = make_rsrc(a.pool, 0u);
         int32_t slot_lim = 0;
         auto issue = [&](int tau) {
-            if (!LEAN || (tau & 1) == 0) {
-                const int j = min(tau >> 1, gn - 1);
-                const int64_t pr = readlane64(lane_prow0, j);
-                const int64_t prow0 = tau < ntiles ? pr : -1;
-                const bool ok = prow0 >= 0;
-                const int64_t p0 = ok ? prow0 : 0;
-                const uint32_t bytes = ok ? (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - p0) * kRowBytes : 0u;
-                slot_r = make_rsrc(a.pool + p0 * kRowBytes, bytes);
-                slot_lim = ok ? r.limit - __builtin_amdgcn_readlane(lane_ebase, j) : 0;
+            if constexpr (BS != kBlock) {
+                const int u0 = U * min(tau >> 1, gn - 1) + 2 * (tau & 1);
+                __amdgpu_buffer_rsrc_t rq[2];
+                int32_t lq[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t pr = readlane64(lane_prow0, u0 + h);
+                    const int64_t p = tau < ntiles ? pr : -1;
+                    const bool ok = p >= 0;
+                    const int64_t p0 = ok ? p : 0;
+                    const uint32_t bytes = ok ? (uint32_t)min<int64_t>(BS, a.n_pool_rows - p0) * kRowBytes : 0u;
+                    rq[h] = make_rsrc(a.pool + p0 * kRowBytes, bytes);
+                    lq[h] = ok ? min(r.limit - __builtin_amdgcn_readlane(lane_ebase, u0 + h), BS) : 0;
+                }
+                lim_t[tau & 1] = n32 < BS ? lq[0] : lq[1] + BS;
+                load_tile16(rq[0], rq[1], lane_lo, ring + (tau & 1) * TB);
+            } else {
+                if (!LEAN || (tau & 1) == 0) {
+                    const int j = min(tau >> 1, gn - 1);
+                    const int64_t pr = readlane64(lane_prow0, j);
+                    const int64_t prow0 = tau < ntiles ? pr : -1;
+                    const bool ok = prow0 >= 0;
+                    const int64_t p0 = ok ? prow0 : 0;
+                    const uint32_t bytes = ok ? (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - p0) * kRowBytes : 0u;
+                    slot_r = make_rsrc(a.pool + p0 * kRowBytes, bytes);
+                    slot_lim = ok ? r.limit - __builtin_amdgcn_readlane(lane_ebase, j) : 0;
+                }
+                lim_t[tau & 1] = slot_lim - 32 * (tau & 1);
+                load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * TB);
             }
-            lim_t[tau & 1] = slot_lim - 32 * (tau & 1);
-            load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * kTileBytes);
         };
         // a tile's epilogue inputs, kept with its accumulators because the
         // ring slot is reloaded before the epilogue runs
@@ -587,14 +648,14 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         // soon as the lane has read it, and that reload goes out before the
         // MFMAs, so the contraction and the caller's next epilogue form one
         // straight-line stretch for the scheduler to interleave.  The wait
-        // for the tile's loads counts only the five loads of tile tau + 1 as
-        // later: vector memory loads complete in order, so this holds
-        // whatever order stores take.
+        // for the tile's loads counts only the loads of tile tau + 1 (five,
+        // six with 16-row blocks) as later: vector memory loads complete in
+        // order, so this holds whatever order stores take.
         auto mma = [&](int tau, Stage &st_) {
             const int k = tau & 1;
-            wait_vmem<5>();
+            wait_vmem<loads_per_tile<BS>()>();
             KeyHalf kh;
-            read_tile(ring + k * kTileBytes, kh);
+            read_tile<BS>(ring + k * TB, kh);
             wait_lds();
             st_.keep = n32 < lim_t[k];
             // ACCUM: the earlier logit is read before the next tile's loads
@@ -655,14 +716,16 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // FLAT: the (row, slot) work of all rows is flattened and split evenly over
 // every wave of the grid (rows of very different lengths); otherwise each
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM>
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM, int BS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
+    constexpr int U = kBlock / BS;                    // pool blocks per slot
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
     __shared__ int32_t sh_pre[FLAT ? kFlatRows + 1 : 1];
-    __shared__ int32_t sh_rreq[FLAT ? kFlatRows : 1], sh_rlim[FLAT ? kFlatRows : 1], sh_rslots[FLAT ? kFlatRows : 1];
+    // sh_runits: each row's pool blocks (its slots follow from them)
+    __shared__ int32_t sh_rreq[FLAT ? kFlatRows : 1], sh_rlim[FLAT ? kFlatRows : 1], sh_runits[FLAT ? kFlatRows : 1];
     __shared__ uint32_t sh_scan[kWaves];
     __shared__ __attribute__((aligned(16))) uint16_t sh_q[FLAT ? 2 : 1][kQStage];
-    __shared__ __attribute__((aligned(16))) uint8_t sh_ring[kWaves][2 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t sh_ring[kWaves][2 * tile_bytes<BS>()];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int lane = threadIdx.x & 63;
     const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
@@ -671,7 +734,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (!FLAT) {
         const int b = blockIdx.x / a.splits;
         const int split = blockIdx.x - b * a.splits;
-        const RowCtx r = uniform_row(a, b, st);
+        const RowCtx r = uniform_row<BS>(a, b, st);
         const int col_end = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
         const int slot_stop = OWN_COLS ? min(r.nslots, slot_cols) : slot_cols;
         if (OWN_COLS && split == 0 && threadIdx.x == 0) {
@@ -685,7 +748,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int j1 = min(j0 + spw, slot_stop);
         // the first group's table reads, then q[b] staged in LDS once for
         // the four waves
-        const SlotRaw raw0 = slot_raw<CHUNKED>(a, r.req, b, j0 + lane, lane < min(64, j1 - j0));
+        const SlotRaw raw0 = slot_raw<CHUNKED>(a, r.req, b, U * j0 + lane, lane < min(64, U * (j1 - j0)));
         QRows<Q8, 1> qv;
         fetch_q_rows<1>(a, b, qv);
         const auto qfin = [&](typename QSel<Q8>::Op &qa) {
@@ -694,7 +757,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put_q_rows<1>(a, b, qv, sh_q);            // the workgroup's one barrier
             __syncthreads();
@@ -708,10 +771,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int k2 = 0; k2 < 2; ++k2) {
             const int row = 2 * threadIdx.x + k2;
             if (row < a.B) {
-                const RowCtx rr = row_context(a, raw[k2], st_rows);
+                const RowCtx rr = row_context<BS>(a, raw[k2], st_rows);
                 sh_rreq[row] = rr.req;
                 sh_rlim[row] = rr.limit;
-                sh_rslots[row] = rr.nslots;
+                sh_runits[row] = rr.nunits;
                 cnt[k2] = OWN_COLS ? max(0, min(rr.nslots, slot_cols)) : slot_cols;
                 if (OWN_COLS && blockIdx.x == 0) {
                     a.row_cols[row] = (uint32_t)max(0, min(rr.nslots * kBlock, a.n_cols));
@@ -756,8 +819,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         RowCtx r0;
         r0.req = __builtin_amdgcn_readfirstlane(sh_rreq[b]);
         r0.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
-        r0.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
-        const SlotRaw raw0 = slot_raw<CHUNKED>(a, r0.req, b, f - pb + lane, lane < min(64, min(fend, pe) - f));
+        r0.nunits = __builtin_amdgcn_readfirstlane(sh_runits[b]);
+        r0.nslots = (r0.nunits + U - 1) / U;
+        const SlotRaw raw0 =
+            slot_raw<CHUNKED>(a, r0.req, b, U * (f - pb) + lane, lane < min(64, U * (min(fend, pe) - f)));
         // q of the workgroup's first two rows, staged in LDS once for its
         // four waves (most workgroups lie within one or two rows)
         const int fw = (int)blockIdx.x * kWaves * chunk;
@@ -778,7 +843,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
                                                     qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
@@ -788,9 +853,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 RowCtx r;
                 r.req = __builtin_amdgcn_readfirstlane(sh_rreq[b]);
                 r.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
-                r.nslots = __builtin_amdgcn_readfirstlane(sh_rslots[b]);
+                r.nunits = __builtin_amdgcn_readfirstlane(sh_runits[b]);
+                r.nslots = (r.nunits + U - 1) / U;
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
                 f = min(fend, pe);
             }
         }
@@ -804,10 +870,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8, bool ACCUM>
 void launch_score_qa(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 g((unsigned)grid), blk(256);
-    if (a.chunk_ids)
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM>), g, blk, 0, s, e0, e1, 0, a);
-    else
-        hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM>), g, blk, 0, s, e0, e1, 0, a);
+    const bool small = a.block_size == kSmallBlock;
+    if (a.chunk_ids) {
+        if (small)
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kSmallBlock>), g, blk, 0, s, e0,
+                                  e1, 0, a);
+        else
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kBlock>), g, blk, 0, s, e0, e1,
+                                  0, a);
+    } else {
+        if (small)
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kSmallBlock>), g, blk, 0, s,
+                                  e0, e1, 0, a);
+        else
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kBlock>), g, blk, 0, s, e0,
+                                  e1, 0, a);
+    }
 }
 
 // The accumulating second head half exists for bf16 queries only.
@@ -830,6 +908,7 @@ void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.B <= 0) return hipSuccess;
     if (a.accum && a.q8) return hipErrorInvalidValue;
+    if (a.block_size != kBlock && a.block_size != kSmallBlock) return hipErrorInvalidValue;
     // the top-k feed (row_cols) never asks for scores
     const bool own = a.row_cols != nullptr;
     const bool scores = !own && a.scores != nullptr;

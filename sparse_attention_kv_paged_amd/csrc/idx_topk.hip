@@ -343,8 +343,10 @@ __device__ __forceinline__ void write_final(const SegArgs &a, int b, WinCursor c
                 make_rsrc(a.chunk_ids + (int64_t)b * a.max_chunks, (uint32_t)a.max_chunks * 4u);
 #pragma unroll
             for (int j = 0; j < kG; ++j) {
-                const uint32_t off = pos[j] == kLoses ? kDrop : (col(g + j) / kBlock) * 4u;
-                e[j] = __builtin_amdgcn_raw_buffer_load_b32(cr, off, 0, 0) * kBlock + col(g + j) % kBlock;
+                const uint32_t c = col(g + j);
+                const uint32_t off = pos[j] == kLoses ? kDrop : (c >> a.chunk_shift) * 4u;
+                e[j] = (__builtin_amdgcn_raw_buffer_load_b32(cr, off, 0, 0) << a.chunk_shift) |
+                       (c & ((1u << a.chunk_shift) - 1u));
             }
 #pragma unroll
             for (int j = 0; j < kG; ++j) {

@@ -467,5 +467,55 @@ def small_config(i: int, seed: Optional[int] = None) -> Workload:
     raise ValueError(f"no workload {i}")
 
 
+def reblock(wl: Workload, seed: int, block_size: int = 16, ragged: bool = True,
+            name: Optional[str] = None) -> Workload:
+    """The same keys in pool blocks of `block_size` rows ("DeepSeek-V4.1
+    native paged runtime": a block id names 16 index rows).
+
+    Each 64-row block of wl's pool is cut into 64 / block_size small blocks
+    and every small block moves to its own place in a new pool (a seeded
+    permutation), so the blocks one 64-entry stretch of a row reads lie
+    apart; the block table grows to name the small blocks.  A chunk list is
+    expanded the same way; with `ragged`, each row's small chunks are then
+    shuffled and a few dropped, so chunk counts are not multiples of
+    64 / block_size and one 64-column stretch mixes chunks of different
+    64-entry blocks.  Without a block table only block_size changes (rows
+    are entries).  Every key row keeps its bytes, so each logical entry
+    scores as it did in wl."""
+    bs = int(block_size)
+    if bs <= 0 or BLOCK % bs:
+        raise ValueError("block_size must divide 64")
+    U = BLOCK // bs
+    rng = np.random.default_rng(seed)
+    out = dataclasses.replace(wl, block_size=bs, name=name or f"{wl.name}-b{bs}",
+                              description=f"{wl.description}; {bs}-row blocks, seed {seed}")
+    if wl.block_table is not None:
+        n_small = wl.n_pool_rows // bs
+        perm = rng.permutation(n_small)
+        pool = np.empty_like(wl.pool)
+        pool.reshape(n_small, bs, -1)[perm] = wl.pool.reshape(n_small, bs, -1)
+        t = wl.block_table.astype(np.int64)
+        small = perm[np.maximum(t, 0)[:, :, None] * U + np.arange(U)]
+        table = np.where(t[:, :, None] >= 0, small, -1).reshape(t.shape[0], -1)
+        out.pool = pool
+        out.block_table = table.astype(np.int32)
+    if wl.chunk_ids is not None:
+        B, mc = wl.chunk_ids.shape
+        ids = np.full((B, mc * U), -1, dtype=np.int32)
+        counts = np.zeros(B, dtype=np.int32)
+        for b in range(B):
+            nc = min(int(wl.n_chunks[b]), mc)
+            c = wl.chunk_ids[b, :nc].astype(np.int64)
+            c = np.where(c[:, None] >= 0, c[:, None] * U + np.arange(U), -1).ravel()
+            if ragged and c.size:
+                c = c[rng.permutation(c.size)]
+                c = c[:c.size - int(rng.integers(0, min(2 * U, c.size) + 1))]
+            ids[b, :c.size] = c
+            counts[b] = c.size
+        out.chunk_ids = ids
+        out.n_chunks = counts
+    return out
+
+
 WORKLOAD_NAMES = {0: "tiny-decode", 1: "decode-batch", 2: "long-decode",
                   3: "chunked-prefill", 4: "resident-subset"}

@@ -92,7 +92,9 @@ def _score(lib, q=0x1000, w=0x1000, B=1, H=64, D=128, keys=None, n_cols=64, logi
     (dict(w=0x1008), L.IDX_E_ALIGN),
     (dict(logits=None), L.IDX_E_ARG),
     (dict(logits=0x3004), L.IDX_E_ALIGN),
-    (dict(keys=_keys(block_size=16)), L.IDX_E_SHAPE),
+    (dict(keys=_keys(block_size=32)), L.IDX_E_SHAPE),
+    (dict(keys=_keys(block_size=0)), L.IDX_E_SHAPE),
+    (dict(keys=_keys(block_size=16, block_table=0x4000, n_req=1, max_blocks=4, n_pool_rows=40)), L.IDX_E_SHAPE),
     (dict(keys=_keys(pool=0x1001)), L.IDX_E_ALIGN),
     (dict(keys=_keys(limits=None)), L.IDX_E_ARG),
     (dict(keys=_keys(block_table=0x4000, n_req=0, max_blocks=4)), L.IDX_E_SHAPE),

@@ -57,6 +57,9 @@ MUTANTS = {
     "q8-head-stride-wrong": ("const uint8_t *qrow = q8 + ((int64_t)b * H + h) * row_bytes;",
                              "const uint8_t *qrow = q8 + ((int64_t)b * H + h) * D;"),
     "level1-empty-pages-eligible": ("pr[p].rank = pr[p].density > 0 ? 1 : 0;", "pr[p].rank = 1;"),
+    "block-row-stride-64": ("prow = pblk * block_size + s;", "prow = pblk * 64 + s % 64;"),
+    "chunk-entry-stride-64": ("e = chunk_ids[(int64_t)b * max_chunks + j] * block_size + s;",
+                              "e = chunk_ids[(int64_t)b * max_chunks + j] * 64 + s;"),
 }
 
 PIN_TESTS = [
@@ -82,6 +85,8 @@ PIN_TESTS = [
     pins.test_level1_layer_order_and_single_layer,
     pins.test_quantised_query_equals_plain_query_when_quantisation_is_exact,
     pins.test_quantised_query_closed_form,
+    pins.test_16_row_blocks_are_a_relabelling,
+    pins.test_16_row_chunk_lists_read_the_listed_small_blocks,
 ]
 
 

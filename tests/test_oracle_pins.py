@@ -216,6 +216,45 @@ def test_paging_is_a_relabelling():
         assert np.array_equal(got, ref)
 
 
+def test_16_row_blocks_are_a_relabelling():
+    """The same keys in 16-row pool blocks, each moved to its own place
+    ("DeepSeek-V4.1 native paged runtime": a block id names 16 index rows):
+    every logical entry scores exactly as with 64-row blocks."""
+    for cfg in (0, 1, 2, 3):
+        wl = W.small_config(cfg)
+        wl16 = W.reblock(wl, seed=20 + cfg)
+        assert wl16.block_size == 16
+        assert np.array_equal(oracle.score(wl16), oracle.score(wl))
+
+
+def test_16_row_chunk_lists_read_the_listed_small_blocks():
+    """A chunk list of 16-row blocks, shuffled and ragged: column 16 j + s is
+    entry s of the j-th listed block.  Each column is looked up by hand in
+    the 64-row workload's logits (where entry e sits at column 64 i + e % 64
+    for the i-th listed chunk e // 64); columns past the list are -inf."""
+    wl = W.small_config(4)
+    ref = oracle.score(wl)
+    wl16 = W.reblock(wl, seed=24)
+    got = oracle.score(wl16)
+    assert got.shape == ref.shape
+    for b in range(wl.B):
+        where = {int(c): i for i, c in enumerate(wl.chunk_ids[b])}
+        n16 = int(wl16.n_chunks[b])
+        for j in range(n16):
+            c16 = int(wl16.chunk_ids[b, j])
+            for s_ in (0, 7, 15):
+                e = c16 * 16 + s_
+                assert got[b, 16 * j + s_] == ref[b, 64 * where[e // 64] + e % 64]
+        assert np.all(got[b, 16 * n16:] == -np.inf)
+    assert (wl16.n_chunks % 4 != 0).any()                 # some lists end inside a 64-column slot
+    # top-k ids map through the small blocks
+    ent, _, lg = oracle.score_topk(wl16)
+    cols, _ = oracle.topk(lg, wl16.k)
+    for b in range(wl16.B):
+        for c, e in zip(cols[b], ent[b]):
+            assert e == (-1 if c < 0 else wl16.chunk_ids[b][c // 16] * 16 + c % 16)
+
+
 def test_resident_subset_equals_masked_full_row():
     """Scoring a chunk list == scoring the full row with non-resident blocks
     absent (-inf), read at the listed chunks ("Two-level recall algorithm")."""

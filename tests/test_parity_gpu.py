@@ -37,8 +37,9 @@ def _entry_logit_fn(wl, ref_logits, rows=None):
             cols = ids
         else:
             row = b if rows is None else rows[b]
-            pos = {int(c): j for j, c in enumerate(wl.chunk_ids[row])}
-            cols = np.array([pos[int(e) // 64] * 64 + int(e) % 64 for e in ids])
+            bs = wl.block_size
+            pos = {int(c): j for j, c in enumerate(wl.chunk_ids[row][:wl.n_chunks[row]])}
+            cols = np.array([pos[int(e) // bs] * bs + int(e) % bs for e in ids], dtype=np.int64)
         return ref_logits[b, cols]
     return f
 

@@ -62,8 +62,9 @@ def _check_q8(wl, rows=None, tag=""):
         if wl.chunk_ids is None:
             return ref[b, ids]
         row = b if rows is None else rows[b]
-        pos = {int(c): j for j, c in enumerate(wl.chunk_ids[row])}
-        return ref[b, np.array([pos[int(e) // 64] * 64 + int(e) % 64 for e in ids])]
+        bs = wl.block_size
+        pos = {int(c): j for j, c in enumerate(wl.chunk_ids[row][:wl.n_chunks[row]])}
+        return ref[b, np.array([pos[int(e) // bs] * bs + int(e) % bs for e in ids], dtype=np.int64)]
     assert_topk_near_tie(g_idx[sel], ref_ids, logit_of, wl.k, f"{tag} q8")
 
 
