@@ -439,7 +439,9 @@ int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float 
     for (int l = 0; l < n_layers; ++l) {
         idx::ScoreArgs a = score_args(q[l], w[l], B, &keys[l], n_cols);
         a.ld = R.ld;
-        a.logits = reinterpret_cast<float *>(ws + R.logits);
+        // 64 heads: only the sigmoid scores are read later, so no logits
+        // are stored; 128 heads keep them for the second head half
+        a.logits = H == idx::kHeads ? nullptr : reinterpret_cast<float *>(ws + R.logits);
         a.scores = scores + (int64_t)l * B * R.ld;
         if ((e = launch_heads(a, H, s)) != hipSuccess) return hip_fail(e, "score kernel");
     }

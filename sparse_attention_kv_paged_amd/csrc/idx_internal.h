@@ -40,7 +40,7 @@ struct ScoreArgs {
     uint32_t *status;           // optional
     int32_t n_cols;             // columns per output row
     int64_t ld;                 // output row stride (floats)
-    float *logits;              // [B, ld]
+    float *logits;              // [B, ld], or null when only scores are wanted (not with accum)
     float *scores;              // [B, ld] or null
     // top-k feed (row_cols != null): only each row's own columns are written
     // (those below 64 x its tile-list length) and that count goes to row_cols

@@ -543,7 +543,9 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     constexpr int GS = 64 / U;                        // slots per group: one block per lane
     constexpr int TB = tile_bytes<BS>();
     const bool live = r.req >= 0 && j0 < r.nslots;
-    float *out_row = a.logits + (int64_t)b * a.ld;
+    // no logits buffer (scores only): the logit stores get an empty
+    // descriptor and are dropped
+    float *out_row = a.logits ? a.logits + (int64_t)b * a.ld : a.scores + (int64_t)b * a.ld;
     float *score_row = SCORES ? a.scores + (int64_t)b * a.ld : nullptr;
 
     // Start-up reads, issued back to back in the order they are needed (the
@@ -567,7 +569,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     // j of the group (one vector load per table level), then its tiles stream
     // through the wave's two-slot LDS ring.  Tiles of absent blocks and
     // ring slots past the group's end get an empty descriptor (no traffic).
-    const __amdgpu_buffer_rsrc_t out_r = make_rsrc(out_row, (uint32_t)col_end * 4u);
+    const __amdgpu_buffer_rsrc_t out_r = make_rsrc(out_row, a.logits ? (uint32_t)col_end * 4u : 0u);
     const __amdgpu_buffer_rsrc_t sc_r =
         make_rsrc(score_row ? score_row : out_row, score_row ? (uint32_t)col_end * 4u : 0u);
     const uint32_t lane_lo = tile_load_offset(lane);
@@ -909,6 +911,7 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEve
     if (a.B <= 0) return hipSuccess;
     if (a.accum && a.q8) return hipErrorInvalidValue;
     if (a.block_size != kBlock && a.block_size != kSmallBlock) return hipErrorInvalidValue;
+    if (!a.logits && (a.accum || !a.scores || a.row_cols)) return hipErrorInvalidValue;
     // the top-k feed (row_cols) never asks for scores
     const bool own = a.row_cols != nullptr;
     const bool scores = !own && a.scores != nullptr;
