@@ -8,8 +8,9 @@
 // Work decomposition: a workgroup is 4 independent waves on ONE query row;
 // wave w of split s owns `slots_per_wave` consecutive 64-entry slots of that
 // row's tile list ("DeepSeek-V4.1 native paged runtime", "Current execution
-// scope": per-row bound + per-row tile list read in place).  A slot is one
-// paged block, scored as two 32-entry tiles.
+// scope": per-row bound + per-row tile list read in place).  A slot is 64
+// entries -- one 64-row pool block, or four 16-row blocks (the same page's
+// index rows under 16-row block ids) -- scored as two 32-entry tiles.
 //
 // Per tile, on MFMA v_mfma_f32_32x32x16_bf16 with heads as the 32 rows and
 // entries as the 32 columns:

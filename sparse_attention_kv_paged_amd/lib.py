@@ -145,7 +145,7 @@ class Keys:
     chunk_ids: Optional[torch.Tensor] = None    # int32 [B, max_chunks]
     n_chunks: Optional[torch.Tensor] = None     # int32 [B]
     status: Optional[torch.Tensor] = None       # int32 [1] (bits OR-ed in)
-    block_size: int = 64
+    block_size: int = 64                        # rows per pool block: 64 or 16
 
     def struct(self) -> IdxKeys:
         pool = _dev(self.pool, torch.uint8, "pool")
