@@ -140,3 +140,25 @@ def test_b16_repeat_runs_are_bitwise_identical():
     b = L.idx_score_topk(d.q, d.w, d.keys, d.n_cols, wl.k)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))
+
+
+def test_b16_contiguous_pool_chunk_lists_and_unaligned_columns():
+    """Chunk lists of 16-row blocks over a contiguous pool (no block table):
+    21 listed blocks make 336 columns, not a multiple of a 64-column slot;
+    a shorter list, an empty one and a bound inside a listed block."""
+    wl = W.reblock(W.contiguous(2048, B=3, seed=75, name="b16-contig"), seed=76)
+    rng = np.random.default_rng(77)
+    wl.chunk_ids = np.stack([rng.choice(128, 21, replace=False) for _ in range(3)]).astype(np.int32)
+    wl.n_chunks = np.array([21, 17, 0], np.int32)
+    wl.chunk_ids[1, 17:] = -1
+    wl.limits = np.array([2048, 1000, 2048], np.int32)
+    wl.n_cols = 21 * 16
+    wl.k = 64
+    _check_workload(wl, tag="b16-contig-chunks")
+
+
+@pytest.mark.parametrize("k", [1, 2048])
+def test_b16_k_extremes(k):
+    wl = W.reblock(W.small_config(1), seed=78)
+    wl.k = k
+    _check_workload(wl, tag=f"b16-k{k}")
