@@ -195,8 +195,10 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H,
  *     logit = sum_h relu( sum_d k[d] * e4m3(q8[b,h,d]) * s_q[b,h] ) * w[b,h]
  *
  * (s_q >= 0, so relu(s_q x) = s_q relu(x) and the kernel folds s_q into w).
- * q8 is [B, H, D + 4] bytes, 4-byte aligned; every other argument, output
- * and rule is as for idx_score / idx_score_topk.
+ * q8 is [B, H, D + 4] bytes, 4-byte aligned, with H = 64 (128 heads are
+ * taken by the bf16 entry points only: IDX_E_SHAPE here); every other
+ * argument, output and rule, 16-row blocks included, is as for idx_score /
+ * idx_score_topk.
  */
 int idx_score_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H,
                  int32_t D, const idx_keys *keys, int32_t n_cols, float *logits,
