@@ -1,25 +1,39 @@
 """Benchmark of the CSA indexer hot path (score + top-512) on one MI355X.
 
-One step = one idx_score_topk call over the decode-batch workload (32 requests
-x 1 query, context lengths U[32k, 128k] tokens, N_b = L_b // 4 compressed
-entries in a shuffled paged pool of 64-entry blocks, top-512 per request).
-Inputs are resident in HBM before timing; the pool and q are replicated so
-consecutive steps read different copies (more bytes than the 256 MB MALL), and
-the K timed steps run as replays of a captured HIP graph so host launch cost
-stays out of the GPU timeline.
+By default one run measures all five scoring workloads and prints ONE JSON
+line whose headline is chunked prefill (4096 query rows of one request over a
+65,536-token prefix plus the chunk itself: 69.2 M scored pairs, the largest of
+the five by scored pairs and FLOP).  The line's `workloads` object holds every
+workload's own step time, pairs/s, queries/s and step-level fraction of its
+roofline (HBM for the decode shapes, bf16 MFMA for prefill) next to the
+target fraction, so one run's clock covers all five:
 
-Prints ONE JSON line.  `value` is scored (query, entry) pairs per second of
-the whole path; `roofline` covers the score kernel (the dominant kernel),
-timed live with HIP events that each launch's dispatch stamps with the
-kernel's start and end on the stream it runs on.
+  tiny-decode      B = 1, 2048 contiguous entries
+  decode-batch     B = 32, L_b ~ U[32k, 128k] tokens, N_b = L_b // 4, paged
+  long-decode      B = 8 x 262,144 entries (1M tokens), paged
+  resident-subset  B = 40 x 384 resident 64-entry chunks of 4096, chunk lists
+  chunked-prefill  4096 rows, causal bounds (65537 + i) // 4, 272 blocks
 
-`--workload index-fill` measures the index-plane writer instead: one step is
-one idx_write_keys call that quantises the 262,144 compressed keys of one
+One step = one idx_score_topk call.  Inputs are resident in HBM before timing;
+the pool and q are replicated so consecutive steps read different copies (more
+bytes than the 256 MB MALL), and the K timed steps run as replays of a
+captured HIP graph so host launch cost stays out of the GPU timeline.
+`value` is scored (query, entry) pairs per second of the whole path;
+`roofline` covers the score kernel (the dominant kernel), timed live with HIP
+events that each launch's dispatch stamps with the kernel's start and end on
+the stream it runs on.  Algorithmic bytes: one 132-byte key row per scored
+pair on the decode shapes (the request's rows once for prefill, whose rows
+share them), q, w, bounds, tables and chunk lists once, the output indices
+once; logits and candidate lists are overhead, not counted.
+
+`--workload NAME` measures one workload alone (its own line).
+`--workload index-fill` measures the index-plane writer: one step is one
+idx_write_keys call that quantises the 262,144 compressed keys of one
 1M-token request into a shuffled paged pool; `value` is keys written per
 second and `roofline` covers the writer kernel.
 
-`--q8` measures the quantised-query variant on any scoring workload: each
-step quantises q per head (the writer kernel) and runs idx_score_topk_q8; the
+`--q8` measures the quantised-query variant on a scoring workload: each step
+quantises q per head (the writer kernel) and runs idx_score_topk_q8; the
 prefill roofline is then priced at the fp8 MFMA peak.
 
 `--block-size 16` re-lays a scoring workload's pool into 16-row blocks, each
@@ -76,22 +90,43 @@ def score_source_hash(sources=SCORE_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
+SUITE = ["tiny-decode", "decode-batch", "long-decode", "resident-subset", "chunked-prefill"]
+HEADLINE = "chunked-prefill"
+# target fractions of the roofline for the whole score + top-k step
+TARGET_HBM_FRAC = 0.70            # decode shapes
+TARGET_MFMA_FRAC = 0.50           # prefill
+
+
+def shares_request_keys(wl) -> bool:
+    """Every query row reads the same request's blocks (prefill): the keys
+    are counted once, not once per row."""
+    return wl.q_req is not None and wl.block_table is not None and wl.block_table.shape[0] == 1
+
+
 def algorithmic_bytes(wl, pairs: int, q8: bool = False) -> int:
-    """Bytes the score kernel must move at minimum: one 132-byte key row per
-    scored (query, entry) pair for decode shapes (rows shared by every query
-    of a prefill request are counted once), one 4-byte logit written per
-    pair, plus q (bf16, or 132-byte quantised rows per head), w, bounds and
-    tables."""
-    if wl.q_req is not None and wl.block_table is not None and wl.block_table.shape[0] == 1:
-        keys = int((wl.block_table >= 0).sum()) * wl.block_size * 132   # one request
+    """Bytes the whole path must move at minimum: one 132-byte key row per
+    scored (query, entry) pair on the decode shapes (rows shared by every
+    query of a prefill request are counted once), q (bf16, or 132-byte
+    quantised rows per head), w, bounds, tables and chunk lists once, and the
+    selected indices written once.  Logits and candidate lists are overhead
+    of a particular kernel design and are not counted."""
+    if shares_request_keys(wl):
+        keys = int((wl.block_table >= 0).sum()) * wl.block_size * 132
     else:
         keys = pairs * 132
     q_bytes = wl.B * wl.H * (wl.D + 4) if q8 else wl.q.nbytes
-    extra = pairs * 4 + q_bytes + wl.w.nbytes + wl.limits.nbytes
+    extra = q_bytes + wl.w.nbytes + wl.limits.nbytes + wl.B * wl.k * 4
     for a in (wl.block_table, wl.q_req, wl.chunk_ids, wl.n_chunks):
         if a is not None:
             extra += a.nbytes
     return keys + extra
+
+
+def score_kernel_bytes(wl, pairs: int, q8: bool = False, logits_written: bool = True) -> int:
+    """Algorithmic bytes of one score-kernel launch taken alone (the roofline
+    of that kernel): the path's bytes without the indices, plus a 4-byte
+    logit per pair when the launch stores logits for a separate selection."""
+    return algorithmic_bytes(wl, pairs, q8) - wl.B * wl.k * 4 + (pairs * 4 if logits_written else 0)
 
 
 def _read_kv(path):
@@ -471,12 +506,14 @@ def bench_resident(args):
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
     wl = rl.layers[-1]
-    algo = algorithmic_bytes(wl, pairs_layer[-1]) + pairs_layer[-1] * 4     # + the scores written
+    algo = score_kernel_bytes(wl, pairs_layer[-1])      # one layer's launch, its scores stored
     roofline = {"kernel": "score_kernel", "bound": "hbm", "achieved": algo / (kern_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": read_traffic(RESIDENT_WORKLOAD),
                 "algorithmic_bytes": algo, "kernel_ms": kern_ms, **kern_spread}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
-    step_bytes = sum(algorithmic_bytes(w_, p_) + p_ * 4 for w_, p_ in zip(rl.layers, pairs_layer))
+    # the step: every layer's keys, q, w and tables once, the pages written
+    step_bytes = sum(score_kernel_bytes(w_, p_, logits_written=False) for w_, p_ in zip(rl.layers, pairs_layer))
+    step_bytes += rl.B * rl.kmax * 4
     out = {
         "metric": "Level-1 resident-set selection: scored pairs/s over all layers; % of HBM peak, 1 MI355X",
         "value": pairs / (ms_per_step * 1e-3),
@@ -522,8 +559,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=96)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode-batch",
-                    choices=sorted(WORKLOADS) + [WRITE_WORKLOAD, RESIDENT_WORKLOAD])
+    ap.add_argument("--workload", default="suite",
+                    choices=["suite"] + sorted(WORKLOADS) + [WRITE_WORKLOAD, RESIDENT_WORKLOAD],
+                    help="suite (default): all five scoring workloads in one run, headline chunked-prefill")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for >= 1 GB)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--q8", action="store_true",
@@ -573,16 +611,43 @@ def main():
         bench_resident(args)
         return
 
-    import numpy as np
     import torch
-    from sparse_attention_kv_paged_amd import lib, workloads
-
     torch.cuda.set_device(0)
-    cfg = WORKLOADS[args.workload]
+    names = SUITE if args.workload == "suite" else [args.workload]
+    results = {}
+    for name in names:
+        results[name] = measure_scoring(name, args)
+    head = HEADLINE if args.workload == "suite" else args.workload
+    out = results[head].pop("_line")
+    for r in results.values():
+        r.pop("_line", None)
+    if args.workload == "suite":
+        out["workloads"] = results
+    if not args.no_cpu_baseline:
+        from sparse_attention_kv_paged_amd import workloads
+        wl = scoring_workload(head, args, workloads)
+        out["cpu_baseline"] = cpu_baseline(wl, out["config"]["pairs"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def scoring_workload(name, args, workloads):
+    cfg = WORKLOADS[name]
     wl = workloads.config(cfg)
     if args.block_size != 64:
         wl = workloads.reblock(wl, seed=50 + cfg, block_size=args.block_size, name=f"{wl.name}-b{args.block_size}")
+    return wl
+
+
+def measure_scoring(name, args):
+    """K steps of idx_score_topk (or the quantised-query step) over one
+    scoring workload.  Returns the workload's summary; its "_line" entry is
+    the full JSON line for that workload alone."""
+    import torch
+    from sparse_attention_kv_paged_amd import lib, workloads
+
+    wl = scoring_workload(name, args, workloads)
     pairs = wl.pairs()
+    prof_name = wl.name + ("-q8" if args.q8 else "")
     print(f"[bench] workload {wl.name}: {wl.description}; pairs {pairs}", file=sys.stderr, flush=True)
     d = lib.to_device(wl)
     pool_bytes = d.keys.pool.numel()
@@ -596,8 +661,7 @@ def main():
     k = wl.k
     out_idx = torch.empty((wl.B, k), dtype=torch.int32, device="cuda")
     out_val = torch.empty((wl.B, k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(lib.workspace_bytes(lib.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, k),
-                     dtype=torch.uint8, device="cuda")
+    ws = lib.new_workspace(lib.workspace_bytes(lib.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, k), "cuda")
 
     if args.q8:
         q8 = torch.empty((wl.B, wl.H, wl.D + 4), dtype=torch.uint8, device="cuda")
@@ -625,26 +689,47 @@ def main():
         copy_calibration(args.copy_calibration)
 
     algo = algorithmic_bytes(wl, pairs, q8=args.q8)
+    kern_bytes = score_kernel_bytes(wl, pairs, q8=args.q8, logits_written=False)
+    flop = 2.0 * wl.H * wl.D * pairs
+    mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_BF16_PEAK_TFLOPS
     traffic = read_traffic(prof_name)
-    if args.workload == "chunked-prefill":
+    prefill = shares_request_keys(wl)
+    if prefill:
         # one request's keys are shared by every query: the contraction bounds it
-        flop = 2.0 * wl.H * wl.D * pairs
         roofline = {"kernel": "score_kernel", "bound": "mfma",
-                    "achieved": flop / (kern_ms * 1e-3) / 1e12,
-                    "peak": MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_BF16_PEAK_TFLOPS,
+                    "achieved": flop / (kern_ms * 1e-3) / 1e12, "peak": mfma_peak,
                     "unit": "TFLOP/s", "traffic": traffic, "algorithmic_flop": flop,
-                    "algorithmic_bytes": algo, "kernel_ms": kern_ms, **kern_spread}
+                    "algorithmic_bytes": kern_bytes, "kernel_ms": kern_ms, **kern_spread}
         # counters: the MFMA pipe's busy fraction and the clock the chip held
         busy, clock = read_mfma(prof_name)
         roofline["mfma_busy_frac"] = busy
         roofline["clock_ghz"] = clock
+        path = {"bound": "mfma", "frac": flop / (ms_per_step * 1e-3) / 1e12 / mfma_peak,
+                "target_frac": TARGET_MFMA_FRAC,
+                "target_ms": flop / (TARGET_MFMA_FRAC * mfma_peak * 1e12) * 1e3}
     else:
         roofline = {"kernel": "score_kernel", "bound": "hbm",
-                    "achieved": algo / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "traffic": traffic, "algorithmic_bytes": algo, "kernel_ms": kern_ms,
+                    "achieved": kern_bytes / (kern_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "traffic": traffic, "algorithmic_bytes": kern_bytes, "kernel_ms": kern_ms,
                     **kern_spread}
+        path = {"bound": "hbm", "frac": algo / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "target_frac": TARGET_HBM_FRAC if wl.name != "tiny-decode" else None,
+                "target_ms": algo / (TARGET_HBM_FRAC * HBM_PEAK_GBS * 1e9) * 1e3}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
-    out = {
+    summary = {
+        "ms_per_step": ms_per_step,
+        "pairs": pairs,
+        "queries": wl.B,
+        "pairs_per_s": pairs / (ms_per_step * 1e-3),
+        "queries_per_s": wl.B / (ms_per_step * 1e-3),
+        "algorithmic_bytes": algo,
+        "algorithmic_flop": flop,
+        "path": path,
+        "score_kernel_ms": kern_ms,
+        "score_kernel_ms_p50": kern_spread["kernel_ms_p50"],
+        "description": wl.description,
+    }
+    summary["_line"] = {
         "metric": "indexer scored pairs/s + top-512 queries/s; % of HBM/MFMA peak, 1 MI355X",
         "value": pairs / (ms_per_step * 1e-3),
         "unit": "pairs/s",
@@ -662,12 +747,13 @@ def main():
                    "block": wl.block_size, "k": k, "n_cols": wl.n_cols, "pairs": pairs,
                    "description": wl.description, "replicas": R, "graph": not args.no_graph},
         "queries_per_s": wl.B / (ms_per_step * 1e-3),
-        "path_hbm_frac": algo / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "path": path,
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, pairs, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    del pools, qs, keys, d, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return summary
 
 
 if __name__ == "__main__":

@@ -29,7 +29,9 @@
  *    stream) and returns before it finishes.  Bounds, block ids and chunk
  *    lists stay on the device, so calls can be captured in a HIP graph.
  *  - Supported shapes: H = 64 or 128 heads, D = 128, block_size = 64 or 16,
- *    1 <= k <= 2048.
+ *    1 <= k <= 2048, 1 <= n_cols <= IDX_MAX_COLS.  Every per-row array
+ *    (limits, q_req, n_chunks, and chunk_ids' rows) holds B entries: the
+ *    kernels read that many.
  *  - The return value is IDX_OK (0) or an IDX_E_* code; nothing is launched
  *    when a host-side check fails.  idx_last_error() gives a message for the
  *    calling thread's last failure.
@@ -75,6 +77,10 @@ enum idx_op { IDX_OP_SCORE = 0, IDX_OP_TOPK = 1, IDX_OP_SCORE_TOPK = 2 };
 #define IDX_BLOCK 64
 #define IDX_ROW_BYTES (IDX_HEAD_DIM + 4)
 #define IDX_MAX_K 2048
+/* Largest n_cols any call takes (2^27 columns = 2^29 tokens at C4): column
+ * byte offsets and the work index stay within 32 bits.  Larger values are
+ * rejected with IDX_E_SHAPE. */
+#define IDX_MAX_COLS (1 << 27)
 
 /*
  * The paged index plane and each query row's tile list.  Host struct holding

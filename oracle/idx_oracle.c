@@ -301,6 +301,16 @@ double oracle_sigmoid(double x)
     return 1.0 / (1.0 + exp(-x));
 }
 
+/* [FM] "Retriever architecture": score = sigmoid(logit), for a whole array
+ * of logits (an unscored column's -inf gives exp(+inf) = inf, so score 0). */
+void oracle_sigmoid_array(const double *x, int64_t n, double *out)
+{
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i)
+        out[i] = oracle_sigmoid(x[i]);
+}
+
 typedef struct {
     double v;
     int32_t c;

@@ -53,6 +53,8 @@ def _load():
     lib.oracle_logit.argtypes = [_c_u16p, _c_f32p, ctypes.c_int32, ctypes.c_int32, _c_u8p]
     lib.oracle_sigmoid.restype = ctypes.c_double
     lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+    lib.oracle_sigmoid_array.restype = None
+    lib.oracle_sigmoid_array.argtypes = [_c_f64p, ctypes.c_int64, _c_f64p]
     lib.oracle_score.restype = ctypes.c_int
     lib.oracle_score.argtypes = [
         _c_u16p, _c_f32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -118,9 +120,17 @@ def logit(q_row: np.ndarray, w_row: np.ndarray, key_row: np.ndarray) -> float:
 
 
 def sigmoid(x) -> np.ndarray:
-    lib = _load()
-    x = np.asarray(x, dtype=np.float64)
-    return np.vectorize(lambda v: lib.oracle_sigmoid(float(v)), otypes=[np.float64])(x)
+    """The oracle's sigmoid of each logit (double); -inf gives 0."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    _load().oracle_sigmoid_array(_ptr(x.reshape(-1), ctypes.c_double), x.size,
+                                 _ptr(out.reshape(-1), ctypes.c_double))
+    return out
+
+
+def sigmoid_scalar(x: float) -> float:
+    """The oracle's scalar sigmoid (the function the array form applies)."""
+    return float(_load().oracle_sigmoid(float(x)))
 
 
 def _i32(a):

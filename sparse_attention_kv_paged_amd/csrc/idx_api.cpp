@@ -247,6 +247,12 @@ idx::ScoreArgs score_args(const uint16_t *q, const float *w, int32_t B, const id
     return a;
 }
 
+int check_cols(int32_t n_cols) {
+    if (n_cols < 1 || n_cols > IDX_MAX_COLS)
+        return fail(IDX_E_SHAPE, "n_cols must be in [1, %d] (got %d)", IDX_MAX_COLS, n_cols);
+    return IDX_OK;
+}
+
 int hip_fail(hipError_t e, const char *what) {
     return fail(IDX_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -288,7 +294,7 @@ int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, 
     int rc = check_qw8(q, q8, w, B, H, D);
     if (rc) return rc;
     if ((rc = check_keys(keys, B))) return rc;
-    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if ((rc = check_cols(n_cols))) return rc;
     if (B == 0) return IDX_OK;
     if (q8 == nullptr && q == nullptr) return fail(IDX_E_ARG, "q must be non-null");
     if (!logits) return fail(IDX_E_ARG, "logits must be non-null");
@@ -309,7 +315,7 @@ int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_
     int rc = check_qw8(q, q8, w, B, H, D);
     if (rc) return rc;
     if ((rc = check_keys(keys, B))) return rc;
-    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if ((rc = check_cols(n_cols))) return rc;
     if (k < 1 || k > idx::kMaxK) return fail(IDX_E_SHAPE, "k must be in [1, 2048] (got %d)", k);
     if (B == 0) return IDX_OK;
     if (q8 == nullptr && q == nullptr) return fail(IDX_E_ARG, "q must be non-null");
@@ -362,7 +368,8 @@ int idx_profile_events(void *before, void *after) {
 }
 
 size_t idx_workspace_bytes(int32_t op, int32_t B, int32_t n_cols, int32_t k) {
-    if (B < 0 || n_cols < 0 || (op != IDX_OP_SCORE && (k < 1 || k > idx::kMaxK))) return (size_t)-1;
+    if (B < 0 || n_cols < 0 || n_cols > IDX_MAX_COLS || (op != IDX_OP_SCORE && (k < 1 || k > idx::kMaxK)))
+        return (size_t)-1;
     switch (op) {
     case IDX_OP_SCORE: return 0;
     case IDX_OP_TOPK: return topk_plan(false, B, n_cols, k).total;
@@ -385,6 +392,7 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t
              float *out_val, void *workspace, size_t ws_bytes, void *stream) {
     g_last_error[0] = 0;
     if (B < 0 || n_cols < 1 || ld < n_cols) return fail(IDX_E_SHAPE, "need B >= 0, n_cols >= 1, ld >= n_cols");
+    if (check_cols(n_cols)) return IDX_E_SHAPE;
     if (k < 1 || k > idx::kMaxK) return fail(IDX_E_SHAPE, "k must be in [1, 2048] (got %d)", k);
     if (B == 0) return IDX_OK;
     if (!logits || !out_col) return fail(IDX_E_ARG, "logits and out_col must be non-null");
@@ -400,7 +408,8 @@ int idx_topk(const float *logits, int32_t B, int32_t n_cols, int64_t ld, int32_t
 }
 
 size_t idx_resident_workspace_bytes(int32_t n_layers, int32_t B, int32_t n_cols, int32_t kmax) {
-    if (n_layers < 1 || n_layers > IDX_MAX_LAYERS || B < 0 || n_cols < 1 || kmax < 1 || kmax > idx::kMaxK)
+    if (n_layers < 1 || n_layers > IDX_MAX_LAYERS || B < 0 || n_cols < 1 || n_cols > IDX_MAX_COLS || kmax < 1 ||
+        kmax > idx::kMaxK)
         return (size_t)-1;
     return resident_plan(n_layers, B, n_cols, kmax).total;
 }
@@ -412,7 +421,7 @@ int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float 
     if (n_layers < 1 || n_layers > IDX_MAX_LAYERS)
         return fail(IDX_E_SHAPE, "n_layers must be in [1, %d] (got %d)", IDX_MAX_LAYERS, n_layers);
     if (!q || !w || !keys || !cfg) return fail(IDX_E_ARG, "q, w, keys and cfg must be non-null");
-    if (n_cols < 1) return fail(IDX_E_SHAPE, "n_cols must be >= 1 (got %d)", n_cols);
+    if (check_cols(n_cols)) return IDX_E_SHAPE;
     if (cfg->ensemble != IDX_ENSEMBLE_MAX && cfg->ensemble != IDX_ENSEMBLE_MEAN)
         return fail(IDX_E_ARG, "ensemble must be IDX_ENSEMBLE_MAX or IDX_ENSEMBLE_MEAN");
     if (!(cfg->threshold == cfg->threshold)) return fail(IDX_E_ARG, "threshold is NaN");

@@ -24,6 +24,7 @@ STATUS_LIMIT_CLAMPED, STATUS_BAD_BLOCK, STATUS_BAD_REQUEST, STATUS_BAD_CHUNK = 1
 STATUS_BAD_SLOT = 16
 ENSEMBLE_MAX, ENSEMBLE_MEAN = 0, 1
 MAX_LAYERS = 8
+MAX_COLS = 1 << 27                # IDX_MAX_COLS
 
 EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_score_q8", "idx_score_topk_q8",
            "idx_write_keys", "idx_select_resident",
@@ -147,10 +148,31 @@ class Keys:
     status: Optional[torch.Tensor] = None       # int32 [1] (bits OR-ed in)
     block_size: int = 64                        # rows per pool block: 64 or 16
 
-    def struct(self) -> IdxKeys:
+    def struct(self, B: int) -> IdxKeys:
+        """The C struct for a call over B query rows.  Every per-row tensor
+        must hold B rows: the kernels size their reads from B, so a short one
+        is rejected here instead of being read past its end."""
         pool = _dev(self.pool, torch.uint8, "pool")
         bt = _dev(self.block_table, torch.int32, "block_table")
         ci = _dev(self.chunk_ids, torch.int32, "chunk_ids")
+        limits = _dev(self.limits, torch.int32, "limits")
+        q_req = _dev(self.q_req, torch.int32, "q_req")
+        n_chunks = _dev(self.n_chunks, torch.int32, "n_chunks")
+        status = _dev(self.status, torch.int32, "status")
+        if pool.dim() != 2:
+            raise ValueError("pool must be [n_pool_rows, D + 4]")
+        for name, t in (("limits", limits), ("q_req", q_req), ("n_chunks", n_chunks)):
+            if t is not None and (t.dim() != 1 or t.shape[0] != B):
+                raise ValueError(f"{name} must hold one int32 per query row ({B}), got shape {tuple(t.shape)}")
+        if bt is not None and bt.dim() != 2:
+            raise ValueError("block_table must be [n_req, max_blocks]")
+        if ci is not None:
+            if ci.dim() != 2 or ci.shape[0] != B:
+                raise ValueError(f"chunk_ids must be [{B}, max_chunks], got shape {tuple(ci.shape)}")
+            if n_chunks is None:
+                raise ValueError("n_chunks is required with chunk_ids")
+        if status is not None and status.numel() < 1:
+            raise ValueError("status must hold at least one int32")
         k = IdxKeys()
         k.pool = pool.data_ptr()
         k.n_pool_rows = pool.shape[0]
@@ -159,11 +181,11 @@ class Keys:
         k.block_table = None if bt is None else bt.data_ptr()
         k.max_blocks = 0 if bt is None else bt.shape[1]
         k.max_chunks = 0 if ci is None else ci.shape[1]
-        k.q_req = None if self.q_req is None else _dev(self.q_req, torch.int32, "q_req").data_ptr()
+        k.q_req = None if q_req is None else q_req.data_ptr()
         k.chunk_ids = None if ci is None else ci.data_ptr()
-        k.n_chunks = None if self.n_chunks is None else _dev(self.n_chunks, torch.int32, "n_chunks").data_ptr()
-        k.limits = _dev(self.limits, torch.int32, "limits").data_ptr()
-        k.status = None if self.status is None else _dev(self.status, torch.int32, "status").data_ptr()
+        k.n_chunks = None if n_chunks is None else n_chunks.data_ptr()
+        k.limits = limits.data_ptr()
+        k.status = None if status is None else status.data_ptr()
         return k
 
 
@@ -186,8 +208,15 @@ def idx_workspace_bytes(op: int, B: int, n_cols: int, k: int) -> int:
     return workspace_bytes(op, B, n_cols, k)
 
 
+def new_workspace(n: int, device="cuda") -> torch.Tensor:
+    """A device workspace of n bytes, zeroed (the library's per-row arrival
+    counters must read zero on a workspace's first use; every call leaves
+    them zero)."""
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+
+
 def _workspace(n: int, device) -> torch.Tensor:
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return new_workspace(n, device)
 
 
 def _qw(q, w):
@@ -212,7 +241,7 @@ def idx_score(q, w, keys: Keys, n_cols: int, with_scores: bool = False,
         scores = torch.empty((B, n_cols), dtype=torch.float32, device=q.device)
     _dev(logits, torch.float32, "logits")
     _dev(scores, torch.float32, "scores")
-    ks = keys.struct()
+    ks = keys.struct(B)
     _check(load().idx_score(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols,
                             _ptr(logits), _ptr(scores), _stream(stream)))
     return (logits, scores) if with_scores else logits
@@ -250,7 +279,7 @@ def idx_score_topk(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=
     need = workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k)
     if workspace is None:
         workspace = _workspace(need, q.device)
-    ks = keys.struct()
+    ks = keys.struct(B)
     _check(load().idx_score_topk(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
                                  _ptr(out_idx), _ptr(out_val), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
@@ -289,7 +318,7 @@ def idx_score_q8(q8, w, keys: Keys, n_cols: int, with_scores: bool = False,
         scores = torch.empty((B, n_cols), dtype=torch.float32, device=q8.device)
     _dev(logits, torch.float32, "logits")
     _dev(scores, torch.float32, "scores")
-    ks = keys.struct()
+    ks = keys.struct(B)
     _check(load().idx_score_q8(_ptr(q8), _ptr(w), B, H, D4 - 4, ctypes.byref(ks), n_cols,
                                _ptr(logits), _ptr(scores), _stream(stream)))
     return (logits, scores) if with_scores else logits
@@ -307,7 +336,7 @@ def idx_score_topk_q8(q8, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_
     need = workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k)
     if workspace is None:
         workspace = _workspace(need, q8.device)
-    ks = keys.struct()
+    ks = keys.struct(B)
     _check(load().idx_score_topk_q8(_ptr(q8), _ptr(w), B, H, D4 - 4, ctypes.byref(ks), n_cols, k,
                                     _ptr(out_idx), _ptr(out_val), _ptr(workspace), workspace.numel(),
                                     _stream(stream)))
@@ -366,7 +395,7 @@ def idx_select_resident(qs, ws, keys_list, n_cols: int, kmax: int, ensemble: int
         workspace = _workspace(need, dev)
     qa = (ctypes.c_void_p * L)(*[q.data_ptr() for q, _ in pairs])
     wa = (ctypes.c_void_p * L)(*[w.data_ptr() for _, w in pairs])
-    ka = (IdxKeys * L)(*[k.struct() for k in keys_list])
+    ka = (IdxKeys * L)(*[k.struct(B) for k in keys_list])
     cfg = ResidentCfg(ensemble, threshold, n_sink, n_recent, kmax)
     _check(load().idx_select_resident(L, qa, wa, B, H, D, ka, n_cols, ctypes.byref(cfg), _ptr(out_pages),
                                       _ptr(out_count), _ptr(workspace), workspace.numel(), _stream(stream)))

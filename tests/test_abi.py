@@ -87,6 +87,8 @@ def _score(lib, q=0x1000, w=0x1000, B=1, H=64, D=128, keys=None, n_cols=64, logi
     (dict(D=64), L.IDX_E_SHAPE),
     (dict(B=-1), L.IDX_E_ARG),
     (dict(n_cols=0), L.IDX_E_SHAPE),
+    (dict(n_cols=L.MAX_COLS + 1), L.IDX_E_SHAPE),
+    (dict(n_cols=-5), L.IDX_E_SHAPE),
     (dict(q=None), L.IDX_E_ARG),
     (dict(q=0x1004), L.IDX_E_ALIGN),
     (dict(w=0x1008), L.IDX_E_ALIGN),
@@ -255,3 +257,25 @@ def test_h128_accepted_for_bf16_rejected_for_q8(lib):
     assert lib.idx_score_q8(0x1004, 0x2000, 1, 128, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_SHAPE
     # 128 heads pass every host check (B = 0 returns before any launch)
     assert _score(lib, H=128, B=0, q=None, w=None, logits=None) == L.IDX_OK
+
+
+def test_column_limit(lib):
+    """n_cols above IDX_MAX_COLS (2^27: column byte offsets and the work index
+    stay within 32 bits) is refused by every entry point, before anything is
+    launched; the limit itself is accepted by the workspace query."""
+    assert L.MAX_COLS == 1 << 27
+    big = L.MAX_COLS + 1
+    keys = _keys()
+    assert lib.idx_score_topk(0x1000, 0x1000, 1, 64, 128, ctypes.byref(keys), big, 16, 0x2000, None,
+                              0x10000, 1 << 40, None) == L.IDX_E_SHAPE
+    assert lib.idx_score_q8(0x1000, 0x1000, 1, 64, 128, ctypes.byref(keys), big, 0x3000, None, None) == L.IDX_E_SHAPE
+    assert lib.idx_topk(0x1000, 1, big, big, 16, 0x2000, None, 0x10000, 1 << 40, None) == L.IDX_E_SHAPE
+    assert lib.idx_workspace_bytes(L.IDX_OP_SCORE_TOPK, 1, big, 16) == ctypes.c_size_t(-1).value
+    assert lib.idx_workspace_bytes(L.IDX_OP_TOPK, 1, L.MAX_COLS, 16) != ctypes.c_size_t(-1).value
+    assert lib.idx_resident_workspace_bytes(1, 1, big, 16) == ctypes.c_size_t(-1).value
+    qa = (ctypes.c_void_p * 1)(0x1000)
+    wa = (ctypes.c_void_p * 1)(0x1000)
+    ka = (L.IdxKeys * 1)(keys)
+    cfg = L.ResidentCfg(0, 0.5, 0, 0, 16)
+    assert lib.idx_select_resident(1, qa, wa, 1, 64, 128, ka, big, ctypes.byref(cfg), 0x2000, None,
+                                   0x10000, 1 << 40, None) == L.IDX_E_SHAPE

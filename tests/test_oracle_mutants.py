@@ -58,6 +58,8 @@ MUTANTS = {
                              "const uint8_t *qrow = q8 + ((int64_t)b * H + h) * D;"),
     "level1-empty-pages-eligible": ("pr[p].rank = pr[p].density > 0 ? 1 : 0;", "pr[p].rank = 1;"),
     "block-row-stride-64": ("prow = pblk * block_size + s;", "prow = pblk * 64 + s % 64;"),
+    "sigmoid-sign-flipped": ("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
+    "sigmoid-half-slope": ("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(-0.5 * x));"),
     "chunk-entry-stride-64": ("e = chunk_ids[(int64_t)b * max_chunks + j] * block_size + s;",
                               "e = chunk_ids[(int64_t)b * max_chunks + j] * 64 + s;"),
 }
@@ -87,6 +89,7 @@ PIN_TESTS = [
     pins.test_quantised_query_closed_form,
     pins.test_16_row_blocks_are_a_relabelling,
     pins.test_16_row_chunk_lists_read_the_listed_small_blocks,
+    pins.test_sigmoid_values_closed_form,
 ]
 
 

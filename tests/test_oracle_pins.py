@@ -355,6 +355,29 @@ def test_topk_on_sigmoid_equals_topk_on_logits():
     assert np.array_equal(c1, c2)
 
 
+def test_sigmoid_values_closed_form():
+    """The logistic function's values fixed by the mathematics ([FM]
+    "Retriever architecture": score = sigmoid(logit)): sigma(0) = 1/2,
+    sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4, sigma(ln 2) = 2/3, sigma(ln 9) =
+    9/10, sigma(+inf) = 1, sigma(-inf) = 0 (an unscored column's score), and
+    sigma(x) + sigma(-x) = 1; the array form the tests compare GPU scores
+    against applies the scalar form element by element."""
+    import math
+    assert oracle.sigmoid_scalar(0.0) == 0.5
+    for x, want in [(math.log(3.0), 0.75), (-math.log(3.0), 0.25), (math.log(2.0), 2.0 / 3.0),
+                    (-math.log(2.0), 1.0 / 3.0), (math.log(9.0), 0.9)]:
+        assert abs(oracle.sigmoid_scalar(x) - want) <= 4e-16, (x, oracle.sigmoid_scalar(x), want)
+    xs = np.array([-np.inf, -30.0, -math.log(3.0), -1.0, 0.0, 0.5, math.log(3.0), 30.0, np.inf])
+    s = oracle.sigmoid(xs)
+    assert s[0] == 0.0 and s[-1] == 1.0 and s[4] == 0.5
+    assert abs(s[2] - 0.25) <= 4e-16 and abs(s[6] - 0.75) <= 4e-16
+    assert np.all(np.abs(s + oracle.sigmoid(-xs) - 1.0) <= 1e-15)
+    assert np.array_equal(s, np.array([oracle.sigmoid_scalar(v) for v in xs]))
+    grid = np.linspace(-8.0, 8.0, 4097).reshape(17, 241)
+    sg = oracle.sigmoid(grid)
+    assert sg.shape == grid.shape and np.all(np.diff(sg.reshape(-1)) > 0)
+
+
 def test_topk_merge_associativity():
     """top-k(A u B) == top-k(top-k(A) u top-k(B)): the rule a cross-block merge
     relies on."""
