@@ -150,8 +150,8 @@ class Keys:
 
     def struct(self, B: int) -> IdxKeys:
         """The C struct for a call over B query rows.  Every per-row tensor
-        must hold B rows: the kernels size their reads from B, so a short one
-        is rejected here instead of being read past its end."""
+        must hold at least B rows: the kernels read rows 0 .. B - 1, so a
+        short one is rejected here instead of being read past its end."""
         pool = _dev(self.pool, torch.uint8, "pool")
         bt = _dev(self.block_table, torch.int32, "block_table")
         ci = _dev(self.chunk_ids, torch.int32, "chunk_ids")
@@ -162,12 +162,12 @@ class Keys:
         if pool.dim() != 2:
             raise ValueError("pool must be [n_pool_rows, D + 4]")
         for name, t in (("limits", limits), ("q_req", q_req), ("n_chunks", n_chunks)):
-            if t is not None and (t.dim() != 1 or t.shape[0] != B):
+            if t is not None and (t.dim() != 1 or t.shape[0] < B):
                 raise ValueError(f"{name} must hold one int32 per query row ({B}), got shape {tuple(t.shape)}")
         if bt is not None and bt.dim() != 2:
             raise ValueError("block_table must be [n_req, max_blocks]")
         if ci is not None:
-            if ci.dim() != 2 or ci.shape[0] != B:
+            if ci.dim() != 2 or ci.shape[0] < B:
                 raise ValueError(f"chunk_ids must be [{B}, max_chunks], got shape {tuple(ci.shape)}")
             if n_chunks is None:
                 raise ValueError("n_chunks is required with chunk_ids")
