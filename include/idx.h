@@ -183,6 +183,29 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H,
                    size_t ws_bytes, void *stream);
 
 /*
+ * idx_score_topk_noalloc: idx_score_topk for callers that cannot allocate
+ * device memory -- code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, rules and results as
+ * idx_score_topk, without the workspace: the library's own static device
+ * scratch of IDX_STATIC_SCRATCH_BYTES (16 MiB) takes its place.  Each GPU the
+ * library runs on holds one such scratch from the first call on it until the
+ * process ends.  Calls whose workspace would exceed it
+ * (idx_workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k) > 16 MiB: every
+ * decode shape up to 8 rows x 262,144 columns fits, a 4096-row prefill does
+ * not) return IDX_E_WORKSPACE before anything is launched.  The call itself
+ * allocates nothing; its first call on a device looks up that device's
+ * scratch address.  Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's contents: calls that overlap on one GPU (other
+ * streams, other threads) race and must not be issued.
+ */
+#define IDX_STATIC_SCRATCH_BYTES (16u << 20)
+
+int idx_score_topk_noalloc(const uint16_t *q, const float *w, int32_t B,
+                           int32_t H, int32_t D, const idx_keys *keys,
+                           int32_t n_cols, int32_t k, int32_t *out_idx,
+                           float *out_val, void *stream);
+
+/*
  * idx_score_q8 / idx_score_topk_q8: the same path with the query quantised
  * to e4m3 as well, so that the contraction runs on fp8 MFMA with both
  * operands taken as stored.  The pages' deployed indexers quantise the

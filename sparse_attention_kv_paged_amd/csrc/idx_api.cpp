@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/idx.h"
 #include "idx_internal.h"
@@ -308,10 +309,11 @@ int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, 
     return e == hipSuccess ? IDX_OK : hip_fail(e, "score kernel");
 }
 
-int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
-                    const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
-                    void *workspace, size_t ws_bytes, void *stream) {
-    g_last_error[0] = 0;
+// Host-side checks of a score + top-k call; on success P is its plan.  A
+// call with B == 0 passes with an empty plan (nothing to launch).
+int score_topk_check(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
+                     const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
+                     TopkPlan &P) {
     int rc = check_qw8(q, q8, w, B, H, D);
     if (rc) return rc;
     if ((rc = check_keys(keys, B))) return rc;
@@ -321,11 +323,14 @@ int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_
     if (q8 == nullptr && q == nullptr) return fail(IDX_E_ARG, "q must be non-null");
     if (!out_idx) return fail(IDX_E_ARG, "out_idx must be non-null");
     if (!aligned(out_idx, 4) || !aligned(out_val, 4)) return fail(IDX_E_ALIGN, "outputs must be 4-byte aligned");
-    const TopkPlan P = topk_plan(true, B, n_cols, k);
-    if (P.total > 0 && (!workspace || ws_bytes < P.total))
-        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
-    if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
-    char *ws = static_cast<char *>(workspace);
+    P = topk_plan(true, B, n_cols, k);
+    return IDX_OK;
+}
+
+// Enqueue a checked score + top-k call (B > 0) on a workspace of P.total bytes.
+int score_topk_launch(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H,
+                      const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
+                      const TopkPlan &P, char *ws, void *stream) {
     idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
     a.q8 = q8;
     a.ld = P.ld;
@@ -339,6 +344,52 @@ int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_
     e = enqueue_topk(P, ws, a.logits, P.ld, a.row_cols, B, n_cols, k, out_idx, out_val,
                      keys->chunk_ids, keys->max_chunks, keys->block_size == idx::kSmallBlock ? 4 : 6, s);
     return e == hipSuccess ? IDX_OK : hip_fail(e, "top-k");
+}
+
+int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
+                    const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
+                    void *workspace, size_t ws_bytes, void *stream) {
+    g_last_error[0] = 0;
+    TopkPlan P;
+    int rc = score_topk_check(q, q8, w, B, H, D, keys, n_cols, k, out_idx, out_val, P);
+    if (rc || B == 0) return rc;
+    if (P.total > 0 && (!workspace || ws_bytes < P.total))
+        return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
+    if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
+    return score_topk_launch(q, q8, w, B, H, keys, n_cols, k, out_idx, out_val, P, static_cast<char *>(workspace),
+                             stream);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: a file-scope device array that
+// holds idx_score_topk's workspace.  Every GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` is a host-side
+// stand-in, not a device address: the address kernels may use comes from
+// hipGetSymbolAddress, taken once per device with that device current and
+// kept in g_scratch_ptr.  Nothing in it must start at zero (the score kernel
+// clears the per-row counters the top-k's in-launch merge uses), and every
+// call on a GPU overwrites what the last one left there.
+static __device__ __align__(256) uint8_t scratch[IDX_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(IDX_E_ARG, "device %d is beyond the %d this library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static scratch");
+        if (!p || !aligned(p, 256)) return fail(IDX_E_HIP, "the static scratch has no 256-byte aligned device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return IDX_OK;
 }
 
 }  // namespace
@@ -504,6 +555,24 @@ int idx_score_topk(const uint16_t *q, const float *w, int32_t B, int32_t H, int3
                    void *workspace, size_t ws_bytes, void *stream) {
     return score_topk_impl(q, nullptr, w, B, H, D, keys, n_cols, k, out_idx, out_val, workspace, ws_bytes,
                            stream);
+}
+
+int idx_score_topk_noalloc(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D,
+                           const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
+                           void *stream) {
+    g_last_error[0] = 0;
+    TopkPlan P;
+    int rc = score_topk_check(q, nullptr, w, B, H, D, keys, n_cols, k, out_idx, out_val, P);
+    if (rc || B == 0) return rc;
+    if (P.total > (size_t)IDX_STATIC_SCRATCH_BYTES)
+        return fail(IDX_E_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(call idx_score_topk with a workspace instead)",
+                    P.total, (size_t)IDX_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((rc = static_scratch(&ws))) return rc;
+    return score_topk_launch(q, nullptr, w, B, H, keys, n_cols, k, out_idx, out_val, P, static_cast<char *>(ws),
+                             stream);
 }
 
 int idx_score_topk_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,

@@ -25,8 +25,9 @@ STATUS_BAD_SLOT = 16
 ENSEMBLE_MAX, ENSEMBLE_MEAN = 0, 1
 MAX_LAYERS = 8
 MAX_COLS = 1 << 27                # IDX_MAX_COLS
+STATIC_SCRATCH_BYTES = 16 << 20   # IDX_STATIC_SCRATCH_BYTES
 
-EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_score_q8", "idx_score_topk_q8",
+EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_score_topk_noalloc", "idx_score_q8", "idx_score_topk_q8",
            "idx_write_keys", "idx_select_resident",
            "idx_resident_workspace_bytes", "idx_workspace_bytes",
            "idx_error_string", "idx_last_error", "idx_profile_events", "idx_abi_version")
@@ -86,6 +87,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.idx_topk.restype = ctypes.c_int
     lib.idx_score_topk.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
     lib.idx_score_topk.restype = ctypes.c_int
+    lib.idx_score_topk_noalloc.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp]
+    lib.idx_score_topk_noalloc.restype = ctypes.c_int
     lib.idx_score_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, vp, vp, vp]
     lib.idx_score_q8.restype = ctypes.c_int
     lib.idx_score_topk_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
@@ -283,6 +286,23 @@ def idx_score_topk(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=
     _check(load().idx_score_topk(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
                                  _ptr(out_idx), _ptr(out_val), _ptr(workspace),
                                  workspace.numel(), _stream(stream)))
+    return out_idx, out_val
+
+
+def idx_score_topk_noalloc(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=None, stream=None):
+    """idx_score_topk on the library's static device scratch (no workspace;
+    the call allocates nothing when out_idx and out_val are passed in)."""
+    q, w = _qw(q, w)
+    B, H, D = q.shape
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    if out_val is None:
+        out_val = torch.empty((B, k), dtype=torch.float32, device=q.device)
+    _dev(out_idx, torch.int32, "out_idx")
+    _dev(out_val, torch.float32, "out_val")
+    ks = keys.struct(B)
+    _check(load().idx_score_topk_noalloc(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
+                                         _ptr(out_idx), _ptr(out_val), _stream(stream)))
     return out_idx, out_val
 
 

@@ -279,3 +279,24 @@ def test_column_limit(lib):
     cfg = L.ResidentCfg(0, 0.5, 0, 0, 16)
     assert lib.idx_select_resident(1, qa, wa, 1, 64, 128, ka, big, ctypes.byref(cfg), 0x2000, None,
                                    0x10000, 1 << 40, None) == L.IDX_E_SHAPE
+
+
+def test_noalloc_rejects_calls_beyond_the_static_scratch(lib):
+    """The allocation-free entry point refuses, before touching a device, a
+    call whose workspace exceeds the static scratch (a 4096-row prefill), and
+    checks its arguments like idx_score_topk."""
+    assert L.STATIC_SCRATCH_BYTES == 16 << 20
+    keys = _keys(n_pool_rows=64 * 272, block_table=0x4000, n_req=1, max_blocks=272)
+    assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 4096, 17408, 512) > L.STATIC_SCRATCH_BYTES
+    rc = lib.idx_score_topk_noalloc(0x1000, 0x1000, 4096, 64, 128, ctypes.byref(keys), 17408, 512, 0x2000, None, None)
+    assert rc == L.IDX_E_WORKSPACE and b"static scratch" in lib.idx_last_error()
+    rc = lib.idx_score_topk_noalloc(0x1000, 0x1000, 1, 64, 128, ctypes.byref(_keys()), 64, 4096, 0x2000, None, None)
+    assert rc == L.IDX_E_SHAPE
+    rc = lib.idx_score_topk_noalloc(0x1000, 0x1000, 1, 32, 128, ctypes.byref(_keys()), 64, 16, 0x2000, None, None)
+    assert rc == L.IDX_E_SHAPE
+    rc = lib.idx_score_topk_noalloc(0x1000, 0x1000, 1, 64, 128, ctypes.byref(_keys()), 64, 16, None, None, None)
+    assert rc == L.IDX_E_ARG
+    assert lib.idx_score_topk_noalloc(None, None, 0, 64, 128, ctypes.byref(_keys()), 64, 16, None, None, None) == L.IDX_OK
+    # the decode shapes fit
+    for B, n in [(32, 32768), (8, 262144), (40, 24576)]:
+        assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, B, n, 512) <= L.STATIC_SCRATCH_BYTES
