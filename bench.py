@@ -487,8 +487,7 @@ def bench_resident(args):
     pairs = int(sum(pairs_layer))
     out_pages = torch.empty((rl.B, rl.kmax), dtype=torch.int32, device="cuda")
     out_count = torch.empty(rl.B, dtype=torch.int32, device="cuda")
-    ws = torch.empty(lib.resident_workspace_bytes(len(dls), rl.B, rl.n_cols, rl.kmax), dtype=torch.uint8,
-                     device="cuda")
+    ws = lib.new_workspace(lib.resident_workspace_bytes(len(dls), rl.B, rl.n_cols, rl.kmax), "cuda")
 
     def step(i):
         lib.idx_select_resident([d.q for d in dls], [d.w for d in dls], [d.keys for d in dls], rl.n_cols,

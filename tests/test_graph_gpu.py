@@ -77,7 +77,7 @@ def test_score_topk_replays(name, wl):
     d = L.to_device(wl)
     out_idx = torch.empty((wl.B, wl.k), dtype=torch.int32, device="cuda")
     out_val = torch.empty((wl.B, wl.k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(L.workspace_bytes(L.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, wl.k), dtype=torch.uint8, device="cuda")
+    ws = L.new_workspace(L.workspace_bytes(L.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, wl.k), "cuda")
     q2 = _other_q(d, 1)
     o2 = (torch.empty_like(out_idx), torch.empty_like(out_val))
 
@@ -111,7 +111,7 @@ def test_topk_replays(n, k):
     lg = torch.from_numpy(rng.standard_normal((3, n), dtype=np.float32)).cuda()
     oc = torch.empty((3, k), dtype=torch.int32, device="cuda")
     ov = torch.empty((3, k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(L.workspace_bytes(L.IDX_OP_TOPK, 3, n, k), 1), dtype=torch.uint8, device="cuda")
+    ws = L.new_workspace(max(L.workspace_bytes(L.IDX_OP_TOPK, 3, n, k), 1), "cuda")
     lg2 = -lg
 
     def call():
@@ -127,7 +127,7 @@ def test_quantised_query_replays():
     slots = torch.arange(wl.B * wl.H, dtype=torch.int64, device="cuda")
     out_idx = torch.empty((wl.B, wl.k), dtype=torch.int32, device="cuda")
     out_val = torch.empty((wl.B, wl.k), dtype=torch.float32, device="cuda")
-    ws = torch.empty(L.workspace_bytes(L.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, wl.k), dtype=torch.uint8, device="cuda")
+    ws = L.new_workspace(L.workspace_bytes(L.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, wl.k), "cuda")
     q2 = _other_q(d, 3)
 
     def call():
@@ -145,7 +145,7 @@ def test_select_resident_replays():
     dl = [L.to_device(x) for x in rl.layers]
     pages = torch.empty((rl.B, rl.kmax), dtype=torch.int32, device="cuda")
     count = torch.empty(rl.B, dtype=torch.int32, device="cuda")
-    ws = torch.empty(L.resident_workspace_bytes(3, rl.B, rl.n_cols, rl.kmax), dtype=torch.uint8, device="cuda")
+    ws = L.new_workspace(L.resident_workspace_bytes(3, rl.B, rl.n_cols, rl.kmax), "cuda")
     q2 = [_other_q(d, 10 + i) for i, d in enumerate(dl)]
 
     def run(qs, p, c):
