@@ -33,8 +33,9 @@ idx_write_keys call that quantises the 262,144 compressed keys of one
 second and `roofline` covers the writer kernel.
 
 `--q8` measures the quantised-query variant on a scoring workload: each step
-quantises q per head (the writer kernel) and runs idx_score_topk_q8; the
-prefill roofline is then priced at the fp8 MFMA peak.
+is one idx_score_topk_fp8q (the score kernel quantises q per head by the
+writer's rule, then scores on fp8 MFMA); the prefill roofline is then priced
+at the fp8 MFMA peak.
 
 `--block-size 16` re-lays a scoring workload's pool into 16-row blocks, each
 placed on its own (the block table grows fourfold, chunk lists are cut into
@@ -564,8 +565,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="pool copies (0 = enough for >= 1 GB)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--q8", action="store_true",
-                    help="quantised-query variant: each step quantises q per head (writer kernel) and scores "
-                         "with idx_score_topk_q8 on fp8 MFMA")
+                    help="quantised-query variant: idx_score_topk_fp8q (q quantised per head inside the score "
+                         "kernel, fp8 MFMA)")
     ap.add_argument("--block-size", type=int, default=64, choices=(64, 16),
                     help="pool block rows of the scoring workloads (16: the same keys re-laid in 16-row blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -663,13 +664,11 @@ def measure_scoring(name, args):
     ws = lib.new_workspace(lib.workspace_bytes(lib.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, k), "cuda")
 
     if args.q8:
-        q8 = torch.empty((wl.B, wl.H, wl.D + 4), dtype=torch.uint8, device="cuda")
-        q8_slots = torch.arange(wl.B * wl.H, dtype=torch.int64, device="cuda")
-
+        # the query quantised inside the score kernel (one launch before the
+        # top-k, as the bf16 path)
         def step(i):
-            lib.quantize_q(qs[i % R], out=q8, slots=q8_slots)
-            lib.idx_score_topk_q8(q8, d.w, keys[i % R], wl.n_cols, k,
-                                  out_idx=out_idx, out_val=out_val, workspace=ws)
+            lib.idx_score_topk_fp8q(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
+                                    out_idx=out_idx, out_val=out_val, workspace=ws)
     else:
         def step(i):
             lib.idx_score_topk(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
@@ -687,8 +686,9 @@ def measure_scoring(name, args):
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
 
-    algo = algorithmic_bytes(wl, pairs, q8=args.q8)
-    kern_bytes = score_kernel_bytes(wl, pairs, q8=args.q8, logits_written=False)
+    # the quantised-query step reads q as bf16 too (the kernel quantises it)
+    algo = algorithmic_bytes(wl, pairs)
+    kern_bytes = score_kernel_bytes(wl, pairs, logits_written=False)
     flop = 2.0 * wl.H * wl.D * pairs
     mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_BF16_PEAK_TFLOPS
     traffic = read_traffic(prof_name)
@@ -742,7 +742,7 @@ def measure_scoring(name, args):
         "dtype": "fp8" if args.q8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "queries": wl.B, "heads": wl.H, "head_dim": wl.D,
-                   "query": "e4m3, quantised per head each step" if args.q8 else "bf16",
+                   "query": "e4m3, quantised per head in the score kernel" if args.q8 else "bf16",
                    "block": wl.block_size, "k": k, "n_cols": wl.n_cols, "pairs": pairs,
                    "description": wl.description, "replicas": R, "graph": not args.no_graph},
         "queries_per_s": wl.B / (ms_per_step * 1e-3),

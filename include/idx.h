@@ -238,6 +238,27 @@ int idx_score_topk_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H,
                       void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * idx_score_fp8q / idx_score_topk_fp8q: the quantised-query path with the
+ * query quantised inside the score kernel, as the pages' deployed paged
+ * scorer does ("DeepSeek-V4.1 native paged runtime", section "Current
+ * execution scope": the paged scorer quantises the query itself), so no
+ * separate quantising launch precedes the scoring.  Arguments as for
+ * idx_score / idx_score_topk (q bf16 [B, H, D], 16-byte aligned), H = 64.
+ * Each query head is quantised exactly as idx_write_keys would quantise it
+ * (the amax/448 rule, nearest-even e4m3 codes), so the results are bit for bit
+ * those of idx_write_keys on q viewed as B*H keys followed by idx_score_q8 /
+ * idx_score_topk_q8 on the written rows.
+ */
+int idx_score_fp8q(const uint16_t *q, const float *w, int32_t B, int32_t H,
+                   int32_t D, const idx_keys *keys, int32_t n_cols,
+                   float *logits, float *scores, void *stream);
+int idx_score_topk_fp8q(const uint16_t *q, const float *w, int32_t B,
+                        int32_t H, int32_t D, const idx_keys *keys,
+                        int32_t n_cols, int32_t k, int32_t *out_idx,
+                        float *out_val, void *workspace, size_t ws_bytes,
+                        void *stream);
+
+/*
  * idx_write_keys: the index-plane writer -- quantise new compressed keys and
  * store them as pool rows in the layout idx_score reads ("FlashMemory-
  * DeepSeek-V4" README, section "compressed_k format": D float8_e4m3 bytes

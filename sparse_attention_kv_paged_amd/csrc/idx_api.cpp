@@ -289,10 +289,20 @@ int check_qw8(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, i
     return IDX_OK;
 }
 
+// A bf16 query quantised inside the score kernel: bf16 q as for idx_score,
+// 64 heads (the quantised path's operand holds one head block pair).
+int check_qw_quant(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D) {
+    const int rc = check_qw(q, w, B, H, D);
+    if (rc) return rc;
+    if (H != idx::kHeads) return fail(IDX_E_SHAPE, "the in-kernel quantised query takes H=64 (got H=%d)", H);
+    return IDX_OK;
+}
+
 int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
-               const idx_keys *keys, int32_t n_cols, float *logits, float *scores, void *stream) {
+               const idx_keys *keys, int32_t n_cols, float *logits, float *scores, void *stream,
+               bool quant_q = false) {
     g_last_error[0] = 0;
-    int rc = check_qw8(q, q8, w, B, H, D);
+    int rc = quant_q ? check_qw_quant(q, w, B, H, D) : check_qw8(q, q8, w, B, H, D);
     if (rc) return rc;
     if ((rc = check_keys(keys, B))) return rc;
     if ((rc = check_cols(n_cols))) return rc;
@@ -302,6 +312,7 @@ int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, 
     if (!aligned(logits, 16) || !aligned(scores, 4)) return fail(IDX_E_ALIGN, "logits must be 16-byte aligned");
     idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
     a.q8 = q8;
+    a.quant_q = quant_q;
     a.ld = n_cols;
     a.logits = logits;
     a.scores = scores;
@@ -313,8 +324,8 @@ int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, 
 // call with B == 0 passes with an empty plan (nothing to launch).
 int score_topk_check(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
                      const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
-                     TopkPlan &P) {
-    int rc = check_qw8(q, q8, w, B, H, D);
+                     TopkPlan &P, bool quant_q = false) {
+    int rc = quant_q ? check_qw_quant(q, w, B, H, D) : check_qw8(q, q8, w, B, H, D);
     if (rc) return rc;
     if ((rc = check_keys(keys, B))) return rc;
     if ((rc = check_cols(n_cols))) return rc;
@@ -330,9 +341,10 @@ int score_topk_check(const uint16_t *q, const uint8_t *q8, const float *w, int32
 // Enqueue a checked score + top-k call (B > 0) on a workspace of P.total bytes.
 int score_topk_launch(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H,
                       const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
-                      const TopkPlan &P, char *ws, void *stream) {
+                      const TopkPlan &P, char *ws, void *stream, bool quant_q = false) {
     idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
     a.q8 = q8;
+    a.quant_q = quant_q;
     a.ld = P.ld;
     a.logits = reinterpret_cast<float *>(ws + P.logits);
     a.scores = nullptr;
@@ -348,16 +360,16 @@ int score_topk_launch(const uint16_t *q, const uint8_t *q8, const float *w, int3
 
 int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
                     const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
-                    void *workspace, size_t ws_bytes, void *stream) {
+                    void *workspace, size_t ws_bytes, void *stream, bool quant_q = false) {
     g_last_error[0] = 0;
     TopkPlan P;
-    int rc = score_topk_check(q, q8, w, B, H, D, keys, n_cols, k, out_idx, out_val, P);
+    int rc = score_topk_check(q, q8, w, B, H, D, keys, n_cols, k, out_idx, out_val, P, quant_q);
     if (rc || B == 0) return rc;
     if (P.total > 0 && (!workspace || ws_bytes < P.total))
         return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
     if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
     return score_topk_launch(q, q8, w, B, H, keys, n_cols, k, out_idx, out_val, P, static_cast<char *>(workspace),
-                             stream);
+                             stream, quant_q);
 }
 
 // ---------------------------------------------------------------------------
@@ -573,6 +585,18 @@ int idx_score_topk_noalloc(const uint16_t *q, const float *w, int32_t B, int32_t
     if ((rc = static_scratch(&ws))) return rc;
     return score_topk_launch(q, nullptr, w, B, H, keys, n_cols, k, out_idx, out_val, P, static_cast<char *>(ws),
                              stream);
+}
+
+int idx_score_fp8q(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,
+                   int32_t n_cols, float *logits, float *scores, void *stream) {
+    return score_impl(q, nullptr, w, B, H, D, keys, n_cols, logits, scores, stream, true);
+}
+
+int idx_score_topk_fp8q(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,
+                        int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val, void *workspace,
+                        size_t ws_bytes, void *stream) {
+    return score_topk_impl(q, nullptr, w, B, H, D, keys, n_cols, k, out_idx, out_val, workspace, ws_bytes, stream,
+                           true);
 }
 
 int idx_score_topk_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,

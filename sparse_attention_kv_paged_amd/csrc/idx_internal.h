@@ -24,6 +24,7 @@ struct ScoreArgs {
     int64_t q_row;              // elements from one q row to the next (64 * 128, or 128 * 128 for a head half)
     int32_t w_row;              // floats from one w row to the next (64, or 128)
     bool accum;                 // add to the logits already in the output (the second head half)
+    bool quant_q;               // q is bf16 and is quantised here by the writer's rule (q8 null)
     const float *w;             // [B, 64]
     int32_t B;
     const uint8_t *pool;        // [n_pool_rows, 132]

@@ -38,6 +38,7 @@
 
 #include "idx_device.h"
 #include "idx_internal.h"
+#include "idx_quant.h"
 
 namespace idx {
 namespace {
@@ -57,6 +58,7 @@ struct QBf16 {
 };
 struct QFp8 {
     v8i v[2][2];
+    float qs;       // the quantisation scale of head `lane` (the head whose weight the lane holds)
 };
 template <bool Q8> struct QSel {
     using Op = QBf16;
@@ -402,24 +404,63 @@ __device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QBf16 &
 // Quantised q: rows of 132 bytes (128 e4m3 bytes, then the head's scale).
 constexpr int kQ8Row = kHeadDim + 4;
 
-__device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QFp8 &qa) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-        const u32x4a4 *qp = reinterpret_cast<const u32x4a4 *>(
-            a.q8 + ((int64_t)b * kHeads + 32 * hb + (lane & 31)) * kQ8Row + 64 * (lane >> 5));
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const u32x4a4 x = qp[2 * kk], y = qp[2 * kk + 1];
-            qa.v[hb][kk] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
-        }
-    }
-}
-
-// The scale of head `lane` of quantised q[b] (0 for the bf16 path).
+// The scale of head `lane` of quantised q[b].
 __device__ __forceinline__ float q8_scale(const ScoreArgs &a, int b, int lane) {
     return *reinterpret_cast<const float *>(a.q8 + ((int64_t)b * kHeads + lane) * kQ8Row + kHeadDim);
 }
+
+// Quantised q from global memory: the caller's bytes (a.q8), or bf16 q
+// quantised here by the index-plane writer's rule (a.q8 null): the lane holds
+// 64 values of each of its two heads, its partner lane ^ 32 the other 64, so
+// each head's absolute maximum is the larger of the two lanes'.
+__device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QFp8 &qa) {
+    const int lane = threadIdx.x & 63;
+    if (a.q8) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const u32x4a4 *qp = reinterpret_cast<const u32x4a4 *>(
+                a.q8 + ((int64_t)b * kHeads + 32 * hb + (lane & 31)) * kQ8Row + 64 * (lane >> 5));
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4a4 x = qp[2 * kk], y = qp[2 * kk + 1];
+                qa.v[hb][kk] = v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+            }
+        }
+        qa.qs = q8_scale(a, b, lane);
+        return;
+    }
+    // two passes over the (cached) row: the heads' maxima, then the codes,
+    // so that only one 16-byte chunk is held at a time
+    float scale[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+            a.q + (int64_t)b * a.q_row + (int64_t)(32 * hb + (lane & 31)) * kHeadDim + 64 * (lane >> 5));
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const u32x4 x = qp[j];
+            const uint32_t raw[4] = {x.x, x.y, x.z, x.w};
+            m = fmaxf(m, amax8(raw));
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        const float amax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint32_t c[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 x = qp[4 * kk + j];
+                const uint32_t raw[4] = {x.x, x.y, x.z, x.w};
+                quantize8(raw, amax, c[2 * j], c[2 * j + 1], scale[hb]);
+            }
+            qa.v[hb][kk] = v8i{(int)c[0], (int)c[1], (int)c[2], (int)c[3], (int)c[4], (int)c[5], (int)c[6], (int)c[7]};
+        }
+    }
+    // lane l holds the weight of head l: head block 0 for l < 32, else 1
+    qa.qs = lane < 32 ? scale[0] : scale[1];
+}
+
 
 // q of rows rb .. rb + NR - 1 (those below B) for padded LDS rows, read by
 // all 256 threads of the workgroup: fetch_q_rows issues the reads,
@@ -496,6 +537,35 @@ __device__ __forceinline__ void put_q_rows(const ScoreArgs &a, int rb, const QRo
     }
 }
 
+// A staged bf16 row (LDS, padded rows) quantised in place into the quantised
+// rows' layout, by the writer's rule.  Thread t owns chunks t + 256 i (16
+// bytes, head (t + 256 i) / 16), so the 16 chunks of a head lie in one DPP
+// row.  Every thread reads its chunks before any writes (the quantised row is
+// shorter and overwrites the front of the bf16 one); the caller synchronises
+// before (the bf16 row written) and after.
+__device__ __forceinline__ void quantize_staged_row(uint16_t *slot) {
+    u32x4 x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        x[i] = *reinterpret_cast<const u32x4 *>(slot + (c >> 4) * kQPad + 8 * (c & 15));
+    }
+    __syncthreads();
+    uint8_t *dst = reinterpret_cast<uint8_t *>(slot);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        const uint32_t raw[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+        const float amax = row_amax(amax8(raw));
+        uint32_t lo, hi;
+        float scale;
+        quantize8(raw, amax, lo, hi, scale);
+        uint8_t *row = dst + (c >> 4) * kQ8Stage;
+        *reinterpret_cast<uint2 *>(row + 8 * (c & 15)) = uint2{lo, hi};
+        if ((c & 15) == 0) *reinterpret_cast<float *>(row + kHeadDim) = scale;
+    }
+}
+
 __device__ __forceinline__ void load_q_staged(const uint16_t *row, QBf16 &qa) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -509,6 +579,7 @@ __device__ __forceinline__ void load_q_staged(const uint16_t *row, QBf16 &qa) {
 __device__ __forceinline__ void load_q_staged(const uint16_t *row, QFp8 &qa) {
     const int lane = threadIdx.x & 63;
     const uint8_t *base = reinterpret_cast<const uint8_t *>(row);
+    qa.qs = *reinterpret_cast<const float *>(base + lane * kQ8Stage + kHeadDim);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
         const u32x4 *qp = reinterpret_cast<const u32x4 *>(base + (32 * hb + (lane & 31)) * kQ8Stage + 64 * (lane >> 5));
@@ -531,12 +602,14 @@ struct NoQ {
 // USE_PRE: pre holds the first group's table reads, already issued by the
 // caller, and qfin(qa) -- called once, right after the first ring of key
 // loads has been issued, by every wave of the workgroup (it synchronises
-// the workgroup) -- delivers the MFMA operands of q[b].
+// the workgroup) -- delivers the MFMA operands of q[b].  Otherwise q[b] is
+// read from q_lds when the workgroup has staged it there, else from memory.
 template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, int BS, bool USE_PRE = false,
           class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
-                                           const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{}) {
+                                           const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{},
+                                           const uint16_t *q_lds = nullptr) {
     const int lane = threadIdx.x & 63;
     const int hf = lane >> 5;
     const int n32 = lane & 31;
@@ -559,11 +632,10 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     typename QSel<Q8>::Op qa;
     if (live) {
         w_lane = a.w[(int64_t)b * a.w_row + lane];
-        // quantised q: relu(s_q x) = s_q relu(x) for s_q >= 0, so each head's
-        // q scale joins its weight
-        if (Q8) w_lane *= q8_scale(a, b, lane);
         raw0 = USE_PRE ? pre : slot_raw<CHUNKED>(a, r.req, b, U * j0 + lane, lane < min(64, U * (j1 - j0)));
-        if (!USE_PRE) load_q_global(a, b, qa);
+        if (!USE_PRE) {
+            if (q_lds) load_q_staged(q_lds, qa); else load_q_global(a, b, qa);
+        }
     }
 
     // Slots go in groups of up to GS (64 pool blocks): lane j resolves block
@@ -682,7 +754,9 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         issue(1);
         if (USE_PRE && g0 == j0) qfin(qa);            // q arrives while the ring is in flight
         if (g0 == j0) {
-            sh_w[lane] = w_lane;                        // w[b] into the wave's LDS slot
+            // w[b] into the wave's LDS slot; a quantised query's per-head scale
+            // joins its weight: relu(s_q x) = s_q relu(x) for s_q >= 0
+            if constexpr (Q8) sh_w[lane] = w_lane * qa.qs; else sh_w[lane] = w_lane;
             __builtin_amdgcn_wave_barrier();
             const float4 *w4 = reinterpret_cast<const float4 *>(sh_w);
 #pragma unroll
@@ -719,7 +793,8 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // FLAT: the (row, slot) work of all rows is flattened and split evenly over
 // every wave of the grid (rows of very different lengths); otherwise each
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM, int BS>
+// QQ (with Q8): q arrives as bf16 and is quantised here, while it is staged.
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM, int BS, bool QQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     constexpr int U = kBlock / BS;                    // pool blocks per slot
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
@@ -752,17 +827,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // the first group's table reads, then q[b] staged in LDS once for
         // the four waves
         const SlotRaw raw0 = slot_raw<CHUNKED>(a, r.req, b, U * j0 + lane, lane < min(64, U * (j1 - j0)));
-        QRows<Q8, 1> qv;
+        QRows<Q8 && !QQ, 1> qv;
         fetch_q_rows<1>(a, b, qv);
-        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
+        const auto put = [&] {
             put_q_rows<1>(a, b, qv, sh_q);
+            if constexpr (QQ) {
+                __syncthreads();
+                quantize_staged_row(sh_q[0]);
+            }
+        };
+        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
+            put();
             __syncthreads();
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
             score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
-            put_q_rows<1>(a, b, qv, sh_q);            // the workgroup's one barrier
+            put();                                    // the workgroup's one barrier
             __syncthreads();
         }
     } else {
@@ -830,10 +912,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // four waves (most workgroups lie within one or two rows)
         const int fw = (int)blockIdx.x * kWaves * chunk;
         const int rb = fw < total ? row_of(fw) : a.B;
-        QRows<Q8, 2> qv;
+        QRows<Q8 && !QQ, 2> qv;
         fetch_q_rows<2>(a, rb, qv);
-        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
+        // QQ: the staged bf16 rows that the workgroup scores are quantised
+        // in place (row rb + 1 only when the workgroup reaches it)
+        const int wend = min(fw + kWaves * chunk, total);
+        const int nquant = __builtin_amdgcn_readfirstlane(rb >= a.B ? 0 : rb + 1 < a.B && sh_pre[rb + 1] < wend ? 2 : 1);
+        const auto put = [&] {
             put_q_rows<2>(a, rb, qv, sh_q);
+            if constexpr (QQ) {
+#pragma unroll 1
+                for (int rr = 0; rr < nquant; ++rr) {
+                    __syncthreads();
+                    quantize_staged_row(sh_q[rr]);
+                }
+            }
+        };
+        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
+            put();
             __syncthreads();
             if (b == rb || b == rb + 1)
                 load_q_staged(sh_q[b - rb], qa);
@@ -842,7 +938,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         };
 
         if (!(f < fend)) {
-            put_q_rows<2>(a, rb, qv, sh_q);           // the workgroup's one barrier
+            put();                                    // the workgroup's one barrier
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
@@ -859,7 +955,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.nunits = __builtin_amdgcn_readfirstlane(sh_runits[b]);
                 r.nslots = (r.nunits + U - 1) / U;
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st);
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st,
+                                                                      SlotRaw{-1, -1, false}, NoQ{},
+                                                                      b == rb + 1 ? sh_q[1] : nullptr);
                 f = min(fend, pe);
             }
         }
@@ -870,39 +968,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8, bool ACCUM>
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8, bool ACCUM, bool QQ>
 void launch_score_qa(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 g((unsigned)grid), blk(256);
     const bool small = a.block_size == kSmallBlock;
     if (a.chunk_ids) {
         if (small)
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kSmallBlock>), g, blk, 0, s, e0,
-                                  e1, 0, a);
-        else
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kBlock>), g, blk, 0, s, e0, e1,
-                                  0, a);
-    } else {
-        if (small)
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kSmallBlock>), g, blk, 0, s,
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kSmallBlock, QQ>), g, blk, 0, s,
                                   e0, e1, 0, a);
         else
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kBlock>), g, blk, 0, s, e0,
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kBlock, QQ>), g, blk, 0, s, e0,
                                   e1, 0, a);
+    } else {
+        if (small)
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kSmallBlock, QQ>), g, blk, 0,
+                                  s, e0, e1, 0, a);
+        else
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kBlock, QQ>), g, blk, 0, s,
+                                  e0, e1, 0, a);
     }
 }
 
-// The accumulating second head half exists for bf16 queries only.
+// The accumulating second head half exists for bf16 queries only; a bf16
+// query quantised in the kernel (a.quant_q) takes the quantised path.
 template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8>
 void launch_score_q(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if constexpr (!Q8) {
-        if (a.accum) return launch_score_qa<OWN_COLS, SCORES, FLAT, false, true>(a, grid, s, e0, e1);
+        if (a.accum) return launch_score_qa<OWN_COLS, SCORES, FLAT, false, true, false>(a, grid, s, e0, e1);
+        launch_score_qa<OWN_COLS, SCORES, FLAT, false, false, false>(a, grid, s, e0, e1);
+    } else {
+        if (a.quant_q) return launch_score_qa<OWN_COLS, SCORES, FLAT, true, false, true>(a, grid, s, e0, e1);
+        launch_score_qa<OWN_COLS, SCORES, FLAT, true, false, false>(a, grid, s, e0, e1);
     }
-    launch_score_qa<OWN_COLS, SCORES, FLAT, Q8, false>(a, grid, s, e0, e1);
 }
 
 template <bool OWN_COLS, bool SCORES, bool FLAT>
 void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-    if (a.q8)
+    if (a.q8 || a.quant_q)
         launch_score_q<OWN_COLS, SCORES, FLAT, true>(a, grid, s, e0, e1);
     else
         launch_score_q<OWN_COLS, SCORES, FLAT, false>(a, grid, s, e0, e1);
@@ -910,7 +1012,8 @@ void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.B <= 0) return hipSuccess;
-    if (a.accum && a.q8) return hipErrorInvalidValue;
+    if (a.accum && (a.q8 || a.quant_q)) return hipErrorInvalidValue;
+    if (a.quant_q && (a.q8 || !a.q)) return hipErrorInvalidValue;
     if (a.block_size != kBlock && a.block_size != kSmallBlock) return hipErrorInvalidValue;
     if (!a.logits && (a.accum || !a.scores || a.row_cols)) return hipErrorInvalidValue;
     // the top-k feed (row_cols) never asks for scores

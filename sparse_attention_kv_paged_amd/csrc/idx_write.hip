@@ -24,6 +24,7 @@
 
 #include "../../include/idx.h"
 #include "idx_internal.h"
+#include "idx_quant.h"
 #include "idx_write.h"
 
 namespace idx {
@@ -35,49 +36,6 @@ constexpr int kKeysPerLoad = 64 / kLanesPerKey;               // 4 keys per wave
 constexpr int kKeysPerWaveStep = 2 * kKeysPerLoad;            // 8
 constexpr int kKeysPerGroupStep = (kWriteThreads / 64) * kKeysPerWaveStep;  // 32
 constexpr int kMaxWriteGroups = 2048;                         // 8 workgroups per CU
-
-// Quotients q[i] = v[i] / s, rounded to binary32 as an IEEE division would
-// round them, as far as the e4m3 code can tell: r = 1/s is divided once per
-// key, then each quotient is q0 = v*r corrected once with the exact residual
-// v - q0*s (Markstein's correction step, two FMAs).  Checked against the IEEE
-// quotient over every bf16 pair |v| <= amax: the e4m3 codes agree for every
-// amax >= 2^-104 once the sign is taken from v (the correction turns -0 into
-// +0); below that the residual underflows, so keys with amax < 2^-100 divide
-// each element instead.
-__device__ __forceinline__ void quotients(const float *v, float scale, bool tiny, float *q) {
-#pragma clang fp contract(off)
-    const float r = 1.0f / scale;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float q0 = v[i] * r;
-        const float rho = __builtin_fmaf(-q0, scale, v[i]);
-        q[i] = __builtin_fmaf(rho, r, q0);
-    }
-    if (tiny) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = v[i] / scale;
-    }
-}
-
-// Codes of four elements, byte i for element i: the magnitude from the
-// hardware's packed binary32 -> e4m3fn conversion of |q| (nearest, ties to
-// even; |q| never exceeds 448 by more than a few ulps, which still rounds to
-// 448), the sign bit from the bf16 value itself.  raw_lo / raw_hi hold the
-// four bf16 values (sign bits at 15 and 31 of each).
-__device__ __forceinline__ uint32_t codes4(const float *q, uint32_t raw_lo, uint32_t raw_hi) {
-    uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fabsf(q[0]), __builtin_fabsf(q[1]), 0, false);
-    c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fabsf(q[2]), __builtin_fabsf(q[3]), (int)c, true);
-    const uint32_t sign = ((raw_lo >> 8) & 0x80u) | ((raw_lo >> 16) & 0x8000u) |
-                          ((raw_hi << 8) & 0x800000u) | (raw_hi & 0x80000000u);
-    return (c & 0x7F7F7F7Fu) | sign;
-}
-
-// The value of the lane N places further along this lane's 16-lane DPP row,
-// wrapping within the row (row_ror:N).
-template <int N>
-__device__ __forceinline__ float row_ror(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
-}
 
 // A pair of dwords stored with one 8-byte store at a 4-byte aligned address
 // (pool rows are 132 bytes apart).
@@ -102,32 +60,13 @@ __device__ __forceinline__ KeyLoad load_key(const WriteArgs &a, int64_t key, int
 
 // Quantise one key slice and store it; returns whether the slot was bad.
 __device__ __forceinline__ bool store_key(const WriteArgs &a, const KeyLoad &l, int64_t key, int part) {
-    // bf16 -> binary32 is exact: the 16 bits are the high half of the float
-    float v[8];
+    // bf16 -> binary32 is exact: the 16 bits are the high half of the float;
+    // the key's maximum over the 16 lanes of its DPP row
     const uint32_t w4[4] = {l.raw.x, l.raw.y, l.raw.z, l.raw.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w4[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
-    // maximum over the 16 lanes of this key: a DPP row is 16 lanes, so row
-    // rotations by 8, 4, 2, 1 leave every lane of the row with the maximum
-    amax = fmaxf(amax, row_ror<8>(amax));
-    amax = fmaxf(amax, row_ror<4>(amax));
-    amax = fmaxf(amax, row_ror<2>(amax));
-    amax = fmaxf(amax, row_ror<1>(amax));
-
-    const float scale = amax / 448.0f;
-    float q[8];
-    quotients(v, scale, amax < 0x1p-100f, q);
-    // a key of zeros: zero bytes (its quotients are 0/0)
-    const bool zero = amax == 0.0f;
+    const float amax = row_amax(amax8(w4));
     Dword2 codes;
-    codes.lo = zero ? 0u : codes4(q, l.raw.x, l.raw.y);
-    codes.hi = zero ? 0u : codes4(q + 4, l.raw.z, l.raw.w);
+    float scale;
+    quantize8(w4, amax, codes.lo, codes.hi, scale);
 
     const bool in_pool = l.slot >= 0 && l.slot < a.n_pool_rows;
     if (in_pool) {

@@ -28,6 +28,7 @@ MAX_COLS = 1 << 27                # IDX_MAX_COLS
 STATIC_SCRATCH_BYTES = 16 << 20   # IDX_STATIC_SCRATCH_BYTES
 
 EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_score_topk_noalloc", "idx_score_q8", "idx_score_topk_q8",
+           "idx_score_fp8q", "idx_score_topk_fp8q",
            "idx_write_keys", "idx_select_resident",
            "idx_resident_workspace_bytes", "idx_workspace_bytes",
            "idx_error_string", "idx_last_error", "idx_profile_events", "idx_abi_version")
@@ -89,6 +90,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.idx_score_topk.restype = ctypes.c_int
     lib.idx_score_topk_noalloc.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp]
     lib.idx_score_topk_noalloc.restype = ctypes.c_int
+    lib.idx_score_fp8q.argtypes = [vp, vp, i32, i32, i32, kp, i32, vp, vp, vp]
+    lib.idx_score_fp8q.restype = ctypes.c_int
+    lib.idx_score_topk_fp8q.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
+    lib.idx_score_topk_fp8q.restype = ctypes.c_int
     lib.idx_score_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, vp, vp, vp]
     lib.idx_score_q8.restype = ctypes.c_int
     lib.idx_score_topk_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
@@ -303,6 +308,43 @@ def idx_score_topk_noalloc(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, 
     ks = keys.struct(B)
     _check(load().idx_score_topk_noalloc(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
                                          _ptr(out_idx), _ptr(out_val), _stream(stream)))
+    return out_idx, out_val
+
+
+def idx_score_fp8q(q, w, keys: Keys, n_cols: int, with_scores: bool = False,
+                   logits: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None, stream=None):
+    """idx_score with the query quantised inside the score kernel (the
+    writer's rule per head; equal to quantize_q followed by idx_score_q8)."""
+    q, w = _qw(q, w)
+    B, H, D = q.shape
+    if logits is None:
+        logits = torch.empty((B, n_cols), dtype=torch.float32, device=q.device)
+    if with_scores and scores is None:
+        scores = torch.empty((B, n_cols), dtype=torch.float32, device=q.device)
+    _dev(logits, torch.float32, "logits")
+    _dev(scores, torch.float32, "scores")
+    ks = keys.struct(B)
+    _check(load().idx_score_fp8q(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols,
+                                 _ptr(logits), _ptr(scores), _stream(stream)))
+    return (logits, scores) if with_scores else logits
+
+
+def idx_score_topk_fp8q(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=None,
+                        workspace=None, stream=None):
+    """idx_score_topk with the query quantised inside the score kernel."""
+    q, w = _qw(q, w)
+    B, H, D = q.shape
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=q.device)
+    if out_val is None:
+        out_val = torch.empty((B, k), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(IDX_OP_SCORE_TOPK, B, n_cols, k)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    ks = keys.struct(B)
+    _check(load().idx_score_topk_fp8q(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
+                                      _ptr(out_idx), _ptr(out_val), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
     return out_idx, out_val
 
 

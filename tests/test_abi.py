@@ -257,6 +257,17 @@ def test_h128_accepted_for_bf16_rejected_for_q8(lib):
     assert lib.idx_score_q8(0x1004, 0x2000, 1, 128, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_SHAPE
     # 128 heads pass every host check (B = 0 returns before any launch)
     assert _score(lib, H=128, B=0, q=None, w=None, logits=None) == L.IDX_OK
+    # the query quantised in the kernel: bf16 q as for idx_score, 64 heads
+    assert lib.idx_score_fp8q(0x1000, 0x2000, 1, 128, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_SHAPE
+    assert lib.idx_score_fp8q(0x1004, 0x2000, 1, 64, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_ALIGN
+    assert lib.idx_score_fp8q(None, None, 1, 64, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_ARG
+    assert lib.idx_score_fp8q(None, None, 0, 64, 128, ctypes.byref(keys), 64, None, None, None) == L.IDX_OK
+    need = L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 1, 64, 16)
+    assert lib.idx_score_topk_fp8q(0x1000, 0x2000, 1, 128, 128, ctypes.byref(keys), 64, 16, 0x3000, None,
+                                   0x10000, need, None) == L.IDX_E_SHAPE
+    assert need > 0
+    assert lib.idx_score_topk_fp8q(0x1000, 0x2000, 1, 64, 128, ctypes.byref(keys), 64, 16, 0x3000, None,
+                                   0x10000, need - 1, None) == L.IDX_E_WORKSPACE
 
 
 def test_column_limit(lib):

@@ -140,6 +140,23 @@ def test_quantised_query_replays():
     _replay_check("quantised query", call, [q8, out_idx, out_val], between)
 
 
+def test_query_quantised_in_kernel_replays():
+    wl = W.small_config(1)
+    d = L.to_device(wl)
+    out_idx = torch.empty((wl.B, wl.k), dtype=torch.int32, device="cuda")
+    out_val = torch.empty((wl.B, wl.k), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(L.workspace_bytes(L.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, wl.k), "cuda")
+    q2 = _other_q(d, 4)
+
+    def call():
+        L.idx_score_topk_fp8q(d.q, d.w, d.keys, wl.n_cols, wl.k, out_idx=out_idx, out_val=out_val, workspace=ws)
+
+    def between():
+        L.idx_score_topk_fp8q(q2, d.w, d.keys, wl.n_cols, wl.k, workspace=ws)
+
+    _replay_check("query quantised in the kernel", call, [out_idx, out_val], between)
+
+
 def test_select_resident_replays():
     rl = W.memory_indexer(entries=[20000, 9000, 64, 40000], n_layers=3, kmax=96, seed=73)
     dl = [L.to_device(x) for x in rl.layers]

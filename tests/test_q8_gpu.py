@@ -141,3 +141,79 @@ def test_q8_zero_heads_negative_scales_and_padding_rows():
     wl.block_table = wl.block_table.copy()
     wl.block_table[3, 1] = -1                          # absent block
     _check_q8(wl, tag="edge")
+
+
+# ------------------------------------------------ query quantised in the kernel
+
+def _check_fp8q_equals_writer_then_q8(wl, tag, oracle_rows=None):
+    """idx_score_fp8q / idx_score_topk_fp8q quantise q inside the score kernel
+    by the writer's rule: bit for bit the writer followed by the quantised
+    path, and (through that) the oracle's quantised-query scoring on
+    oracle_rows (all rows by default).  Returns the fp8q logits."""
+    _log(f"[fp8q] {tag} {wl.name}: {wl.description}")
+    d = L.to_device(wl)
+    lg, sc = L.idx_score_fp8q(d.q, d.w, d.keys, d.n_cols, with_scores=True)
+    q8 = L.quantize_q(d.q)
+    lg8, sc8 = L.idx_score_q8(q8, d.w, d.keys, d.n_cols, with_scores=True)
+    idx, val = L.idx_score_topk_fp8q(d.q, d.w, d.keys, d.n_cols, wl.k)
+    idx8, val8 = L.idx_score_topk_q8(q8, d.w, d.keys, d.n_cols, wl.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(lg.cpu().numpy().view(np.uint32), lg8.cpu().numpy().view(np.uint32)), f"{tag}: logits"
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), sc8.cpu().numpy().view(np.uint32)), f"{tag}: scores"
+    assert np.array_equal(idx.cpu().numpy(), idx8.cpu().numpy()), f"{tag}: ids"
+    assert np.array_equal(val.cpu().numpy().view(np.uint32), val8.cpu().numpy().view(np.uint32)), f"{tag}: values"
+    g = lg.cpu().numpy()
+    rows = np.arange(wl.B) if oracle_rows is None else np.asarray(oracle_rows)
+    ref = oracle.score(wl, rows=rows, q8=oracle.quantize_q(wl.q))
+    assert_logits_close(g[rows], ref, f"{tag} fp8q logits")
+    return g
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_fp8q_small_workloads(cfg):
+    _check_fp8q_equals_writer_then_q8(W.small_config(cfg), f"small{cfg}")
+
+
+def test_fp8q_flat_split_rows_crossing_workgroups():
+    """Decode-batch at full size: most rows are staged per workgroup, the
+    waves that start a row outside their workgroup's staged rows quantise q
+    in registers."""
+    _check_fp8q_equals_writer_then_q8(W.config(1), "full1")
+
+
+def test_fp8q_per_row_path_and_16_row_blocks():
+    _check_fp8q_equals_writer_then_q8(W.prefill(8192, 603, seed=15, name="fp8q-rows"), "per-row")
+    _check_fp8q_equals_writer_then_q8(W.reblock(W.small_config(4), seed=57), "b16-chunks")
+
+
+def test_fp8q_zero_tiny_and_huge_heads_negative_scales_padding():
+    """Zero heads (scale 0), heads below 2^-100 (the writer divides each
+    element there), keys with negative and zero scales, a padding row, an
+    absent block, and a row scaled by 2^100.  The writer's rule gives that
+    row exactly the codes of the unscaled row (amax and every quotient scale
+    alike), so its logits are exactly 2^100 times the unscaled row's; the
+    other rows are compared with the oracle."""
+    wl = W.paged_decode([700, 64, 1, 129, 2048], seed=93, max_blocks=40, k=64, name="fp8q-edge")
+    q = wl.q.copy().view(np.uint16)
+    rng = np.random.default_rng(94)
+    q[0, 3:9] = 0
+    tiny = (rng.standard_normal((4, 128)) * 2.0 ** -110).astype(np.float32)
+    q[1, 10:14] = W.bf16_bits(tiny)
+    base = rng.standard_normal((64, 128)).astype(np.float32)
+    q[4] = W.bf16_bits(base)
+    pool = wl.pool.copy()
+    s = pool[:, 128:].copy().view("<f4")[:, 0]
+    s[::5] *= -1.0
+    s[1::7] = 0.0
+    pool[:, 128:] = s.astype("<f4").view(np.uint8).reshape(-1, 4)
+    wl.pool = pool
+    wl.q_req = np.arange(wl.B, dtype=np.int32)
+    wl.q_req[2] = -1
+    wl.block_table = wl.block_table.copy()
+    wl.block_table[3, 1] = -1
+    wl.q = q.copy()
+    plain = _check_fp8q_equals_writer_then_q8(wl, "edge")
+    q[4] = W.bf16_bits(base * np.float32(2.0 ** 100))
+    wl.q = q
+    scaled = _check_fp8q_equals_writer_then_q8(wl, "edge-2^100", oracle_rows=[0, 1, 2, 3])
+    assert np.array_equal(scaled[4].astype(np.float64), plain[4].astype(np.float64) * 2.0 ** 100)
