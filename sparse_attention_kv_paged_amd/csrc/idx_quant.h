@@ -19,9 +19,8 @@ namespace {
 // amax >= 2^-104 once the sign is taken from v (the correction turns -0 into
 // +0); below that the residual underflows, so keys with amax < 2^-100 divide
 // each element instead.
-__device__ __forceinline__ void quotients(const float *v, float scale, bool tiny, float *q) {
+__device__ __forceinline__ void quotients(const float *v, float scale, float r, bool tiny, float *q) {
 #pragma clang fp contract(off)
-    const float r = 1.0f / scale;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float q0 = v[i] * r;
@@ -68,10 +67,31 @@ __device__ __forceinline__ void quantize8(const uint32_t (&raw)[4], float amax, 
     }
     scale = amax / 448.0f;
     float q[8];
-    quotients(v, scale, amax < 0x1p-100f, q);
+    quotients(v, scale, 1.0f / scale, amax < 0x1p-100f, q);
     const bool zero = amax == 0.0f;
     lo = zero ? 0u : codes4(q, raw[0], raw[1]);
     hi = zero ? 0u : codes4(q + 4, raw[2], raw[3]);
+}
+
+// Quantise 32 bf16 values of a head (raw: sixteen dwords, two values each)
+// whose absolute maximum is amax: byte i of codes = value i; the scale once.
+__device__ __forceinline__ void quantize32(const uint32_t (&raw)[16], float amax, uint32_t (&codes)[8],
+                                           float &scale) {
+    scale = amax / 448.0f;
+    const float r = 1.0f / scale;
+    const bool tiny = amax < 0x1p-100f, zero = amax == 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float v[8], q[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(raw[4 * j + i] << 16);
+            v[2 * i + 1] = __uint_as_float(raw[4 * j + i] & 0xFFFF0000u);
+        }
+        quotients(v, scale, r, tiny, q);
+        codes[2 * j] = zero ? 0u : codes4(q, raw[4 * j], raw[4 * j + 1]);
+        codes[2 * j + 1] = zero ? 0u : codes4(q + 4, raw[4 * j + 2], raw[4 * j + 3]);
+    }
 }
 
 // Absolute maximum of the eight bf16 values of a lane.

@@ -538,32 +538,42 @@ __device__ __forceinline__ void put_q_rows(const ScoreArgs &a, int rb, const QRo
 }
 
 // A staged bf16 row (LDS, padded rows) quantised in place into the quantised
-// rows' layout, by the writer's rule.  Thread t owns chunks t + 256 i (16
-// bytes, head (t + 256 i) / 16), so the 16 chunks of a head lie in one DPP
-// row.  Every thread reads its chunks before any writes (the quantised row is
-// shorter and overwrites the front of the bf16 one); the caller synchronises
-// before (the bf16 row written) and after.
+// rows' layout, by the writer's rule.  Four threads share a head: thread t
+// takes dims 32 (t % 4) .. + 31 of head t / 4, so the head's amax is a
+// reduction over one DPP quad and each thread divides for one scale.  Every
+// thread reads its values before any writes (the quantised row is shorter and
+// overwrites the front of the bf16 one); the caller synchronises before (the
+// bf16 row written) and after.
 __device__ __forceinline__ void quantize_staged_row(uint16_t *slot) {
-    u32x4 x[4];
+    const int h = threadIdx.x >> 2, qt = threadIdx.x & 3;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(slot + h * kQPad + 32 * qt);
+    uint32_t raw[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        x[i] = *reinterpret_cast<const u32x4 *>(slot + (c >> 4) * kQPad + 8 * (c & 15));
+    for (int j = 0; j < 4; ++j) {
+        const u32x4 x = src[j];
+        raw[4 * j] = x.x;
+        raw[4 * j + 1] = x.y;
+        raw[4 * j + 2] = x.z;
+        raw[4 * j + 3] = x.w;
     }
     __syncthreads();
-    uint8_t *dst = reinterpret_cast<uint8_t *>(slot);
+    float m = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = threadIdx.x + 256 * i;
-        const uint32_t raw[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-        const float amax = row_amax(amax8(raw));
-        uint32_t lo, hi;
-        float scale;
-        quantize8(raw, amax, lo, hi, scale);
-        uint8_t *row = dst + (c >> 4) * kQ8Stage;
-        *reinterpret_cast<uint2 *>(row + 8 * (c & 15)) = uint2{lo, hi};
-        if ((c & 15) == 0) *reinterpret_cast<float *>(row + kHeadDim) = scale;
+    for (int i = 0; i < 16; ++i) {
+        m = fmaxf(m, __builtin_fabsf(__uint_as_float(raw[i] << 16)));
+        m = fmaxf(m, __builtin_fabsf(__uint_as_float(raw[i] & 0xFFFF0000u)));
     }
+    // quad_perm [1,0,3,2] then [2,3,0,1]: the max over the quad's four lanes
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xB1, 0xF, 0xF, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+    uint32_t codes[8];
+    float scale;
+    quantize32(raw, m, codes, scale);
+    uint8_t *row = reinterpret_cast<uint8_t *>(slot) + h * kQ8Stage;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(row + 32 * qt);
+    dst[0] = u32x4{codes[0], codes[1], codes[2], codes[3]};
+    dst[1] = u32x4{codes[4], codes[5], codes[6], codes[7]};
+    if (qt == 0) *reinterpret_cast<float *>(row + kHeadDim) = scale;
 }
 
 __device__ __forceinline__ void load_q_staged(const uint16_t *row, QBf16 &qa) {
