@@ -25,6 +25,11 @@ def assert_logits_close(gpu, ref, what=""):
     bad = err > bound
     assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} logits out of tolerance; "
                            f"worst err {err.max():.3e} (bound there {bound[np.argmax(err)]:.3e})")
+    # how much of the tolerance the worst logit uses (printed for the record)
+    used = float((err / bound).max()) if err.size else 0.0
+    print(f"[tol] {what}: {err.size} logits, worst err/bound {used:.4f}, "
+          f"median err {float(np.median(err)) if err.size else 0.0:.3e}", flush=True)
+    return used
 
 
 def assert_topk_near_tie(gpu_idx, ref_idx, ref_logit_of_entry, k, what=""):
