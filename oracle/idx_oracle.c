@@ -43,6 +43,8 @@
  *  - Level-1 resident-set selection: per-entry ensemble (max or mean) of the
  *    layers' sigmoid scores, threshold, page density, sink and recent pages,
  *    the densest pages up to KMAX (see the Level-1 section below).
+ *  - MXFP4 variant: query and key rounded to MXFP4 blocks of 32 before the
+ *    score (see the MXFP4 section below).
  *
  * Build: plain C99, `gcc -O2 -fopenmp -shared -fPIC` (no -ffast-math).
  */
@@ -157,6 +159,83 @@ int64_t oracle_resolve(int32_t b, int32_t col, int64_t n_pool_rows,
     return prow;
 }
 
+/* ---------------------------------------------------------------------------
+ * MXFP4 rounding of query and key.  [AT] "Current execution scope": the
+ * published model rounds the index query and key alike to FP4 before the
+ * index score, whatever the index plane holds.  [BG] the fp8-fallback commit
+ * names that quantisation MXFP4 (selector auto | mxfp4 | fp8) with an e4m3
+ * fallback at one scale per block of 32 values, and the Phase 3 summary
+ * lists fp4 quantisation of the indexer's q and k.  MXFP4 is the OCP
+ * Microscaling format: a block of 32 values shares one power-of-two scale
+ * X = 2^e (an E8M0 byte), each value is an E2M1 number (1 sign, 2 exponent,
+ * 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ * Readings where the pages are silent:
+ *  - a block is 32 consecutive dims of one query head or one key row;
+ *  - e = floor(log2(amax)) - 2 (2 is E2M1's largest exponent), clamped to
+ *    the E8M0 range [-127, 127]; a block of zeros stays zero;
+ *  - each value becomes the E2M1 value nearest v / X (ties to the even
+ *    code), magnitudes above 6 saturate to 6, the sign is kept;
+ *  - the key is rounded as the index plane holds it: its e4m3 values are
+ *    the block's values, and its fp32 row scale stays a factor outside the
+ *    rounding (the row scale is not a power of two, so rounding e4m3 * scale
+ *    instead would move the block's grid).
+ * Inputs are finite.
+ */
+static const double e2m1_magnitudes[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* The E2M1 value nearest x (search over the eight magnitudes; on a tie the
+ * even code -- the one whose mantissa bit is 0 -- wins), saturating at 6. */
+double oracle_e2m1_round(double x)
+{
+    double a = fabs(x), best = 0.0, best_d = INFINITY;
+    int c, best_c = 0;
+    if (a > 6.0)
+        a = 6.0;
+    for (c = 0; c < 8; ++c) {
+        double d = fabs(a - e2m1_magnitudes[c]);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best_c & 1) == 1)) {
+            best_d = d;
+            best = e2m1_magnitudes[c];
+            best_c = c;
+        }
+    }
+    return x < 0.0 ? -best : best;
+}
+
+/* The block exponent e for a block whose largest magnitude is amax > 0. */
+int oracle_mxfp4_exponent(double amax)
+{
+    int ex, e;
+    frexp(amax, &ex);                    /* amax = m * 2^ex, 0.5 <= m < 1 */
+    e = (ex - 1) - 2;                    /* floor(log2(amax)) - 2 */
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
+/* Round v[0 .. n) block by block (n a multiple of 32) into out (which may
+ * be v itself). */
+void oracle_mxfp4_round(const double *v, int32_t n, double *out)
+{
+    int32_t b, i;
+    for (b = 0; b + 32 <= n; b += 32) {
+        double amax = 0.0, x;
+        for (i = 0; i < 32; ++i)
+            if (fabs(v[b + i]) > amax)
+                amax = fabs(v[b + i]);
+        if (amax == 0.0) {
+            for (i = 0; i < 32; ++i)
+                out[b + i] = 0.0;
+            continue;
+        }
+        x = ldexp(1.0, oracle_mxfp4_exponent(amax));
+        for (i = 0; i < 32; ++i)
+            out[b + i] = oracle_e2m1_round(v[b + i] / x) * x;
+    }
+}
+
 /* One logit, straight from the definition in [FM] "Retriever architecture":
  *   k_d     = e4m3(byte_d) * scale                       (dequant)
  *   dot_h   = sum_d k_d * q[h,d]                          (k @ q^T)
@@ -165,13 +244,23 @@ int64_t oracle_resolve(int32_t b, int32_t col, int64_t n_pool_rows,
  * q_row holds the query row already widened to double (exact for bf16).
  * Sums run in index order in double. */
 static double logit_of_row(const double *q_row, const float *w_row, int32_t H,
-                           int32_t D, const uint8_t *key_row, double *k)
+                           int32_t D, const uint8_t *key_row, double *k, int mx)
 {
     double scale = le_f32_value(key_row + D);
     double logit = 0.0;
     int32_t h, d;
-    for (d = 0; d < D; ++d)
-        k[d] = oracle_e4m3_value(key_row[d]) * scale;
+    if (mx) {
+        /* MXFP4 variant: the key's e4m3 values rounded block by block, then
+         * the row scale */
+        for (d = 0; d < D; ++d)
+            k[d] = oracle_e4m3_value(key_row[d]);
+        oracle_mxfp4_round(k, D, k);
+        for (d = 0; d < D; ++d)
+            k[d] = k[d] * scale;
+    } else {
+        for (d = 0; d < D; ++d)
+            k[d] = oracle_e4m3_value(key_row[d]) * scale;
+    }
     for (h = 0; h < H; ++h) {
         double dot = 0.0;
         for (d = 0; d < D; ++d)
@@ -192,7 +281,7 @@ double oracle_logit(const uint16_t *q_row, const float *w_row, int32_t H,
     if (qd && k) {
         for (i = 0; i < (int64_t)H * D; ++i)
             qd[i] = bf16_value(q_row[i]);
-        v = logit_of_row(qd, w_row, H, D, key_row, k);
+        v = logit_of_row(qd, w_row, H, D, key_row, k, 0);
     }
     free(qd);
     free(k);
@@ -204,7 +293,9 @@ double oracle_logit(const uint16_t *q_row, const float *w_row, int32_t H,
  * [B, H, D], widened exactly) or, when q8 is given instead, quantised rows
  * [B, H, D + 4] in the index-plane layout (e4m3 bytes, then the head's fp32
  * scale), dequantised exactly as e4m3(byte) * scale -- the quantised-query
- * variant.  Returns 0, or -1 on bad sizes or allocation failure. */
+ * variant.  With mx set, query heads and keys are rounded to MXFP4 first
+ * (the MXFP4 variant; D a multiple of 32).  Returns 0, or -1 on bad sizes or
+ * allocation failure. */
 static int score_rows(const uint16_t *q, const uint8_t *q8, const float *w,
                       int32_t B, int32_t H, int32_t D, const uint8_t *pool,
                       int64_t n_pool_rows, int32_t block_size,
@@ -212,12 +303,14 @@ static int score_rows(const uint16_t *q, const uint8_t *q8, const float *w,
                       int32_t max_blocks, const int32_t *q_req,
                       const int32_t *chunk_ids, const int32_t *n_chunks,
                       int32_t max_chunks, const int32_t *limits, int32_t n_cols,
-                      double *logits, int32_t n_threads)
+                      double *logits, int32_t n_threads, int mx)
 {
     int64_t row_bytes = (int64_t)D + 4;
     int32_t b;
     int failed = 0;
     if (B < 0 || H <= 0 || D <= 0 || block_size <= 0 || n_cols < 0)
+        return -1;
+    if (mx && D % 32 != 0)
         return -1;
 #ifdef _OPENMP
     if (n_threads > 0)
@@ -249,6 +342,11 @@ static int score_rows(const uint16_t *q, const uint8_t *q8, const float *w,
         } else {
             for (i = 0; i < (int64_t)H * D; ++i)
                 qd[i] = bf16_value(q[(int64_t)b * H * D + i]);
+            if (mx) {
+                int32_t h;
+                for (h = 0; h < H; ++h)
+                    oracle_mxfp4_round(qd + (int64_t)h * D, D, qd + (int64_t)h * D);
+            }
         }
         for (c = 0; c < n_cols; ++c) {
             int64_t entry;
@@ -259,7 +357,7 @@ static int score_rows(const uint16_t *q, const uint8_t *q8, const float *w,
             double v = -INFINITY;
             if (prow >= 0)
                 v = logit_of_row(qd, w + (int64_t)b * H, H, D,
-                                 pool + prow * row_bytes, k);
+                                 pool + prow * row_bytes, k, mx);
             logits[(int64_t)b * n_cols + c] = v;
         }
         free(qd);
@@ -278,7 +376,22 @@ int oracle_score(const uint16_t *q, const float *w, int32_t B, int32_t H,
 {
     return score_rows(q, NULL, w, B, H, D, pool, n_pool_rows, block_size,
                       block_table, n_req, max_blocks, q_req, chunk_ids,
-                      n_chunks, max_chunks, limits, n_cols, logits, n_threads);
+                      n_chunks, max_chunks, limits, n_cols, logits, n_threads, 0);
+}
+
+/* The MXFP4 variant: q (bf16 bits) and the keys rounded to MXFP4 blocks of
+ * 32 (section above), then the same definition. */
+int oracle_score_mxfp4(const uint16_t *q, const float *w, int32_t B, int32_t H,
+                       int32_t D, const uint8_t *pool, int64_t n_pool_rows,
+                       int32_t block_size, const int32_t *block_table,
+                       int32_t n_req, int32_t max_blocks, const int32_t *q_req,
+                       const int32_t *chunk_ids, const int32_t *n_chunks,
+                       int32_t max_chunks, const int32_t *limits, int32_t n_cols,
+                       double *logits, int32_t n_threads)
+{
+    return score_rows(q, NULL, w, B, H, D, pool, n_pool_rows, block_size,
+                      block_table, n_req, max_blocks, q_req, chunk_ids,
+                      n_chunks, max_chunks, limits, n_cols, logits, n_threads, 1);
 }
 
 int oracle_score_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H,
@@ -293,7 +406,7 @@ int oracle_score_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H,
         return -1;
     return score_rows(NULL, q8, w, B, H, D, pool, n_pool_rows, block_size,
                       block_table, n_req, max_blocks, q_req, chunk_ids,
-                      n_chunks, max_chunks, limits, n_cols, logits, n_threads);
+                      n_chunks, max_chunks, limits, n_cols, logits, n_threads, 0);
 }
 
 double oracle_sigmoid(double x)

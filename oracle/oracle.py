@@ -64,6 +64,14 @@ def _load():
         _c_f64p, ctypes.c_int32]
     lib.oracle_score_q8.restype = ctypes.c_int
     lib.oracle_score_q8.argtypes = [_c_u8p] + lib.oracle_score.argtypes[1:]
+    lib.oracle_score_mxfp4.restype = ctypes.c_int
+    lib.oracle_score_mxfp4.argtypes = lib.oracle_score.argtypes
+    lib.oracle_e2m1_round.restype = ctypes.c_double
+    lib.oracle_e2m1_round.argtypes = [ctypes.c_double]
+    lib.oracle_mxfp4_exponent.restype = ctypes.c_int
+    lib.oracle_mxfp4_exponent.argtypes = [ctypes.c_double]
+    lib.oracle_mxfp4_round.restype = None
+    lib.oracle_mxfp4_round.argtypes = [_c_f64p, ctypes.c_int32, _c_f64p]
     lib.oracle_topk.restype = ctypes.c_int
     lib.oracle_topk.argtypes = [_c_f64p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                 ctypes.c_int32, _c_i32p, _c_f64p, ctypes.c_int32]
@@ -133,15 +141,36 @@ def sigmoid_scalar(x: float) -> float:
     return float(_load().oracle_sigmoid(float(x)))
 
 
+def e2m1_round(x: float) -> float:
+    """The E2M1 value nearest x (ties to the even code, saturating at 6)."""
+    return float(_load().oracle_e2m1_round(float(x)))
+
+
+def mxfp4_exponent(amax: float) -> int:
+    """MXFP4 block exponent for a block whose largest magnitude is amax > 0."""
+    return int(_load().oracle_mxfp4_exponent(float(amax)))
+
+
+def mxfp4_round(v) -> np.ndarray:
+    """v (length a multiple of 32) rounded to MXFP4 block by block."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    assert v.size % 32 == 0
+    out = np.empty_like(v)
+    _load().oracle_mxfp4_round(_ptr(v.reshape(-1), ctypes.c_double), v.size,
+                               _ptr(out.reshape(-1), ctypes.c_double))
+    return out
+
+
 def _i32(a):
     return None if a is None else np.ascontiguousarray(a, dtype=np.int32)
 
 
-def score(wl, rows=None, n_threads: int = 0, q8=None) -> np.ndarray:
+def score(wl, rows=None, n_threads: int = 0, q8=None, mxfp4: bool = False) -> np.ndarray:
     """Double logits [B, n_cols] (or [len(rows), n_cols] for a row subset);
     unscored columns are -inf.  With q8 (uint8 [B, H, D + 4] quantised query
     rows, see quantize_q) the query is q8's dequantised values instead of
-    wl.q."""
+    wl.q.  With mxfp4, query heads and keys are rounded to MXFP4 blocks of
+    32 first (the MXFP4 variant)."""
     q = np.ascontiguousarray(wl.q, dtype=np.uint16)
     if q8 is not None:
         q8 = np.ascontiguousarray(q8, dtype=np.uint8)
@@ -172,8 +201,12 @@ def score(wl, rows=None, n_threads: int = 0, q8=None) -> np.ndarray:
     pool = np.ascontiguousarray(wl.pool, dtype=np.uint8)
     assert pool.shape[1] == D + 4
     out = np.empty((B, wl.n_cols), dtype=np.float64)
-    fn, qp = ((_load().oracle_score, _ptr(q, ctypes.c_uint16)) if q8 is None
-              else (_load().oracle_score_q8, _ptr(q8, ctypes.c_uint8)))
+    assert not (mxfp4 and q8 is not None)
+    if q8 is not None:
+        fn, qp = _load().oracle_score_q8, _ptr(q8, ctypes.c_uint8)
+    else:
+        fn = _load().oracle_score_mxfp4 if mxfp4 else _load().oracle_score
+        qp = _ptr(q, ctypes.c_uint16)
     rc = fn(
         qp, _ptr(w, ctypes.c_float), B, H, D,
         _ptr(pool, ctypes.c_uint8), pool.shape[0], wl.block_size,

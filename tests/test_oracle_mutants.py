@@ -62,6 +62,23 @@ MUTANTS = {
     "sigmoid-half-slope": ("return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(-0.5 * x));"),
     "chunk-entry-stride-64": ("e = chunk_ids[(int64_t)b * max_chunks + j] * block_size + s;",
                               "e = chunk_ids[(int64_t)b * max_chunks + j] * 64 + s;"),
+    "mx-ties-to-larger": ("if (d < best_d || (d == best_d && (c & 1) == 0 && (best_c & 1) == 1)) {",
+                          "if (d <= best_d) {"),
+    "mx-ties-to-smaller": ("if (d < best_d || (d == best_d && (c & 1) == 0 && (best_c & 1) == 1)) {",
+                           "if (d < best_d) {"),
+    "mx-sign-dropped": ("return x < 0.0 ? -best : best;", "return best;"),
+    "mx-exponent-ceil": ("e = (ex - 1) - 2;                    /* floor(log2(amax)) - 2 */",
+                         "e = ex - 2;"),
+    "mx-exponent-minus-3": ("e = (ex - 1) - 2;                    /* floor(log2(amax)) - 2 */",
+                            "e = (ex - 1) - 3;"),
+    "mx-no-low-clamp": ("    if (e < -127)\n        e = -127;\n", ""),
+    "mx-key-not-rounded": ("        oracle_mxfp4_round(k, D, k);\n", ""),
+    "mx-query-not-rounded": ("                    oracle_mxfp4_round(qd + (int64_t)h * D, D, qd + (int64_t)h * D);",
+                             "                    (void)h;"),
+    "mx-key-rounded-after-scale": ("            k[d] = oracle_e4m3_value(key_row[d]);\n        oracle_mxfp4_round(k, D, k);\n        for (d = 0; d < D; ++d)\n            k[d] = k[d] * scale;",
+                                   "            k[d] = oracle_e4m3_value(key_row[d]) * scale;\n        oracle_mxfp4_round(k, D, k);"),
+    "mx-blocks-of-16": ("        x = ldexp(1.0, oracle_mxfp4_exponent(amax));\n        for (i = 0; i < 32; ++i)",
+                        "        x = ldexp(1.0, oracle_mxfp4_exponent(amax));\n        for (i = 0; i < 16; ++i)"),
 }
 
 PIN_TESTS = [
@@ -90,6 +107,12 @@ PIN_TESTS = [
     pins.test_16_row_blocks_are_a_relabelling,
     pins.test_16_row_chunk_lists_read_the_listed_small_blocks,
     pins.test_sigmoid_values_closed_form,
+    pins.test_e2m1_round_closed_form,
+    pins.test_mxfp4_exponent_closed_form,
+    pins.test_mxfp4_round_worked_blocks,
+    pins.test_mxfp4_round_is_identity_on_the_grid,
+    pins.test_mxfp4_scores_equal_plain_scores_when_rounding_is_exact,
+    pins.test_mxfp4_score_closed_form,
 ]
 
 

@@ -737,3 +737,118 @@ def test_quantised_query_closed_form():
                     limits=np.array([1], np.int32), n_cols=1)
     got = oracle.score(wl, q8=q8)[0, 0]
     assert got == 1.0 * 0.5 * 1.5 * 0.25 * 3.0
+
+
+# ------------------------------------------------------------ MXFP4 variant
+# E2M1 (1 sign, 2 exponent bits of bias 1, 1 mantissa bit) has the magnitudes
+# 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6; MXFP4 blocks of 32 share a scale
+# 2^e with e = floor(log2(amax)) - 2.  The values below are worked out by
+# hand from those definitions.
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_round_closed_form():
+    """Every E2M1 value maps to itself; the midpoints go to the even code
+    (mantissa bit 0: 0, 1, 2, 4); anything past a midpoint goes to the far
+    side; magnitudes above 6 saturate; the sign is kept."""
+    for g in E2M1:
+        assert oracle.e2m1_round(g) == g and oracle.e2m1_round(-g) == -g
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0}
+    for x, want in ties.items():
+        assert oracle.e2m1_round(x) == want, x
+        assert oracle.e2m1_round(-x) == -want, -x
+    off = {0.2499: 0.0, 0.2501: 0.5, 0.7499: 0.5, 1.2501: 1.5, 1.7499: 1.5, 2.5001: 3.0,
+           3.4999: 3.0, 4.9999: 4.0, 5.0001: 6.0, 6.5: 6.0, 7.99: 6.0, 1e30: 6.0}
+    for x, want in off.items():
+        assert oracle.e2m1_round(x) == want, x
+        assert oracle.e2m1_round(-x) == -want, -x
+
+
+def test_mxfp4_exponent_closed_form():
+    """e = floor(log2(amax)) - 2, clamped to the E8M0 range [-127, 127]."""
+    cases = {1.0: -2, 1.5: -2, 1.999: -2, 2.0: -1, 4.0: 0, 6.0: 0, 7.99: 0, 8.0: 1, 0.75: -3,
+             448.0: 6, 2.0 ** -100: -102, 2.0 ** -130: -127, 2.0 ** 130: 127}
+    for amax, want in cases.items():
+        assert oracle.mxfp4_exponent(amax) == want, amax
+
+
+def test_mxfp4_round_worked_blocks():
+    """Four blocks of 32: (1) amax 7 -> scale 1: 7 saturates to 6, 0.3 -> 0.5,
+    -2.6 -> -3, 0.2 -> 0, the tie 0.25 -> 0; (2) amax 0.02 -> scale 2^-8:
+    0.02 / 2^-8 = 5.12 -> 6, 0.01 / 2^-8 = 2.56 -> 3; (3) zeros stay zero;
+    (4) values already on the block's grid stay put."""
+    v = np.zeros(128)
+    v[0:6] = [7.0, 1.0, 0.3, -2.6, 0.2, 0.25]
+    v[32:34] = [0.02, -0.01]
+    v[96:100] = [6.0 * 2 ** -5, -0.5 * 2 ** -5, 3.0 * 2 ** -5, 1.5 * 2 ** -5]
+    got = oracle.mxfp4_round(v)
+    want = np.zeros(128)
+    want[0:6] = [6.0, 1.0, 0.5, -3.0, 0.0, 0.0]
+    want[32:34] = [6.0 * 2 ** -8, -3.0 * 2 ** -8]
+    want[96:100] = v[96:100]
+    assert np.array_equal(got, want)
+
+
+def test_mxfp4_round_is_identity_on_the_grid():
+    """Blocks of +-E2M1 values times 2^e with a largest magnitude of 4 or 6
+    (so the block's exponent is e) round to themselves."""
+    rng = np.random.default_rng(31)
+    for _ in range(200):
+        e = int(rng.integers(-60, 60))
+        g = np.array(E2M1)[rng.integers(0, 8, size=32)] * np.where(rng.random(32) < 0.5, -1.0, 1.0)
+        g[rng.integers(0, 32)] = rng.choice([4.0, 6.0, -4.0, -6.0])
+        v = g * 2.0 ** e
+        assert np.array_equal(oracle.mxfp4_round(v), v)
+
+
+def _mx_grid_values(rng, shape, e):
+    """+-E2M1 values times 2^e, each block of 32 holding a +-4 or +-6."""
+    g = np.array(E2M1)[rng.integers(0, 8, size=shape)] * np.where(rng.random(shape) < 0.5, -1.0, 1.0)
+    blocks = g.reshape(-1, 32)
+    blocks[np.arange(len(blocks)), rng.integers(0, 32, size=len(blocks))] = rng.choice([4.0, 6.0, -6.0], len(blocks))
+    return blocks.reshape(shape) * np.exp2(np.asarray(e, dtype=np.float64))
+
+
+def test_mxfp4_scores_equal_plain_scores_when_rounding_is_exact():
+    """Query heads and key rows already on MXFP4 grids (blocks of E2M1
+    values times 2^e): the MXFP4 variant's logits equal the plain ones bit
+    for bit."""
+    rng = np.random.default_rng(37)
+    wl = W.small_config(1)
+    e_q = rng.integers(-12, 12, size=(wl.B, wl.H, 1))
+    wl.q = _bf16(_mx_grid_values(rng, (wl.B, wl.H, wl.D), e_q).astype(np.float32))
+    # key codes: e4m3 bytes of E2M1 values times 2^e (e in [-5, 5]: all exact in e4m3)
+    n = wl.pool.shape[0]
+    e_k = rng.integers(-5, 6, size=(n, 1))
+    vals = _mx_grid_values(rng, (n, wl.D), e_k)
+    codes = np.array([oracle.e4m3_encode(float(x)) for x in vals.reshape(-1)], np.uint8).reshape(n, wl.D)
+    assert np.array_equal(np.vectorize(oracle.e4m3_value)(codes), vals)
+    wl.pool = wl.pool.copy()
+    wl.pool[:, :wl.D] = codes
+    a = oracle.score(wl)
+    b = oracle.score(wl, mxfp4=True)
+    assert np.array_equal(a, b)
+
+
+def test_mxfp4_score_closed_form():
+    """One key row whose first block holds e4m3 values 7 and 1 (scale 0.3)
+    and one head whose first block holds 1 and 0.8984375 (bf16 of 0.9):
+    the key block rounds to 6 and 1 at scale 1, the query block to 1 and 1
+    at scale 1/4, so the logit is relu((6 + 1) * 0.3) * w = 2.1 * w for a
+    positive scale and 0 when the scale is negated."""
+    H, D = 64, 128
+    codes = np.zeros(D, np.uint8)
+    codes[0] = oracle.e4m3_encode(7.0)
+    codes[1] = oracle.e4m3_encode(1.0)
+    q = np.zeros((1, H, D), np.float32)
+    q[0, 3, 0], q[0, 3, 1] = 1.0, 0.9
+    w = np.zeros((1, H), np.float32)
+    w[0, 3] = 2.0
+    for s, want in ((0.3, 7.0 * np.float64(np.float32(0.3)) * 2.0), (-0.3, 0.0)):
+        row = _key_row(codes, s)
+        wl = W.Workload(name="mx-one-hot", q=_bf16(q), w=w, pool=row[None].copy(),
+                        limits=np.array([1], np.int32), n_cols=1)
+        assert oracle.score(wl, mxfp4=True)[0, 0] == want
+        plain = (7.0 + 1.0 * float(np.float32(0.8984375))) * np.float64(np.float32(s)) * 2.0
+        assert oracle.score(wl)[0, 0] == max(plain, 0.0)
