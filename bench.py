@@ -35,7 +35,9 @@ second and `roofline` covers the writer kernel.
 `--q8` measures the quantised-query variant on a scoring workload: each step
 is one idx_score_topk_fp8q (the score kernel quantises q per head by the
 writer's rule, then scores on fp8 MFMA); the prefill roofline is then priced
-at the fp8 MFMA peak.
+at the fp8 MFMA peak.  `--mxfp4` measures the MXFP4 variant the same way (one
+idx_score_topk_mxfp4 per step: query and keys rounded to MXFP4 blocks inside
+the score kernel, e2m1 MFMA; the prefill roofline priced at the fp4 peak).
 
 `--block-size 16` re-lays a scoring workload's pool into 16-row blocks, each
 placed on its own (the block table grows fourfold, chunk lists are cut into
@@ -62,6 +64,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, TFLOP/s
+MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 MFMA, TFLOP/s
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 SCORE_SOURCES = ["sparse_attention_kv_paged_amd/csrc/idx_score.hip",
                  "sparse_attention_kv_paged_amd/csrc/idx_device.h",
@@ -567,6 +570,9 @@ def main():
     ap.add_argument("--q8", action="store_true",
                     help="quantised-query variant: idx_score_topk_fp8q (q quantised per head inside the score "
                          "kernel, fp8 MFMA)")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="MXFP4 variant: idx_score_topk_mxfp4 (q and keys rounded to MXFP4 blocks of 32 inside the "
+                         "score kernel, e2m1 MFMA)")
     ap.add_argument("--block-size", type=int, default=64, choices=(64, 16),
                     help="pool block rows of the scoring workloads (16: the same keys re-laid in 16-row blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -582,7 +588,8 @@ def main():
 
     trace_prefix = {WRITE_WORKLOAD: "write_keys", RESIDENT_WORKLOAD: "select_resident"}.get(args.workload,
                                                                                           "score_topk")
-    prof_name = args.workload + ("-b16" if args.block_size == 16 else "") + ("-q8" if args.q8 else "")
+    prof_name = (args.workload + ("-b16" if args.block_size == 16 else "") + ("-q8" if args.q8 else "")
+                 + ("-mxfp4" if args.mxfp4 else ""))
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, prof_name, args.command,
                         os.path.join(PROFILE_DIR, f"{trace_prefix}_{prof_name}_trace.txt"))
@@ -601,8 +608,12 @@ def main():
               f"the library runs on one GPU and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
-    if (args.q8 or args.block_size != 64) and args.workload in (WRITE_WORKLOAD, RESIDENT_WORKLOAD):
-        print(f"--q8 and --block-size apply to the scoring workloads, not {args.workload}", file=sys.stderr)
+    if (args.q8 or args.mxfp4 or args.block_size != 64) and args.workload in (WRITE_WORKLOAD, RESIDENT_WORKLOAD):
+        print(f"--q8, --mxfp4 and --block-size apply to the scoring workloads, not {args.workload}",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.q8 and args.mxfp4:
+        print("--q8 and --mxfp4 are two different variants; pick one", file=sys.stderr)
         sys.exit(2)
     if args.workload == WRITE_WORKLOAD:
         bench_writer(args)
@@ -647,7 +658,7 @@ def measure_scoring(name, args):
 
     wl = scoring_workload(name, args, workloads)
     pairs = wl.pairs()
-    prof_name = wl.name + ("-q8" if args.q8 else "")
+    prof_name = wl.name + ("-q8" if args.q8 else "") + ("-mxfp4" if args.mxfp4 else "")
     print(f"[bench] workload {wl.name}: {wl.description}; pairs {pairs}", file=sys.stderr, flush=True)
     d = lib.to_device(wl)
     pool_bytes = d.keys.pool.numel()
@@ -669,6 +680,10 @@ def measure_scoring(name, args):
         def step(i):
             lib.idx_score_topk_fp8q(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
                                     out_idx=out_idx, out_val=out_val, workspace=ws)
+    elif args.mxfp4:
+        def step(i):
+            lib.idx_score_topk_mxfp4(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
+                                     out_idx=out_idx, out_val=out_val, workspace=ws)
     else:
         def step(i):
             lib.idx_score_topk(qs[i % R], d.w, keys[i % R], wl.n_cols, k,
@@ -690,7 +705,8 @@ def measure_scoring(name, args):
     algo = algorithmic_bytes(wl, pairs)
     kern_bytes = score_kernel_bytes(wl, pairs, logits_written=False)
     flop = 2.0 * wl.H * wl.D * pairs
-    mfma_peak = MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_BF16_PEAK_TFLOPS
+    mfma_peak = (MFMA_FP8_PEAK_TFLOPS if args.q8 else MFMA_FP4_PEAK_TFLOPS if args.mxfp4
+                 else MFMA_BF16_PEAK_TFLOPS)
     traffic = read_traffic(prof_name)
     prefill = shares_request_keys(wl)
     if prefill:
@@ -739,10 +755,11 @@ def measure_scoring(name, args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8" if args.q8 else "bf16",
+        "dtype": "fp8" if args.q8 else "fp4" if args.mxfp4 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "queries": wl.B, "heads": wl.H, "head_dim": wl.D,
-                   "query": "e4m3, quantised per head in the score kernel" if args.q8 else "bf16",
+                   "query": ("e4m3, quantised per head in the score kernel" if args.q8 else
+                             "MXFP4 (blocks of 32, keys too), rounded in the score kernel" if args.mxfp4 else "bf16"),
                    "block": wl.block_size, "k": k, "n_cols": wl.n_cols, "pairs": pairs,
                    "description": wl.description, "replicas": R, "graph": not args.no_graph},
         "queries_per_s": wl.B / (ms_per_step * 1e-3),

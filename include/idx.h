@@ -259,6 +259,36 @@ int idx_score_topk_fp8q(const uint16_t *q, const float *w, int32_t B,
                         void *stream);
 
 /*
+ * idx_score_mxfp4 / idx_score_topk_mxfp4: the MXFP4 variant.  The published
+ * model rounds the index query and key alike to FP4 before the index score,
+ * whatever the index plane holds ("DeepSeek-V4.1 native paged runtime",
+ * section "Current execution scope"); the batchgen pull request names the
+ * format MXFP4 (its fp8-fallback commit: selector auto | mxfp4 | fp8, with an
+ * e4m3 fallback at one scale per 32 values).  Here both are rounded inside
+ * the score kernel to OCP MXFP4 blocks of 32 consecutive dims (one query
+ * head's, or one key row's): the block scale is 2^e with
+ * e = floor(log2(amax)) - 2 (clamped to >= -127), each value the nearest E2M1
+ * value (0, 0.5, 1, 1.5, 2, 3, 4, 6) of v / 2^e, ties to the even code,
+ * saturating at 6.  A key's e4m3 values are the block's values and its fp32
+ * row scale stays a factor outside the rounding:
+ *
+ *     logit = sum_h relu( s * sum_d mx(e4m3(key))[d] * mx(q[b,h])[d] ) * w[b,h]
+ *
+ * The contraction runs on v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1
+ * operands and the blocks' E8M0 scales.  Arguments, outputs, rules and
+ * errors as for idx_score / idx_score_topk (q bf16 [B, H, D], 16-byte
+ * aligned), with H = 64 (IDX_E_SHAPE otherwise).
+ */
+int idx_score_mxfp4(const uint16_t *q, const float *w, int32_t B, int32_t H,
+                    int32_t D, const idx_keys *keys, int32_t n_cols,
+                    float *logits, float *scores, void *stream);
+int idx_score_topk_mxfp4(const uint16_t *q, const float *w, int32_t B,
+                         int32_t H, int32_t D, const idx_keys *keys,
+                         int32_t n_cols, int32_t k, int32_t *out_idx,
+                         float *out_val, void *workspace, size_t ws_bytes,
+                         void *stream);
+
+/*
  * idx_write_keys: the index-plane writer -- quantise new compressed keys and
  * store them as pool rows in the layout idx_score reads ("FlashMemory-
  * DeepSeek-V4" README, section "compressed_k format": D float8_e4m3 bytes

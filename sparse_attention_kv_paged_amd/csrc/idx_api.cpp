@@ -300,9 +300,9 @@ int check_qw_quant(const uint16_t *q, const float *w, int32_t B, int32_t H, int3
 
 int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
                const idx_keys *keys, int32_t n_cols, float *logits, float *scores, void *stream,
-               bool quant_q = false) {
+               bool quant_q = false, bool mx = false) {
     g_last_error[0] = 0;
-    int rc = quant_q ? check_qw_quant(q, w, B, H, D) : check_qw8(q, q8, w, B, H, D);
+    int rc = quant_q || mx ? check_qw_quant(q, w, B, H, D) : check_qw8(q, q8, w, B, H, D);
     if (rc) return rc;
     if ((rc = check_keys(keys, B))) return rc;
     if ((rc = check_cols(n_cols))) return rc;
@@ -313,6 +313,7 @@ int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, 
     idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
     a.q8 = q8;
     a.quant_q = quant_q;
+    a.mxfp4 = mx;
     a.ld = n_cols;
     a.logits = logits;
     a.scores = scores;
@@ -324,8 +325,8 @@ int score_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, 
 // call with B == 0 passes with an empty plan (nothing to launch).
 int score_topk_check(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
                      const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
-                     TopkPlan &P, bool quant_q = false) {
-    int rc = quant_q ? check_qw_quant(q, w, B, H, D) : check_qw8(q, q8, w, B, H, D);
+                     TopkPlan &P, bool quant_q = false, bool mx = false) {
+    int rc = quant_q || mx ? check_qw_quant(q, w, B, H, D) : check_qw8(q, q8, w, B, H, D);
     if (rc) return rc;
     if ((rc = check_keys(keys, B))) return rc;
     if ((rc = check_cols(n_cols))) return rc;
@@ -341,10 +342,11 @@ int score_topk_check(const uint16_t *q, const uint8_t *q8, const float *w, int32
 // Enqueue a checked score + top-k call (B > 0) on a workspace of P.total bytes.
 int score_topk_launch(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H,
                       const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
-                      const TopkPlan &P, char *ws, void *stream, bool quant_q = false) {
+                      const TopkPlan &P, char *ws, void *stream, bool quant_q = false, bool mx = false) {
     idx::ScoreArgs a = score_args(q, w, B, keys, n_cols);
     a.q8 = q8;
     a.quant_q = quant_q;
+    a.mxfp4 = mx;
     a.ld = P.ld;
     a.logits = reinterpret_cast<float *>(ws + P.logits);
     a.scores = nullptr;
@@ -360,16 +362,16 @@ int score_topk_launch(const uint16_t *q, const uint8_t *q8, const float *w, int3
 
 int score_topk_impl(const uint16_t *q, const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D,
                     const idx_keys *keys, int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val,
-                    void *workspace, size_t ws_bytes, void *stream, bool quant_q = false) {
+                    void *workspace, size_t ws_bytes, void *stream, bool quant_q = false, bool mx = false) {
     g_last_error[0] = 0;
     TopkPlan P;
-    int rc = score_topk_check(q, q8, w, B, H, D, keys, n_cols, k, out_idx, out_val, P, quant_q);
+    int rc = score_topk_check(q, q8, w, B, H, D, keys, n_cols, k, out_idx, out_val, P, quant_q, mx);
     if (rc || B == 0) return rc;
     if (P.total > 0 && (!workspace || ws_bytes < P.total))
         return fail(IDX_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", P.total, ws_bytes);
     if (!aligned(workspace, 256)) return fail(IDX_E_ALIGN, "workspace must be 256-byte aligned");
     return score_topk_launch(q, q8, w, B, H, keys, n_cols, k, out_idx, out_val, P, static_cast<char *>(workspace),
-                             stream, quant_q);
+                             stream, quant_q, mx);
 }
 
 // ---------------------------------------------------------------------------
@@ -597,6 +599,18 @@ int idx_score_topk_fp8q(const uint16_t *q, const float *w, int32_t B, int32_t H,
                         size_t ws_bytes, void *stream) {
     return score_topk_impl(q, nullptr, w, B, H, D, keys, n_cols, k, out_idx, out_val, workspace, ws_bytes, stream,
                            true);
+}
+
+int idx_score_mxfp4(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,
+                    int32_t n_cols, float *logits, float *scores, void *stream) {
+    return score_impl(q, nullptr, w, B, H, D, keys, n_cols, logits, scores, stream, false, true);
+}
+
+int idx_score_topk_mxfp4(const uint16_t *q, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,
+                         int32_t n_cols, int32_t k, int32_t *out_idx, float *out_val, void *workspace,
+                         size_t ws_bytes, void *stream) {
+    return score_topk_impl(q, nullptr, w, B, H, D, keys, n_cols, k, out_idx, out_val, workspace, ws_bytes, stream,
+                           false, true);
 }
 
 int idx_score_topk_q8(const uint8_t *q8, const float *w, int32_t B, int32_t H, int32_t D, const idx_keys *keys,

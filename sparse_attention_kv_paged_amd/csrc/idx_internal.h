@@ -25,6 +25,7 @@ struct ScoreArgs {
     int32_t w_row;              // floats from one w row to the next (64, or 128)
     bool accum;                 // add to the logits already in the output (the second head half)
     bool quant_q;               // q is bf16 and is quantised here by the writer's rule (q8 null)
+    bool mxfp4;                 // q (bf16) and the keys are rounded to MXFP4 blocks of 32 here (q8 null)
     const float *w;             // [B, 64]
     int32_t B;
     const uint8_t *pool;        // [n_pool_rows, 132]

@@ -60,11 +60,23 @@ struct QFp8 {
     v8i v[2][2];
     float qs;       // the quantisation scale of head `lane` (the head whose weight the lane holds)
 };
-template <bool Q8> struct QSel {
+// MXFP4 path (query and key rounded to MXFP4 blocks of 32 in the kernel):
+// 2 head blocks x 2 k-steps of 32 e2m1 codes (16 bytes, value j in nibble
+// j % 8 of dword j / 8, low nibble first), and per head block the E8M0
+// scales of the lane's two 32-value blocks (byte kk for k-step kk), for
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands e2m1.
+struct QFp4 {
+    u32x4 v[2][2];
+    uint32_t sc[2];
+};
+template <bool Q8, bool MX = false> struct QSel {
     using Op = QBf16;
 };
-template <> struct QSel<true> {
+template <> struct QSel<true, false> {
     using Op = QFp8;
+};
+template <bool Q8> struct QSel<Q8, true> {
+    using Op = QFp4;
 };
 
 struct RowCtx {
@@ -334,6 +346,113 @@ __device__ __forceinline__ void tile_mma(KeyHalf &k, const QFp8 &qa, TileAcc &ac
     acc.h1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa.v[1][1], b1, acc.h1, 0, 0, 0, 127, 0, 127);
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// One MXFP4 block ("DeepSeek-V4.1 native paged runtime", "Current execution
+// scope": the published model rounds index query and key to FP4; the format
+// is OCP MXFP4): 32 bf16 values (raw: 16 dwords of two values, the lower
+// half first) -> 32 e2m1 codes and the block's E8M0 scale byte e + 127, with
+// e = floor(log2(amax)) - 2 clamped to >= -127.  Each code is the nearest
+// e2m1 value of v / 2^e, ties to even, saturating at 6: the packed
+// conversion divides by its scale operand and rounds so.  Blocks with
+// e = -127 (amax < 2^-124, zero blocks included) are converted from binary32
+// values scaled by 2^64 against 2^-63, so the scale operand stays normal
+// (both products exact).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t d, uint32_t raw, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, raw), scale, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair_f32(uint32_t d, float lo, float hi, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, lo, hi, scale, SEL);
+}
+__device__ __forceinline__ uint32_t mx_block_bf16(const uint32_t (&raw)[16], u32x4 &codes) {
+    // bf16 magnitudes order like their bit patterns: a packed 16-bit max
+    u16x2 m2 = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, raw[i] & 0x7FFF7FFFu));
+    const uint32_t amax = m2.x > m2.y ? m2.x : m2.y;
+    const int ex = (int)(amax >> 7);                 // biased exponent of the block's amax
+    const int e = max(ex - 129, -127);
+    uint32_t d[4];
+    if (e > -127) {
+        const float scale = __uint_as_float((uint32_t)(e + 127) << 23);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t x = fp4_pair<0>(0u, raw[4 * w], scale);
+            x = fp4_pair<1>(x, raw[4 * w + 1], scale);
+            x = fp4_pair<2>(x, raw[4 * w + 2], scale);
+            d[w] = fp4_pair<3>(x, raw[4 * w + 3], scale);
+        }
+    } else {
+        const float scale = 0x1p-63f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t x = 0u;
+            const float l0 = __uint_as_float(raw[4 * w] << 16) * 0x1p64f;
+            const float h0 = __uint_as_float(raw[4 * w] & 0xFFFF0000u) * 0x1p64f;
+            const float l1 = __uint_as_float(raw[4 * w + 1] << 16) * 0x1p64f;
+            const float h1 = __uint_as_float(raw[4 * w + 1] & 0xFFFF0000u) * 0x1p64f;
+            const float l2 = __uint_as_float(raw[4 * w + 2] << 16) * 0x1p64f;
+            const float h2 = __uint_as_float(raw[4 * w + 2] & 0xFFFF0000u) * 0x1p64f;
+            const float l3 = __uint_as_float(raw[4 * w + 3] << 16) * 0x1p64f;
+            const float h3 = __uint_as_float(raw[4 * w + 3] & 0xFFFF0000u) * 0x1p64f;
+            x = fp4_pair_f32<0>(x, l0, h0, scale);
+            x = fp4_pair_f32<1>(x, l1, h1, scale);
+            x = fp4_pair_f32<2>(x, l2, h2, scale);
+            d[w] = fp4_pair_f32<3>(x, l3, h3, scale);
+        }
+    }
+    codes = u32x4{d[0], d[1], d[2], d[3]};
+    return (uint32_t)(e + 127);
+}
+
+__device__ __forceinline__ v8i fp4_operand(const u32x4 &x) {
+    return v8i{(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+}
+
+// The MXFP4 path: the lane's 64 key bytes are its two 32-value blocks
+// (d = 64*hf + 32*kk + 0..31 for k-step kk, as in q); each is widened
+// exactly to bf16, rounded to an MXFP4 block, and the contraction runs on
+// e2m1 operands with the blocks' E8M0 scales.  The row scale stays outside
+// (its sign flipped into the fp8 bytes first, as in tile_mma above).
+__device__ __forceinline__ void tile_mma(KeyHalf &k, const QFp4 &qa, TileAcc &acc) {
+    if (__any(k.s < 0.f)) {
+        const uint32_t m = (k.s < 0.f) ? 0x80808080u : 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k.v[i] ^= u32x4{m, m, m, m};
+    }
+    u32x4 kc[2];
+    uint32_t ksc = 0;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        uint32_t raw[16];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x4 &x = k.v[2 * blk + j];
+            const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                raw[8 * j + 2 * i] = cvt_fp8x2_bf16x2<false>(w4[i]);
+                raw[8 * j + 2 * i + 1] = cvt_fp8x2_bf16x2<true>(w4[i]);
+            }
+        }
+        ksc |= mx_block_bf16(raw, kc[blk]) << (8 * blk);
+    }
+    const f32x16 z = {};
+    // format 4 = e2m1 for both operands; op_sel picks scale byte kk
+    acc.h0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[0][0]), fp4_operand(kc[0]), z, 4, 4, 0,
+                                                            (int)qa.sc[0], 0, (int)ksc);
+    acc.h1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[1][0]), fp4_operand(kc[0]), z, 4, 4, 0,
+                                                            (int)qa.sc[1], 0, (int)ksc);
+    acc.h0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[0][1]), fp4_operand(kc[1]), acc.h0, 4,
+                                                            4, 1, (int)qa.sc[0], 1, (int)ksc);
+    acc.h1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[1][1]), fp4_operand(kc[1]), acc.h1, 4,
+                                                            4, 1, (int)qa.sc[1], 1, (int)ksc);
+}
+
 // Epilogue half: relu, head weights and head sum, then the row scale.
 // wr[hb][g][i%4] holds the weight w[b] of the head that accumulator
 // register i = 4*g + i%4 of head block hb carries on this lane.  Returns the
@@ -459,6 +578,33 @@ __device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QFp8 &q
     }
     // lane l holds the weight of head l: head block 0 for l < 32, else 1
     qa.qs = lane < 32 ? scale[0] : scale[1];
+}
+
+// q[b] rounded to MXFP4 from global memory: the lane's four 32-value blocks
+// (head 32*hb + (lane & 31), d = 64*(lane >> 5) + 32*kk + 0..31), each held
+// whole by the lane.
+__device__ __forceinline__ void load_q_global(const ScoreArgs &a, int b, QFp4 &qa) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        uint32_t sc = 0;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const u32x4 *qp = reinterpret_cast<const u32x4 *>(
+                a.q + (int64_t)b * a.q_row + (int64_t)(32 * hb + (lane & 31)) * kHeadDim + 64 * (lane >> 5) + 32 * kk);
+            uint32_t raw[16];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 x = qp[j];
+                raw[4 * j] = x.x;
+                raw[4 * j + 1] = x.y;
+                raw[4 * j + 2] = x.z;
+                raw[4 * j + 3] = x.w;
+            }
+            sc |= mx_block_bf16(raw, qa.v[hb][kk]) << (8 * kk);
+        }
+        qa.sc[hb] = sc;
+    }
 }
 
 
@@ -601,6 +747,48 @@ __device__ __forceinline__ void load_q_staged(const uint16_t *row, QFp8 &qa) {
     }
 }
 
+// MXFP4 staged rows: per head 64 code bytes (blocks 0..3 of 16 bytes), its
+// four scale bytes, padding to 80 bytes (the 16 heads a quarter-wave reads
+// then sit in different bank groups).
+constexpr int kMxStage = 80;
+
+// A staged bf16 row (LDS, padded rows) rounded in place to MXFP4: thread t
+// takes block t % 4 of head t / 4.  Every thread reads its values before any
+// writes (the rounded row is shorter and overwrites the front of the bf16
+// one); the caller synchronises before (the bf16 row written) and after.
+__device__ __forceinline__ void quantize_staged_row_mx(uint16_t *slot) {
+    const int h = threadIdx.x >> 2, blk = threadIdx.x & 3;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(slot + h * kQPad + 32 * blk);
+    uint32_t raw[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x4 x = src[j];
+        raw[4 * j] = x.x;
+        raw[4 * j + 1] = x.y;
+        raw[4 * j + 2] = x.z;
+        raw[4 * j + 3] = x.w;
+    }
+    __syncthreads();
+    u32x4 codes;
+    const uint32_t sb = mx_block_bf16(raw, codes);
+    uint8_t *row = reinterpret_cast<uint8_t *>(slot) + h * kMxStage;
+    *reinterpret_cast<u32x4 *>(row + 16 * blk) = codes;
+    row[64 + blk] = (uint8_t)sb;
+}
+
+__device__ __forceinline__ void load_q_staged(const uint16_t *row, QFp4 &qa) {
+    const int lane = threadIdx.x & 63, hf = lane >> 5;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(row);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+        const uint8_t *hr = base + (32 * hb + (lane & 31)) * kMxStage;
+        qa.v[hb][0] = *reinterpret_cast<const u32x4 *>(hr + 32 * hf);
+        qa.v[hb][1] = *reinterpret_cast<const u32x4 *>(hr + 32 * hf + 16);
+        const uint32_t s4 = *reinterpret_cast<const uint32_t *>(hr + 64);
+        qa.sc[hb] = hf ? s4 >> 16 : s4;                 // byte kk: block 2*hf + kk
+    }
+}
+
 struct NoQ {
     template <class Op>
     __device__ void operator()(Op &) const {}
@@ -614,8 +802,8 @@ struct NoQ {
 // loads has been issued, by every wave of the workgroup (it synchronises
 // the workgroup) -- delivers the MFMA operands of q[b].  Otherwise q[b] is
 // read from q_lds when the workgroup has staged it there, else from memory.
-template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, int BS, bool USE_PRE = false,
-          class QFin = NoQ>
+template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, int BS, bool MX,
+          bool USE_PRE = false, class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
                                            const SlotRaw &pre = SlotRaw{-1, -1, false}, QFin qfin = QFin{},
@@ -639,7 +827,7 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     // out before q is waited on.
     float w_lane = 0.f;
     SlotRaw raw0{-1, -1, false};
-    typename QSel<Q8>::Op qa;
+    typename QSel<Q8, MX>::Op qa;
     if (live) {
         w_lane = a.w[(int64_t)b * a.w_row + lane];
         raw0 = USE_PRE ? pre : slot_raw<CHUNKED>(a, r.req, b, U * j0 + lane, lane < min(64, U * (j1 - j0)));
@@ -804,7 +992,8 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // every wave of the grid (rows of very different lengths); otherwise each
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
 // QQ (with Q8): q arrives as bf16 and is quantised here, while it is staged.
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM, int BS, bool QQ>
+// MX (with QQ): q and keys rounded to MXFP4 blocks here instead.
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM, int BS, bool QQ, bool MX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     constexpr int U = kBlock / BS;                    // pool blocks per slot
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
@@ -843,16 +1032,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             put_q_rows<1>(a, b, qv, sh_q);
             if constexpr (QQ) {
                 __syncthreads();
-                quantize_staged_row(sh_q[0]);
+                if constexpr (MX) quantize_staged_row_mx(sh_q[0]); else quantize_staged_row(sh_q[0]);
             }
         };
-        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
+        const auto qfin = [&](typename QSel<Q8, MX>::Op &qa) {
             put();
             __syncthreads();
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put();                                    // the workgroup's one barrier
             __syncthreads();
@@ -934,11 +1123,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll 1
                 for (int rr = 0; rr < nquant; ++rr) {
                     __syncthreads();
-                    quantize_staged_row(sh_q[rr]);
+                    if constexpr (MX) quantize_staged_row_mx(sh_q[rr]); else quantize_staged_row(sh_q[rr]);
                 }
             }
         };
-        const auto qfin = [&](typename QSel<Q8>::Op &qa) {
+        const auto qfin = [&](typename QSel<Q8, MX>::Op &qa) {
             put();
             __syncthreads();
             if (b == rb || b == rb + 1)
@@ -952,7 +1141,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
                                                     qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
@@ -965,7 +1154,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.nunits = __builtin_amdgcn_readfirstlane(sh_runits[b]);
                 r.nslots = (r.nunits + U - 1) / U;
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st,
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st,
                                                                       SlotRaw{-1, -1, false}, NoQ{},
                                                                       b == rb + 1 ? sh_q[1] : nullptr);
                 f = min(fend, pe);
@@ -978,23 +1167,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 }  // namespace
 
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8, bool ACCUM, bool QQ>
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8, bool ACCUM, bool QQ, bool MX = false>
 void launch_score_qa(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 g((unsigned)grid), blk(256);
     const bool small = a.block_size == kSmallBlock;
     if (a.chunk_ids) {
         if (small)
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kSmallBlock, QQ>), g, blk, 0, s,
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kSmallBlock, QQ, MX>), g, blk, 0, s,
                                   e0, e1, 0, a);
         else
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kBlock, QQ>), g, blk, 0, s, e0,
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kBlock, QQ, MX>), g, blk, 0, s, e0,
                                   e1, 0, a);
     } else {
         if (small)
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kSmallBlock, QQ>), g, blk, 0,
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kSmallBlock, QQ, MX>), g, blk, 0,
                                   s, e0, e1, 0, a);
         else
-            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kBlock, QQ>), g, blk, 0, s,
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kBlock, QQ, MX>), g, blk, 0, s,
                                   e0, e1, 0, a);
     }
 }
@@ -1014,6 +1203,7 @@ void launch_score_q(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t 
 
 template <bool OWN_COLS, bool SCORES, bool FLAT>
 void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+    if (a.mxfp4) return launch_score_qa<OWN_COLS, SCORES, FLAT, false, false, true, true>(a, grid, s, e0, e1);
     if (a.q8 || a.quant_q)
         launch_score_q<OWN_COLS, SCORES, FLAT, true>(a, grid, s, e0, e1);
     else
@@ -1022,8 +1212,9 @@ void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.B <= 0) return hipSuccess;
-    if (a.accum && (a.q8 || a.quant_q)) return hipErrorInvalidValue;
+    if (a.accum && (a.q8 || a.quant_q || a.mxfp4)) return hipErrorInvalidValue;
     if (a.quant_q && (a.q8 || !a.q)) return hipErrorInvalidValue;
+    if (a.mxfp4 && (a.q8 || a.quant_q || !a.q)) return hipErrorInvalidValue;
     if (a.block_size != kBlock && a.block_size != kSmallBlock) return hipErrorInvalidValue;
     if (!a.logits && (a.accum || !a.scores || a.row_cols)) return hipErrorInvalidValue;
     // the top-k feed (row_cols) never asks for scores

@@ -28,7 +28,7 @@ MAX_COLS = 1 << 27                # IDX_MAX_COLS
 STATIC_SCRATCH_BYTES = 16 << 20   # IDX_STATIC_SCRATCH_BYTES
 
 EXPORTS = ("idx_score", "idx_topk", "idx_score_topk", "idx_score_topk_noalloc", "idx_score_q8", "idx_score_topk_q8",
-           "idx_score_fp8q", "idx_score_topk_fp8q",
+           "idx_score_fp8q", "idx_score_topk_fp8q", "idx_score_mxfp4", "idx_score_topk_mxfp4",
            "idx_write_keys", "idx_select_resident",
            "idx_resident_workspace_bytes", "idx_workspace_bytes",
            "idx_error_string", "idx_last_error", "idx_profile_events", "idx_abi_version")
@@ -94,6 +94,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.idx_score_fp8q.restype = ctypes.c_int
     lib.idx_score_topk_fp8q.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
     lib.idx_score_topk_fp8q.restype = ctypes.c_int
+    lib.idx_score_mxfp4.argtypes = [vp, vp, i32, i32, i32, kp, i32, vp, vp, vp]
+    lib.idx_score_mxfp4.restype = ctypes.c_int
+    lib.idx_score_topk_mxfp4.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
+    lib.idx_score_topk_mxfp4.restype = ctypes.c_int
     lib.idx_score_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, vp, vp, vp]
     lib.idx_score_q8.restype = ctypes.c_int
     lib.idx_score_topk_q8.argtypes = [vp, vp, i32, i32, i32, kp, i32, i32, vp, vp, vp, sz, vp]
@@ -311,10 +315,7 @@ def idx_score_topk_noalloc(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, 
     return out_idx, out_val
 
 
-def idx_score_fp8q(q, w, keys: Keys, n_cols: int, with_scores: bool = False,
-                   logits: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None, stream=None):
-    """idx_score with the query quantised inside the score kernel (the
-    writer's rule per head; equal to quantize_q followed by idx_score_q8)."""
+def _score_quantised(fn, q, w, keys: Keys, n_cols: int, with_scores, logits, scores, stream):
     q, w = _qw(q, w)
     B, H, D = q.shape
     if logits is None:
@@ -324,14 +325,11 @@ def idx_score_fp8q(q, w, keys: Keys, n_cols: int, with_scores: bool = False,
     _dev(logits, torch.float32, "logits")
     _dev(scores, torch.float32, "scores")
     ks = keys.struct(B)
-    _check(load().idx_score_fp8q(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols,
-                                 _ptr(logits), _ptr(scores), _stream(stream)))
+    _check(fn(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, _ptr(logits), _ptr(scores), _stream(stream)))
     return (logits, scores) if with_scores else logits
 
 
-def idx_score_topk_fp8q(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=None,
-                        workspace=None, stream=None):
-    """idx_score_topk with the query quantised inside the score kernel."""
+def _score_topk_quantised(fn, q, w, keys: Keys, n_cols: int, k: int, out_idx, out_val, workspace, stream):
     q, w = _qw(q, w)
     B, H, D = q.shape
     if out_idx is None:
@@ -342,10 +340,37 @@ def idx_score_topk_fp8q(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out
     if workspace is None:
         workspace = _workspace(need, q.device)
     ks = keys.struct(B)
-    _check(load().idx_score_topk_fp8q(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k,
-                                      _ptr(out_idx), _ptr(out_val), _ptr(workspace), workspace.numel(),
-                                      _stream(stream)))
+    _check(fn(_ptr(q), _ptr(w), B, H, D, ctypes.byref(ks), n_cols, k, _ptr(out_idx), _ptr(out_val),
+              _ptr(workspace), workspace.numel(), _stream(stream)))
     return out_idx, out_val
+
+
+def idx_score_fp8q(q, w, keys: Keys, n_cols: int, with_scores: bool = False,
+                   logits: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None, stream=None):
+    """idx_score with the query quantised inside the score kernel (the
+    writer's rule per head; equal to quantize_q followed by idx_score_q8)."""
+    return _score_quantised(load().idx_score_fp8q, q, w, keys, n_cols, with_scores, logits, scores, stream)
+
+
+def idx_score_topk_fp8q(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=None,
+                        workspace=None, stream=None):
+    """idx_score_topk with the query quantised inside the score kernel."""
+    return _score_topk_quantised(load().idx_score_topk_fp8q, q, w, keys, n_cols, k, out_idx, out_val, workspace,
+                                 stream)
+
+
+def idx_score_mxfp4(q, w, keys: Keys, n_cols: int, with_scores: bool = False,
+                    logits: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None, stream=None):
+    """idx_score with query heads and keys rounded to MXFP4 blocks of 32
+    inside the score kernel (the contraction on e2m1 MFMA)."""
+    return _score_quantised(load().idx_score_mxfp4, q, w, keys, n_cols, with_scores, logits, scores, stream)
+
+
+def idx_score_topk_mxfp4(q, w, keys: Keys, n_cols: int, k: int, out_idx=None, out_val=None,
+                         workspace=None, stream=None):
+    """idx_score_topk of the MXFP4 variant."""
+    return _score_topk_quantised(load().idx_score_topk_mxfp4, q, w, keys, n_cols, k, out_idx, out_val, workspace,
+                                 stream)
 
 
 def quantize_q(q: torch.Tensor, out: Optional[torch.Tensor] = None, slots: Optional[torch.Tensor] = None,

@@ -311,3 +311,21 @@ def test_noalloc_rejects_calls_beyond_the_static_scratch(lib):
     # the decode shapes fit
     for B, n in [(32, 32768), (8, 262144), (40, 24576)]:
         assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, B, n, 512) <= L.STATIC_SCRATCH_BYTES
+
+
+def test_mxfp4_entry_points_reject_bad_arguments(lib):
+    """The MXFP4 variant: bf16 q as for idx_score, 64 heads only."""
+    keys = _keys()
+    assert lib.idx_score_mxfp4(0x1000, 0x2000, 1, 128, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_SHAPE
+    assert lib.idx_score_mxfp4(0x1000, 0x2000, 1, 64, 96, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_SHAPE
+    assert lib.idx_score_mxfp4(0x1004, 0x2000, 1, 64, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_ALIGN
+    assert lib.idx_score_mxfp4(None, None, 1, 64, 128, ctypes.byref(keys), 64, 0x3000, None, None) == L.IDX_E_ARG
+    assert lib.idx_score_mxfp4(None, None, 0, 64, 128, ctypes.byref(keys), 64, None, None, None) == L.IDX_OK
+    assert lib.idx_score_mxfp4(0x1000, 0x2000, 1, 64, 128, ctypes.byref(keys), 0, 0x3000, None, None) == L.IDX_E_SHAPE
+    need = L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 1, 64, 16)
+    assert lib.idx_score_topk_mxfp4(0x1000, 0x2000, 1, 128, 128, ctypes.byref(keys), 64, 16, 0x3000, None,
+                                    0x10000, need, None) == L.IDX_E_SHAPE
+    assert lib.idx_score_topk_mxfp4(0x1000, 0x2000, 1, 64, 128, ctypes.byref(keys), 64, 16, 0x3000, None,
+                                    0x10000, need - 1, None) == L.IDX_E_WORKSPACE
+    assert lib.idx_score_topk_mxfp4(0x1000, 0x2000, 1, 64, 128, ctypes.byref(keys), 64, 0, 0x3000, None,
+                                    0x10000, need, None) == L.IDX_E_SHAPE
