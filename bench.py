@@ -46,7 +46,11 @@ small blocks), and measures the same step over that layout.
 `--workload memory-indexer` measures the Level-1 resident-set selection: one
 step is one idx_select_resident call over 8 requests at 1M tokens (262,144
 entries each) scored at 3 layers, KMAX 384 pages; `value` is scored pairs per
-second over all layers and `roofline` covers one layer's score-kernel launch.
+second over all layers.  The layers' queries and weights are stacked, so the
+step is one score launch over every (layer, row) writing selection bits, a
+page pass and the page top-k, and `roofline` covers that score launch;
+`--separate-layers` gives each layer its own tensors (one score launch per
+layer writing scores; `roofline` then covers the last layer's launch).
 """
 from __future__ import annotations
 
@@ -487,6 +491,14 @@ def bench_resident(args):
     rl = workloads.memory_indexer()
     print(f"[bench] workload {rl.name}: {rl.description}", file=sys.stderr, flush=True)
     dls = [lib.to_device(wl) for wl in rl.layers]
+    if args.separate_layers:
+        # each layer's q and w its own tensor: one score launch per layer
+        qs, wts = [d.q for d in dls], [d.w for d in dls]
+    else:
+        # the layers' q and w stacked: one score launch over every (layer, row)
+        q_all = torch.stack([d.q for d in dls])
+        w_all = torch.stack([d.w for d in dls])
+        qs, wts = [q_all[l] for l in range(len(dls))], [w_all[l] for l in range(len(dls))]
     pairs_layer = [wl.pairs() for wl in rl.layers]
     pairs = int(sum(pairs_layer))
     out_pages = torch.empty((rl.B, rl.kmax), dtype=torch.int32, device="cuda")
@@ -494,7 +506,7 @@ def bench_resident(args):
     ws = lib.new_workspace(lib.resident_workspace_bytes(len(dls), rl.B, rl.n_cols, rl.kmax), "cuda")
 
     def step(i):
-        lib.idx_select_resident([d.q for d in dls], [d.w for d in dls], [d.keys for d in dls], rl.n_cols,
+        lib.idx_select_resident(qs, wts, [d.keys for d in dls], rl.n_cols,
                                 rl.kmax, ensemble=rl.ensemble, threshold=rl.threshold, n_sink=rl.n_sink,
                                 n_recent=rl.n_recent, out_pages=out_pages, out_count=out_count, workspace=ws)
 
@@ -504,12 +516,17 @@ def bench_resident(args):
     # the three layers' pools (830 MB) exceed the 256 MB MALL: no replicas needed
     ms_per_step = run_steps(step, args.steps, 1, not args.no_graph)
     # the hook stamps every score launch of a step; the events keep the last
-    # layer's launch, whose bytes are one layer's
+    # launch: the one over every layer (stacked), or the last layer's
     kern_ms, kern_spread = spread(kernel_ms_live(step, args.steps))
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
-    wl = rl.layers[-1]
-    algo = score_kernel_bytes(wl, pairs_layer[-1])      # one layer's launch, its scores stored
+    if args.separate_layers:
+        algo = score_kernel_bytes(rl.layers[-1], pairs_layer[-1])      # one layer's launch, its scores stored
+    else:
+        # every layer's keys, q, w and tables, and the selection bits written
+        words = -(-rl.n_cols // 64) * 2
+        algo = sum(score_kernel_bytes(w_, p_, logits_written=False) for w_, p_ in zip(rl.layers, pairs_layer))
+        algo += len(rl.layers) * rl.B * words * 4
     roofline = {"kernel": "score_kernel", "bound": "hbm", "achieved": algo / (kern_ms * 1e-3) / 1e9,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": read_traffic(RESIDENT_WORKLOAD),
                 "algorithmic_bytes": algo, "kernel_ms": kern_ms, **kern_spread}
@@ -533,6 +550,7 @@ def bench_resident(args):
         "config": {"workload": rl.name, "queries": rl.B, "layers": len(rl.layers), "n_cols": rl.n_cols,
                    "kmax": rl.kmax, "threshold": rl.threshold, "n_sink": rl.n_sink, "n_recent": rl.n_recent,
                    "ensemble": "max" if rl.ensemble == 0 else "mean", "pairs": pairs,
+                   "layers_stacked": not args.separate_layers,
                    "description": rl.description, "graph": not args.no_graph},
         "requests_per_s": rl.B / (ms_per_step * 1e-3),
         "path_hbm_frac": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
@@ -573,6 +591,8 @@ def main():
     ap.add_argument("--mxfp4", action="store_true",
                     help="MXFP4 variant: idx_score_topk_mxfp4 (q and keys rounded to MXFP4 blocks of 32 inside the "
                          "score kernel, e2m1 MFMA)")
+    ap.add_argument("--separate-layers", action="store_true",
+                    help="memory-indexer: each layer's q and w in a tensor of its own (one score launch per layer)")
     ap.add_argument("--block-size", type=int, default=64, choices=(64, 16),
                     help="pool block rows of the scoring workloads (16: the same keys re-laid in 16-row blocks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

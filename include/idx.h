@@ -363,6 +363,13 @@ int idx_write_keys(const uint16_t *k, int64_t n, int32_t D,
  * workspace / ws_bytes: at least idx_resident_workspace_bytes(n_layers, B,
  *           n_cols, kmax) bytes, 256-byte aligned; contents on entry do not
  *           matter.  Calls that share one workspace must not overlap.
+ *
+ * Layout that runs in one score launch: when q[l] == q[0] + l*B*H*D and
+ * w[l] == w[0] + l*B*H for every layer (the layers stacked in one tensor),
+ * H = 64, the ensemble is IDX_ENSEMBLE_MAX, every layer has the same status
+ * word and block size, and n_layers * B <= 512, all layers are scored by one
+ * launch that records only which entries reach the threshold.  The result
+ * is the same either way.
  */
 #define IDX_ENSEMBLE_MAX 0
 #define IDX_ENSEMBLE_MEAN 1

@@ -510,7 +510,42 @@ int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float 
     float *scores = reinterpret_cast<float *>(ws + R.scores);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
-    for (int l = 0; l < n_layers; ++l) {
+    idx::PageArgs pa{};
+    // One score launch over every (layer, row) when the layers' queries and
+    // weights are stacked ([L][B][H][D], [L][B][H]), they share one status
+    // word, 64 heads and the max ensemble (an entry is selected iff some
+    // layer's score reaches the threshold, so the launch only needs to
+    // write each layer's selection bits); otherwise one launch per layer
+    // writing scores.
+    bool fused = n_layers > 1 && H == idx::kHeads && cfg->ensemble == IDX_ENSEMBLE_MAX &&
+                 (int64_t)n_layers * B <= 512;
+    for (int l = 1; fused && l < n_layers; ++l)
+        fused = q[l] == q[0] + (int64_t)l * B * H * D && w[l] == w[0] + (int64_t)l * B * H &&
+                keys[l].status == keys[0].status && keys[l].block_size == keys[0].block_size;
+    if (fused) {
+        idx::ScoreArgs a = score_args(q[0], w[0], n_layers * B, &keys[0], n_cols);
+        a.rows_per_layer = B;
+        for (int l = 0; l < n_layers; ++l) {
+            idx::LayerKeys &k = a.layer[l];
+            k.pool = keys[l].pool;
+            k.n_pool_rows = keys[l].n_pool_rows;
+            k.block_table = keys[l].block_table;
+            k.n_req = keys[l].n_req;
+            k.max_blocks = keys[l].max_blocks;
+            k.q_req = keys[l].q_req;
+            k.limits = keys[l].limits;
+        }
+        a.ld = R.ld;
+        a.logits = nullptr;
+        a.scores = nullptr;
+        a.page_bits = reinterpret_cast<uint32_t *>(ws + R.scores);
+        a.bits_ld = R.ld / 32;
+        a.threshold = cfg->threshold;
+        if ((e = launch_score_timed(a, s)) != hipSuccess) return hip_fail(e, "score kernel");
+        pa.bits = a.page_bits;
+        pa.bits_ld = a.bits_ld;
+    }
+    for (int l = 0; !fused && l < n_layers; ++l) {
         idx::ScoreArgs a = score_args(q[l], w[l], B, &keys[l], n_cols);
         a.ld = R.ld;
         // 64 heads: only the sigmoid scores are read later, so no logits
@@ -519,7 +554,6 @@ int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float 
         a.scores = scores + (int64_t)l * B * R.ld;
         if ((e = launch_heads(a, H, s)) != hipSuccess) return hip_fail(e, "score kernel");
     }
-    idx::PageArgs pa{};
     pa.scores = scores;
     pa.L = n_layers;
     pa.B = B;

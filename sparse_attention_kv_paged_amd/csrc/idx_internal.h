@@ -18,6 +18,19 @@ constexpr int kMaxK = 2048;
 constexpr int kSegLogitCap = 32768;          // logits per top-k workgroup
 constexpr int kSegListCap = 16384;           // (key, column) items per merge workgroup
 
+constexpr int kMaxLayers = 8;                // layers one score launch can take (IDX_MAX_LAYERS)
+
+// The keys of one layer when a launch scores several layers' rows.
+struct LayerKeys {
+    const uint8_t *pool;
+    int64_t n_pool_rows;
+    const int32_t *block_table;
+    int32_t n_req;
+    int32_t max_blocks;
+    const int32_t *q_req;
+    const int32_t *limits;
+};
+
 struct ScoreArgs {
     const uint16_t *q;          // [B, 64, 128] bf16 (unused when q8 is set)
     const uint8_t *q8;          // [B, 64, 132] quantised q rows (e4m3 bytes, then the head's scale), or null
@@ -50,6 +63,17 @@ struct ScoreArgs {
     uint32_t *row_done;         // [B] zeroed here for the top-k's fused merge (or null)
     int32_t slots_per_wave;
     int32_t splits;             // workgroups per row
+    // Several layers in one launch (rows_per_layer > 0, the flattened split
+    // only): row v of the launch is row v % rows_per_layer of layer
+    // v / rows_per_layer; q, w and the outputs are indexed by v (the layers'
+    // rows stacked), the keys come from layer[v / rows_per_layer].
+    int32_t rows_per_layer;
+    LayerKeys layer[kMaxLayers];
+    // Selection bits (or null): word j of row v holds, for columns
+    // 32*j .. 32*j + 31, the bits (sigmoid(logit) >= threshold), binary32.
+    uint32_t *page_bits;
+    int64_t bits_ld;            // words per row
+    float threshold;
 };
 
 // One launch of the segment top-k (idx_topk.hip).  Input is either a logits

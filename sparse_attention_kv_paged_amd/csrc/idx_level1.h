@@ -22,6 +22,10 @@ struct PageArgs {
     float *page_keys;           // [B, ldp] out
     int64_t ldp;
     int32_t n_pages;            // ceil(n_cols / 64)
+    // selection bits instead of scores (max ensemble): [L][B][bits_ld] words,
+    // bit i of word j of a row = (score of column 32*j + i >= threshold)
+    const uint32_t *bits;
+    int64_t bits_ld;
 };
 
 hipError_t launch_pages(const PageArgs &a, hipStream_t s);

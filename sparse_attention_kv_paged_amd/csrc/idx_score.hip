@@ -93,6 +93,27 @@ struct RowRaw {
     int32_t qreq, limit, nchunks;
 };
 
+// The arguments row v of a launch sees: the launch's own, or, when it scores
+// several layers, the same with the keys of row v's layer (bl: the row's
+// index within its layer, for that layer's per-row arrays).
+__device__ __forceinline__ ScoreArgs key_view(const ScoreArgs &a, int v, int &bl) {
+    bl = v;
+    if (a.rows_per_layer <= 0) return a;
+    const int l = v / a.rows_per_layer;
+    bl = v - l * a.rows_per_layer;
+    ScoreArgs k = a;
+    const LayerKeys &L = a.layer[l];
+    k.pool = L.pool;
+    k.n_pool_rows = L.n_pool_rows;
+    k.block_table = L.block_table;
+    k.n_req = L.n_req;
+    k.max_blocks = L.max_blocks;
+    k.q_req = L.q_req;
+    k.limits = L.limits;
+    k.B = a.rows_per_layer;
+    return k;
+}
+
 __device__ __forceinline__ RowRaw row_raw(const ScoreArgs &a, int b) {
     const uint32_t nb = (uint32_t)a.B * 4u, off = (uint32_t)b * 4u;
     RowRaw r;
@@ -843,6 +864,10 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     const __amdgpu_buffer_rsrc_t out_r = make_rsrc(out_row, a.logits ? (uint32_t)col_end * 4u : 0u);
     const __amdgpu_buffer_rsrc_t sc_r =
         make_rsrc(score_row ? score_row : out_row, score_row ? (uint32_t)col_end * 4u : 0u);
+    // selection bits of the row: one word per 32 columns below col_end
+    const __amdgpu_buffer_rsrc_t bits_r =
+        make_rsrc(a.page_bits ? (const void *)(a.page_bits + (int64_t)b * a.bits_ld) : (const void *)a.pool,
+                  a.page_bits ? (uint32_t)((col_end + 31) / 32) * 4u : 0u);
     const uint32_t lane_lo = tile_load_offset(lane);
     // the lane's logit store offset within a tile (the upper half's lanes
     // hold the same entries and store nothing: kDrop plus any column stays
@@ -946,6 +971,13 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
             if (SCORES) {
                 const float score = 1.0f / (1.0f + expf(-logit));
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), sc_r, off, 0, 0);
+            }
+            if (!SCORES && !OWN_COLS && a.page_bits) {
+                // lanes 0-31 hold the tile's 32 entries (lanes 32-63 repeat them)
+                const float score = 1.0f / (1.0f + expf(-logit));
+                const uint32_t word = (uint32_t)__ballot(score >= a.threshold);
+                const uint32_t woff = lane == 0 ? (uint32_t)((g0 + (tau >> 1)) * 2 + (tau & 1)) * 4u : kDrop;
+                __builtin_amdgcn_raw_buffer_store_b32(word, bits_r, woff, 0, 0);
             }
         };
         issue(0);
@@ -1051,11 +1083,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         uint32_t st_rows = 0;
         int32_t cnt[2] = {0, 0};
         RowRaw raw[2];
-        for (int k2 = 0; k2 < 2; ++k2) raw[k2] = row_raw(a, 2 * threadIdx.x + k2);    // all in flight
+        for (int k2 = 0; k2 < 2; ++k2) {                                       // all in flight
+            int bl;
+            const int row = min(2 * (int)threadIdx.x + k2, max(a.B - 1, 0));
+            raw[k2] = row_raw(key_view(a, row, bl), bl);
+        }
         for (int k2 = 0; k2 < 2; ++k2) {
             const int row = 2 * threadIdx.x + k2;
             if (row < a.B) {
-                const RowCtx rr = row_context<BS>(a, raw[k2], st_rows);
+                int bl;
+                const RowCtx rr = row_context<BS>(key_view(a, row, bl), raw[k2], st_rows);
                 sh_rreq[row] = rr.req;
                 sh_rlim[row] = rr.limit;
                 sh_runits[row] = rr.nunits;
@@ -1105,8 +1142,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         r0.limit = __builtin_amdgcn_readfirstlane(sh_rlim[b]);
         r0.nunits = __builtin_amdgcn_readfirstlane(sh_runits[b]);
         r0.nslots = (r0.nunits + U - 1) / U;
+        int bl0;
+        const ScoreArgs a0 = key_view(a, b, bl0);
         const SlotRaw raw0 =
-            slot_raw<CHUNKED>(a, r0.req, b, U * (f - pb) + lane, lane < min(64, U * (min(fend, pe) - f)));
+            slot_raw<CHUNKED>(a0, r0.req, b, U * (f - pb) + lane, lane < min(64, U * (min(fend, pe) - f)));
         // q of the workgroup's first two rows, staged in LDS once for its
         // four waves (most workgroups lie within one or two rows)
         const int fw = (int)blockIdx.x * kWaves * chunk;
@@ -1141,7 +1180,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, true>(a, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, true>(a0, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
                                                     qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
@@ -1154,7 +1193,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.nunits = __builtin_amdgcn_readfirstlane(sh_runits[b]);
                 r.nslots = (r.nunits + U - 1) / U;
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
-                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX>(a, b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st,
+                int bl;
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX>(key_view(a, b, bl), b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st,
                                                                       SlotRaw{-1, -1, false}, NoQ{},
                                                                       b == rb + 1 ? sh_q[1] : nullptr);
                 f = min(fend, pe);
@@ -1216,7 +1256,13 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEve
     if (a.quant_q && (a.q8 || !a.q)) return hipErrorInvalidValue;
     if (a.mxfp4 && (a.q8 || a.quant_q || !a.q)) return hipErrorInvalidValue;
     if (a.block_size != kBlock && a.block_size != kSmallBlock) return hipErrorInvalidValue;
-    if (!a.logits && (a.accum || !a.scores || a.row_cols)) return hipErrorInvalidValue;
+    if (!a.logits && (a.accum || (!a.scores && !a.page_bits) || a.row_cols)) return hipErrorInvalidValue;
+    // several layers in one launch: the flattened split, selection bits, no
+    // quantised query
+    if (a.rows_per_layer > 0 &&
+        (a.B > kFlatRows || a.row_cols || a.scores || a.logits || !a.page_bits || a.q8 || a.quant_q || a.mxfp4 ||
+         a.accum || a.chunk_ids || a.B % a.rows_per_layer || a.B / a.rows_per_layer > kMaxLayers))
+        return hipErrorInvalidValue;
     // the top-k feed (row_cols) never asks for scores
     const bool own = a.row_cols != nullptr;
     const bool scores = !own && a.scores != nullptr;

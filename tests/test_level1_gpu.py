@@ -58,6 +58,25 @@ def _select(rl, dls, **over):
     return pages.cpu().numpy(), count.cpu().numpy(), cfg
 
 
+def _stacked(dls):
+    """The layers' q and w stacked into one [L, B, H, D] / [L, B, H] tensor
+    each (the layout for which one score launch covers every layer), as
+    per-layer views."""
+    q = torch.stack([d.q for d in dls])
+    w = torch.stack([d.w for d in dls])
+    return [q[l] for l in range(len(dls))], [w[l] for l in range(len(dls))]
+
+
+def _select_stacked(rl, dls, **over):
+    cfg = dict(kmax=rl.kmax, ensemble=rl.ensemble, threshold=rl.threshold, n_sink=rl.n_sink,
+               n_recent=rl.n_recent)
+    cfg.update(over)
+    qs, ws = _stacked(dls)
+    pages, count = L.idx_select_resident(qs, ws, [d.keys for d in dls], rl.n_cols, **cfg)
+    torch.cuda.synchronize()
+    return pages.cpu().numpy(), count.cpu().numpy(), cfg
+
+
 def _densities(s, limits, ens, tau):
     """[B, pages] densities of per-layer scores s [L, B, n] (binary32)."""
     Ly, B, n = s.shape
@@ -235,3 +254,54 @@ def test_resident_selection_with_128_head_layers():
         assert_logits_close(g[l], ref[l], f"h128 layer {l} scores")
     for over in [dict(), dict(ensemble=L.ENSEMBLE_MEAN, threshold=0.6), dict(kmax=4, n_sink=1, n_recent=2)]:
         _check(rl, dls, g, ref, **over)
+
+
+def test_one_launch_over_stacked_layers():
+    """Stacked queries and weights, max ensemble: one score launch over every
+    (layer, row) writes selection bits instead of scores.  Its pages and
+    counts equal the oracle's selection on the per-layer binary32 scores
+    (and so the per-layer launches' result) for several settings, including
+    thresholds at or below 0 that select masked entries' score 0."""
+    rl = W.memory_indexer(entries=[16384, 9001, 700, 40], n_layers=3, seed=80, kmax=32, threshold=0.72,
+                          ensemble=L.ENSEMBLE_MAX, name="memory-indexer-stacked")
+    _log(f"[level1] {rl.description} (stacked layers)")
+    dls = _device_layers(rl)
+    g = _gpu_scores(dls, rl.n_cols)
+    for over in [dict(), dict(threshold=0.8, kmax=8), dict(threshold=0.6, n_sink=2, n_recent=3, kmax=40),
+                 dict(threshold=2.0), dict(threshold=0.0, kmax=12), dict(threshold=-1.0, kmax=7, n_sink=0),
+                 dict(kmax=1, n_sink=1, n_recent=0), dict(kmax=2048, threshold=0.7)]:
+        pages, count, cfg = _select_stacked(rl, dls, **over)
+        want_p, want_c = oracle.level1_select(g, rl.limits, cfg["ensemble"], cfg["threshold"], cfg["n_sink"],
+                                              cfg["n_recent"], cfg["kmax"])
+        assert np.array_equal(count, want_c), (cfg, count, want_c)
+        assert np.array_equal(pages, want_p), cfg
+        p2, c2, _ = _select(rl, dls, **over)
+        assert np.array_equal(pages, p2) and np.array_equal(count, c2), cfg
+
+
+def test_one_launch_over_stacked_layers_two_and_eight_layers():
+    """Two layers, and eight layers (the most one launch takes), of ragged
+    rows with different block tables per layer."""
+    for n_layers, entries in ((2, [5000, 64, 1, 3333]), (8, [4096, 777, 129])):
+        rl = W.memory_indexer(entries=entries, n_layers=n_layers, seed=81 + n_layers, kmax=16, threshold=0.7,
+                              ensemble=L.ENSEMBLE_MAX, name=f"memory-indexer-{n_layers}-layers")
+        _log(f"[level1] {rl.description}")
+        dls = _device_layers(rl)
+        g = _gpu_scores(dls, rl.n_cols)
+        pages, count, cfg = _select_stacked(rl, dls)
+        want_p, want_c = oracle.level1_select(g, rl.limits, cfg["ensemble"], cfg["threshold"], cfg["n_sink"],
+                                              cfg["n_recent"], cfg["kmax"])
+        assert np.array_equal(count, want_c) and np.array_equal(pages, want_p), n_layers
+
+
+def test_one_launch_over_stacked_layers_full_size():
+    """The benchmark's shape through one launch: every row's pages equal the
+    oracle's selection on the GPU's per-layer scores."""
+    rl = W.memory_indexer()
+    _log(f"[level1] full size, stacked layers: {rl.description}")
+    dls = _device_layers(rl)
+    g = _gpu_scores(dls, rl.n_cols)
+    pages, count, cfg = _select_stacked(rl, dls)
+    want_p, want_c = oracle.level1_select(g, rl.limits, cfg["ensemble"], cfg["threshold"], cfg["n_sink"],
+                                          cfg["n_recent"], cfg["kmax"])
+    assert np.array_equal(count, want_c) and np.array_equal(pages, want_p)
