@@ -568,6 +568,14 @@ int idx_select_resident(int32_t n_layers, const uint16_t *const *q, const float 
     pa.page_keys = reinterpret_cast<float *>(ws + R.page_keys);
     pa.ldp = R.ldp;
     pa.n_pages = R.n_pages;
+    if (fused) {
+        // densities are small integers: one counting selection per row
+        pa.kmax = cfg->kmax;
+        pa.out_pages = out_pages;
+        pa.out_count = out_count;
+        e = idx::launch_select_bits(pa, s);
+        return e == hipSuccess ? IDX_OK : hip_fail(e, "page selection");
+    }
     if ((e = idx::launch_pages(pa, s)) != hipSuccess) return hip_fail(e, "page kernel");
     e = enqueue_topk(R.top, ws + R.topk, pa.page_keys, R.ldp, nullptr, B, R.n_pages, cfg->kmax, out_pages,
                      nullptr, nullptr, 0, 6, s, out_count);

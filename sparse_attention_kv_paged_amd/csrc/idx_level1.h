@@ -26,8 +26,15 @@ struct PageArgs {
     // bit i of word j of a row = (score of column 32*j + i >= threshold)
     const uint32_t *bits;
     int64_t bits_ld;
+    // the selection itself (launch_select_bits): kmax pages per row
+    int32_t kmax;
+    int32_t *out_pages;         // [B, kmax]
+    int32_t *out_count;         // [B] or null
 };
 
 hipError_t launch_pages(const PageArgs &a, hipStream_t s);
+// Pages straight from the selection bits (max ensemble), without page keys
+// and a separate top-k: one workgroup per row.
+hipError_t launch_select_bits(const PageArgs &a, hipStream_t s);
 
 }  // namespace idx
