@@ -49,5 +49,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // Cache-policy operand of buffer loads/stores: sc1 (device scope), i.e. the
 // access is coherent across the per-XCD L2 caches.
 constexpr int kDeviceCoherent = 16;
+// Cache-policy operand: nt (non-temporal), a streaming access the caches
+// need not keep.
+constexpr int kNonTemporal = 2;
 
 }  // namespace idx

@@ -967,10 +967,12 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
             float logit = tile_logit(st_.acc, wr, st_.s, st_.keep);
             if (ACCUM) logit += st_.prev;             // -inf stays -inf: both halves mask alike
             const uint32_t off = out_off(tau);
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, 0);
+            // per-row path (many rows over one key set): the logits stream
+            // past the caches (non-temporal) so the keys stay resident in L2
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), out_r, off, 0, LEAN ? kNonTemporal : 0);
             if (SCORES) {
                 const float score = 1.0f / (1.0f + expf(-logit));
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), sc_r, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(score), sc_r, off, 0, LEAN ? kNonTemporal : 0);
             }
             if (!SCORES && !OWN_COLS && a.page_bits) {
                 // lanes 0-31 hold the tile's 32 entries (lanes 32-63 repeat them)
