@@ -295,11 +295,13 @@ def summarize_mfma(pmc_dir, workload, command, out):
     print("\n".join(lines))
 
 
-def cpu_baseline(wl, pairs: int, min_seconds: float, max_sample_pairs: int = 4_000_000):
+def cpu_baseline(wl, pairs: int, min_seconds: float, max_sample_pairs: int = 4_000_000, mxfp4: bool = False):
     """The oracle as it stands on the host cores, timed on a bounded sample:
     full passes of the workload until `min_seconds` of wall time, or, when one
     pass holds more than `max_sample_pairs` pairs, passes over evenly spaced
-    rows (score + top-k of those rows) scaled by the pairs they score."""
+    rows (score + top-k of those rows) scaled by the pairs they score.  With
+    mxfp4, the oracle's MXFP4 scoring (the quantised-query variant's oracle
+    consumes quantised rows, so --q8 times the plain definition)."""
     import numpy as np
     from oracle import oracle
     threads = oracle.max_threads()
@@ -312,7 +314,7 @@ def cpu_baseline(wl, pairs: int, min_seconds: float, max_sample_pairs: int = 4_0
         what = f"pass(es) over 1 row in {stride} ({len(rows)} of {wl.B} rows) of the {wl.name} workload"
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.score_topk(wl, rows=rows)
+        oracle.score_topk(wl, rows=rows, mxfp4=mxfp4)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -657,7 +659,7 @@ def main():
     if not args.no_cpu_baseline:
         from sparse_attention_kv_paged_amd import workloads
         wl = scoring_workload(head, args, workloads)
-        out["cpu_baseline"] = cpu_baseline(wl, out["config"]["pairs"], args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, out["config"]["pairs"], args.cpu_seconds, mxfp4=args.mxfp4)
     print(json.dumps(out), flush=True)
 
 

@@ -248,9 +248,10 @@ def cols_to_entries(wl, cols: np.ndarray, rows=None) -> np.ndarray:
     return out
 
 
-def score_topk(wl, rows=None, n_threads: int = 0):
-    """Oracle of the whole path: (entry ids [B,k], their logits [B,k], logits [B,n_cols])."""
-    lg = score(wl, rows=rows, n_threads=n_threads)
+def score_topk(wl, rows=None, n_threads: int = 0, mxfp4: bool = False):
+    """Oracle of the whole path: (entry ids [B,k], their logits [B,k], logits
+    [B,n_cols]); with mxfp4, of the MXFP4 variant."""
+    lg = score(wl, rows=rows, n_threads=n_threads, mxfp4=mxfp4)
     cols, vals = topk(lg, wl.k, n_threads=n_threads)
     return cols_to_entries(wl, cols, rows=rows), vals, lg
 

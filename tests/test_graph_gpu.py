@@ -173,6 +173,44 @@ def test_select_resident_replays():
                   lambda: run(q2, None, None))
 
 
+def test_mxfp4_replays():
+    wl = W.small_config(4)
+    d = L.to_device(wl)
+    out_idx = torch.empty((wl.B, wl.k), dtype=torch.int32, device="cuda")
+    out_val = torch.empty((wl.B, wl.k), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(L.workspace_bytes(L.IDX_OP_SCORE_TOPK, wl.B, wl.n_cols, wl.k), "cuda")
+    q2 = _other_q(d, 5)
+
+    def call():
+        L.idx_score_topk_mxfp4(d.q, d.w, d.keys, wl.n_cols, wl.k, out_idx=out_idx, out_val=out_val, workspace=ws)
+
+    def between():
+        L.idx_score_topk_mxfp4(q2, d.w, d.keys, wl.n_cols, wl.k, workspace=ws)
+
+    _replay_check("mxfp4", call, [out_idx, out_val], between)
+
+
+def test_select_resident_stacked_layers_replays():
+    """The one-launch Level 1 (stacked layers, selection bits, counting
+    selection) under capture."""
+    rl = W.memory_indexer(entries=[20000, 9000, 64, 40000], n_layers=3, kmax=96, seed=74)
+    dl = [L.to_device(x) for x in rl.layers]
+    q_all = torch.stack([d.q for d in dl])
+    w_all = torch.stack([d.w for d in dl])
+    q_oth = torch.stack([_other_q(d, 20 + i) for i, d in enumerate(dl)])
+    pages = torch.empty((rl.B, rl.kmax), dtype=torch.int32, device="cuda")
+    count = torch.empty(rl.B, dtype=torch.int32, device="cuda")
+    ws = L.new_workspace(L.resident_workspace_bytes(3, rl.B, rl.n_cols, rl.kmax), "cuda")
+
+    def run(q, p, c):
+        L.idx_select_resident([q[l] for l in range(3)], [w_all[l] for l in range(3)], [d.keys for d in dl],
+                              rl.n_cols, rl.kmax, threshold=rl.threshold, n_sink=1, n_recent=1, out_pages=p,
+                              out_count=c, workspace=ws)
+
+    _replay_check("select_resident, stacked layers", lambda: run(q_all, pages, count), [pages, count],
+                  lambda: run(q_oth, None, None))
+
+
 def test_write_keys_replays():
     wk = W.index_fill(n_keys=5000, seed=74)
     k = torch.from_numpy(wk.k.view(np.int16)).cuda()
