@@ -22,8 +22,9 @@ struct PageArgs {
     float *page_keys;           // [B, ldp] out
     int64_t ldp;
     int32_t n_pages;            // ceil(n_cols / 64)
-    // selection bits instead of scores (max ensemble): [L][B][bits_ld] words,
-    // bit i of word j of a row = (score of column 32*j + i >= threshold)
+    // selection bits instead of scores (max ensemble, launch_select_bits):
+    // [L][B][bits_ld] words, bit i of word j of a row = (score of column
+    // 32*j + i >= threshold)
     const uint32_t *bits;
     int64_t bits_ld;
     // the selection itself (launch_select_bits): kmax pages per row

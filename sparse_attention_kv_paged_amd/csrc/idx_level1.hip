@@ -91,37 +91,6 @@ __global__ __launch_bounds__(64 * kPageWaves) void page_kernel(PageArgs a) {
     }
 }
 
-// The same page keys from the score launch's selection bits (max ensemble:
-// an entry is selected iff some layer's score reaches the threshold, so the
-// page's selected entries are the OR of the layers' words): one thread per
-// page, entries at or past the row's history masked off.
-__global__ __launch_bounds__(256) void page_bits_kernel(PageArgs a) {
-    const int b = blockIdx.y;
-    const int p = blockIdx.x * 256 + (int)threadIdx.x;
-    if (p >= a.n_pages) return;
-    const int hist = max(0, min(a.limits[b], a.n_cols));
-    const int P = (hist + kBlock - 1) / kBlock;
-    uint64_t m = 0;
-    for (int l = 0; l < a.L; ++l) {
-        const uint32_t *row = a.bits + ((int64_t)l * a.B + b) * a.bits_ld;
-        m |= (uint64_t)row[2 * p] | ((uint64_t)row[2 * p + 1] << 32);
-    }
-    const int valid = max(0, min(hist - p * kBlock, kBlock));
-    m = valid == 0 ? 0 : valid == kBlock ? m : m & ((1ull << valid) - 1);
-    const int count = __popcll(m);
-    const bool forced = p < P && (p < a.n_sink || p >= P - a.n_recent);
-    float key = -__builtin_inff();
-    if (a.n_pages <= (1 << kPageBits)) {
-        const int tie = (1 << kPageBits) - 1 - p;
-        if (forced) key = (float)((kBlock + 1) * (1 << kPageBits) + tie);
-        else if (p < P && count > 0) key = (float)(count * (1 << kPageBits) + tie);
-    } else {
-        if (forced) key = __builtin_inff();
-        else if (p < P && count > 0) key = (float)count;
-    }
-    a.page_keys[(int64_t)b * a.ldp + p] = key;
-}
-
 constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;                           // consecutive pages per thread and chunk
 constexpr int kForcedRank = kBlock + 1;               // above every density
@@ -296,12 +265,6 @@ hipError_t launch_select_bits(const PageArgs &a, hipStream_t s) {
 
 hipError_t launch_pages(const PageArgs &a, hipStream_t s) {
     if (a.B <= 0 || a.n_pages <= 0) return hipSuccess;
-    if (a.bits) {
-        if (a.ensemble != IDX_ENSEMBLE_MAX || a.bits_ld < 2 * (int64_t)a.n_pages) return hipErrorInvalidValue;
-        const dim3 grid((unsigned)((a.n_pages + 255) / 256), (unsigned)a.B);
-        hipLaunchKernelGGL(page_bits_kernel, grid, dim3(256), 0, s, a);
-        return hipGetLastError();
-    }
     const int per_group = kPageWaves * kPagesPerWave;
     const dim3 grid((unsigned)((a.n_pages + per_group - 1) / per_group), (unsigned)a.B);
     hipLaunchKernelGGL(page_kernel, grid, dim3(64 * kPageWaves), 0, s, a);

@@ -305,3 +305,22 @@ def test_one_launch_over_stacked_layers_full_size():
     want_p, want_c = oracle.level1_select(g, rl.limits, cfg["ensemble"], cfg["threshold"], cfg["n_sink"],
                                           cfg["n_recent"], cfg["kmax"])
     assert np.array_equal(count, want_c) and np.array_equal(pages, want_p)
+
+
+def test_one_launch_over_stacked_layers_rows_beyond_the_rank_cache():
+    """Two stacked layers of one row of 16,400 pages (more than the 16,384
+    page ranks the selection keeps in LDS, so its second pass recomputes
+    them): the pages equal the oracle's selection on the GPU's scores."""
+    n = 16400 * 64 - 17
+    rl = W.memory_indexer(entries=[n], n_layers=2, seed=88, kmax=500, threshold=0.75, n_sink=3, n_recent=2,
+                          ensemble=L.ENSEMBLE_MAX, name="memory-indexer-long-row")
+    _log(f"[level1] {rl.description}")
+    dls = _device_layers(rl)
+    g = _gpu_scores(dls, rl.n_cols)
+    for over in [dict(), dict(kmax=2048, threshold=0.7)]:
+        pages, count, cfg = _select_stacked(rl, dls, **over)
+        want_p, want_c = oracle.level1_select(g, rl.limits, cfg["ensemble"], cfg["threshold"], cfg["n_sink"],
+                                              cfg["n_recent"], cfg["kmax"])
+        assert np.array_equal(count, want_c) and np.array_equal(pages, want_p), cfg
+    del dls
+    torch.cuda.empty_cache()
