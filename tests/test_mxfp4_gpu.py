@@ -91,6 +91,12 @@ def test_mxfp4_full_size_prefill_sampled_rows():
     _check_mx(wl, rows=rows, tag="full3")
 
 
+def test_mxfp4_full_size_prefill_all_rows():
+    """Chunked prefill at full size: every one of the 4096 rows' logits,
+    scores and top-512 against the oracle's MXFP4 scoring."""
+    _check_mx(W.config(3), tag="full3-all")
+
+
 def test_mxfp4_per_row_path_and_16_row_blocks():
     _check_mx(W.prefill(8192, 603, seed=72, name="mx-rows"), tag="per-row")
     _check_mx(W.reblock(W.small_config(4), seed=73), tag="b16-chunks")
