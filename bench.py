@@ -530,7 +530,9 @@ def bench_resident(args):
         algo = sum(score_kernel_bytes(w_, p_, logits_written=False) for w_, p_ in zip(rl.layers, pairs_layer))
         algo += len(rl.layers) * rl.B * words * 4
     roofline = {"kernel": "score_kernel", "bound": "hbm", "achieved": algo / (kern_ms * 1e-3) / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "traffic": read_traffic(RESIDENT_WORKLOAD),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                # the counters were taken on the one launch over every layer
+                "traffic": None if args.separate_layers else read_traffic(RESIDENT_WORKLOAD),
                 "algorithmic_bytes": algo, "kernel_ms": kern_ms, **kern_spread}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
     # the step: every layer's keys, q, w and tables once, the pages written

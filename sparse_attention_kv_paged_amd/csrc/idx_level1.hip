@@ -91,8 +91,11 @@ __global__ __launch_bounds__(64 * kPageWaves) void page_kernel(PageArgs a) {
     }
 }
 
-constexpr int kSelThreads = 256;
-constexpr int kSelPer = 16;                           // consecutive pages per thread and chunk
+// One 1024-thread workgroup per row, four pages per thread and chunk: the
+// selection is latency-bound on a few workgroups, so short per-thread chains
+// beat more loads in flight per thread (16 pages on 256 threads took 40% longer).
+constexpr int kSelThreads = 1024;
+constexpr int kSelPer = 4;                            // consecutive pages per thread and chunk
 constexpr int kForcedRank = kBlock + 1;               // above every density
 
 // Rank of page p of row b for the selection: kForcedRank for a sink or
@@ -111,7 +114,8 @@ __device__ __forceinline__ int page_rank(const PageArgs &a, int b, int p, int hi
     return __popcll(m);
 }
 
-// Exclusive prefix of v over the workgroup (256 threads); *total gets the sum.
+// Exclusive prefix of v over the workgroup (kSelThreads threads); *total gets
+// the sum.
 __device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t *sh, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t incl = wave_scan(v);
@@ -133,7 +137,7 @@ __device__ __forceinline__ uint32_t block_excl(uint32_t v, uint32_t *sh, uint32_
 // the page top-k over the page keys).  Densities are integers 0..64, so a
 // histogram of the ranks finds the cut: every page above the cut rank is
 // kept, and at the cut rank the lowest `need` pages.  The first pass reads
-// the bits in coalesced order (thread t: pages t, t + 256, ...) and keeps
+// the bits in coalesced order (thread t: pages t, t + kSelThreads, ...) and keeps
 // each page's rank in LDS for rows of up to kSelCap pages; longer rows
 // recompute the ranks in the second pass.
 constexpr int kSelCap = 16384;
@@ -149,8 +153,8 @@ __global__ __launch_bounds__(kSelThreads) void select_bits_kernel(PageArgs a) {
     const bool cached = P <= kSelCap;
     for (int i = threadIdx.x; i <= kForcedRank; i += kSelThreads) sh_hist[i] = 0u;
     __syncthreads();
-    // pages t + 256 k (k < 16) of each chunk: the chunk's loads of one layer
-    // all in flight at once
+    // pages t + kSelThreads k (k < kSelPer) of each chunk: the chunk's loads of
+    // one layer all in flight at once
     for (int base = 0; base < P; base += kSelThreads * kSelPer) {
         uint64_t m[kSelPer];
 #pragma unroll
