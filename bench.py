@@ -411,6 +411,72 @@ def copy_calibration(n):
     torch.cuda.synchronize()
 
 
+GEMM_CAL_SIZE = 8192
+
+
+def gemm_calibration(n, size=GEMM_CAL_SIZE):
+    """n plain bf16 GEMMs C = A B (size x size x size, torch.matmul, which
+    dispatches to the vendor GEMM library): the dense bf16 MFMA rate a
+    library kernel sustains on this chip, for context next to the spec peak.
+    Prints one JSON line."""
+    import torch
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(size, size, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(size, size, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.empty(size, size, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(n):
+        torch.matmul(a, b, out=c)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / n
+    tflops = 2.0 * size ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"calibration": "bf16 GEMM, torch.matmul", "m": size, "n": size, "k": size,
+                      "gemms": n, "ms_per_gemm": ms, "tflops": tflops,
+                      "frac_of_spec_peak": tflops / MFMA_BF16_PEAK_TFLOPS}), flush=True)
+
+
+def summarize_gemm_mfma(pmc_dir, command, out, size=GEMM_CAL_SIZE):
+    """MFMA utilisation and clock of the library GEMM kernel of a
+    `--gemm-calibration` run under the MFMA_COUNTERS (the most frequent
+    kernel that issues MFMAs), computed as for the score kernel, plus the
+    TFLOP/s of a dispatch from its duration."""
+    import statistics
+    per, names = {}, {}
+    for r in _csv_rows(_find(pmc_dir, "counter_collection.csv")):
+        d = per.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    rows = [d for d in per.values() if all(c in d for c in MFMA_COUNTERS) and d["SQ_INSTS_MFMA"] > 0]
+    for d in rows:
+        names[d["name"]] = names.get(d["name"], 0) + 1
+    kname = max(names, key=names.get)
+    rows = [d for d in rows if d["name"] == kname]
+    med = {c: statistics.median(d[c] for d in rows) for c in MFMA_COUNTERS + ["ns"]}
+    active = med["GRBM_GUI_ACTIVE"] / 8
+    busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * SIMDS)
+    tflops = 2.0 * size ** 3 / med["ns"] / 1e3
+    lines = [f"# rocprofv3 MFMA counters for the library bf16 GEMM ({size} x {size} x {size}, torch.matmul)",
+             f"# command: {command}",
+             f"# medians over dispatches; busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x {SIMDS} SIMDs)",
+             f"kernel = {kname[:100]}",
+             f"dispatches = {len(rows)}"]
+    lines += [f"{c.lower()} = {med[c]:.0f}" for c in MFMA_COUNTERS]
+    lines += [f"dispatch_ns = {med['ns']:.0f}",
+              f"tflops = {tflops:.1f}",
+              f"frac_of_spec_peak = {tflops / MFMA_BF16_PEAK_TFLOPS:.4f}",
+              f"clock_ghz = {active / med['ns']:.3f}",
+              f"mfma_busy_frac = {busy:.4f}"]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def bench_writer(args):
     """One step = one idx_write_keys of the index-fill workload (262,144 keys
     of one 1M-token request into a shuffled paged pool)."""
@@ -607,6 +673,10 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summary of FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--summarize-mfma", metavar="DIR", help="write profiles/ summary of an MFMA counter run")
+    ap.add_argument("--gemm-calibration", type=int, default=0, metavar="N",
+                    help="only time N plain bf16 GEMMs of 8192^3 (torch.matmul): the library's sustained MFMA rate")
+    ap.add_argument("--summarize-gemm", metavar="DIR",
+                    help="write profiles/ summary of an MFMA counter run of --gemm-calibration")
     ap.add_argument("--command", default="", help="the profiled command, recorded in the summary")
     args = ap.parse_args()
 
@@ -617,6 +687,13 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, prof_name, args.command,
                         os.path.join(PROFILE_DIR, f"{trace_prefix}_{prof_name}_trace.txt"))
+        return
+    if args.summarize_gemm:
+        summarize_gemm_mfma(args.summarize_gemm, args.command,
+                            os.path.join(PROFILE_DIR, "gemm_bf16_calibration_mfma.txt"))
+        return
+    if args.gemm_calibration:
+        gemm_calibration(args.gemm_calibration)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma, prof_name, args.command,
