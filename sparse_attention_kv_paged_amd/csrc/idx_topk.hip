@@ -134,24 +134,45 @@ __device__ __forceinline__ void sel_reset(SelScratch<NT, CAND> &sh) {
     if (threadIdx.x == 0) sh.ncand = 0u;
 }
 
-// The exact k-th largest key (kstar) among the items the workgroup holds in
-// registers (thread t: key[0..PER) of a column-ordered sequence; key 0 = not
-// selectable), how many of its copies win (need_ties, lowest columns first)
-// and the number of selectable items (total).  kstar = 0 when every
-// selectable item wins.  All threads call it, after sel_reset.  With
-// HAVE_V, val[j] is the float whose order key is key[j] (saves decoding it).
-//   1. key range of the selectable items;
-//   2. histogram of 2048 bins linear in value between min and max;
-//   3. the bin t holding the k-th largest value (and the selectable count);
-//   4. t's members go to LDS; one wave ranks up to 64 of them against each
-//      other, larger bins take radix passes over their keys (bits 31:21,
-//      20:10, 9:0).
-template <int NT, int PER, int CAND, bool HAVE_V = false>
-__device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k, SelScratch<NT, CAND> &sh,
-                                         uint32_t &kstar, uint32_t &need_ties, uint32_t &total,
-                                         const float *val = nullptr) {
+// Bins of a thread's PER slots, kept from the histogram pass for the passes
+// after it: one per register up to 16 slots, else two 16-bit bins per
+// register (bins < 2080).
+template <int PER>
+struct SlotBins {
+    static constexpr bool kWide = PER <= 16;
+    uint32_t r[kWide ? PER : (PER + 1) / 2];
+    __device__ __forceinline__ uint32_t get(int j) const {
+        if (kWide) return r[j];
+        return (j & 1) ? r[j >> 1] >> 16 : r[j >> 1] & 0xFFFFu;
+    }
+    __device__ __forceinline__ void set(int j, uint32_t bn) {
+        if (kWide)
+            r[j] = bn;
+        else if (j & 1)
+            r[j >> 1] |= bn << 16;
+        else
+            r[j >> 1] = bn;
+    }
+};
+
+// Where the k-th largest selectable item lies after the value histogram:
+// bin cbin, with `above` selectable items in higher bins and n_in_bin in it;
+// total = the selectable count.  every: every selectable item wins (total
+// <= k, none selectable included), and cbin, above and n_in_bin mean
+// nothing.
+struct CutBin {
+    uint32_t cbin, above, n_in_bin, total;
+    bool every;
+};
+
+// Steps 1-3 of find_cut over the items the workgroup holds in registers;
+// bins gets each slot's bin (selectable items below kBins, the others at or
+// above it), set whenever total > 0.  All threads call it, after sel_reset.
+template <int NT, int PER, int CAND, bool HAVE_V>
+__device__ __forceinline__ CutBin hist_cut(const uint32_t (&key)[PER], uint32_t k, SelScratch<NT, CAND> &sh,
+                                           SlotBins<PER> &bins, const float *val) {
     constexpr int kW = NT / 64;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // 1. integer min/max of the order-preserving keys
     uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
 #pragma unroll
@@ -172,10 +193,8 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
         kmn = min(kmn, sh.kmin[w]);
         kmx = max(kmx, sh.kmax[w]);
     }
-    kstar = 0u;
-    need_ties = 0u;
-    total = 0u;
-    if (kmx == 0u) return;                            // uniform: nothing selectable
+    CutBin c{0u, 0u, 0u, 0u, true};
+    if (kmx == 0u) return c;                          // uniform: nothing selectable
 
     // 2. value-linear bins (monotone in value); other items go to the extra
     // bins, 32 of them so that a wave's lanes hit distinct LDS banks
@@ -191,44 +210,43 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     // from 0 in a narrow range the error exceeds 1, and a negative bin would
     // wrap past the top bin below
     if (fmaf(vmin, scale, off) < 0.f) off = next_up(off);
-    const auto bin_of = [&](int j) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
         const uint32_t kj = key[j];
         // fma(v, scale, off) is monotone in v like (v - vmin)*scale and at
         // least fma(vmin, scale, off) >= 0; it only has to be the same
         // function in every pass
         const float v = HAVE_V ? val[j] : key_value(kj);
         const int x = __float2int_rz(fmaf(v, scale, off));                // >= 0 (NaN -> 0)
-        return kj ? min((uint32_t)x, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (lane & 31));
-    };
-    // the bins are kept for step 4: one per register up to 16 slots, else
-    // two 16-bit bins per register (bins < 2080)
-    constexpr bool kWide = PER <= 16;
-    uint32_t bins[kWide ? PER : (PER + 1) / 2];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const uint32_t bn = bin_of(j);
-        if (kWide)
-            bins[j] = bn;
-        else if (j & 1)
-            bins[j >> 1] |= bn << 16;
-        else
-            bins[j >> 1] = bn;
+        const uint32_t bn = kj ? min((uint32_t)x, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (lane & 31));
+        bins.set(j, bn);
         atomicAdd(&sh.hist[bn], 1u);
     }
     __syncthreads();
     // 3.
     find_from_top<NT>(sh.hist, kBins, k, sh.res, sh.scan_a);
-    total = (uint32_t)sh.res[2];
-    if (total <= k) return;                           // uniform: every selectable item wins
-    const uint32_t cbin = (uint32_t)sh.res[0];
-    uint32_t rem = k - (uint32_t)sh.res[1];
-    const uint32_t n_in_bin = sh.hist[cbin];
-    const auto in_cut_bin = [&](int j) {
-        if (kWide) return bins[j] == cbin;
-        return ((j & 1) ? bins[j >> 1] >> 16 : bins[j >> 1] & 0xFFFFu) == cbin;
-    };
-    // 4. few members: their keys go to LDS (in any order) and one wave
-    // ranks them against each other
+    c.total = (uint32_t)sh.res[2];
+    if (c.total <= k) return c;                       // uniform: every selectable item wins
+    c.every = false;
+    c.cbin = (uint32_t)sh.res[0];
+    c.above = (uint32_t)sh.res[1];
+    c.n_in_bin = sh.hist[c.cbin];
+    return c;
+}
+
+// Step 4 of find_cut: the exact k-th largest key among the members of bin
+// c.cbin (the slots j with bins.get(j) == c.cbin) and how many of its copies
+// win.  All threads call it, with c.every false.
+template <int NT, int PER, int CAND>
+__device__ __forceinline__ void resolve_cut(const uint32_t (&key)[PER], const SlotBins<PER> &bins, const CutBin &c,
+                                            uint32_t k, SelScratch<NT, CAND> &sh, uint32_t &kstar,
+                                            uint32_t &need_ties) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t rem = k - c.above;
+    const uint32_t n_in_bin = c.n_in_bin;
+    const auto in_cut_bin = [&](int j) { return bins.get(j) == c.cbin; };
+    // few members: their keys go to LDS (in any order) and one wave ranks
+    // them against each other
     if (n_in_bin <= 64u) {
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -262,10 +280,15 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
         for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
         __syncthreads();
         const uint32_t mask = (1u << (hi - lo)) - 1u;
+        // the cut bin as a value the compiler cannot carry across stages, so
+        // the slots' membership is tested again in each stage rather than
+        // held in scalar registers (one 64-bit mask per slot)
+        uint32_t cb = c.cbin;
+        asm volatile("" : "+v"(cb));
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const uint32_t kk = key[j];
-            if (in_cut_bin(j) && (hi == 32 || (kk >> hi) == prefix)) atomicAdd(&sh.hist[(kk >> lo) & mask], 1u);
+            if (bins.get(j) == cb && (hi == 32 || (kk >> hi) == prefix)) atomicAdd(&sh.hist[(kk >> lo) & mask], 1u);
         }
         __syncthreads();
         find_from_top<NT>(sh.hist, kBins, rem, sh.res, sh.scan_a);
@@ -274,6 +297,30 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     }
     kstar = prefix;
     need_ties = rem;
+}
+
+// The exact k-th largest key (kstar) among the items the workgroup holds in
+// registers (thread t: key[0..PER) of a column-ordered sequence; key 0 = not
+// selectable), how many of its copies win (need_ties, lowest columns first)
+// and the number of selectable items (total).  kstar = 0 when every
+// selectable item wins.  All threads call it, after sel_reset.  With
+// HAVE_V, val[j] is the float whose order key is key[j] (saves decoding it).
+//   1. key range of the selectable items;
+//   2. histogram of 2048 bins linear in value between min and max;
+//   3. the bin t holding the k-th largest value (and the selectable count);
+//   4. t's members go to LDS; one wave ranks up to 64 of them against each
+//      other, larger bins take radix passes over their keys (bits 31:21,
+//      20:10, 9:0).
+template <int NT, int PER, int CAND, bool HAVE_V = false>
+__device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k, SelScratch<NT, CAND> &sh,
+                                         uint32_t &kstar, uint32_t &need_ties, uint32_t &total,
+                                         const float *val = nullptr) {
+    SlotBins<PER> bins;
+    const CutBin c = hist_cut<NT, PER, CAND, HAVE_V>(key, k, sh, bins, val);
+    total = c.total;
+    kstar = 0u;
+    need_ties = 0u;
+    if (!c.every) resolve_cut<NT, PER, CAND>(key, bins, c, k, sh, kstar, need_ties);
 }
 
 constexpr uint32_t kLoses = 0xFFFFFFFFu;              // position of a slot that does not win
@@ -424,12 +471,24 @@ __device__ __forceinline__ void load_items(const uint2 *src, int n, int i0, uint
 // last part of a row to finish (per-row arrival counter, zeroed by the score
 // kernel) merges all of the row's lists, up to MMUL x CAP items, in the same
 // launch.
+// 512-thread workgroups over long segments are held to 128 VGPRs (four waves
+// per SIMD) so that two share a CU: many rows then keep the CU busy while one
+// workgroup sits in its barrier-separated, latency-bound phases.
 template <int CAP, bool LIST, int NT, int MMUL>
-__global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
+constexpr int seg_waves_per_eu() { return !LIST && MMUL == 0 && NT == 512 && CAP / NT >= 16 ? 4 : 1; }
+
+template <int CAP, bool LIST, int NT, int MMUL>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(seg_waves_per_eu<CAP, LIST, NT, MMUL>())))
+void topk_segment_kernel(SegArgs a) {
     constexpr bool kFused = MMUL > 0;
     constexpr int kPer = CAP / NT;                    // items per thread
     constexpr int kMPer = kFused ? MMUL * kPer : kPer;    // merge items per thread
+    // long segments of logits: the items that can still win after the
+    // histogram are compacted into LDS, one per thread (see below)
+    constexpr bool kCompact = !LIST && !kFused && kPer >= 16;
+    constexpr int kCI = 1024 / NT;                    // compacted items per thread (up to 1024 in all)
     __shared__ SelScratch<NT, 64> sh;
+    __shared__ uint2 sh_items[kCompact ? kCI * NT : 1];
 
     const int tid = threadIdx.x;
     const int b = blockIdx.x / a.parts;
@@ -478,15 +537,76 @@ __global__ __launch_bounds__(NT) void topk_segment_kernel(SegArgs a) {
     }
     const auto col_of = [&](int j) { return LIST ? col[LIST ? j : 0] : (uint32_t)(col0 + i0 + j); };
 
-    uint32_t kstar, need_ties, total;
+    uint32_t kstar = 0u, need_ties = 0u, total;
     WinCursor cur;
-    find_cut<NT, kPer, 64, !LIST>(key, k, sh, kstar, need_ties, total, v);
-    scan_winners<NT, kPer>(key, kstar, need_ties, sh, cur);
-    uint32_t count = min(total, k);
-    if (a.out_list)
-        write_list<NT, kPer, kFused>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key, col_of, count);
-    else
-        write_final<NT, kPer>(a, b, cur, key, col_of, count);
+    if constexpr (kCompact) {
+        // After the histogram only the items in the cut bin or above can
+        // win (every selectable item when none is cut): at most k plus the
+        // cut bin's members.  When they number at most 1024, one counting
+        // pass, a block scan and one writing pass put them into LDS in
+        // column order (thread t's slots are columns i0 .. i0 + kPer - 1),
+        // and the exact cut, the winner scan and the output run on those
+        // few items (kCI per thread) instead of on every slot again.  The
+        // bins come from the keys (the loaded floats are not kept: registers
+        // decide how many workgroups share a CU).
+        SlotBins<kPer> bins;
+        const CutBin c = hist_cut<NT, kPer, 64, false>(key, k, sh, bins, nullptr);
+        total = c.total;
+        const uint32_t count = min(total, k);
+        const uint32_t cands = c.every ? c.total : c.above + c.n_in_bin;    // uniform
+        if (cands <= (uint32_t)(kCI * NT)) {
+            // can win: lo <= bin < kBins (the other bins hold non-selectable items)
+            const uint32_t lo = c.every ? 0u : c.cbin;
+            uint32_t m = 0;
+            if (c.total > 0u) {                       // uniform; bins are set
+#pragma unroll
+                for (int j = 0; j < kPer; ++j) m += bins.get(j) - lo < (uint32_t)kBins - lo;
+            }
+            uint32_t pos = block_scan<NT>(m, sh.scan_b) - m;
+            if (c.total > 0u) {
+#pragma unroll
+                for (int j = 0; j < kPer; ++j) {
+                    const uint32_t bn = bins.get(j);
+                    if (bn - lo < (uint32_t)kBins - lo) sh_items[pos++] = make_uint2(key[j], (uint32_t)(i0 + j) << 16 | bn);
+                }
+            }
+            __syncthreads();
+            // items tid * kCI ..: (key, segment column << 16 | bin); none:
+            // key 0 and a bin that is no member
+            uint32_t key1[kCI], cl[kCI];
+            SlotBins<kCI> bin1;
+#pragma unroll
+            for (int i = 0; i < kCI; ++i) {
+                const int x = tid * kCI + i;
+                const uint2 it = x < (int)cands ? sh_items[x] : make_uint2(0u, (uint32_t)kBins);
+                key1[i] = it.x;
+                cl[i] = it.y >> 16;
+                bin1.set(i, it.y & 0xFFFFu);
+            }
+            if (!c.every) resolve_cut<NT, kCI, 64>(key1, bin1, c, k, sh, kstar, need_ties);
+            scan_winners<NT, kCI>(key1, kstar, need_ties, sh, cur);
+            const auto col1 = [&](int i) { return (uint32_t)(col0 + cl[i]); };
+            if (a.out_list)
+                write_list<NT, kCI, false>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key1, col1, count);
+            else
+                write_final<NT, kCI>(a, b, cur, key1, col1, count);
+        } else {
+            if (!c.every) resolve_cut<NT, kPer, 64>(key, bins, c, k, sh, kstar, need_ties);
+            scan_winners<NT, kPer>(key, kstar, need_ties, sh, cur);
+            if (a.out_list)
+                write_list<NT, kPer, false>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key, col_of, count);
+            else
+                write_final<NT, kPer>(a, b, cur, key, col_of, count);
+        }
+    } else {
+        find_cut<NT, kPer, 64, !LIST>(key, k, sh, kstar, need_ties, total, v);
+        scan_winners<NT, kPer>(key, kstar, need_ties, sh, cur);
+        const uint32_t count = min(total, k);
+        if (a.out_list)
+            write_list<NT, kPer, kFused>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key, col_of, count);
+        else
+            write_final<NT, kPer>(a, b, cur, key, col_of, count);
+    }
     if constexpr (kFused) {
         // ---- fused merge: the row's last part to arrive merges its lists.
         // Once every list store of the workgroup has completed (vmcnt 0 in
@@ -520,8 +640,8 @@ hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
 
 // Capacities (items per workgroup / threads): logits 4096/512 (4096/1024 when
 // the row's last part merges: the latency-bound phases run faster on more
-// waves), 8192/1024,
-// 16384/1024, 20480/1024, 24576/1024, 32768/1024 (the smallest that holds a
+// waves), 8192/1024, 16384/512, 20480/512, 24576/512 (two workgroups per CU:
+// many long rows, one part each), 32768/1024 (the smallest that holds a
 // part: every slot costs work whether it holds a column or not); lists
 // 4096/512, 16384/1024.  `fused` (logits with
 // several parts per row whose lists, parts * (k rounded up to even) items,
@@ -541,9 +661,9 @@ hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused,
     switch (cap) {
     case 4096: return launch_seg<4096, false, 512>(a, s);
     case 8192: return launch_seg<8192, false, 1024>(a, s);
-    case 16384: return launch_seg<16384, false, 1024>(a, s);
-    case 20480: return launch_seg<20480, false, 1024>(a, s);
-    case 24576: return launch_seg<24576, false, 1024>(a, s);
+    case 16384: return launch_seg<16384, false, 512>(a, s);
+    case 20480: return launch_seg<20480, false, 512>(a, s);
+    case 24576: return launch_seg<24576, false, 512>(a, s);
     default: return launch_seg<kSegLogitCap, false, 1024>(a, s);
     }
 }
