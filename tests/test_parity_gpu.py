@@ -434,6 +434,40 @@ def test_topk_standalone_one_segment_per_row(n, k):
 
 
 
+@pytest.mark.parametrize("k", [512, 1000])
+def test_topk_one_segment_compaction_boundaries(k):
+    """Rows of one long segment each (256 rows of 20000 columns): after the
+    histogram the items that can still win are compacted when they number at
+    most 1024, else the selection stays on every slot.  Rows at and around
+    that bound and the degenerate cases: nothing selectable, fewer selectable
+    items than k, NaN with signed zeros, exactly 1024 and 1025 tied items in
+    the top bin, one value everywhere, half the row masked."""
+    rng = np.random.default_rng(k)
+    B, n = 256, 20000
+    vals = rng.standard_normal((B, n)).astype(np.float32)
+    vals[0] = -np.inf                                         # nothing selectable
+    vals[1] = -np.inf
+    vals[1, rng.choice(n, 300, replace=False)] = rng.standard_normal(300)   # fewer than k
+    vals[2, rng.random(n) < 0.01] = np.nan
+    vals[2, :50] = -0.0
+    vals[2, 50:100] = 0.0
+    vals[3, rng.choice(n, 1024, replace=False)] = 100.0      # 1024 tied in the top bin
+    vals[4, rng.choice(n, 1025, replace=False)] = 100.0      # one past the compaction bound
+    vals[5] = 0.5                                             # one value everywhere
+    vals[6, n // 2:] = -np.inf
+    vals[7, : k - 3] = 7.0                                    # k - 3 clear winners, then the cut
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    got = cols.cpu().numpy()
+    for r in range(8):
+        assert np.array_equal(got[r], ref_cols[r]), f"row {r}"
+    assert np.array_equal(got, ref_cols)
+    ok = ref_cols >= 0
+    assert np.array_equal(v.cpu().numpy()[ok], ref_v[ok].astype(np.float32))
+    assert (got[0] == -1).all() and (got[1] >= 0).sum() == 300
+
+
 @pytest.mark.parametrize("n,k", [(100, 4), (4096, 384), (70000, 512)])
 def test_topk_standalone_values_far_from_zero_in_a_narrow_range(n, k):
     """Values whose magnitude is large against their spread (|min| / range
