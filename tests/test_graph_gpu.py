@@ -104,14 +104,16 @@ def test_score_with_scores_replays():
                   lambda: L.idx_score(q2, d.w, d.keys, wl.n_cols, with_scores=True))
 
 
-@pytest.mark.parametrize("n,k", [(300000, 2048), (40000, 512)])
-def test_topk_replays(n, k):
-    """Rows longer than one merge: separate list-merge launches."""
+@pytest.mark.parametrize("B,n,k", [(3, 300000, 2048), (3, 40000, 512), (256, 20000, 512)])
+def test_topk_replays(B, n, k):
+    """Rows longer than one merge (separate list-merge launches), and many
+    rows of one long segment each (candidates compacted in LDS, two
+    workgroups per CU)."""
     rng = np.random.default_rng(72)
-    lg = torch.from_numpy(rng.standard_normal((3, n), dtype=np.float32)).cuda()
-    oc = torch.empty((3, k), dtype=torch.int32, device="cuda")
-    ov = torch.empty((3, k), dtype=torch.float32, device="cuda")
-    ws = L.new_workspace(max(L.workspace_bytes(L.IDX_OP_TOPK, 3, n, k), 1), "cuda")
+    lg = torch.from_numpy(rng.standard_normal((B, n), dtype=np.float32)).cuda()
+    oc = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    ov = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(max(L.workspace_bytes(L.IDX_OP_TOPK, B, n, k), 1), "cuda")
     lg2 = -lg
 
     def call():
