@@ -640,7 +640,7 @@ hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
 
 // Capacities (items per workgroup / threads): logits 4096/512 (4096/1024 when
 // the row's last part merges: the latency-bound phases run faster on more
-// waves), 8192/1024, 16384/512, 20480/512, 24576/512 (two workgroups per CU:
+// waves), 8192/512, 16384/512, 20480/512, 24576/512 (two workgroups per CU:
 // many long rows, one part each), 32768/1024 (the smallest that holds a
 // part: every slot costs work whether it holds a column or not); lists
 // 4096/512, 16384/1024.  `fused` (logits with
@@ -660,7 +660,7 @@ hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused,
     }
     switch (cap) {
     case 4096: return launch_seg<4096, false, 512>(a, s);
-    case 8192: return launch_seg<8192, false, 1024>(a, s);
+    case 8192: return launch_seg<8192, false, 512>(a, s);
     case 16384: return launch_seg<16384, false, 512>(a, s);
     case 20480: return launch_seg<20480, false, 512>(a, s);
     case 24576: return launch_seg<24576, false, 512>(a, s);

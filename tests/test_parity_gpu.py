@@ -416,7 +416,7 @@ def test_topk_standalone_multilevel(n, k):
     assert np.array_equal(v.cpu().numpy(), ref_v.astype(np.float32))
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("n,k", [(17408, 512), (20000, 512), (24000, 2048), (24576, 7)])
+@pytest.mark.parametrize("n,k", [(6000, 512), (8192, 1000), (17408, 512), (20000, 512), (24000, 2048), (24576, 7)])
 def test_topk_standalone_one_segment_per_row(n, k):
     """Many rows (one top-k workgroup per row) whose segment sizes are not a
     multiple of the write-out's 8-slot groups (20 and 24 slots per thread)."""
