@@ -277,7 +277,12 @@ int idx_score_topk_fp8q(const uint16_t *q, const float *w, int32_t B,
  * The contraction runs on v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1
  * operands and the blocks' E8M0 scales.  Arguments, outputs, rules and
  * errors as for idx_score / idx_score_topk (q bf16 [B, H, D], 16-byte
- * aligned), with H = 64 (IDX_E_SHAPE otherwise).
+ * aligned), with H = 64 (IDX_E_SHAPE otherwise).  idx_score_topk_mxfp4 with
+ * more than 512 rows of one request (n_req = 1, a block table, 64-row
+ * blocks, no chunk lists) rounds that request's key blocks once into its
+ * workspace before the score launch, by the same rule, so its result equals
+ * idx_score_mxfp4's bit for bit; the workspace size already includes the
+ * room (idx_workspace_bytes(IDX_OP_SCORE_TOPK, ...)).
  */
 int idx_score_mxfp4(const uint16_t *q, const float *w, int32_t B, int32_t H,
                     int32_t D, const idx_keys *keys, int32_t n_cols,

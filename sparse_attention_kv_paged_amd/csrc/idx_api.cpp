@@ -45,6 +45,10 @@ struct TopkPlan {
     bool fused = false;         // one launch: the row's last part merges the lists
     size_t logits = 0, row_cols = 0, row_done = 0, list[2] = {0, 0}, total = 0;
     int64_t ld = 0;
+    // the per-row split (B > kFlatRows): room for one request's key blocks
+    // rounded to MXFP4 ahead of the score launch (idx_score_topk_mxfp4)
+    size_t mx = 0;
+    int32_t mx_blocks = 0;
 };
 
 // Items per merge list: k rounded up to even (the kernels pad every list
@@ -84,6 +88,10 @@ TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
         // the score kernel zeroes row_done, so score_topk can merge in place
         P.fused = P.parts0 > 1 && P.cap0 <= 16384 &&
                   (int64_t)P.parts0 * list_cap(k) <= (P.cap0 <= 8192 ? 2 : 1) * (int64_t)P.cap0;
+        if (B > idx::kFlatRows) {
+            P.mx_blocks = (int32_t)(((int64_t)n_cols + idx::kBlock - 1) / idx::kBlock);
+            P.mx = take((size_t)P.mx_blocks * idx::kMxKeyBlockBytes);
+        }
     }
     if (P.parts0 > 1) {
         const int per = idx::kSegListCap / list_cap(k);
@@ -354,6 +362,16 @@ int score_topk_launch(const uint16_t *q, const uint8_t *q8, const float *w, int3
     a.row_done = reinterpret_cast<uint32_t *>(ws + P.row_done);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e;
+    // MXFP4 over many rows of one request: its key blocks are rounded once,
+    // ahead of the score launch, instead of once per row in the tile loop
+    if (mx && P.mx_blocks > 0 && keys->block_table && !keys->chunk_ids && keys->block_size == idx::kBlock &&
+        keys->n_req == 1) {
+        const int32_t nblk = std::min<int32_t>(keys->max_blocks, P.mx_blocks);
+        uint8_t *mxk = reinterpret_cast<uint8_t *>(ws + P.mx);
+        if ((e = idx::launch_mx_keys(a, mxk, nblk, s)) != hipSuccess) return hip_fail(e, "MXFP4 key rounding");
+        a.mx_keys = mxk;
+        a.mx_blocks = nblk;
+    }
     if ((e = launch_heads(a, H, s)) != hipSuccess) return hip_fail(e, "score kernel");
     e = enqueue_topk(P, ws, a.logits, P.ld, a.row_cols, B, n_cols, k, out_idx, out_val,
                      keys->chunk_ids, keys->max_chunks, keys->block_size == idx::kSmallBlock ? 4 : 6, s);

@@ -14,6 +14,7 @@ constexpr int kBlock = 64;                   // entries per slot (and per paged 
 constexpr int kSmallBlock = 16;              // the other supported pool block size
 constexpr int kRowBytes = kHeadDim + 4;      // 128 e4m3 bytes + fp32 scale
 constexpr int kWaves = 4;                    // waves per score workgroup
+constexpr int kFlatRows = 512;               // rows up to which the score launch shares work evenly over waves
 constexpr int kMaxK = 2048;
 constexpr int kSegLogitCap = 32768;          // logits per top-k workgroup
 constexpr int kSegListCap = 16384;           // (key, column) items per merge workgroup
@@ -74,7 +75,18 @@ struct ScoreArgs {
     uint32_t *page_bits;
     int64_t bits_ld;            // words per row
     float threshold;
+    // MXFP4 keys rounded ahead of the score launch (mxfp4, the per-row path,
+    // one request, 64-row blocks, no chunk lists): logical block j of
+    // request 0 at mx_keys + j * kMxKeyBlockBytes for j < mx_blocks, laid out
+    // as mx_keys_kernel writes it.  Null: the score kernel rounds each tile.
+    const uint8_t *mx_keys;
+    int32_t mx_blocks;
 };
+
+// One 64-row block of pre-rounded MXFP4 keys: per row 64 code bytes (the
+// four 32-value blocks, two e2m1 values a byte), then per row the four E8M0
+// block scales (one word), then per row the fp32 row scale.
+constexpr int kMxKeyBlockBytes = 64 * 64 + 64 * 4 + 64 * 4;
 
 // One launch of the segment top-k (idx_topk.hip).  Input is either a logits
 // matrix cut into `parts` segments of the kernel's capacity per row, or the
@@ -110,6 +122,9 @@ struct SegArgs {
 // kernel's start and end time (hipExtLaunchKernelGGL).
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t ev_start = nullptr,
                         hipEvent_t ev_stop = nullptr);
+// Round logical blocks 0 .. nblocks - 1 of request 0's keys (a's pool and
+// block table) to MXFP4 into dst (nblocks * kMxKeyBlockBytes bytes).
+hipError_t launch_mx_keys(const ScoreArgs &a, uint8_t *dst, int32_t nblocks, hipStream_t s);
 hipError_t launch_topk_segment(const SegArgs &a, bool list, int cap, bool fused, hipStream_t s);
 
 }  // namespace idx

@@ -33,6 +33,7 @@
 // per tile (conversion + epilogue) is close to the MFMA time and the two
 // only overlap when they sit in one straight-line stretch of code.
 #include <algorithm>
+#include <type_traits>
 
 #include <hip/hip_ext.h>
 
@@ -474,6 +475,104 @@ __device__ __forceinline__ void tile_mma(KeyHalf &k, const QFp4 &qa, TileAcc &ac
                                                             4, 1, (int)qa.sc[1], 1, (int)ksc);
 }
 
+// Pre-rounded MXFP4 keys (ScoreArgs::mx_keys, written by mx_keys_kernel): a
+// 32-row tile in LDS holds the rows' code bytes -- 16-byte chunk c of row n
+// at granule 4n + (c ^ ((n >> 2) & 3)), so that the 16 lanes of a read pass
+// reach 16 different bank groups -- then the rows' E8M0 scale words, then
+// their row scales: 2304 bytes, brought by three loads.
+constexpr int kMxTileBytes = 32 * 64 + 32 * 4 + 32 * 4;
+
+struct KeyMx {
+    u32x4 kc[2];    // the codes of the lane's two 32-value blocks (d = 64*hf + 32*kk ..)
+    uint32_t ksc;   // their E8M0 scales in bytes 0 and 1
+    float s;        // the row's scale (a negative one's sign is in the codes)
+};
+
+// Issue the three loads of tile half `half` (rows 32*half .. 32*half + 31)
+// of the pre-rounded block described by r into the LDS slot dst.
+__device__ __forceinline__ void load_tile_mx(__amdgpu_buffer_rsrc_t r, int half, uint8_t *dst) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int p = 64 * i + lane;                  // the LDS granule this lane fills
+        const int n = p >> 2, c = (p & 3) ^ ((n >> 2) & 3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 1024 * i), 16,
+                                                 (uint32_t)(2048 * half + 64 * n + 16 * c), 0, 0, 0);
+    }
+    // lanes 0-31: the rows' scale words; lanes 32-63: their row scales
+    const uint32_t so = lane < 32 ? (uint32_t)(4096 + 128 * half + 4 * lane)
+                                  : (uint32_t)(4352 + 128 * half + 4 * (lane - 32));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + 2048), 4, so, 0, 0, 0);
+}
+
+__device__ __forceinline__ void read_tile(const uint8_t *slot, KeyMx &k) {
+    const int lane = threadIdx.x & 63, n = lane & 31, hf = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        k.kc[kk] = *reinterpret_cast<const u32x4 *>(slot + 16 * (4 * n + ((2 * hf + kk) ^ ((n >> 2) & 3))));
+    k.ksc = *reinterpret_cast<const uint32_t *>(slot + 2048 + 4 * n) >> (16 * hf);
+    k.s = *reinterpret_cast<const float *>(slot + 2176 + 4 * n);
+}
+
+// The MXFP4 contraction on codes rounded ahead: the same four MFMAs as
+// tile_mma(KeyHalf &, const QFp4 &, ...) on the same operands.
+__device__ __forceinline__ void tile_mma(const KeyMx &k, const QFp4 &qa, TileAcc &acc) {
+    const f32x16 z = {};
+    acc.h0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[0][0]), fp4_operand(k.kc[0]), z, 4, 4, 0,
+                                                            (int)qa.sc[0], 0, (int)k.ksc);
+    acc.h1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[1][0]), fp4_operand(k.kc[0]), z, 4, 4, 0,
+                                                            (int)qa.sc[1], 0, (int)k.ksc);
+    acc.h0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[0][1]), fp4_operand(k.kc[1]), acc.h0, 4,
+                                                            4, 1, (int)qa.sc[0], 1, (int)k.ksc);
+    acc.h1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(qa.v[1][1]), fp4_operand(k.kc[1]), acc.h1, 4,
+                                                            4, 1, (int)qa.sc[1], 1, (int)k.ksc);
+}
+
+// MXFP4 rounding of one request's key blocks ahead of the score launch, for
+// many query rows sharing them: logical block j (64 rows) of request 0
+// becomes, in the kMxKeyBlockBytes layout, each row's four 32-value blocks
+// rounded exactly as tile_mma(KeyHalf &, const QFp4 &, ...) rounds them
+// (fp8 sign bits flipped first for a negative row scale), their E8M0 scales
+// and the row scale.  Absent and out-of-range blocks read as zeros.  One
+// wave per block, lane = row.
+__global__ __launch_bounds__(64) void mx_keys_kernel(ScoreArgs a, uint8_t *dst) {
+    const int j = blockIdx.x, lane = threadIdx.x;
+    const int64_t nb = a.n_pool_rows / kBlock;
+    const int32_t pb = j < a.max_blocks ? a.block_table[j] : -1;      // request 0's table row
+    const bool ok = pb >= 0 && pb < nb;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(a.pool + (ok ? (int64_t)pb : 0) * kBlock * kRowBytes, ok ? (uint32_t)(kBlock * kRowBytes) : 0u);
+    const uint32_t ro = (uint32_t)lane * kRowBytes;
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, ro + 16u * i, 0, 0);
+    const float s = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, ro + kHeadDim, 0, 0));
+    const uint32_t m = s < 0.f ? 0x80808080u : 0u;
+    uint32_t esc = 0;
+    u32x4 codes[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        uint32_t raw[16];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const u32x4 x = v[2 * blk + jj] ^ u32x4{m, m, m, m};
+            const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                raw[8 * jj + 2 * i] = cvt_fp8x2_bf16x2<false>(w4[i]);
+                raw[8 * jj + 2 * i + 1] = cvt_fp8x2_bf16x2<true>(w4[i]);
+            }
+        }
+        esc |= mx_block_bf16(raw, codes[blk]) << (8 * blk);
+    }
+    const __amdgpu_buffer_rsrc_t o = make_rsrc(dst + (int64_t)j * kMxKeyBlockBytes, (uint32_t)kMxKeyBlockBytes);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+        __builtin_amdgcn_raw_buffer_store_b128(codes[blk], o, (uint32_t)(64 * lane + 16 * blk), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(esc, o, (uint32_t)(4096 + 4 * lane), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), o, (uint32_t)(4352 + 4 * lane), 0, 0);
+}
+
 // Epilogue half: relu, head weights and head sum, then the row scale.
 // wr[hb][g][i%4] holds the weight w[b] of the head that accumulator
 // register i = 4*g + i%4 of head block hb carries on this lane.  Returns the
@@ -508,7 +607,6 @@ __device__ __forceinline__ float tile_logit(const TileAcc &acc, const float (&wr
 // its loaded latency; deeper rings (three slots measured on every workload)
 // only lengthen the memory queues, which delays the dependent block-table
 // reads of the waves that start last.
-constexpr int kFlatRows = 512;  // rows up to which waves share work evenly
 
 template <int BS>
 __device__ __forceinline__ RowCtx uniform_row(const ScoreArgs &a, int b, uint32_t &st) {
@@ -823,7 +921,9 @@ struct NoQ {
 // loads has been issued, by every wave of the workgroup (it synchronises
 // the workgroup) -- delivers the MFMA operands of q[b].  Otherwise q[b] is
 // read from q_lds when the workgroup has staged it there, else from memory.
-template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, int BS, bool MX,
+// MXP (with MX, 64-row blocks, no chunk lists): the key tiles come already
+// rounded from a.mx_keys instead of from the pool.
+template <bool OWN_COLS, bool SCORES, bool CHUNKED, bool LEAN, bool Q8, bool ACCUM, int BS, bool MX, bool MXP,
           bool USE_PRE = false, class QFin = NoQ>
 __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, int j1, const RowCtx &r,
                                            int col_end, float *sh_w, uint8_t *ring, uint32_t &st,
@@ -834,7 +934,10 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
     const int n32 = lane & 31;
     constexpr int U = kBlock / BS;                    // pool blocks per slot
     constexpr int GS = 64 / U;                        // slots per group: one block per lane
-    constexpr int TB = tile_bytes<BS>();
+    static_assert(!MXP || (MX && BS == kBlock && !CHUNKED), "pre-rounded keys: MXFP4, 64-row blocks, no chunk lists");
+    constexpr int TB = MXP ? kMxTileBytes : tile_bytes<BS>();
+    constexpr int LPT = MXP ? 3 : loads_per_tile<BS>();   // loads per tile
+    using Key = typename std::conditional<MXP, KeyMx, KeyHalf>::type;
     const bool live = r.req >= 0 && j0 < r.nslots;
     // no logits buffer (scores only): the logit stores get an empty
     // descriptor and are dropped
@@ -922,11 +1025,22 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
                     const bool ok = prow0 >= 0;
                     const int64_t p0 = ok ? prow0 : 0;
                     const uint32_t bytes = ok ? (uint32_t)min<int64_t>(kBlock, a.n_pool_rows - p0) * kRowBytes : 0u;
-                    slot_r = make_rsrc(a.pool + p0 * kRowBytes, bytes);
-                    slot_lim = ok ? r.limit - __builtin_amdgcn_readlane(lane_ebase, j) : 0;
+                    const int eb = __builtin_amdgcn_readlane(lane_ebase, j);   // the slot's first logical entry
+                    if constexpr (MXP) {
+                        // logical block eb / 64 of request 0, rounded ahead
+                        const bool okm = ok && (eb >> 6) < a.mx_blocks;
+                        slot_r = make_rsrc(a.mx_keys + (int64_t)(okm ? eb >> 6 : 0) * kMxKeyBlockBytes,
+                                           okm ? (uint32_t)kMxKeyBlockBytes : 0u);
+                    } else {
+                        slot_r = make_rsrc(a.pool + p0 * kRowBytes, bytes);
+                    }
+                    slot_lim = ok ? r.limit - eb : 0;
                 }
                 lim_t[tau & 1] = slot_lim - 32 * (tau & 1);
-                load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * TB);
+                if constexpr (MXP)
+                    load_tile_mx(slot_r, tau & 1, ring + (tau & 1) * TB);
+                else
+                    load_tile(slot_r, (uint32_t)(32 * (tau & 1)) * kRowBytes, lane_lo, ring + (tau & 1) * TB);
             }
         };
         // a tile's epilogue inputs, kept with its accumulators because the
@@ -951,9 +1065,12 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
         // order, so this holds whatever order stores take.
         auto mma = [&](int tau, Stage &st_) {
             const int k = tau & 1;
-            wait_vmem<loads_per_tile<BS>()>();
-            KeyHalf kh;
-            read_tile<BS>(ring + k * TB, kh);
+            wait_vmem<LPT>();
+            Key kh;
+            if constexpr (MXP)
+                read_tile(ring + k * TB, kh);
+            else
+                read_tile<BS>(ring + k * TB, kh);
             wait_lds();
             st_.keep = n32 < lim_t[k];
             // ACCUM: the earlier logit is read before the next tile's loads
@@ -1027,7 +1144,9 @@ __device__ __forceinline__ void score_span(const ScoreArgs &a, int b, int j0, in
 // workgroup owns `slots_per_wave` x 4 consecutive slots of one row.
 // QQ (with Q8): q arrives as bf16 and is quantised here, while it is staged.
 // MX (with QQ): q and keys rounded to MXFP4 blocks here instead.
-template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM, int BS, bool QQ, bool MX>
+// MXP (with MX, the per-row split): the keys come rounded from a.mx_keys.
+template <bool OWN_COLS, bool SCORES, bool FLAT, bool CHUNKED, bool Q8, bool ACCUM, int BS, bool QQ, bool MX,
+          bool MXP = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_kernel(ScoreArgs a) {
     constexpr int U = kBlock / BS;                    // pool blocks per slot
     __shared__ __attribute__((aligned(16))) float sh_w[kWaves][kHeads];
@@ -1042,6 +1161,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int slot_cols = (a.n_cols + kBlock - 1) / kBlock;
     uint32_t st = 0;
 
+    static_assert(!MXP || (!FLAT && MX && !CHUNKED && BS == kBlock), "pre-rounded keys on the per-row split only");
     if (!FLAT) {
         const int b = blockIdx.x / a.splits;
         const int split = blockIdx.x - b * a.splits;
@@ -1075,7 +1195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, MXP, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put();                                    // the workgroup's one barrier
             __syncthreads();
@@ -1182,7 +1302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             __syncthreads();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
-            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, true>(a0, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
+            score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, false, true>(a0, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
                                                     qfin);
             f = min(fend, pe);
             for (++b; f < fend; ++b) {
@@ -1196,7 +1316,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 r.nslots = (r.nunits + U - 1) / U;
                 const int ce = OWN_COLS ? max(0, min(r.nslots * kBlock, a.n_cols)) : a.n_cols;
                 int bl;
-                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX>(key_view(a, b, bl), b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st,
+                score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, false>(key_view(a, b, bl), b, f - pb, min(fend, pe) - pb, r, ce, sh_w[wave], sh_ring[wave], st,
                                                                       SlotRaw{-1, -1, false}, NoQ{},
                                                                       b == rb + 1 ? sh_q[1] : nullptr);
                 f = min(fend, pe);
@@ -1213,6 +1333,13 @@ template <bool OWN_COLS, bool SCORES, bool FLAT, bool Q8, bool ACCUM, bool QQ, b
 void launch_score_qa(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     const dim3 g((unsigned)grid), blk(256);
     const bool small = a.block_size == kSmallBlock;
+    if constexpr (MX && !FLAT) {
+        if (a.mx_keys) {                              // the keys rounded ahead (launch_score checked the shape)
+            hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, false, Q8, ACCUM, kBlock, QQ, MX, true>), g, blk,
+                                  0, s, e0, e1, 0, a);
+            return;
+        }
+    }
     if (a.chunk_ids) {
         if (small)
             hipExtLaunchKernelGGL((score_kernel<OWN_COLS, SCORES, FLAT, true, Q8, ACCUM, kSmallBlock, QQ, MX>), g, blk, 0, s,
@@ -1252,11 +1379,23 @@ void launch_score_as(const ScoreArgs &a, int64_t grid, hipStream_t s, hipEvent_t
         launch_score_q<OWN_COLS, SCORES, FLAT, false>(a, grid, s, e0, e1);
 }
 
+hipError_t launch_mx_keys(const ScoreArgs &a, uint8_t *dst, int32_t nblocks, hipStream_t s) {
+    if (nblocks <= 0) return hipSuccess;
+    if (!a.block_table || !a.pool || !dst || a.max_blocks < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mx_keys_kernel, dim3((unsigned)nblocks), dim3(64), 0, s, a, dst);
+    return hipGetLastError();
+}
+
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
     if (a.B <= 0) return hipSuccess;
     if (a.accum && (a.q8 || a.quant_q || a.mxfp4)) return hipErrorInvalidValue;
     if (a.quant_q && (a.q8 || !a.q)) return hipErrorInvalidValue;
     if (a.mxfp4 && (a.q8 || a.quant_q || !a.q)) return hipErrorInvalidValue;
+    // keys rounded ahead: MXFP4 on the per-row split, 64-row blocks, a block
+    // table and no chunk lists
+    if (a.mx_keys && (!a.mxfp4 || a.B <= kFlatRows || a.block_size != kBlock || !a.block_table || a.chunk_ids ||
+                      a.mx_blocks < 0))
+        return hipErrorInvalidValue;
     if (a.block_size != kBlock && a.block_size != kSmallBlock) return hipErrorInvalidValue;
     if (!a.logits && (a.accum || (!a.scores && !a.page_bits) || a.row_cols)) return hipErrorInvalidValue;
     // several layers in one launch: the flattened split, selection bits, no

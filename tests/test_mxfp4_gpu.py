@@ -126,6 +126,30 @@ def test_mxfp4_zero_tiny_and_huge_heads_negative_scales_padding():
     _check_mx(wl, tag="edge")
 
 
+def test_mxfp4_keys_rounded_ahead_edge_cases():
+    """Many rows of one request (the per-row split) take keys rounded once
+    ahead of the score launch in idx_score_topk_mxfp4, while idx_score_mxfp4
+    rounds them in the tile loop: the two must agree bit for bit (the check
+    compares score_topk with the top-k of the score-only logits) and with the
+    oracle, here with negative and zero key scales, absent and out-of-range
+    block ids, padding rows and a zero bound."""
+    wl = W.prefill(8192, 600, seed=76, k=64, name="mx-ahead-edge")
+    rng = np.random.default_rng(77)
+    sc = wl.pool[:, 128:].copy().view("<f4")
+    sc[rng.random(len(sc)) < 0.3] *= -1
+    sc[rng.random(len(sc)) < 0.05] = 0.0
+    wl.pool = wl.pool.copy()
+    wl.pool[:, 128:] = sc.view(np.uint8)
+    wl.block_table = wl.block_table.copy()
+    wl.block_table[0, 3] = -1
+    wl.block_table[0, 7] = 1 << 20                            # past the pool: absent, flagged
+    wl.q_req = wl.q_req.copy()
+    wl.q_req[[5, 300]] = -1
+    wl.limits = wl.limits.copy()
+    wl.limits[11] = 0
+    _check_mx(wl, tag="ahead-edge")
+
+
 def _grid_values(rng, shape, e):
     g = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])[rng.integers(0, 8, size=shape)]
     g = g * np.where(rng.random(shape) < 0.5, -1.0, 1.0)
