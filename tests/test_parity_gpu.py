@@ -434,6 +434,32 @@ def test_topk_standalone_one_segment_per_row(n, k):
 
 
 
+@pytest.mark.parametrize("B,n,k", [(32, 160000, 512), (32, 190000, 7), (32, 150000, 2048), (16, 200000, 2048),
+                                   (64, 90000, 512)])
+def test_topk_long_segments_writing_lists(B, n, k):
+    """Rows split into parts of 16384-24576 columns that are not merged in the
+    same launch: each part (candidates compacted in LDS, or the register path
+    past 1024 candidates) writes a (key, column) list that a further launch
+    merges.  Some rows are mostly masked so that parts hold fewer selectable
+    items than k, or none."""
+    rng = np.random.default_rng(B + n + k)
+    vals = rng.standard_normal((B, n)).astype(np.float32)
+    vals[0, : n - 300] = -np.inf                              # 300 selectable, all in the last part
+    vals[1] = -np.inf                                         # none
+    vals[2, ::2] = -np.inf
+    vals[3] = np.round(vals[3] * 4) / 4                       # many exact ties
+    vals[4, rng.random(n) < 0.01] = np.nan
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    got = cols.cpu().numpy()
+    for r in range(5):
+        assert np.array_equal(got[r], ref_cols[r]), f"row {r}"
+    assert np.array_equal(got, ref_cols)
+    ok = ref_cols >= 0
+    assert np.array_equal(v.cpu().numpy()[ok], ref_v[ok].astype(np.float32))
+
+
 @pytest.mark.parametrize("k", [512, 1000])
 def test_topk_one_segment_compaction_boundaries(k):
     """Rows of one long segment each (256 rows of 20000 columns): after the
