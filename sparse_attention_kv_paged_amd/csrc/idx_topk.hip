@@ -485,7 +485,7 @@ void topk_segment_kernel(SegArgs a) {
     constexpr int kMPer = kFused ? MMUL * kPer : kPer;    // merge items per thread
     // long segments of logits: the items that can still win after the
     // histogram are compacted into LDS, one per thread (see below)
-    constexpr bool kCompact = !LIST && !kFused && kPer >= 16;
+    constexpr bool kCompact = !LIST && kPer >= 16;
     constexpr int kCI = 1024 / NT;                    // compacted items per thread (up to 1024 in all)
     __shared__ SelScratch<NT, 64> sh;
     __shared__ uint2 sh_items[kCompact ? kCI * NT : 1];
@@ -587,14 +587,14 @@ void topk_segment_kernel(SegArgs a) {
             scan_winners<NT, kCI>(key1, kstar, need_ties, sh, cur);
             const auto col1 = [&](int i) { return (uint32_t)(col0 + cl[i]); };
             if (a.out_list)
-                write_list<NT, kCI, false>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key1, col1, count);
+                write_list<NT, kCI, kFused>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key1, col1, count);
             else
                 write_final<NT, kCI>(a, b, cur, key1, col1, count);
         } else {
             if (!c.every) resolve_cut<NT, kPer, 64>(key, bins, c, k, sh, kstar, need_ties);
             scan_winners<NT, kPer>(key, kstar, need_ties, sh, cur);
             if (a.out_list)
-                write_list<NT, kPer, false>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key, col_of, count);
+                write_list<NT, kPer, kFused>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key, col_of, count);
             else
                 write_final<NT, kPer>(a, b, cur, key, col_of, count);
         }
