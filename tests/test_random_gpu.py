@@ -108,3 +108,49 @@ def test_random_configuration(seed):
         pos = {int(c): j for j, c in enumerate(wl.chunk_ids[b][:wl.n_chunks[b]])}
         return ref[b, np.array([pos[int(e) // bs] * bs + int(e) % bs for e in ids], dtype=np.int64)]
     assert_topk_near_tie(idx, ref_ids, logit_of, wl.k, f"random {seed} {path}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shared_request_rows(seed):
+    """Many query rows of one request (chunked prefill: the per-row split, and
+    for MXFP4 the request's keys rounded once per call) with a random prefix,
+    row count, k, path and masked table entries."""
+    rng = np.random.default_rng(9000 + seed)
+    prefix = int(rng.integers(1, 40)) * 1024
+    rows = int(rng.integers(513, 700))
+    k = int(rng.choice([7, 64, 512, 1000]))
+    path = str(rng.choice(["bf16", "fp8q", "mxfp4"]))
+    wl = W.prefill(prefix, rows, seed=9000 + seed, k=k, name=f"random{seed}-shared")
+    if rng.random() < 0.5:
+        wl.block_table = wl.block_table.copy()
+        wl.block_table[0, rng.integers(0, wl.block_table.shape[1])] = -1
+    if rng.random() < 0.5:
+        sc = wl.pool[:, -4:].copy().view("<f4")
+        sc[rng.random(len(sc)) < 0.2] *= -1
+        wl.pool = wl.pool.copy()
+        wl.pool[:, -4:] = sc.view(np.uint8)
+    print(f"[random] shared {seed}: {wl.description} rows={rows} k={k} path={path}", flush=True)
+    d = L.to_device(wl)
+    if path == "bf16":
+        lg = L.idx_score(d.q, d.w, d.keys, d.n_cols)
+        idx, val = L.idx_score_topk(d.q, d.w, d.keys, d.n_cols, wl.k)
+        ref = oracle.score(wl)
+    elif path == "fp8q":
+        lg = L.idx_score_fp8q(d.q, d.w, d.keys, d.n_cols)
+        idx, val = L.idx_score_topk_fp8q(d.q, d.w, d.keys, d.n_cols, wl.k)
+        ref = oracle.score(wl, q8=oracle.quantize_q(wl.q))
+    else:
+        lg = L.idx_score_mxfp4(d.q, d.w, d.keys, d.n_cols)
+        idx, val = L.idx_score_topk_mxfp4(d.q, d.w, d.keys, d.n_cols, wl.k)
+        ref = oracle.score(wl, mxfp4=True)
+    torch.cuda.synchronize()
+    g = lg.cpu().numpy()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    assert_logits_close(g, ref, f"shared {seed} {path}")
+    own_cols, own_vals = column_order(*oracle.topk(g.astype(np.float64), wl.k))
+    assert np.array_equal(idx, oracle.cols_to_entries(wl, own_cols)), f"seed {seed}: top-k != top-k of own logits"
+    ok = own_cols >= 0
+    assert np.array_equal(val[ok], own_vals[ok].astype(np.float32))
+    ref_ids = oracle.cols_to_entries(wl, oracle.topk(ref, wl.k)[0])
+    assert_topk_near_tie(idx, ref_ids, lambda b, ids: ref[b, np.asarray(ids, dtype=np.int64)], wl.k,
+                         f"shared {seed} {path}")
