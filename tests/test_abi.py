@@ -53,6 +53,10 @@ def test_workspace_bytes(lib):
     # score_topk holds the logits (4 rows x 1024 padded columns x 4 B) and
     # per-row column counts and merge counters, each piece 256-byte aligned
     assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 4, 1000, 512) == 4 * 1024 * 4 + 2 * 256
+    # more than 512 rows (the per-row split): also room for one request's key
+    # blocks rounded to MXFP4 ahead of the score launch, 4608 B per 64 columns
+    assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 600, 1000, 512) == 600 * 1024 * 4 + 2 * 2560 + 16 * 4608
+    assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 512, 1000, 512) == 512 * 1024 * 4 + 2 * 2048
     # long rows: per-part (key, column) lists of k items and their counts
     parts = -(-262144 // 32768)
     need = L.workspace_bytes(L.IDX_OP_TOPK, 8, 262144, 512)
