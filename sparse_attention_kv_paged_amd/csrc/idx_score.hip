@@ -295,6 +295,17 @@ __device__ __forceinline__ void read_tile(const uint8_t *slot, KeyHalf &k) {
 // The compiler does not see that an LDS read depends on a buffer-to-LDS
 // load, so the ring's waits are explicit, and each is also a compiler
 // barrier for memory operations.
+// A workgroup barrier for LDS traffic only: each wave's LDS operations have
+// completed (lgkmcnt 0) when it arrives, but vector-memory loads still in
+// flight -- the first key tiles of the ring -- are not waited for, as
+// __syncthreads would.  The barriers around q's staging and quantisation
+// only order LDS data between the waves.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -821,7 +832,7 @@ __device__ __forceinline__ void quantize_staged_row(uint16_t *slot) {
         raw[4 * j + 2] = x.z;
         raw[4 * j + 3] = x.w;
     }
-    __syncthreads();
+    lds_barrier();
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -887,7 +898,7 @@ __device__ __forceinline__ void quantize_staged_row_mx(uint16_t *slot) {
         raw[4 * j + 2] = x.z;
         raw[4 * j + 3] = x.w;
     }
-    __syncthreads();
+    lds_barrier();
     u32x4 codes;
     const uint32_t sb = mx_block_bf16(raw, codes);
     uint8_t *row = reinterpret_cast<uint8_t *>(slot) + h * kMxStage;
@@ -1185,20 +1196,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const auto put = [&] {
             put_q_rows<1>(a, b, qv, sh_q);
             if constexpr (QQ) {
-                __syncthreads();
+                lds_barrier();
                 if constexpr (MX) quantize_staged_row_mx(sh_q[0]); else quantize_staged_row(sh_q[0]);
             }
         };
         const auto qfin = [&](typename QSel<Q8, MX>::Op &qa) {
             put();
-            __syncthreads();
+            lds_barrier();
             load_q_staged(sh_q[0], qa);
         };
         if (j0 < j1) {
             score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, MXP, true>(a, b, j0, j1, r, col_end, sh_w[wave], sh_ring[wave], st, raw0, qfin);
         } else {
             put();                                    // the workgroup's one barrier
-            __syncthreads();
+            lds_barrier();
         }
     } else {
         // per-row work (slots) and its prefix over rows, in LDS
@@ -1283,14 +1294,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if constexpr (QQ) {
 #pragma unroll 1
                 for (int rr = 0; rr < nquant; ++rr) {
-                    __syncthreads();
+                    lds_barrier();
                     if constexpr (MX) quantize_staged_row_mx(sh_q[rr]); else quantize_staged_row(sh_q[rr]);
                 }
             }
         };
         const auto qfin = [&](typename QSel<Q8, MX>::Op &qa) {
             put();
-            __syncthreads();
+            lds_barrier();
             if (b == rb || b == rb + 1)
                 load_q_staged(sh_q[b - rb], qa);
             else
@@ -1299,7 +1310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         if (!(f < fend)) {
             put();                                    // the workgroup's one barrier
-            __syncthreads();
+            lds_barrier();
         } else {
             const int col_end = OWN_COLS ? max(0, min(r0.nslots * kBlock, a.n_cols)) : a.n_cols;
             score_span<OWN_COLS, SCORES, CHUNKED, !FLAT, Q8, ACCUM, BS, MX, false, true>(a0, b, f - pb, min(fend, pe) - pb, r0, col_end, sh_w[wave], sh_ring[wave], st, raw0,
