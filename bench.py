@@ -295,6 +295,35 @@ def summarize_mfma(pmc_dir, workload, command, out):
     print("\n".join(lines))
 
 
+def summarize_counters(pmc_dir, kname, workload, command, out, items=None):
+    """Medians per dispatch of every counter in one `rocprofv3 --pmc` run for
+    the kernels whose name contains `kname` and, given `items` (work items per
+    dispatch), the VALU instructions per item (SQ_INSTS_VALU counts wave64
+    instructions)."""
+    import statistics
+    per = {}
+    for r in _csv_rows(_find(pmc_dir, "counter_collection.csv")):
+        if kname not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    names = sorted({c for d in per.values() for c in d if c != "ns"})
+    med = {c: statistics.median(d[c] for d in per.values() if c in d) for c in names + ["ns"]}
+    lines = [f"# rocprofv3 counters for {kname}, workload {workload}",
+             f"# command: {command}",
+             f"# medians over dispatches",
+             f"dispatches = {len(per)}"]
+    lines += [f"{c.lower()} = {med[c]:.0f}" for c in names]
+    lines.append(f"dispatch_ns = {med['ns']:.0f}")
+    if items and "SQ_INSTS_VALU" in med:
+        lines.append(f"items_per_dispatch = {items}")
+        lines.append(f"valu_insts_per_item = {med['SQ_INSTS_VALU'] * 64 / items:.2f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(wl, pairs: int, min_seconds: float, max_sample_pairs: int = 4_000_000, mxfp4: bool = False):
     """The oracle as it stands on the host cores, timed on a bounded sample:
     full passes of the workload until `min_seconds` of wall time, or, when one
@@ -673,6 +702,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ summary of FETCH_SIZE / WRITE_SIZE runs")
     ap.add_argument("--summarize-mfma", metavar="DIR", help="write profiles/ summary of an MFMA counter run")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("KERNEL", "DIR"),
+                    help="write profiles/ summary of any --pmc run for kernels whose name contains KERNEL")
     ap.add_argument("--gemm-calibration", type=int, default=0, metavar="N",
                     help="only time N plain bf16 GEMMs of 8192^3 (torch.matmul): the library's sustained MFMA rate")
     ap.add_argument("--summarize-gemm", metavar="DIR",
@@ -687,6 +718,15 @@ def main():
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, prof_name, args.command,
                         os.path.join(PROFILE_DIR, f"{trace_prefix}_{prof_name}_trace.txt"))
+        return
+    if args.summarize_counters:
+        kname, pdir = args.summarize_counters
+        items = None
+        if args.workload in WORKLOADS and "topk" in kname:
+            from sparse_attention_kv_paged_amd import workloads
+            items = int(scoring_workload(args.workload, args, workloads).pairs())   # scored pairs
+        summarize_counters(pdir, kname, prof_name, args.command,
+                           os.path.join(PROFILE_DIR, f"{kname}_{prof_name}_counters.txt"), items)
         return
     if args.summarize_gemm:
         summarize_gemm_mfma(args.summarize_gemm, args.command,
