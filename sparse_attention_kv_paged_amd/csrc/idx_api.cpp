@@ -49,6 +49,9 @@ struct TopkPlan {
     // rounded to MXFP4 ahead of the score launch (idx_score_topk_mxfp4)
     size_t mx = 0;
     int32_t mx_blocks = 0;
+    // level 0 through a sampled threshold first: one flag per workgroup
+    size_t redo = 0;
+    bool sampled = false;
 };
 
 // Items per merge list: k rounded up to even (the kernels pad every list
@@ -93,6 +96,8 @@ TopkPlan topk_plan(bool with_logits, int32_t B, int32_t n_cols, int32_t k) {
             P.mx = take((size_t)P.mx_blocks * idx::kMxKeyBlockBytes);
         }
     }
+    P.sampled = idx::topk_sampled(P.cap0, P.fused, k);
+    if (P.sampled) P.redo = take((size_t)std::max(B, 1) * P.parts0 * sizeof(uint32_t));
     if (P.parts0 > 1) {
         const int per = idx::kSegListCap / list_cap(k);
         const int parts1 = (P.parts0 + per - 1) / per;
@@ -123,6 +128,7 @@ hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_
     a.chunk_ids = chunk_ids;
     a.max_chunks = max_chunks;
     a.chunk_shift = chunk_shift;
+    a.redo = P.sampled ? reinterpret_cast<uint32_t *>(ws + P.redo) : nullptr;
     if (P.parts0 == 1) return idx::launch_topk_segment(a, false, P.cap0, false, s);
     a.out_list = reinterpret_cast<uint2 *>(ws + P.list[0]);
     if (P.fused) {
@@ -136,6 +142,7 @@ hipError_t enqueue_topk(const TopkPlan &P, char *ws, const float *logits, int64_
     int in_parts = P.parts0, cur = 0;
     while (true) {
         idx::SegArgs m = a;
+        m.redo = nullptr;
         m.logits = nullptr;
         m.row_cols = nullptr;
         m.in_list = reinterpret_cast<const uint2 *>(ws + P.list[cur]);

@@ -40,6 +40,16 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
     return v;
 }
 
+// A workgroup barrier for LDS traffic only: each wave's LDS operations have
+// completed (lgkmcnt 0) when it arrives, but its vector-memory loads still in
+// flight are not waited for, as __syncthreads would (it waits for vmcnt 0).
+// For barriers that only order LDS data between the waves.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Raw buffer descriptor over [base, base + bytes): loads outside the range
 // return 0 and stores outside it are dropped, so bounds need no branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {

@@ -116,7 +116,20 @@ struct SegArgs {
     const int32_t *chunk_ids;   // columns -> logical entries, or null
     int32_t max_chunks;
     int32_t chunk_shift;        // log2 of the entries one chunk id names (6, or 4 for 16-row blocks)
+    // [B * parts] or null: the sampled-threshold launch's flag per
+    // workgroup (1 = not settled there); with it, the other launch over the
+    // same segments only runs the flagged workgroups
+    uint32_t *redo;
 };
+
+// Level-0 launches over segments of logits with at least 16 per thread
+// (caps >= 8192), not merged in the same launch, and k <= kTopkPreMaxK
+// first select through a threshold sampled from the segment (up to
+// kTopkPreCap items compacted), then re-run the workgroups it could not
+// settle: they need the redo flags.
+constexpr int kTopkPreCap = 2048;
+constexpr int32_t kTopkPreMaxK = kTopkPreCap * 5 / 16;
+inline bool topk_sampled(int cap, bool fused, int32_t k) { return !fused && cap >= 8192 && k <= kTopkPreMaxK; }
 
 // ev_start / ev_stop (optional): events the dispatch itself stamps with the
 // kernel's start and end time (hipExtLaunchKernelGGL).

@@ -294,17 +294,9 @@ __device__ __forceinline__ void read_tile(const uint8_t *slot, KeyHalf &k) {
 
 // The compiler does not see that an LDS read depends on a buffer-to-LDS
 // load, so the ring's waits are explicit, and each is also a compiler
-// barrier for memory operations.
-// A workgroup barrier for LDS traffic only: each wave's LDS operations have
-// completed (lgkmcnt 0) when it arrives, but vector-memory loads still in
-// flight -- the first key tiles of the ring -- are not waited for, as
-// __syncthreads would.  The barriers around q's staging and quantisation
-// only order LDS data between the waves.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
+// barrier for memory operations.  The barriers around q's staging and
+// quantisation only order LDS data between the waves (lds_barrier: the
+// first key tiles of the ring stay in flight).
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {

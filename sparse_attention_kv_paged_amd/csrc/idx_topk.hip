@@ -24,6 +24,8 @@
 // (concatenated in part order, so column order holds): by the row's last part
 // in the same launch when the lists fit, else by further launches.
 // The result is deterministic and ordered by column.
+#include <algorithm>
+
 #include "idx_device.h"
 #include "idx_internal.h"
 
@@ -61,9 +63,27 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *sh) {
     v = wave_scan(v);
     if (NT == 64) return v;
     if (lane == 63) sh[wave] = v;
-    __syncthreads();
+    lds_barrier();
     uint32_t add = 0;
     for (int i = 0; i < wave; ++i) add += sh[i];
+    return v + add;
+}
+
+// block_scan that also gives every thread the workgroup's total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_total(uint32_t v, uint32_t *sh, uint32_t &total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = wave_scan(v);
+    if (lane == 63) sh[wave] = v;
+    lds_barrier();
+    uint32_t add = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        const uint32_t t = sh[i];
+        add += i < wave ? t : 0u;
+        all += t;
+    }
+    total = all;
     return v + add;
 }
 
@@ -101,7 +121,7 @@ __device__ void find_from_top(const uint32_t *h, int nbins, uint32_t need, int32
             c += n;
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 // The next binary32 value above a finite x.
@@ -155,6 +175,24 @@ struct SlotBins {
     }
 };
 
+// The map v -> fma(v, scale, off) that spreads the values between the keys
+// kmn and kmax over kBins bins, linear in value (scale 0 when the range is
+// empty or not finite: every value in bin 0).
+__device__ __forceinline__ void linear_bins(uint32_t kmn, uint32_t kmx, float &scale, float &off) {
+    const float vmin = key_value(kmn), vmax = key_value(kmx);
+    scale = 0.f;
+    const float range = vmax - vmin;
+    if (range > 0.f && range < __builtin_inff()) scale = (float)kBins / range;
+    if (!(scale < __builtin_inff())) scale = 0.f;
+    off = -vmin * scale;
+    // off is -vmin*scale rounded, so fma(vmin, scale, off) is that rounding's
+    // error (exact, at most half an ulp of off); when it is negative, off
+    // moves up one ulp so that no item's bin is negative -- with values far
+    // from 0 in a narrow range the error exceeds 1, and a negative bin would
+    // wrap past the top bin below
+    if (fmaf(vmin, scale, off) < 0.f) off = next_up(off);
+}
+
 // Where the k-th largest selectable item lies after the value histogram:
 // bin cbin, with `above` selectable items in higher bins and n_in_bin in it;
 // total = the selectable count.  every: every selectable item wins (total
@@ -186,7 +224,7 @@ __device__ __forceinline__ CutBin hist_cut(const uint32_t (&key)[PER], uint32_t 
         sh.kmin[wave] = kmn;
         sh.kmax[wave] = kmx;
     }
-    __syncthreads();
+    lds_barrier();
     kmn = 0xFFFFFFFFu;
     kmx = 0u;
     for (int w = 0; w < kW; ++w) {
@@ -198,18 +236,8 @@ __device__ __forceinline__ CutBin hist_cut(const uint32_t (&key)[PER], uint32_t 
 
     // 2. value-linear bins (monotone in value); other items go to the extra
     // bins, 32 of them so that a wave's lanes hit distinct LDS banks
-    const float vmin = key_value(kmn), vmax = key_value(kmx);
-    float scale = 0.f;
-    const float range = vmax - vmin;
-    if (range > 0.f && range < __builtin_inff()) scale = (float)kBins / range;
-    if (!(scale < __builtin_inff())) scale = 0.f;
-    float off = -vmin * scale;
-    // off is -vmin*scale rounded, so fma(vmin, scale, off) is that rounding's
-    // error (exact, at most half an ulp of off); when it is negative, off
-    // moves up one ulp so that no item's bin is negative -- with values far
-    // from 0 in a narrow range the error exceeds 1, and a negative bin would
-    // wrap past the top bin below
-    if (fmaf(vmin, scale, off) < 0.f) off = next_up(off);
+    float scale, off;
+    linear_bins(kmn, kmx, scale, off);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const uint32_t kj = key[j];
@@ -222,7 +250,7 @@ __device__ __forceinline__ CutBin hist_cut(const uint32_t (&key)[PER], uint32_t 
         bins.set(j, bn);
         atomicAdd(&sh.hist[bn], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     // 3.
     find_from_top<NT>(sh.hist, kBins, k, sh.res, sh.scan_a);
     c.total = (uint32_t)sh.res[2];
@@ -251,7 +279,7 @@ __device__ __forceinline__ void resolve_cut(const uint32_t (&key)[PER], const Sl
 #pragma unroll
         for (int j = 0; j < PER; ++j)
             if (in_cut_bin(j)) sh.cand[atomicAdd(&sh.ncand, 1u)] = key[j];
-        __syncthreads();
+        lds_barrier();
         if (wave == 0) {
             const uint32_t my = lane < (int)n_in_bin ? sh.cand[lane] : 0u;
             uint32_t greater = 0, equal = 0;
@@ -265,7 +293,7 @@ __device__ __forceinline__ void resolve_cut(const uint32_t (&key)[PER], const Sl
                 sh.cut[1] = rem - greater;
             }
         }
-        __syncthreads();
+        lds_barrier();
         kstar = sh.cut[0];
         need_ties = sh.cut[1];
         return;
@@ -276,9 +304,9 @@ __device__ __forceinline__ void resolve_cut(const uint32_t (&key)[PER], const Sl
     for (int stage = 0; stage < 3; ++stage) {
         const int hi = stage == 0 ? 32 : (stage == 1 ? 21 : 10);
         const int lo = stage == 0 ? 21 : (stage == 1 ? 10 : 0);
-        __syncthreads();
+        lds_barrier();
         for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0u;
-        __syncthreads();
+        lds_barrier();
         const uint32_t mask = (1u << (hi - lo)) - 1u;
         // the cut bin as a value the compiler cannot carry across stages, so
         // the slots' membership is tested again in each stage rather than
@@ -290,7 +318,7 @@ __device__ __forceinline__ void resolve_cut(const uint32_t (&key)[PER], const Sl
             const uint32_t kk = key[j];
             if (bins.get(j) == cb && (hi == 32 || (kk >> hi) == prefix)) atomicAdd(&sh.hist[(kk >> lo) & mask], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         find_from_top<NT>(sh.hist, kBins, rem, sh.res, sh.scan_a);
         rem -= (uint32_t)sh.res[1];
         prefix = (hi == 32 ? 0u : (prefix << (hi - lo))) | (uint32_t)sh.res[0];
@@ -321,6 +349,62 @@ __device__ __forceinline__ void find_cut(const uint32_t (&key)[PER], uint32_t k,
     kstar = 0u;
     need_ties = 0u;
     if (!c.every) resolve_cut<NT, PER, CAND>(key, bins, c, k, sh, kstar, need_ties);
+}
+
+// Thresholds for the items of a long segment, from one sample per thread:
+// the samples' histogram linear in value between their min and max, and
+// for a rank r the lower edge of the bin holding the r-th largest
+// selectable sample.  The items at or above such a threshold number about
+// r times the items per sample; the caller counts them exactly and only
+// uses a threshold whose count lies between k and its capacity.
+struct SampleMap {
+    float scale, off;     // linear_bins of the samples (scale 0: no selectable sample, or one value)
+    float vmin;           // the smallest selectable sample
+    bool any;             // a selectable sample exists
+};
+
+// The samples' histogram (s: this thread's sample).  All threads call it,
+// with the histogram zeroed; they all get the same map, and the histogram
+// holds the samples' counts afterwards.
+template <int NT, int CAND>
+__device__ SampleMap sample_hist(float s, SelScratch<NT, CAND> &sh) {
+    constexpr int kW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t sk = order_key(s);
+    uint32_t kmn = wave_min(sk ? sk : 0xFFFFFFFFu), kmx = wave_max(sk);
+    if (lane == 63) {
+        sh.kmin[wave] = kmn;
+        sh.kmax[wave] = kmx;
+    }
+    lds_barrier();
+    kmn = 0xFFFFFFFFu;
+    kmx = 0u;
+    for (int w = 0; w < kW; ++w) {
+        kmn = min(kmn, sh.kmin[w]);
+        kmx = max(kmx, sh.kmax[w]);
+    }
+    SampleMap m{0.f, 0.f, 0.f, kmx != 0u};
+    if (!m.any) return m;                             // uniform: no selectable sample
+    linear_bins(kmn, kmx, m.scale, m.off);
+    m.vmin = key_value(kmn);
+    const int x = __float2int_rz(fmaf(s, m.scale, m.off));
+    const uint32_t bn = sk ? min((uint32_t)x, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (lane & 31));
+    atomicAdd(&sh.hist[bn], 1u);
+    lds_barrier();
+    return m;
+}
+
+// The threshold for rank r on the samples' histogram: -FLT_MAX (every
+// selectable item) when fewer than r samples are selectable.  All threads
+// call it and get the same value.
+template <int NT, int CAND>
+__device__ float sample_cut(uint32_t r, const SampleMap &m, SelScratch<NT, CAND> &sh) {
+    if (!m.any) return -__FLT_MAX__;
+    find_from_top<NT>(sh.hist, kBins, r, sh.res, sh.scan_a);
+    if (sh.res[0] < 0) return -__FLT_MAX__;           // uniform: fewer than r selectable samples
+    // fma(v, scale, off) >= cbin from about here on; any value serves, the
+    // caller's count is exact
+    return m.scale > 0.f ? ((float)sh.res[0] - m.off) / m.scale : m.vmin;
 }
 
 constexpr uint32_t kLoses = 0xFFFFFFFFu;              // position of a slot that does not win
@@ -473,26 +557,182 @@ __device__ __forceinline__ void load_items(const uint2 *src, int n, int i0, uint
 // launch.
 // 512-thread workgroups over long segments are held to 128 VGPRs (four waves
 // per SIMD) so that two share a CU: many rows then keep the CU busy while one
-// workgroup sits in its barrier-separated, latency-bound phases.
-template <int CAP, bool LIST, int NT, int MMUL>
-constexpr int seg_waves_per_eu() { return !LIST && MMUL == 0 && NT == 512 && CAP / NT >= 16 ? 4 : 1; }
+// workgroup sits in its barrier-separated, latency-bound phases.  The
+// sampled-threshold kernels need fewer: at most 85 (three workgroups of 512
+// threads per CU; 64, four per CU, spilled around the retried threshold and
+// ran 15 % slower); 1024 threads: 128.
+// Launch modes of the segment kernel (see topk_segment_kernel).
+constexpr int kSegPlain = 0, kSegSampled = 1, kSegRerun = 2;
 
+template <int CAP, bool LIST, int NT, int MMUL, int MODE>
+constexpr int seg_waves_per_eu() {
+    if (MODE == kSegSampled) return NT == 1024 ? 4 : 6;
+    return !LIST && MMUL == 0 && NT == 512 && CAP / NT >= 16 ? 4 : 1;
+}
+
+// Compacted items after a sampled threshold (PRE; see below).
+constexpr int kPreCap = kTopkPreCap;
+constexpr uint32_t kPreMaxK = (uint32_t)kTopkPreMaxK;
+
+// Logits of workgroup g's segment (row g / parts, part g % parts) as the
+// bits of the values: thread t's slot j is segment column t * CAP / NT + j,
+// -inf past the row's columns.
+template <int CAP, int NT>
+__device__ __forceinline__ void load_segment(const SegArgs &a, int g, uint32_t (&x)[CAP / NT]) {
+    constexpr int kPer = CAP / NT;
+    const int b = g / a.parts;
+    const int part = g - b * a.parts;
+    const int i0 = threadIdx.x * kPer;
+    const int64_t col0 = (int64_t)part * CAP;
+    const int ncols = a.row_cols ? min((int)a.row_cols[b], a.n_cols) : a.n_cols;
+    const int n = (int)max<int64_t>(0, min<int64_t>(CAP, ncols - col0));
+    const float *src = a.logits + (int64_t)b * a.ld + col0 + i0;
+    if ((a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && i0 + kPer <= n) {
+#pragma unroll
+        for (int j = 0; j < kPer; j += 4) {
+            const float4 f = *reinterpret_cast<const float4 *>(src + j);
+            x[j] = __float_as_uint(f.x);
+            x[j + 1] = __float_as_uint(f.y);
+            x[j + 2] = __float_as_uint(f.z);
+            x[j + 3] = __float_as_uint(f.w);
+        }
+    } else {
+        // ragged or unaligned: dword loads at offsets clamped into the
+        // segment, the slots past its end masked
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(src - i0, (uint32_t)n * 4u);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const uint32_t y = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)max(0, min(i0 + j, n - 1)) * 4u, 0, 0);
+            x[j] = i0 + j < n ? y : 0xFF800000u;
+        }
+    }
+}
+
+// Workgroup g's selection through a sampled threshold, over the values'
+// bits in key[] (load_segment): the items at or above a threshold T from
+// the samples (thread t's first slot) are counted exactly, and when there
+// are at least k and at most kPreCap of them, every winner is among them (at
+// least k items reach T, so the k-th largest does), so they are compacted
+// into LDS in column order -- a count pass, a block scan and a writing
+// pass, a few VALU operations per item -- and the exact selection runs on
+// those few items (kPreCap / NT per thread).  The threshold aims at about
+// 2 k items (at least 320, at most 60 % of the capacity): each sample
+// stands for CAP / NT items; a count outside the bounds takes another rank
+// on the same samples, up to three in all.  Other counts (values the samples misrepresent, many ties
+// at T) leave the workgroup's redo flag set, and the re-run launched next
+// over the same segments (kSegRerun) runs those parts alone.  Every barrier
+// is an LDS-only one, so loads issued before the call stay in flight.
+template <int CAP, int NT>
+__device__ __forceinline__ void select_sampled(const SegArgs &a, int g, const uint32_t (&key)[CAP / NT],
+                                               SelScratch<NT, 64> &sh, uint2 *sh_items) {
+    constexpr int kPer = CAP / NT;
+    constexpr int kPreCI = kPreCap / NT;
+    const int tid = threadIdx.x;
+    const int b = g / a.parts;
+    const int part = g - b * a.parts;
+    const uint32_t k = (uint32_t)a.k;
+    const uint32_t lcap = list_cap(k);
+    const int i0 = tid * kPer;
+    const int64_t col0 = (int64_t)part * CAP;
+    uint32_t kstar = 0u, need_ties = 0u, total;
+    WinCursor cur;
+    sel_reset(sh);
+    const uint32_t target = min(max(2u * k, 320u), (uint32_t)(kPreCap * 3 / 5));
+    const SampleMap smap = sample_hist<NT, 64>(__uint_as_float(key[0]), sh);
+    // up to three thresholds: a rank whose count is too small or too large
+    // bounds the next one (bisection once both bounds are known)
+    uint32_t r = max(1u, (target + kPer - 1) / kPer), r_lo = 0, r_hi = 0;
+    float T;
+    uint32_t tot, pos;
+    for (int attempt = 0;; ++attempt) {               // uniform
+        T = sample_cut<NT, 64>(r, smap, sh);
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) m += __uint_as_float(key[j]) >= T;
+        pos = block_scan_total<NT>(m, sh.scan_b, tot) - m;
+        if ((tot >= k && tot <= (uint32_t)kPreCap) || attempt == 2) break;
+        if (tot < k) r_lo = r; else r_hi = r;
+        uint32_t r2;
+        if (r_lo && r_hi)
+            r2 = (r_lo + r_hi) / 2u;
+        else if (tot > (uint32_t)kPreCap)
+            r2 = max(1u, (uint32_t)((uint64_t)r * target / tot));
+        else
+            r2 = min((uint32_t)NT, (uint32_t)((uint64_t)r * target / max(tot, 1u)) + 1u);
+        if (r2 == r) break;
+        r = r2;
+        lds_barrier();                                // the scan's words were read
+    }
+    if (tot >= k && tot <= (uint32_t)kPreCap) {     // uniform
+        // the selection below starts from a zeroed histogram; the
+        // samples' counts were last read before the scan's barrier
+        sel_reset(sh);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (__uint_as_float(key[j]) >= T) sh_items[pos++] = make_uint2(key[j], (uint32_t)(i0 + j));
+        lds_barrier();
+        // items tid * kPreCI ..: (value bits, segment column); none: key 0.
+        // Their bins come from the samples' map (monotone in value; values
+        // past the samples' range clamp to the end bins), so no second
+        // min / max pass: the value histogram, the cut bin, then its exact
+        // cut as in find_cut.
+        uint32_t key1[kPreCI], cl[kPreCI];
+        SlotBins<kPreCI> bin1;
+#pragma unroll
+        for (int i = 0; i < kPreCI; ++i) {
+            const int x = tid * kPreCI + i;
+            const uint2 it = x < (int)tot ? sh_items[x] : make_uint2(0xFF800000u, 0u);
+            const float val = __uint_as_float(it.x);
+            key1[i] = order_key(val);
+            cl[i] = it.y;
+            const int y = max(__float2int_rz(fmaf(val, smap.scale, smap.off)), 0);       // NaN (inf * 0) -> 0
+            const uint32_t bn = key1[i] ? min((uint32_t)y, (uint32_t)(kBins - 1)) : (uint32_t)(kBins + (tid & 31));
+            bin1.set(i, bn);
+            atomicAdd(&sh.hist[bn], 1u);
+        }
+        lds_barrier();
+        find_from_top<NT>(sh.hist, kBins, k, sh.res, sh.scan_a);
+        total = tot;                                  // every compacted item is selectable
+        if (tot > k) {                                // uniform
+            CutBin c;
+            c.cbin = (uint32_t)sh.res[0];
+            c.above = (uint32_t)sh.res[1];
+            c.n_in_bin = sh.hist[c.cbin];
+            c.total = tot;
+            c.every = false;
+            resolve_cut<NT, kPreCI, 64>(key1, bin1, c, k, sh, kstar, need_ties);
+        }
+        scan_winners<NT, kPreCI>(key1, kstar, need_ties, sh, cur);
+        const uint32_t count = min(total, k);
+        const auto col1 = [&](int i) { return (uint32_t)(col0 + cl[i]); };
+        if (a.out_list)
+            write_list<NT, kPreCI, false>(a.out_list + ((int64_t)b * a.parts + part) * lcap, lcap, cur, key1,
+                                          col1, count);
+        else
+            write_final<NT, kPreCI>(a, b, cur, key1, col1, count);
+    }
+    if (tid == 0) a.redo[g] = tot >= k && tot <= (uint32_t)kPreCap ? 0u : 1u;
+}
+
+// LDS items of seg_body's compaction.
+template <int CAP, bool LIST, int NT, bool PRE>
+constexpr int seg_items() { return PRE ? kPreCap : (!LIST && CAP / NT >= 16 ? 1024 : 1); }
+
+// Workgroup g (row g / parts, part g % parts) of a top-k launch.
 template <int CAP, bool LIST, int NT, int MMUL>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(seg_waves_per_eu<CAP, LIST, NT, MMUL>())))
-void topk_segment_kernel(SegArgs a) {
+__device__ __forceinline__ void seg_body(const SegArgs &a, int g, SelScratch<NT, 64> &sh, uint2 *sh_items) {
     constexpr bool kFused = MMUL > 0;
     constexpr int kPer = CAP / NT;                    // items per thread
     constexpr int kMPer = kFused ? MMUL * kPer : kPer;    // merge items per thread
-    // long segments of logits: the items that can still win after the
-    // histogram are compacted into LDS, one per thread (see below)
+    // long segments of logits: the items that can still win are compacted
+    // into LDS, a few per thread (see below)
     constexpr bool kCompact = !LIST && kPer >= 16;
-    constexpr int kCI = 1024 / NT;                    // compacted items per thread (up to 1024 in all)
-    __shared__ SelScratch<NT, 64> sh;
-    __shared__ uint2 sh_items[kCompact ? kCI * NT : 1];
+    constexpr int kCI = 1024 / NT;                    // after the histogram: up to 1024 items in all
+    static_assert(seg_items<CAP, LIST, NT, false>() >= (kCompact ? kCI * NT : 1), "LDS items");
 
     const int tid = threadIdx.x;
-    const int b = blockIdx.x / a.parts;
-    const int part = blockIdx.x - b * a.parts;
+    const int b = g / a.parts;
+    const int part = g - b * a.parts;
     const uint32_t k = (uint32_t)a.k;
     const uint32_t lcap = list_cap(k);
     const int i0 = tid * kPer;
@@ -504,28 +744,9 @@ void topk_segment_kernel(SegArgs a) {
     float v[LIST ? 1 : kPer];                         // logits input: the loaded values
     const int64_t col0 = (int64_t)part * CAP;
     if constexpr (!LIST) {
-        const int ncols = a.row_cols ? min((int)a.row_cols[b], a.n_cols) : a.n_cols;
-        const int n = (int)max<int64_t>(0, min<int64_t>(CAP, ncols - col0));
-        const float *src = a.logits + (int64_t)b * a.ld + col0 + i0;
-        if ((a.ld & 3) == 0 && (reinterpret_cast<uintptr_t>(a.logits) & 15) == 0 && i0 + kPer <= n) {
+        load_segment<CAP, NT>(a, g, key);
 #pragma unroll
-            for (int j = 0; j < kPer; j += 4) {
-                const float4 f = *reinterpret_cast<const float4 *>(src + j);
-                v[j] = f.x;
-                v[j + 1] = f.y;
-                v[j + 2] = f.z;
-                v[j + 3] = f.w;
-            }
-        } else {
-            // ragged or unaligned: dword loads at offsets clamped into the
-            // segment, the slots past its end masked
-            const __amdgpu_buffer_rsrc_t r = make_rsrc(src - i0, (uint32_t)n * 4u);
-#pragma unroll
-            for (int j = 0; j < kPer; ++j) {
-                const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)max(0, min(i0 + j, n - 1)) * 4u, 0, 0);
-                v[j] = i0 + j < n ? __uint_as_float(x) : -__builtin_inff();
-            }
-        }
+        for (int j = 0; j < kPer; ++j) v[j] = __uint_as_float(key[j]);
 #pragma unroll
         for (int j = 0; j < kPer; ++j) key[j] = order_key(v[j]);
     } else {
@@ -570,7 +791,7 @@ void topk_segment_kernel(SegArgs a) {
                     if (bn - lo < (uint32_t)kBins - lo) sh_items[pos++] = make_uint2(key[j], (uint32_t)(i0 + j) << 16 | bn);
                 }
             }
-            __syncthreads();
+            lds_barrier();
             // items tid * kCI ..: (key, segment column << 16 | bin); none:
             // key 0 and a bin that is no member
             uint32_t key1[kCI], cl[kCI];
@@ -628,11 +849,83 @@ void topk_segment_kernel(SegArgs a) {
     }
 }
 
+// kSegPlain and kSegSampled: one workgroup per (row, part).  kSegRerun
+// (after kSegSampled): each workgroup takes the parts blockIdx.x,
+// blockIdx.x + gridDim.x, ..., reads their flags NT at a time (ballots into
+// LDS) and runs only the flagged ones, so that a re-run with nothing to do
+// costs one short wave of workgroups.
+template <int CAP, bool LIST, int NT, int MMUL, int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(seg_waves_per_eu<CAP, LIST, NT, MMUL, MODE>())))
+void topk_segment_kernel(SegArgs a) {
+    constexpr bool PRE = MODE == kSegSampled;
+    constexpr int kPer = CAP / NT;
+    __shared__ SelScratch<NT, 64> sh;
+    __shared__ uint2 sh_items[seg_items<CAP, LIST, NT, PRE>()];
+    if constexpr (MODE == kSegPlain) {
+        seg_body<CAP, LIST, NT, MMUL>(a, (int)blockIdx.x, sh, sh_items);
+    } else if constexpr (MODE == kSegSampled) {
+        static_assert(!LIST && MMUL == 0 && kPer >= 16, "the sampled threshold serves long segments of logits");
+        uint32_t x[kPer];
+        load_segment<CAP, NT>(a, (int)blockIdx.x, x);
+        select_sampled<CAP, NT>(a, (int)blockIdx.x, x, sh, sh_items);
+    } else {
+        __shared__ uint64_t sh_redo[NT / 64];
+        const int tid = threadIdx.x;
+        const int ng = a.B * a.parts;
+        const int mine = ng > (int)blockIdx.x ? (ng - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+        int loaded = -1;                                  // chunk of flags in sh_redo
+        // the first flagged one of this workgroup's parts from index `from` on,
+        // or -1 (uniform: every thread reads the same masks)
+        const auto next_flagged = [&](int from) -> int {
+            for (int c = from - from % NT; c < mine; c += NT) {
+                if (c != loaded) {
+                    const int t = c + tid;
+                    const bool f = t < mine && a.redo[(int64_t)blockIdx.x + (int64_t)t * gridDim.x] != 0u;
+                    const uint64_t m = __ballot(f);
+                    lds_barrier();                      // the previous chunk's masks have been read
+                    if ((tid & 63) == 0) sh_redo[tid >> 6] = m;
+                    lds_barrier();
+                    loaded = c;
+                }
+                for (int w = 0; w < NT / 64; ++w) {
+                    const int lo = from - c - 64 * w;      // positions below `from` are done
+                    if (lo >= 64) continue;
+                    uint64_t mm = sh_redo[w];
+                    if (lo > 0) mm &= ~0ull << lo;
+                    if (mm) return c + 64 * w + __builtin_ctzll(mm);
+                }
+            }
+            return -1;
+        };
+        for (int t = next_flagged(0); t >= 0; t = next_flagged(t + 1)) {     // uniform
+            seg_body<CAP, LIST, NT, MMUL>(a, (int)blockIdx.x + t * (int)gridDim.x, sh, sh_items);
+            lds_barrier();                          // LDS is free for the next part
+        }
+    }
+}
+
 template <int CAP, bool LIST, int NT, int MMUL = 0>
 hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
     const int64_t grid = (int64_t)a.B * a.parts;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((topk_segment_kernel<CAP, LIST, NT, MMUL>), dim3((unsigned)grid), dim3(NT), 0, s, a);
+    SegArgs r = a;
+    if constexpr (!LIST && MMUL == 0 && CAP / NT >= 16) {
+        // the sampled threshold, then the workgroups it left unsettled
+        if (a.redo) {
+            hipLaunchKernelGGL((topk_segment_kernel<CAP, LIST, NT, MMUL, kSegSampled>), dim3((unsigned)grid), dim3(NT),
+                               0, s, a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            // the re-run: as many workgroups as are resident at once (two
+            // per CU of 512 threads, one of 1024), each over its share
+            const int64_t g2 = std::min<int64_t>(grid, NT == 512 ? 512 : 256);
+            hipLaunchKernelGGL((topk_segment_kernel<CAP, LIST, NT, MMUL, kSegRerun>), dim3((unsigned)g2), dim3(NT), 0,
+                               s, a);
+            return hipGetLastError();
+        }
+    }
+    r.redo = nullptr;
+    hipLaunchKernelGGL((topk_segment_kernel<CAP, LIST, NT, MMUL, kSegPlain>), dim3((unsigned)grid), dim3(NT), 0, s, r);
     return hipGetLastError();
 }
 

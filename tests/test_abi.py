@@ -57,6 +57,12 @@ def test_workspace_bytes(lib):
     # blocks rounded to MXFP4 ahead of the score launch, 4608 B per 64 columns
     assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 600, 1000, 512) == 600 * 1024 * 4 + 2 * 2560 + 16 * 4608
     assert L.workspace_bytes(L.IDX_OP_SCORE_TOPK, 512, 1000, 512) == 512 * 1024 * 4 + 2 * 2048
+    # one flag per workgroup when long segments (at least 8192 columns) select
+    # through a sampled threshold first (k up to 640)
+    assert L.workspace_bytes(L.IDX_OP_TOPK, 4096, 17408, 512) == 4096 * 4
+    assert L.workspace_bytes(L.IDX_OP_TOPK, 4096, 17408, 640) == 4096 * 4
+    assert L.workspace_bytes(L.IDX_OP_TOPK, 4096, 17408, 641) == 0
+    assert L.workspace_bytes(L.IDX_OP_TOPK, 4096, 4000, 512) == 0
     # long rows: per-part (key, column) lists of k items and their counts
     parts = -(-262144 // 32768)
     need = L.workspace_bytes(L.IDX_OP_TOPK, 8, 262144, 512)

@@ -494,6 +494,48 @@ def test_topk_one_segment_compaction_boundaries(k):
     assert (got[0] == -1).all() and (got[1] >= 0).sum() == 300
 
 
+@pytest.mark.parametrize("k", [1, 7, 300, 512, 640, 641])
+def test_topk_one_segment_sampled_threshold(k):
+    """Rows of one long segment each (256 rows of 20000 columns, 40 columns
+    per thread, the first of each thread's run sampled): for k up to 640 a
+    threshold from the samples picks the items to compact when at least k and
+    at most 2048 reach it, else the histogram path runs.  Rows whose samples
+    overstate the row (the sampled columns far above the rest: too few items
+    reach the threshold), understate it (far below: too many), one value
+    almost everywhere (too many ties at the threshold), fewer selectable
+    samples than the threshold's rank, NaN and +-inf with signed zeros, and
+    the sampled columns alone being the row's largest."""
+    rng = np.random.default_rng(100 + k)
+    B, n = 256, 20000
+    vals = rng.standard_normal((B, n)).astype(np.float32)
+    sampled = np.arange(0, n, 40)
+    vals[0, sampled] += 1000.0                                # samples overstate the row
+    vals[1, sampled] -= 1000.0                                # samples understate it
+    vals[2] = 1.0
+    vals[2, rng.choice(n, 100, replace=False)] = rng.random(100).astype(np.float32) + 2.0    # ties at T
+    vals[3] = -np.inf
+    keep = rng.choice(n, 300, replace=False)
+    vals[3, keep] = rng.standard_normal(300)                  # few selectable samples
+    vals[4, rng.random(n) < 0.05] = np.nan
+    vals[4, rng.random(n) < 0.05] = np.inf
+    vals[4, rng.random(n) < 0.3] = -np.inf
+    vals[4, :40] = -0.0
+    vals[4, 40:80] = 0.0
+    vals[5] = -np.inf
+    vals[5, sampled] = rng.standard_normal(len(sampled))     # only the sampled columns selectable
+    vals[6, sampled[: k]] = 50.0                              # k tied winners, all sampled
+    vals[7] = np.round(vals[7] * 4) / 4                       # many ties everywhere
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    got = cols.cpu().numpy()
+    for r in range(8):
+        assert np.array_equal(got[r], ref_cols[r]), f"row {r}"
+    assert np.array_equal(got, ref_cols)
+    ok = ref_cols >= 0
+    assert np.array_equal(v.cpu().numpy()[ok], ref_v[ok].astype(np.float32))
+
+
 @pytest.mark.parametrize("n,k", [(100, 4), (4096, 384), (70000, 512)])
 def test_topk_standalone_values_far_from_zero_in_a_narrow_range(n, k):
     """Values whose magnitude is large against their spread (|min| / range
