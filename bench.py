@@ -297,28 +297,30 @@ def summarize_mfma(pmc_dir, workload, command, out):
 
 def summarize_counters(pmc_dir, kname, workload, command, out, items=None):
     """Medians per dispatch of every counter in one `rocprofv3 --pmc` run for
-    the kernels whose name contains `kname` and, given `items` (work items per
-    dispatch), the VALU instructions per item (SQ_INSTS_VALU counts wave64
-    instructions)."""
+    the kernels whose name contains `kname`, one section per kernel (template
+    instantiation) and, given `items` (work items per dispatch), the VALU
+    instructions per item (SQ_INSTS_VALU counts wave64 instructions)."""
     import statistics
     per = {}
     for r in _csv_rows(_find(pmc_dir, "counter_collection.csv")):
         if kname not in r["Kernel_Name"]:
             continue
-        d = per.setdefault(r["Dispatch_Id"], {})
+        d = per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
         d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
-    names = sorted({c for d in per.values() for c in d if c != "ns"})
-    med = {c: statistics.median(d[c] for d in per.values() if c in d) for c in names + ["ns"]}
     lines = [f"# rocprofv3 counters for {kname}, workload {workload}",
              f"# command: {command}",
-             f"# medians over dispatches",
-             f"dispatches = {len(per)}"]
-    lines += [f"{c.lower()} = {med[c]:.0f}" for c in names]
-    lines.append(f"dispatch_ns = {med['ns']:.0f}")
-    if items and "SQ_INSTS_VALU" in med:
-        lines.append(f"items_per_dispatch = {items}")
-        lines.append(f"valu_insts_per_item = {med['SQ_INSTS_VALU'] * 64 / items:.2f}")
+             f"# medians over dispatches, per kernel"]
+    for name in sorted({n for n, _ in per}):
+        ds = [d for (n, _), d in per.items() if n == name]
+        names = sorted({c for d in ds for c in d if c != "ns"})
+        med = {c: statistics.median(d[c] for d in ds if c in d) for c in names + ["ns"]}
+        lines += ["", f"[{name}]", f"dispatches = {len(ds)}"]
+        lines += [f"{c.lower()} = {med[c]:.0f}" for c in names]
+        lines.append(f"dispatch_ns = {med['ns']:.0f}")
+        if items and "SQ_INSTS_VALU" in med:
+            lines.append(f"items_per_dispatch = {items}")
+            lines.append(f"valu_insts_per_item = {med['SQ_INSTS_VALU'] * 64 / items:.2f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
