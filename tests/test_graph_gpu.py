@@ -13,8 +13,10 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import oracle
 from sparse_attention_kv_paged_amd import lib as L
 from sparse_attention_kv_paged_amd import workloads as W
+from tests.parity import column_order
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +122,33 @@ def test_topk_replays(B, n, k):
         L.idx_topk(lg, k, out_col=oc, out_val=ov, workspace=ws)
 
     _replay_check(f"topk {n} {k}", call, [oc, ov], lambda: L.idx_topk(lg2, k, workspace=ws))
+
+
+def test_topk_sampled_threshold_rerun_replays():
+    """Many rows of one long segment each with k <= 640 select through a
+    threshold sampled from the first value of every thread's 40 columns; the
+    rows whose samples misrepresent them (every 7th row: the sampled columns
+    far above the rest) are re-run by a second launch that reads the first
+    launch's flags.  The calls between the replays negate the logits, so other
+    rows (the sampled columns now far below) are flagged: each launch must
+    rewrite every flag."""
+    rng = np.random.default_rng(73)
+    B, n, k = 256, 20000, 512
+    vals = rng.standard_normal((B, n), dtype=np.float32)
+    vals[::7, ::40] += 1000.0
+    lg = torch.from_numpy(vals).cuda()
+    oc = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    ov = torch.empty((B, k), dtype=torch.float32, device="cuda")
+    ws = L.new_workspace(max(L.workspace_bytes(L.IDX_OP_TOPK, B, n, k), 1), "cuda")
+    lg2 = -lg
+
+    def call():
+        L.idx_topk(lg, k, out_col=oc, out_val=ov, workspace=ws)
+
+    _replay_check("topk sampled threshold", call, [oc, ov], lambda: L.idx_topk(lg2, k, workspace=ws))
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    assert np.array_equal(oc.cpu().numpy(), ref_cols)
+    assert np.array_equal(ov.cpu().numpy(), ref_v.astype(np.float32))
 
 
 def test_quantised_query_replays():
