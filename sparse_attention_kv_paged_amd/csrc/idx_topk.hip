@@ -578,11 +578,12 @@ constexpr uint32_t kPreMaxK = (uint32_t)kTopkPreMaxK;
 // bits of the values: thread t's slot j is segment column t * CAP / NT + j,
 // -inf past the row's columns.
 template <int CAP, int NT>
-__device__ __forceinline__ void load_segment(const SegArgs &a, int g, uint32_t (&x)[CAP / NT]) {
+__device__ __forceinline__ void load_segment(const SegArgs &a, int g, uint32_t (&x)[CAP / NT],
+                                             int tid = threadIdx.x) {
     constexpr int kPer = CAP / NT;
     const int b = g / a.parts;
     const int part = g - b * a.parts;
-    const int i0 = threadIdx.x * kPer;
+    const int i0 = tid * kPer;
     const int64_t col0 = (int64_t)part * CAP;
     const int ncols = a.row_cols ? min((int)a.row_cols[b], a.n_cols) : a.n_cols;
     const int n = (int)max<int64_t>(0, min<int64_t>(CAP, ncols - col0));
@@ -612,7 +613,8 @@ __device__ __forceinline__ void load_segment(const SegArgs &a, int g, uint32_t (
 // bits in key[] (load_segment): the items at or above a threshold T from
 // the samples (thread t's first slot) are counted exactly, and when there
 // are at least k and at most kPreCap of them, every winner is among them (at
-// least k items reach T, so the k-th largest does), so they are compacted
+// least k items reach T, so the k-th largest does) -- as when T admits every
+// selectable item and there are fewer than k (all of them win) -- so they are compacted
 // into LDS in column order -- a count pass, a block scan and a writing
 // pass, a few VALU operations per item -- and the exact selection runs on
 // those few items (kPreCap / NT per thread).  The threshold aims at about
@@ -644,13 +646,17 @@ __device__ __forceinline__ void select_sampled(const SegArgs &a, int g, const ui
     uint32_t r = max(1u, (target + kPer - 1) / kPer), r_lo = 0, r_hi = 0;
     float T;
     uint32_t tot, pos;
+    bool settled;
     for (int attempt = 0;; ++attempt) {               // uniform
         T = sample_cut<NT, 64>(r, smap, sh);
         uint32_t m = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) m += __uint_as_float(key[j]) >= T;
         pos = block_scan_total<NT>(m, sh.scan_b, tot) - m;
-        if ((tot >= k && tot <= (uint32_t)kPreCap) || attempt == 2) break;
+        // settled: k to kPreCap items, or every selectable item when there
+        // are fewer than k (they all win)
+        settled = tot <= (uint32_t)kPreCap && (tot >= k || T == -__FLT_MAX__);
+        if (settled || attempt == 2) break;
         if (tot < k) r_lo = r; else r_hi = r;
         uint32_t r2;
         if (r_lo && r_hi)
@@ -663,7 +669,7 @@ __device__ __forceinline__ void select_sampled(const SegArgs &a, int g, const ui
         r = r2;
         lds_barrier();                                // the scan's words were read
     }
-    if (tot >= k && tot <= (uint32_t)kPreCap) {     // uniform
+    if (settled) {                                    // uniform
         // the selection below starts from a zeroed histogram; the
         // samples' counts were last read before the scan's barrier
         sel_reset(sh);
@@ -711,15 +717,17 @@ __device__ __forceinline__ void select_sampled(const SegArgs &a, int g, const ui
         else
             write_final<NT, kPreCI>(a, b, cur, key1, col1, count);
     }
-    if (tid == 0) a.redo[g] = tot >= k && tot <= (uint32_t)kPreCap ? 0u : 1u;
+    if (tid == 0) a.redo[g] = settled ? 0u : 1u;
 }
 
 // LDS items of seg_body's compaction.
 template <int CAP, bool LIST, int NT, bool PRE>
 constexpr int seg_items() { return PRE ? kPreCap : (!LIST && CAP / NT >= 16 ? 1024 : 1); }
 
-// Workgroup g (row g / parts, part g % parts) of a top-k launch.
-template <int CAP, bool LIST, int NT, int MMUL>
+// Workgroup g (row g / parts, part g % parts) of a top-k launch.  OPAQUE
+// (a loop over parts): the thread index is hidden from the optimiser, which
+// would otherwise hoist every slot's column out of the loop (registers).
+template <int CAP, bool LIST, int NT, int MMUL, bool OPAQUE = false>
 __device__ __forceinline__ void seg_body(const SegArgs &a, int g, SelScratch<NT, 64> &sh, uint2 *sh_items) {
     constexpr bool kFused = MMUL > 0;
     constexpr int kPer = CAP / NT;                    // items per thread
@@ -730,7 +738,8 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, int g, SelScratch<NT,
     constexpr int kCI = 1024 / NT;                    // after the histogram: up to 1024 items in all
     static_assert(seg_items<CAP, LIST, NT, false>() >= (kCompact ? kCI * NT : 1), "LDS items");
 
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
+    if constexpr (OPAQUE) asm volatile("" : "+v"(tid));
     const int b = g / a.parts;
     const int part = g - b * a.parts;
     const uint32_t k = (uint32_t)a.k;
@@ -744,7 +753,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, int g, SelScratch<NT,
     float v[LIST ? 1 : kPer];                         // logits input: the loaded values
     const int64_t col0 = (int64_t)part * CAP;
     if constexpr (!LIST) {
-        load_segment<CAP, NT>(a, g, key);
+        load_segment<CAP, NT>(a, g, key, tid);
 #pragma unroll
         for (int j = 0; j < kPer; ++j) v[j] = __uint_as_float(key[j]);
 #pragma unroll
@@ -873,22 +882,22 @@ void topk_segment_kernel(SegArgs a) {
         const int tid = threadIdx.x;
         const int ng = a.B * a.parts;
         const int mine = ng > (int)blockIdx.x ? (ng - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-        int loaded = -1;                                  // chunk of flags in sh_redo
-        // the first flagged one of this workgroup's parts from index `from` on,
-        // or -1 (uniform: every thread reads the same masks)
+        int loaded = -1;                              // chunk of flags in sh_redo
+        // the first flagged one of this workgroup's parts from index `from`
+        // on, or -1 (uniform: every thread reads the same masks)
         const auto next_flagged = [&](int from) -> int {
             for (int c = from - from % NT; c < mine; c += NT) {
                 if (c != loaded) {
                     const int t = c + tid;
                     const bool f = t < mine && a.redo[(int64_t)blockIdx.x + (int64_t)t * gridDim.x] != 0u;
                     const uint64_t m = __ballot(f);
-                    lds_barrier();                      // the previous chunk's masks have been read
+                    lds_barrier();                    // the previous chunk's masks have been read
                     if ((tid & 63) == 0) sh_redo[tid >> 6] = m;
                     lds_barrier();
                     loaded = c;
                 }
                 for (int w = 0; w < NT / 64; ++w) {
-                    const int lo = from - c - 64 * w;      // positions below `from` are done
+                    const int lo = from - c - 64 * w;  // positions below `from` are done
                     if (lo >= 64) continue;
                     uint64_t mm = sh_redo[w];
                     if (lo > 0) mm &= ~0ull << lo;
@@ -898,8 +907,8 @@ void topk_segment_kernel(SegArgs a) {
             return -1;
         };
         for (int t = next_flagged(0); t >= 0; t = next_flagged(t + 1)) {     // uniform
-            seg_body<CAP, LIST, NT, MMUL>(a, (int)blockIdx.x + t * (int)gridDim.x, sh, sh_items);
-            lds_barrier();                          // LDS is free for the next part
+            seg_body<CAP, LIST, NT, MMUL, true>(a, (int)blockIdx.x + t * (int)gridDim.x, sh, sh_items);
+            lds_barrier();                            // LDS is free for the next part
         }
     }
 }
@@ -916,9 +925,11 @@ hipError_t launch_seg(const SegArgs &a, hipStream_t s) {
                                0, s, a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            // the re-run: as many workgroups as are resident at once (two
-            // per CU of 512 threads, one of 1024), each over its share
-            const int64_t g2 = std::min<int64_t>(grid, NT == 512 ? 512 : 256);
+            // the re-run: about as many workgroups as are resident at once
+            // (two per CU of 512 threads, one of 1024), each over its share;
+            // a prime count, so that flagged parts recurring with a period
+            // (every 4th row, say) still spread over all of them
+            const int64_t g2 = std::min<int64_t>(grid, NT == 512 ? 509 : 251);
             hipLaunchKernelGGL((topk_segment_kernel<CAP, LIST, NT, MMUL, kSegRerun>), dim3((unsigned)g2), dim3(NT), 0,
                                s, a);
             return hipGetLastError();
