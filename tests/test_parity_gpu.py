@@ -416,10 +416,12 @@ def test_topk_standalone_multilevel(n, k):
     assert np.array_equal(v.cpu().numpy(), ref_v.astype(np.float32))
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("n,k", [(6000, 512), (8192, 1000), (17408, 512), (20000, 512), (24000, 2048), (24576, 7)])
+@pytest.mark.parametrize("n,k", [(6000, 512), (8192, 1000), (12000, 300), (17408, 512), (20000, 512), (24000, 2048),
+                                 (24576, 7), (30000, 640)])
 def test_topk_standalone_one_segment_per_row(n, k):
     """Many rows (one top-k workgroup per row) whose segment sizes are not a
-    multiple of the write-out's 8-slot groups (20 and 24 slots per thread)."""
+    multiple of the write-out's 8-slot groups (20 and 24 slots per thread);
+    every segment size, through the sampled threshold (k <= 640) or not."""
     rng = np.random.default_rng(n + 7 * k)
     B = 256
     vals = rng.standard_normal((B, n)).astype(np.float32)
