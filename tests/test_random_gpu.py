@@ -154,3 +154,55 @@ def test_random_shared_request_rows(seed):
     ref_ids = oracle.cols_to_entries(wl, oracle.topk(ref, wl.k)[0])
     assert_topk_near_tie(idx, ref_ids, lambda b, ids: ref[b, np.asarray(ids, dtype=np.int64)], wl.k,
                          f"shared {seed} {path}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_long_segment_topk(seed):
+    """Standalone top-k over many rows of one long segment each -- the
+    sampled-threshold path and its re-run -- with a random row length
+    (every segment size), k up to 640 and a random value distribution per
+    row: normal, exponential, uniform, heavy ties, a shift on the sampled
+    columns (thread t's first column) up or down, rows shorter than k, and
+    NaN / +-inf sprinkled in.  The result must equal the oracle's top-k
+    exactly (columns and values)."""
+    rng = np.random.default_rng(11000 + seed)
+    n = int(rng.choice([6000, 8192, 12000, 16384, 17408, 20480, 24000, 30000]))
+    k = int(rng.choice([1, 7, 64, 300, 512, 640]))
+    B = 256
+    per = {8192: 16, 16384: 32, 20480: 40, 24576: 48}.get(next(c for c in (8192, 16384, 20480, 24576, 32768) if n <= c), 32)
+    vals = np.empty((B, n), np.float32)
+    kinds = rng.integers(0, 8, size=B)
+    for r in range(B):
+        kind = int(kinds[r])
+        if kind == 0:
+            v = rng.standard_normal(n) * rng.uniform(0.1, 10)
+        elif kind == 1:
+            v = rng.exponential(size=n)
+        elif kind == 2:
+            v = rng.random(n)
+        elif kind == 3:
+            v = np.round(rng.standard_normal(n) * 2) / 2            # heavy ties
+        elif kind == 4:
+            v = rng.standard_normal(n)
+            v[::per] += rng.choice([-1000.0, 1000.0])                 # the samples mislead
+        elif kind == 5:
+            v = np.full(n, -np.inf)
+            m = int(rng.integers(0, 2 * k + 2))
+            v[rng.choice(n, min(m, n), replace=False)] = rng.standard_normal(min(m, n))   # short rows
+        elif kind == 6:
+            v = rng.standard_normal(n)
+            v[rng.random(n) < 0.02] = np.nan
+            v[rng.random(n) < 0.01] = np.inf
+            v[rng.random(n) < 0.2] = -np.inf
+        else:
+            v = np.full(n, float(rng.standard_normal()))              # one value
+        vals[r] = v.astype(np.float32)
+    print(f"[random] long segments {seed}: n={n} k={k} kinds={np.bincount(kinds, minlength=8).tolist()}", flush=True)
+    cols, v = L.idx_topk(torch.from_numpy(vals).cuda(), k)
+    torch.cuda.synchronize()
+    ref_cols, ref_v = column_order(*oracle.topk(vals.astype(np.float64), k))
+    got = cols.cpu().numpy()
+    bad = np.nonzero((got != ref_cols).any(axis=1))[0]
+    assert bad.size == 0, f"seed {seed}: rows {bad[:8].tolist()} (kinds {kinds[bad[:8]].tolist()}) differ"
+    ok = ref_cols >= 0
+    assert np.array_equal(v.cpu().numpy()[ok], ref_v[ok].astype(np.float32))
