@@ -23,6 +23,11 @@
 // top-k (key, column) list and the lists of a row are merged the same way
 // (concatenated in part order, so column order holds): by the row's last part
 // in the same launch when the lists fit, else by further launches.
+// Long segments (at least 16 items per thread) with k <= 640 first try a
+// threshold sampled from one value per thread: the items at or above it are
+// counted, and when they number between k and 2048 they are compacted into
+// LDS and steps 2-4 run on them alone (select_sampled); the parts it leaves
+// unsettled are re-run by a second launch of the path above.
 // The result is deterministic and ordered by column.
 #include <algorithm>
 
@@ -570,9 +575,8 @@ constexpr int seg_waves_per_eu() {
     return !LIST && MMUL == 0 && NT == 512 && CAP / NT >= 16 ? 4 : 1;
 }
 
-// Compacted items after a sampled threshold (PRE; see below).
+// Compacted items after a sampled threshold (see select_sampled).
 constexpr int kPreCap = kTopkPreCap;
-constexpr uint32_t kPreMaxK = (uint32_t)kTopkPreMaxK;
 
 // Logits of workgroup g's segment (row g / parts, part g % parts) as the
 // bits of the values: thread t's slot j is segment column t * CAP / NT + j,
